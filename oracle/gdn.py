@@ -1,0 +1,136 @@
+"""Gated delta rule state update (fp64 definition) and its chunkwise form.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+Source passages
+---------------
+* 24-ai.news TokenSpeed article, paragraph on the model: the linear-attention
+  layers of the hybrid model are Gated DeltaNet (GDN) layers.
+* zubnet.ai TokenSpeed article, second paragraph: those layers keep a
+  recurrent state that is checkpointed next to the KV in state slots and
+  reached through an index array (``current_input_indices``) instead of
+  tensor copies.
+* 24-ai.news, optimisation list, "Mamba State Update": the intermediate state
+  copy is removed by index indirection, an O(1) pointer update.
+
+The recurrence is the published gated delta rule (Yang, Kautz & Hatamizadeh,
+"Gated Delta Networks: Improving Mamba2 with Delta Rule", ICLR 2025):
+
+    S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+    o_t = S_t q_t,
+
+with S in R^{d_v x d_k}.  ``step`` evaluates exactly that formula with the
+dense (I - beta k k^T) matrix.
+
+Readings (pages silent): the output is o = q_scale * S q with S in
+d_v x d_k (the retrieval property S_t k_t = v_t for beta = 1, |k| = 1 fixes
+the orientation); q_scale = 1 by default; alpha and beta arrive as per
+(token, head) values; q and k arrive L2-normalised; heads are independent;
+slot index -1 means a zero initial state.  State pools are float32
+[n_slots, H, d_v, d_k]; a checkpoint is the float32 rounding (nearest even)
+of the float64 state.
+"""
+
+import numpy as np
+
+
+def step(S, q, k, v, alpha, beta):
+    """One token of the recurrence, dense form.  Returns (S_t, S_t q)."""
+    d_k = k.shape[0]
+    A = np.eye(d_k) - beta * np.outer(k, k)
+    S_new = alpha * (S @ A) + beta * np.outer(v, k)
+    return S_new, S_new @ q
+
+
+def sequential(S0, q, k, v, alpha, beta, q_scale=1.0):
+    """Run T tokens from S0.  q, k [T, d_k]; v [T, d_v]; alpha, beta [T].
+
+    Returns (states [T, d_v, d_k], outputs [T, d_v]).
+    """
+    S = np.asarray(S0, np.float64)
+    T = q.shape[0]
+    states = np.empty((T,) + S.shape)
+    outs = np.empty((T, S.shape[0]))
+    for t in range(T):
+        S, o = step(S, np.asarray(q[t], np.float64), np.asarray(k[t], np.float64),
+                    np.asarray(v[t], np.float64), float(alpha[t]), float(beta[t]))
+        states[t] = S
+        outs[t] = q_scale * o
+    return states, outs
+
+
+def chunked(S0, q, k, v, alpha, beta, chunk, q_scale=1.0):
+    """The same recurrence evaluated chunk by chunk (WY / UT form).
+
+    Within a chunk of C tokens starting from S0, with gamma_t = prod_{i<=t}
+    alpha_i, the delta-rule inputs u_t (S_t = alpha_t S_{t-1} + u_t k_t^T)
+    solve the unit lower-triangular system
+        u_t + beta_t sum_{i<t} (gamma_t/gamma_i)(k_t . k_i) u_i
+            = beta_t (v_t - gamma_t S0 k_t),
+    and then  S_C = gamma_C S0 + sum_i (gamma_C/gamma_i) u_i k_i^T,
+              o_t = gamma_t S0 q_t + sum_{i<=t} (gamma_t/gamma_i)(k_i . q_t) u_i.
+    (Yang et al., "Parallelizing Linear Transformers with the Delta Rule
+    over Sequence Length", NeurIPS 2024, and the Gated DeltaNet paper above;
+    derived here from the recurrence.)  Ratios use log-space cumulative sums.
+    Returns (final state, outputs [T, d_v]).
+    """
+    S = np.asarray(S0, np.float64)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    beta = np.asarray(beta, np.float64)
+    T = q.shape[0]
+    outs = np.empty((T, S.shape[0]))
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        K, Q, Vv = k[c0:c1], q[c0:c1], v[c0:c1]
+        b = beta[c0:c1]
+        lg = np.cumsum(np.log(alpha[c0:c1]))                  # log gamma_t
+        C = c1 - c0
+        ratio = np.exp(lg[:, None] - lg[None, :])             # gamma_t / gamma_i
+        KK = K @ K.T
+        rhs = b[:, None] * (Vv - np.exp(lg)[:, None] * (K @ S.T))
+        U = np.zeros_like(rhs)
+        for t in range(C):                                     # forward substitution
+            acc = rhs[t].copy()
+            for i in range(t):
+                acc -= b[t] * ratio[t, i] * KK[t, i] * U[i]
+            U[t] = acc
+        KQ = K @ Q.T                                           # [i, t] = k_i . q_t
+        for t in range(C):
+            o = np.exp(lg[t]) * (S @ Q[t])
+            for i in range(t + 1):
+                o = o + ratio[t, i] * KQ[i, t] * U[i]
+            outs[c0 + t] = q_scale * o
+        gC = np.exp(lg[-1])
+        S = gC * S + (U * np.exp(lg[-1] - lg)[:, None]).T @ K
+    return S, outs
+
+
+def state_update(pool, in_idx, out_idx, q, k, v, alpha, beta, q_scale=1.0):
+    """Slot-addressed batched update, the operation of one GDN layer.
+
+    pool float32 [n_slots, H, d_v, d_k]; in_idx [S]; out_idx [S, T];
+    q, k [S, T, H, d_k] and v [S, T, H, d_v] float64; alpha, beta [S, T, H].
+    Every input slot is read from ``pool`` as it was before the call; after
+    token t the float32 state is written to slot out_idx[s, t].  Returns
+    (new pool, o float64 [S, T, H, d_v]).
+    """
+    pool = np.asarray(pool, np.float32)
+    new_pool = pool.copy()
+    S_n, T = out_idx.shape
+    H, d_v, d_k = pool.shape[1:]
+    o = np.empty((S_n, T, H, d_v))
+    for s in range(S_n):
+        for h in range(H):
+            if in_idx[s] < 0:
+                S0 = np.zeros((d_v, d_k))
+            else:
+                S0 = pool[in_idx[s], h].astype(np.float64)
+            states, outs = sequential(S0, q[s, :, h], k[s, :, h], v[s, :, h],
+                                      alpha[s, :, h], beta[s, :, h], q_scale)
+            o[s, :, h] = outs
+            for t in range(T):
+                new_pool[out_idx[s, t], h] = states[t].astype(np.float32)
+    return new_pool, o

@@ -1,0 +1,140 @@
+"""Pins for the oracle's gated delta rule (CPU)."""
+
+import os
+
+import numpy as np
+import pytest
+
+from oracle import gdn
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _unit(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _golden():
+    vals = {}
+    with open(os.path.join(GOLDEN, "gdn_step_2x2.txt")) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if line:
+                vals.setdefault(line.split()[0], []).append(line.split()[1:])
+    return vals
+
+
+def test_hand_worked_2x2():
+    g = _golden()
+    f = lambda xs: np.array([float(x) for x in xs])
+    S0 = f(g["S0"][0]).reshape(2, 2)
+    t1 = g["token1"][0]
+    k, v, a, b = f(t1[1:3]), f(t1[4:6]), float(t1[7]), float(t1[9])
+    for row in g["o1"]:
+        q = f(row[1:3])
+        S1, o = gdn.step(S0, q, k, v, a, b)
+        np.testing.assert_allclose(S1, f(g["S1"][0]).reshape(2, 2), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(o, f(row[4:6]), atol=1e-15)
+    t2 = g["token2"][0]
+    S2, _ = gdn.step(S1, np.zeros(2), f(t2[1:3]), f(t2[4:6]), float(t2[7]), float(t2[9]))
+    np.testing.assert_allclose(S2, f(g["S2"][0]).reshape(2, 2), atol=1e-14)
+
+
+def test_scalar_loop_definition():
+    # entrywise: S'[i,j] = a * sum_m S[i,m] (delta_mj - b k_m k_j) + b v_i k_j
+    rng = np.random.default_rng(0)
+    dv, dk = 3, 4
+    S = rng.standard_normal((dv, dk))
+    q, k, v = rng.standard_normal(dk), rng.standard_normal(dk), rng.standard_normal(dv)
+    a, b = 0.93, 0.41
+    ref = np.zeros((dv, dk))
+    for i in range(dv):
+        for j in range(dk):
+            acc = 0.0
+            for m in range(dk):
+                acc += S[i, m] * ((1.0 if m == j else 0.0) - b * k[m] * k[j])
+            ref[i, j] = a * acc + b * v[i] * k[j]
+    S1, o = gdn.step(S, q, k, v, a, b)
+    np.testing.assert_allclose(S1, ref, atol=1e-14)
+    np.testing.assert_allclose(o, [sum(ref[i, j] * q[j] for j in range(dk)) for i in range(dv)], atol=1e-14)
+
+
+def test_beta_zero_alpha_one_leaves_state_unchanged():
+    rng = np.random.default_rng(1)
+    S = rng.standard_normal((8, 8))
+    T = 5
+    states, _ = gdn.sequential(S, rng.standard_normal((T, 8)), _unit(rng, T, 8), rng.standard_normal((T, 8)),
+                               np.ones(T), np.zeros(T))
+    assert np.array_equal(states[-1], S)
+
+
+def test_beta_zero_decays_by_product_of_alphas():
+    rng = np.random.default_rng(2)
+    S = rng.standard_normal((6, 6))
+    al = rng.uniform(0.9, 1.0, 7)
+    states, _ = gdn.sequential(S, rng.standard_normal((7, 6)), _unit(rng, 7, 6), rng.standard_normal((7, 6)),
+                               al, np.zeros(7))
+    np.testing.assert_allclose(states[-1], np.prod(al) * S, rtol=1e-13)
+
+
+def test_retrieval_identity():
+    rng = np.random.default_rng(3)
+    d = 16
+    S = rng.standard_normal((d, d))
+    for _ in range(5):
+        k = rng.standard_normal(d)
+        v = rng.standard_normal(d)
+        a, b = rng.uniform(0.9, 1), rng.uniform(0, 1)
+        S1, _ = gdn.step(S, k, k, v, a, b)
+        kk = k @ k
+        np.testing.assert_allclose(S1 @ k, a * (1 - b * kk) * (S @ k) + b * kk * v, atol=1e-10)
+        # unit key and beta = 1: writing (k, v) then querying with k returns v
+        ku = k / np.linalg.norm(k)
+        S2, o = gdn.step(S, ku, ku, v, a, 1.0)
+        np.testing.assert_allclose(o, v, atol=1e-12)
+        # the transposed orientation does not have this property
+        assert np.max(np.abs(S2.T @ ku - v)) > 1e-3
+        S = S1
+
+
+def test_chunked_equals_sequential():
+    rng = np.random.default_rng(4)
+    T, dk, dv = 37, 8, 6
+    S0 = rng.standard_normal((dv, dk))
+    q, k = _unit(rng, T, dk), _unit(rng, T, dk)
+    v = rng.standard_normal((T, dv))
+    al, be = rng.uniform(0.9, 1.0, T), rng.uniform(0, 1, T)
+    states, outs = gdn.sequential(S0, q, k, v, al, be, 0.5)
+    for C in (1, 4, 16, 64):
+        Sf, oc = gdn.chunked(S0, q, k, v, al, be, C, 0.5)
+        np.testing.assert_allclose(Sf, states[-1], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(oc, outs, rtol=1e-12, atol=1e-12)
+
+
+def test_state_update_slots_and_checkpoints():
+    rng = np.random.default_rng(5)
+    n_slots, H, dv, dk, S_n, T = 8, 2, 4, 4, 2, 3
+    pool = rng.standard_normal((n_slots, H, dv, dk)).astype(np.float32)
+    in_idx = np.array([5, -1])
+    out_idx = np.array([[1, 2, 3], [4, 6, 7]])
+    q = rng.standard_normal((S_n, T, H, dk))
+    k = rng.standard_normal((S_n, T, H, dk))
+    v = rng.standard_normal((S_n, T, H, dv))
+    al = rng.uniform(0.9, 1, (S_n, T, H))
+    be = rng.uniform(0, 1, (S_n, T, H))
+    new, o = gdn.state_update(pool, in_idx, out_idx, q, k, v, al, be)
+    # untouched slots keep their bytes, including the shared input slot
+    for sl in (0, 5):
+        assert np.array_equal(new[sl], pool[sl])
+    for h in range(H):
+        st, outs = gdn.sequential(pool[5, h].astype(np.float64), q[0, :, h], k[0, :, h], v[0, :, h], al[0, :, h], be[0, :, h])
+        for t in range(T):
+            assert np.array_equal(new[out_idx[0, t], h], st[t].astype(np.float32))
+        np.testing.assert_allclose(o[0, :, h], outs, rtol=1e-15)
+        st0, _ = gdn.sequential(np.zeros((dv, dk)), q[1, :, h], k[1, :, h], v[1, :, h], al[1, :, h], be[1, :, h])
+        assert np.array_equal(new[out_idx[1, -1], h], st0[-1].astype(np.float32))
+    # in == out for a single token reads before it writes
+    new2, _ = gdn.state_update(pool, np.array([3]), np.array([[3]]), q[:1, :1], k[:1, :1], v[:1, :1], al[:1, :1], be[:1, :1])
+    st, _ = gdn.sequential(pool[3, 0].astype(np.float64), q[0, :1, 0], k[0, :1, 0], v[0, :1, 0], al[0, :1, 0], be[0, :1, 0])
+    assert np.array_equal(new2[3, 0], st[0].astype(np.float32))
