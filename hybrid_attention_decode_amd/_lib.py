@@ -1,0 +1,401 @@
+"""ctypes binding of libhad.so (argument marshalling only).
+
+Every computation runs in the library: the host page-table/slot manager in
+C++ and the decode path in gfx950 HIP kernels.  Device tensors are torch
+tensors on a ROCm device; their data pointers and torch's current stream
+are handed to the C ABI.  There is no fallback: if the library is missing,
+every call raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhad.so")
+
+OK = 0
+_STATUS = {
+    -1: "invalid",
+    -2: "unsupported_shape",
+    -3: "out_of_pages",
+    -4: "out_of_slots",
+    -5: "bad_seq",
+    -6: "workspace_too_small",
+    -7: "hip",
+    -8: "bad_slot",
+    -9: "capacity",
+    -10: "range",
+}
+DERR_PAGE, DERR_SLOT, DERR_SEQLEN = 1, 2, 4
+
+
+class HadError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, status, message):
+        self.status = status
+        self.kind = _STATUS.get(status, "unknown")
+        super().__init__("libhad status %d (%s): %s" % (status, self.kind, message))
+
+
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class KvLayout(ctypes.Structure):
+    _fields_ = [("num_pages", _i32), ("H_kv", _i32), ("page_size", _i32), ("head_dim", _i32)]
+
+
+class QknrgDesc(ctypes.Structure):
+    _fields_ = [("n_seqs", _i32), ("T", _i32), ("H_q", _i32), ("H_kv", _i32), ("head_dim", _i32),
+                ("rotary_dim", _i32), ("rope_base", ctypes.c_double), ("eps", ctypes.c_float),
+                ("num_pages", _i32), ("page_size", _i32), ("max_pages", _i32)]
+
+
+class QknrgPtrs(ctypes.Structure):
+    _fields_ = [("qg", _p), ("k", _p), ("v", _p), ("w_q", _p), ("w_k", _p), ("page_table", _p),
+                ("seq_lens", _p), ("k_pool", _p), ("v_pool", _p), ("q_out", _p), ("gate_out", _p), ("d_err", _p)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("n_seqs", _i32), ("q_len", _i32), ("H_q", _i32), ("H_kv", _i32), ("head_dim", _i32),
+                ("num_pages", _i32), ("page_size", _i32), ("max_pages", _i32), ("sm_scale", ctypes.c_float),
+                ("max_seq_len", _i32), ("num_splits", _i32)]
+
+
+class AttnPtrs(ctypes.Structure):
+    _fields_ = [("q", _p), ("k_pool", _p), ("v_pool", _p), ("page_table", _p), ("seq_lens", _p),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("out", _p), ("d_err", _p)]
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("n_seqs", _i32), ("T", _i32), ("H", _i32), ("d_k", _i32), ("d_v", _i32), ("n_slots", _i32),
+                ("q_scale", ctypes.c_float)]
+
+
+class GdnPtrs(ctypes.Structure):
+    _fields_ = [("state_pool", _p), ("in_idx", _p), ("out_idx", _p), ("q", _p), ("k", _p), ("v", _p),
+                ("alpha", _p), ("beta", _p), ("o", _p), ("d_err", _p)]
+
+
+_SIGS = {
+    "had_abi_version": ([], ctypes.c_int),
+    "had_last_error": ([], ctypes.c_char_p),
+    "had_kvpt_create": ([_i32, _i32, _i32, _i32, _pi32, ctypes.POINTER(_p)], ctypes.c_int),
+    "had_kvpt_destroy": ([_p], ctypes.c_int),
+    "had_kvpt_seq_create": ([_p, _pi32], ctypes.c_int),
+    "had_kvpt_seq_fork": ([_p, _i32, _i32, _pi32], ctypes.c_int),
+    "had_kvpt_reserve": ([_p, _i32, _i32, _pi32, _pi32], ctypes.c_int),
+    "had_kvpt_truncate": ([_p, _i32, _i32], ctypes.c_int),
+    "had_kvpt_seq_free": ([_p, _i32], ctypes.c_int),
+    "had_kvpt_seq_len": ([_p, _i32, _pi32], ctypes.c_int),
+    "had_kvpt_export": ([_p, _pi32, _i32, _pi32, _i32, _pi32], ctypes.c_int),
+    "had_kvpt_stats": ([_p, _pi32, _pi32], ctypes.c_int),
+    "had_slots_create": ([_i32, _pi32, ctypes.POINTER(_p)], ctypes.c_int),
+    "had_slots_destroy": ([_p], ctypes.c_int),
+    "had_slots_acquire": ([_p, _pi32], ctypes.c_int),
+    "had_slots_retain": ([_p, _i32], ctypes.c_int),
+    "had_slots_release": ([_p, _i32], ctypes.c_int),
+    "had_slots_stats": ([_p, _pi32, _pi32], ctypes.c_int),
+    "had_spec_rollback": ([_p, _p, _i32, _i32, _i32, _i32, _pi32, _pi32], ctypes.c_int),
+    "had_kv_copy_pages": ([ctypes.POINTER(KvLayout), _p, _p, _pi32, _pi32, _i32, _p], ctypes.c_int),
+    "had_kv_append": ([ctypes.POINTER(KvLayout), _p, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _p], ctypes.c_int),
+    "had_qk_norm_rope_gate": ([ctypes.POINTER(QknrgDesc), ctypes.POINTER(QknrgPtrs), _p], ctypes.c_int),
+    "had_decode_attn_plan": ([ctypes.POINTER(AttnDesc), _pi32, _pi32], ctypes.c_int),
+    "had_decode_attn_workspace_bytes": ([ctypes.POINTER(AttnDesc)], ctypes.c_size_t),
+    "had_decode_attn": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
+    "had_decode_attn_combine": ([ctypes.POINTER(AttnDesc), _i32, _p, _p, _p], ctypes.c_int),
+    "had_gdn_state_update": ([ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnPtrs), _p], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libhad.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhad.so is not built (%s); run `python -m hybrid_attention_decode_amd.build`"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGS)
+
+
+def _check(status):
+    if status != OK:
+        raise HadError(status, lib().had_last_error().decode(errors="replace"))
+
+
+def abi_version():
+    return lib().had_abi_version()
+
+
+def _i32_array(values):
+    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return a, a.ctypes.data_as(_pi32)
+
+
+# ----------------------------------------------------------------- host side
+
+class PageTable:
+    """Handle on the C++ page-table manager (had_kvpt_*)."""
+
+    def __init__(self, num_pages, page_size, max_seqs, max_pages_per_seq, free_order=None):
+        self._h = _p()
+        if free_order is not None:
+            self._order, ptr = _i32_array(free_order)
+        else:
+            ptr = None
+        _check(lib().had_kvpt_create(num_pages, page_size, max_seqs, max_pages_per_seq, ptr, ctypes.byref(self._h)))
+        self.page_size = page_size
+
+    def close(self):
+        if self._h:
+            lib().had_kvpt_destroy(self._h)
+            self._h = _p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def seq_create(self):
+        out = _i32()
+        _check(lib().had_kvpt_seq_create(self._h, ctypes.byref(out)))
+        return out.value
+
+    def seq_fork(self, src, prefix_len):
+        out = _i32()
+        _check(lib().had_kvpt_seq_fork(self._h, src, prefix_len, ctypes.byref(out)))
+        return out.value
+
+    def reserve(self, seq, n_tokens):
+        """Returns None or the copy-on-write triple (src, dst, valid)."""
+        cow = (_i32 * 3)()
+        n = _i32()
+        _check(lib().had_kvpt_reserve(self._h, seq, n_tokens, cow, ctypes.byref(n)))
+        return (cow[0], cow[1], cow[2]) if n.value else None
+
+    def truncate(self, seq, new_len):
+        _check(lib().had_kvpt_truncate(self._h, seq, new_len))
+
+    def seq_free(self, seq):
+        _check(lib().had_kvpt_seq_free(self._h, seq))
+
+    def seq_len(self, seq):
+        out = _i32()
+        _check(lib().had_kvpt_seq_len(self._h, seq, ctypes.byref(out)))
+        return out.value
+
+    def export(self, seqs, max_pages):
+        seqs_a, sp = _i32_array(seqs)
+        n = len(seqs_a)
+        table = np.zeros((n, max_pages), dtype=np.int32)
+        lens = np.zeros(n, dtype=np.int32)
+        _check(lib().had_kvpt_export(self._h, sp, n, table.ctypes.data_as(_pi32), max_pages,
+                                     lens.ctypes.data_as(_pi32)))
+        return table, lens
+
+    def stats(self):
+        f, u = _i32(), _i32()
+        _check(lib().had_kvpt_stats(self._h, ctypes.byref(f), ctypes.byref(u)))
+        return f.value, u.value
+
+
+class SlotPool:
+    """Handle on the C++ state-slot pool (had_slots_*)."""
+
+    def __init__(self, n_slots, free_order=None):
+        self._h = _p()
+        if free_order is not None:
+            self._order, ptr = _i32_array(free_order)
+        else:
+            ptr = None
+        _check(lib().had_slots_create(n_slots, ptr, ctypes.byref(self._h)))
+
+    def close(self):
+        if self._h:
+            lib().had_slots_destroy(self._h)
+            self._h = _p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def acquire(self):
+        out = _i32()
+        _check(lib().had_slots_acquire(self._h, ctypes.byref(out)))
+        return out.value
+
+    def retain(self, slot):
+        _check(lib().had_slots_retain(self._h, slot))
+
+    def release(self, slot):
+        _check(lib().had_slots_release(self._h, slot))
+
+    def stats(self):
+        f, u = _i32(), _i32()
+        _check(lib().had_slots_stats(self._h, ctypes.byref(f), ctypes.byref(u)))
+        return f.value, u.value
+
+
+def spec_rollback(pt, slots, seq, T, accepted, in_slot, out_slots):
+    outs, op = _i32_array(out_slots)
+    cur = _i32()
+    _check(lib().had_spec_rollback(pt._h, slots._h, seq, T, accepted, in_slot, op, ctypes.byref(cur)))
+    return cur.value
+
+
+# --------------------------------------------------------------- device side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return _p(t.data_ptr())
+
+
+def _opt(t, name):
+    return None if t is None else _dev(t, _torch().int32, name)
+
+
+def kv_copy_pages(k_pool, v_pool, src, dst):
+    """Copy whole pages src[i] -> dst[i] in both pools (src, dst: host ints)."""
+    torch = _torch()
+    N, H_kv, P, D = k_pool.shape
+    L = KvLayout(N, H_kv, P, D)
+    s_a, sp = _i32_array(src)
+    d_a, dp = _i32_array(dst)
+    if len(s_a) != len(d_a):
+        raise ValueError("src and dst differ in length")
+    _check(lib().had_kv_copy_pages(ctypes.byref(L), _dev(k_pool, torch.bfloat16, "k_pool"),
+                                   _dev(v_pool, torch.bfloat16, "v_pool"), sp, dp, len(s_a), _stream()))
+
+
+def kv_append(k_pool, v_pool, page_table, seq_lens, k_new, v_new, d_err=None):
+    torch = _torch()
+    N, H_kv, P, D = k_pool.shape
+    n_seqs, t_new = k_new.shape[0], k_new.shape[1]
+    L = KvLayout(N, H_kv, P, D)
+    _check(lib().had_kv_append(ctypes.byref(L), _dev(k_pool, torch.bfloat16, "k_pool"),
+                               _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
+                               page_table.shape[1], _dev(seq_lens, torch.int32, "seq_lens"),
+                               _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
+                               n_seqs, t_new, _opt(d_err, "d_err"), _stream()))
+
+
+def qk_norm_rope_gate(qg, k, v, w_q, w_k, page_table, seq_lens, k_pool, v_pool, rotary_dim,
+                      rope_base=10000.0, eps=1e-6, q_out=None, gate_out=None, d_err=None):
+    """qg [S, T, H_q, 2, D], k/v [S, T, H_kv, D] -> (q_out, gate_out) [S, T, H_q, D]."""
+    torch = _torch()
+    S, T, H_q, two, D = qg.shape
+    H_kv = k.shape[2]
+    if q_out is None:
+        q_out = torch.empty((S, T, H_q, D), dtype=torch.bfloat16, device=qg.device)
+    if gate_out is None:
+        gate_out = torch.empty((S, T, H_q, D), dtype=torch.bfloat16, device=qg.device)
+    desc = QknrgDesc(S, T, H_q, H_kv, D, rotary_dim, float(rope_base), float(eps), k_pool.shape[0],
+                     k_pool.shape[2], page_table.shape[1])
+    ptrs = QknrgPtrs(_dev(qg, torch.bfloat16, "qg"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+                     _dev(w_q, torch.float32, "w_q"), _dev(w_k, torch.float32, "w_k"),
+                     _dev(page_table, torch.int32, "page_table"), _dev(seq_lens, torch.int32, "seq_lens"),
+                     _dev(k_pool, torch.bfloat16, "k_pool"), _dev(v_pool, torch.bfloat16, "v_pool"),
+                     _dev(q_out, torch.bfloat16, "q_out"), _dev(gate_out, torch.bfloat16, "gate_out"),
+                     _opt(d_err, "d_err"))
+    _check(lib().had_qk_norm_rope_gate(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
+    return q_out, gate_out
+
+
+def attn_desc(q_shape, k_pool_shape, max_pages, sm_scale=None, max_seq_len=0, num_splits=0):
+    S, q_len, H_q, D = q_shape
+    N, H_kv, P, D2 = k_pool_shape
+    if D != D2:
+        raise ValueError("q and pool head_dim differ")
+    if sm_scale is None:
+        sm_scale = 1.0 / float(np.sqrt(D))
+    return AttnDesc(S, q_len, H_q, H_kv, D, N, P, max_pages, float(sm_scale), int(max_seq_len), int(num_splits))
+
+
+def decode_attn_plan(desc):
+    ns, pps = _i32(), _i32()
+    _check(lib().had_decode_attn_plan(ctypes.byref(desc), ctypes.byref(ns), ctypes.byref(pps)))
+    return ns.value, pps.value
+
+
+def decode_attn_workspace_bytes(desc):
+    n = lib().had_decode_attn_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        # the call reports an invalid descriptor by returning 0: surface why
+        _check(lib().had_decode_attn_plan(ctypes.byref(desc), ctypes.byref(_i32()), ctypes.byref(_i32())))
+    return n
+
+
+def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_len=0, num_splits=0,
+                workspace=None, out=None, d_err=None):
+    """q [S, q_len, H_q, D] bf16 -> out [S, q_len, H_q, D] bf16."""
+    torch = _torch()
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits)
+    need = decode_attn_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    ptrs = AttnPtrs(_dev(q, torch.bfloat16, "q"), _dev(k_pool, torch.bfloat16, "k_pool"),
+                    _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
+                    _dev(seq_lens, torch.int32, "seq_lens"), _dev(workspace, torch.uint8, "workspace"),
+                    workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"))
+    _check(lib().had_decode_attn(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
+    return out
+
+
+def decode_attn_combine(desc, num_splits, workspace, out):
+    torch = _torch()
+    _check(lib().had_decode_attn_combine(ctypes.byref(desc), num_splits, _dev(workspace, workspace.dtype, "workspace"),
+                                         _dev(out, torch.bfloat16, "out"), _stream()))
+    return out
+
+
+def gdn_state_update(state_pool, in_idx, out_idx, q, k, v, alpha, beta, o=None, q_scale=1.0, d_err=None):
+    """state_pool [n_slots, H, d_v, d_k] fp32; q, k [S, T, H, d_k]; v [S, T, H, d_v] bf16;
+    alpha, beta [S, T, H] fp32; in_idx [S], out_idx [S, T] int32 -> o [S, T, H, d_v] fp32."""
+    torch = _torch()
+    n_slots, H, d_v, d_k = state_pool.shape
+    S, T = out_idx.shape
+    if o is None:
+        o = torch.empty((S, T, H, d_v), dtype=torch.float32, device=state_pool.device)
+    desc = GdnDesc(S, T, H, d_k, d_v, n_slots, float(q_scale))
+    ptrs = GdnPtrs(_dev(state_pool, torch.float32, "state_pool"), _dev(in_idx, torch.int32, "in_idx"),
+                   _dev(out_idx, torch.int32, "out_idx"), _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
+                   _dev(v, torch.bfloat16, "v"), _dev(alpha, torch.float32, "alpha"),
+                   _dev(beta, torch.float32, "beta"), _dev(o, torch.float32, "o"), _opt(d_err, "d_err"))
+    _check(lib().had_gdn_state_update(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
+    return o

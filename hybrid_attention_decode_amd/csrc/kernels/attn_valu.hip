@@ -1,0 +1,348 @@
+// Split-K GQA decode attention, VALU path (query rows per KV head < 16).
+//
+// Operation: softmax(sm_scale * q K^T) V over the paged context of one
+// sequence and KV head, for up to 8 query rows at once (GQA group x draft
+// tokens), split over the context; each workgroup writes one unnormalised
+// partial (o, m, l) that a separate kernel merges.  Full-attention layers of
+// the hybrid model (24-ai.news TokenSpeed article, model paragraph), paged KV
+// (zubnet.ai TokenSpeed article, second paragraph), contexts to 1M tokens
+// (24-ai.news long-context table).
+//
+// gfx950 mapping (one workgroup = 4 waves, each wave streams its own tiles
+// of 8 tokens; the workgroup owns a contiguous range of pages):
+//  * QK: a tile step covers TPS tokens with LPT lanes per token; lane j of a
+//    token loads 16-byte chunks j, j+LPT of the K row (coalesced 128-bit
+//    loads straight into registers) and accumulates all 8 rows with
+//    v_dot2c_f32_bf16 against q held in registers.  q is stored in a
+//    lane-dependent row order (slot s of lane j holds row s ^ sigma(j)) so the
+//    cross-lane sum is a reduce-scatter of 7 DPP adds after which lane j holds
+//    the full score of row sigma(j): no lane idles and no selects are needed.
+//  * Online softmax in base 2 (scores prescaled by sm_scale*log2 e), row max
+//    by DPP/bpermute across the tile, p rounded once to bf16 and used for
+//    both the numerator and the running sum.
+//  * PV: lanes own 4 consecutive d of V rows (coalesced 64-bit loads); p
+//    pairs of two tokens are broadcast through LDS and v pairs are formed
+//    with v_perm_b32, so every MAC is a bf16 dot2.
+//  * K/V of a wave's next two tiles are in flight while it computes one.
+//  * The 4 waves' partials are merged through LDS before the single store.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_internal.h"
+#include "kcommon.h"
+
+namespace had {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRows = 8;  // rows handled per launch (padded with zero queries)
+constexpr int kTT = 8;    // tokens per tile
+
+template <int D>
+struct Cfg {
+  static constexpr int LPT = (D == 64) ? 8 : 16;  // lanes per token in QK
+  static constexpr int CH = D / (LPT * 8);         // 16-byte K chunks per lane per token
+  static constexpr int TPS = 64 / LPT;             // tokens per QK step
+  static constexpr int TS = kTT / TPS;             // QK steps per tile
+  static constexpr int DPL = 4;                    // d per lane in PV
+  static constexpr int TG = 256 / D;               // token groups in PV
+  static constexpr int VPL = kTT / TG;             // V rows per lane per tile
+  static constexpr int NPAIR = VPL / 2;            // dot2 token pairs per lane per tile
+  static_assert(CH >= 1 && TS >= 1 && NPAIR >= 1, "unsupported head_dim");
+};
+
+// Lane -> row permutation used by the reduce-scatter: the partners of the
+// three DPP levels (j^7, j^2, j^1 inside groups of 8) hold rows differing in
+// bit 2, 1 and 0 respectively.
+__device__ __forceinline__ int sigma(int j) { return (j & 3) ^ ((j & 4) ? 7 : 0); }
+
+template <int D>
+struct Tile {
+  uint4 k[Cfg<D>::TS][Cfg<D>::CH];
+  uint2 v[Cfg<D>::VPL];
+};
+
+struct Lds {
+  float o[kWaves][kRows][256];      // per-wave partial outputs for the merge
+  float ml[kWaves][kRows][2];       // per-wave (m, l)
+  uint32_t p[kWaves][4][kRows];     // bf16 p pairs: [pair][row]
+  float alpha[kWaves][kRows];       // per-row rescale factor of the current tile
+  int32_t pages[kMaxPagesPerSplit];  // page ids of the workgroup's range (-1 = invalid)
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(Tile<D>& T, const ValuArgs& a, const Lds& sh, int tile, int pg0, int tpp,
+                                          int h, int tg, int j, int tgv, int dl) {
+  using C = Cfg<D>;
+  const int pid_raw = sh.pages[tile / tpp - pg0];
+  const int pid = __builtin_amdgcn_readfirstlane(pid_raw < 0 ? 0 : pid_raw);
+  const int off = (tile % tpp) * kTT;
+  const size_t base = ((static_cast<size_t>(pid) * a.H_kv + h) * a.page_size + off) * D;
+  const uint16_t* kb = a.k_pool + base;
+  const uint16_t* vb = a.v_pool + base;
+#pragma unroll
+  for (int i = 0; i < C::TS; ++i)
+#pragma unroll
+    for (int c = 0; c < C::CH; ++c)
+      T.k[i][c] = *reinterpret_cast<const uint4*>(kb + (i * C::TPS + tg) * D + (j + c * C::LPT) * 8);
+#pragma unroll
+  for (int i = 0; i < C::VPL; ++i)
+    T.v[i] = *reinterpret_cast<const uint2*>(vb + (tgv + C::TG * i) * D + dl * C::DPL);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_valu_kernel(ValuArgs a) {
+  using C = Cfg<D>;
+  __shared__ Lds sh;
+  const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tg = lane / C::LPT, j = lane % C::LPT, j8 = j & 7;
+  const int tgv = lane / (D / C::DPL), dl = lane % (D / C::DPL);
+  const int P = a.page_size;
+  const int tpp = P / kTT;
+
+  const int L = a.seq_lens[s];
+  const bool bad_len = L < a.q_len || L > a.max_pages * P;
+  if (bad_len && threadIdx.x == 0) set_err(a.d_err, HAD_DERR_SEQLEN);
+  const int n_pages = bad_len ? 0 : (L + P - 1) / P;
+  const int pg0 = sp * a.pps;
+  const int pg1 = min(pg0 + a.pps, n_pages);
+  const int npg = max(pg1 - pg0, 0);
+
+  // page ids of this split -> LDS (checked; -1 marks an invalid id)
+  for (int i = threadIdx.x; i < npg; i += 256) {
+    int pid = a.page_table[static_cast<size_t>(s) * a.max_pages + pg0 + i];
+    if (pid < 0 || pid >= a.num_pages) {
+      set_err(a.d_err, HAD_DERR_PAGE);
+      pid = -1;
+    }
+    sh.pages[i] = pid;
+  }
+
+  // q rows in lane order: slot r holds row (r ^ sigma(j8)) of this launch
+  uint32_t qr[kRows][C::CH * 4];
+  int my_row = a.row_base + sigma(j8);
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int row = a.row_base + (r ^ sigma(j8));
+#pragma unroll
+    for (int c = 0; c < C::CH; ++c) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < a.rows) {
+        const int jq = row / a.G, g = row % a.G;
+        const uint16_t* qp = a.q + ((static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g) * D;
+        v = *reinterpret_cast<const uint4*>(qp + (j + c * C::LPT) * 8);
+      }
+      qr[r][c * 4 + 0] = v.x;
+      qr[r][c * 4 + 1] = v.y;
+      qr[r][c * 4 + 2] = v.z;
+      qr[r][c * 4 + 3] = v.w;
+    }
+  }
+  // visible-key limit of this lane's QK row (causal inside the draft)
+  const int lim = (my_row < a.rows) ? (L - a.q_len + my_row / a.G + 1) : L;
+  const int lim_min = L - a.q_len + 1;  // every row sees positions below this
+
+  __syncthreads();
+
+  float o[kRows][C::DPL];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int d = 0; d < C::DPL; ++d) o[r][d] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int t_begin = pg0 * tpp, t_end = pg0 * tpp + npg * tpp;
+  // this wave's tiles: t_begin + wave + kWaves * i
+  const int my_first = t_begin + wave;
+  const int n_my = (t_end > my_first) ? (t_end - my_first + kWaves - 1) / kWaves : 0;
+
+  Tile<D> buf[2];
+  if (n_my > 0) load_tile<D>(buf[0], a, sh, my_first, pg0, tpp, h, tg, j, tgv, dl);
+  if (n_my > 1) load_tile<D>(buf[1], a, sh, my_first + kWaves, pg0, tpp, h, tg, j, tgv, dl);
+
+  for (int it = 0; it < n_my; it += 2) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int ii = it + b;
+      if (ii >= n_my) break;
+      const int tile = my_first + ii * kWaves;
+      Tile<D>& T = buf[b];
+      const int pos0 = (tile / tpp) * P + (tile % tpp) * kTT;  // logical position of the tile's token 0
+      const bool tile_ok = sh.pages[tile / tpp - pg0] >= 0;
+
+      // ---- scores
+      float sc[C::TS];
+#pragma unroll
+      for (int i = 0; i < C::TS; ++i) {
+        float acc[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < C::CH; ++c) {
+          const uint32_t kw[4] = {T.k[i][c].x, T.k[i][c].y, T.k[i][c].z, T.k[i][c].w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) acc[r] = dot2_bf16(qr[r][c * 4 + w], kw[w], acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += dpp<DPP_ROW_HALF_MIRROR>(acc[r + 4]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) acc[r] += dpp<DPP_QUAD_XOR2>(acc[r + 2]);
+        acc[0] += dpp<DPP_QUAD_XOR1>(acc[1]);
+        if (C::LPT == 16) acc[0] += dpp<DPP_ROW_ROR8>(acc[0]);
+        sc[i] = acc[0] * a.scale_log2;
+      }
+      // the next-but-one tile reuses these K registers
+      const bool masked = !tile_ok || (pos0 + kTT > lim_min);
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < C::TS; ++i) {
+          const int pos = pos0 + i * C::TPS + tg;
+          if (!tile_ok || pos >= lim) sc[i] = -INFINITY;
+        }
+      }
+
+      // ---- online softmax (rows are lane-uniform within groups of LPT)
+      float mt = sc[0];
+#pragma unroll
+      for (int i = 1; i < C::TS; ++i) mt = fmaxf(mt, sc[i]);
+      if (C::LPT == 8) mt = fmaxf(mt, dpp<DPP_ROW_ROR8>(mt));
+      mt = fmaxf(mt, shfl_xor_f(mt, 16));
+      mt = fmaxf(mt, shfl_xor_f(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const float m_sub = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_sub);
+      float lsum = 0.f;
+      uint16_t pb[C::TS];
+#pragma unroll
+      for (int i = 0; i < C::TS; ++i) {
+        pb[i] = f32_to_bf16(exp2f(sc[i] - m_sub));
+        lsum += bf16_to_f32(pb[i]);
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+
+      // ---- publish p pairs and alpha to the wave's LDS slice
+      if (C::LPT == 8 || j < 8) {
+        uint16_t* pw = reinterpret_cast<uint16_t*>(&sh.p[wave][0][0]);
+#pragma unroll
+        for (int i = 0; i < C::TS; ++i) {
+          const int t = i * C::TPS + tg;  // token within the tile
+          const int g = t % C::TG, vi = t / C::TG;
+          const int pair = (vi >> 1) * C::TG + g, half = vi & 1;
+          pw[(pair * kRows + sigma(j8)) * 2 + half] = pb[i];
+        }
+        if (tg == 0) sh.alpha[wave][sigma(j8)] = alpha;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+      // ---- rescale and accumulate P V
+      const float4 a0 = *reinterpret_cast<const float4*>(&sh.alpha[wave][0]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&sh.alpha[wave][4]);
+      const float al[kRows] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      bool need = false;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) need |= al[r] != 1.f;
+      if (need) {
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+#pragma unroll
+          for (int d = 0; d < C::DPL; ++d) o[r][d] *= al[r];
+      }
+      if (masked) {  // never multiply stale or unchecked rows: zero invalid V
+#pragma unroll
+        for (int i = 0; i < C::VPL; ++i) {
+          const int pos = pos0 + tgv + C::TG * i;
+          if (!tile_ok || pos >= L) T.v[i] = make_uint2(0, 0);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < C::NPAIR; ++k) {
+        const uint4 p0 = *reinterpret_cast<const uint4*>(&sh.p[wave][k * C::TG + tgv][0]);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(&sh.p[wave][k * C::TG + tgv][4]);
+        const uint32_t pr[kRows] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const uint2 va = T.v[2 * k], vb = T.v[2 * k + 1];
+        const uint32_t vp[4] = {perm_b32(vb.x, va.x, 0x05040100u), perm_b32(vb.x, va.x, 0x07060302u),
+                                perm_b32(vb.y, va.y, 0x05040100u), perm_b32(vb.y, va.y, 0x07060302u)};
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) o[r][d] = dot2_bf16(pr[r], vp[d], o[r][d]);
+      }
+      __builtin_amdgcn_wave_barrier();
+
+      if (ii + 2 < n_my) load_tile<D>(T, a, sh, tile + 2 * kWaves, pg0, tpp, h, tg, j, tgv, dl);
+    }
+  }
+
+  // ---- wave totals: l over token groups, o over PV token groups
+  if (C::LPT == 8) l_run += dpp<DPP_ROW_ROR8>(l_run);
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int d = 0; d < C::DPL; ++d) {
+      if (C::TG >= 4) o[r][d] += shfl_xor_f(o[r][d], 16);
+      if (C::TG >= 2) o[r][d] += shfl_xor_f(o[r][d], 32);
+    }
+  if (tgv == 0) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+      *reinterpret_cast<float4*>(&sh.o[wave][r][dl * 4]) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+  }
+  if (tg == 0 && j < 8) {
+    sh.ml[wave][sigma(j8)][0] = m_run;
+    sh.ml[wave][sigma(j8)][1] = l_run;
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves and store the split's partial
+  const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.num_splits + sp;
+  for (int idx = threadIdx.x; idx < kRows * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    const int row = a.row_base + r;
+    if (row >= a.rows) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][r][0]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = exp2f(sh.ml[w][r][0] - Ms);
+      acc += wt * sh.o[w][r][d];
+      lsum += wt * sh.ml[w][r][1];
+    }
+    a.ws_o[(unit * a.rows + row) * D + d] = acc;
+    if (d == 0) {
+      a.ws_ml[(unit * a.rows + row) * 2 + 0] = M;
+      a.ws_ml[(unit * a.rows + row) * 2 + 1] = lsum;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 64:
+      hipLaunchKernelGGL(attn_valu_kernel<64>, grid, dim3(256), 0, stream, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(attn_valu_kernel<128>, grid, dim3(256), 0, stream, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(attn_valu_kernel<256>, grid, dim3(256), 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace had

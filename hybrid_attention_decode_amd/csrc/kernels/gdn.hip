@@ -1,0 +1,167 @@
+// Gated delta rule update of slot-addressed recurrent states.
+//
+// For sequence s, head h, with S (d_v x d_k, fp32) read from slot in_idx[s]
+// (zero state for -1), for each of the T tokens:
+//   S <- alpha S (I - beta k k^T) + beta v k^T     evaluated as
+//   u = beta (v - alpha S k),  S <- alpha S + u k^T
+//   o = q_scale * S q,  and S is stored to slot out_idx[s][t].
+// Gated DeltaNet layers of the hybrid model (24-ai.news TokenSpeed article,
+// model paragraph; recurrence of Yang, Kautz & Hatamizadeh, ICLR 2025).  The
+// state never moves between slots by copy: a step reads one slot index and
+// writes another (zubnet.ai TokenSpeed article, second paragraph,
+// current_input_indices; 24-ai.news "Mamba State Update", O(1) pointer
+// update).  With T > 1 the state stays in registers across tokens and every
+// token's state is written as a checkpoint.
+//
+// Mapping: one wave per (s, h, block of 8 rows of S).  Lane (r, c) holds
+// row r's columns {4c + 32i .. 4c + 32i + 3}, so each row's 8 lanes read a
+// contiguous 128-byte segment per float4; the dot products S k and S q are
+// all-reduced across those 8 lanes with three DPP adds.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../host/status.h"
+#include "had.h"
+#include "kcommon.h"
+
+using had::fail;
+
+namespace had {
+namespace {
+
+struct GdnArgs {
+  float* pool;
+  const int32_t* in_idx;
+  const int32_t* out_idx;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  int32_t* d_err;
+  int T, H, d_v, n_slots;
+  float q_scale;
+};
+
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<DPP_QUAD_XOR1>(x);
+  x += dpp<DPP_QUAD_XOR2>(x);
+  x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  return x;
+}
+
+template <int DK>
+__global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
+  constexpr int NC = DK / 32;  // float4 column chunks per lane
+  const int rb = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int r = lane >> 3, c = lane & 7;
+  const int row = rb * 8 + r;
+  const size_t head_elems = static_cast<size_t>(a.d_v) * DK;
+  const size_t row_off = static_cast<size_t>(h) * head_elems + static_cast<size_t>(row) * DK;
+  const size_t slot_elems = static_cast<size_t>(a.H) * head_elems;
+
+  int in = a.in_idx[s];
+  if (in < -1 || in >= a.n_slots) {
+    if (lane == 0) set_err(a.d_err, HAD_DERR_SLOT);
+    in = -1;
+  }
+  float S[NC][4];
+  if (in >= 0) {
+    const float* src = a.pool + static_cast<size_t>(in) * slot_elems + row_off;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const float4 t = *reinterpret_cast<const float4*>(src + 4 * c + 32 * i);
+      S[i][0] = t.x; S[i][1] = t.y; S[i][2] = t.z; S[i][3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+  }
+
+  for (int t = 0; t < a.T; ++t) {
+    const size_t th = (static_cast<size_t>(s) * a.T + t) * a.H + h;
+    const uint16_t* kp = a.k + th * DK;
+    const uint16_t* qp = a.q + th * DK;
+    const float al = a.alpha[th], be = a.beta[th];
+    const float vi = bf16_to_f32(a.v[th * a.d_v + row]);
+    float kk[NC][4], qq[NC][4];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const uint2 kw = *reinterpret_cast<const uint2*>(kp + 4 * c + 32 * i);
+      const uint2 qw = *reinterpret_cast<const uint2*>(qp + 4 * c + 32 * i);
+      kk[i][0] = bf16_lo(kw.x); kk[i][1] = bf16_hi(kw.x); kk[i][2] = bf16_lo(kw.y); kk[i][3] = bf16_hi(kw.y);
+      qq[i][0] = bf16_lo(qw.x); qq[i][1] = bf16_hi(qw.x); qq[i][2] = bf16_lo(qw.y); qq[i][3] = bf16_hi(qw.y);
+    }
+    float sk = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sk = fmaf(S[i][e], kk[i][e], sk);
+    sk = sum8(sk);
+    const float u = be * (vi - al * sk);
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        S[i][e] = fmaf(u, kk[i][e], al * S[i][e]);
+        sq = fmaf(S[i][e], qq[i][e], sq);
+      }
+    sq = sum8(sq);
+    if (c == 0) a.o[th * a.d_v + row] = a.q_scale * sq;
+    const int out = a.out_idx[static_cast<size_t>(s) * a.T + t];
+    if (out < 0 || out >= a.n_slots) {
+      if (lane == 0) set_err(a.d_err, HAD_DERR_SLOT);
+      continue;
+    }
+    float* dst = a.pool + static_cast<size_t>(out) * slot_elems + row_off;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      *reinterpret_cast<float4*>(dst + 4 * c + 32 * i) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+  }
+}
+
+}  // namespace
+}  // namespace had
+
+extern "C" int had_gdn_state_update(const had_gdn_desc* d, const had_gdn_ptrs* p, void* stream) {
+  if (!d || !p) return fail(HAD_ERR_INVALID_ARG, "gdn_state_update: NULL argument");
+  if (d->n_seqs < 0 || d->H < 1 || d->n_slots < 1 || d->T < 1 || d->T > 8)
+    return fail(HAD_ERR_INVALID_ARG, "gdn_state_update: bad sizes (n_seqs=%d T=%d H=%d n_slots=%d)", d->n_seqs, d->T,
+                d->H, d->n_slots);
+  if ((d->d_k != 64 && d->d_k != 128) || (d->d_v != 64 && d->d_v != 128))
+    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "gdn_state_update: d_k=%d d_v=%d must be 64 or 128", d->d_k, d->d_v);
+  if (!p->state_pool || !p->in_idx || !p->out_idx || !p->q || !p->k || !p->v || !p->alpha || !p->beta || !p->o)
+    return fail(HAD_ERR_INVALID_ARG, "gdn_state_update: NULL pointer in ptrs");
+  if ((reinterpret_cast<uintptr_t>(p->state_pool) & 15u) != 0 || (reinterpret_cast<uintptr_t>(p->q) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(p->k) & 7u) != 0)
+    return fail(HAD_ERR_INVALID_ARG, "gdn_state_update: state_pool must be 16-byte and q, k 8-byte aligned");
+  if (d->n_seqs == 0) return had::ok();
+  had::GdnArgs a{};
+  a.pool = p->state_pool;
+  a.in_idx = p->in_idx;
+  a.out_idx = p->out_idx;
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.k = static_cast<const uint16_t*>(p->k);
+  a.v = static_cast<const uint16_t*>(p->v);
+  a.alpha = p->alpha;
+  a.beta = p->beta;
+  a.o = p->o;
+  a.d_err = p->d_err;
+  a.T = d->T;
+  a.H = d->H;
+  a.d_v = d->d_v;
+  a.n_slots = d->n_slots;
+  a.q_scale = d->q_scale;
+  const dim3 grid(d->d_v / 8, d->H, d->n_seqs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->d_k == 64)
+    hipLaunchKernelGGL(had::gdn_kernel<64>, grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(had::gdn_kernel<128>, grid, dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_state_update: launch: %s", hipGetErrorString(e));
+  return had::ok();
+}

@@ -1,0 +1,336 @@
+/*
+ * had.h -- C ABI of the hybrid-attention decode library (libhad.so), gfx950.
+ *
+ * One decode step of a hybrid model (full-attention layers interleaved with
+ * Gated DeltaNet layers) as four groups of calls:
+ *
+ *   kv_page_table      host page-table / state-slot manager and two device
+ *                      helpers that move KV rows (append, copy-on-write copy)
+ *   qk_norm_rope_gate  fused prologue of a full-attention layer
+ *   decode_attn        split-K GQA decode attention over the paged KV cache
+ *   gdn_state_update   gated delta rule update of slot-addressed states
+ *
+ * Sources.  The system is the TokenSpeed inference engine described in a few
+ * news articles: zubnet.ai (Spanish/French), second paragraph -- paged KV,
+ * Mamba/GDN state slots checkpointed next to the KV, index indirection
+ * through current_input_indices instead of tensor copies, copy-on-write reuse
+ * of cached checkpoints, the fused QK-RMSNorm + partial RoPE + gate split;
+ * 24-ai.news -- the hybrid full-attention / Gated DeltaNet model, the
+ * "Mamba State Update" optimisation (O(1) pointer update), hybrid prefix
+ * caching with a C++ logical cache over Python-owned physical tensors, and
+ * the 128K / 256K / 1M long-context table; evermx.com, "Pluggable Kernel
+ * Registry" -- one portable entry point per kernel.  The articles give no
+ * formulas; each call below states the operation it computes.
+ *
+ * Conventions (all calls)
+ * -----------------------
+ * - Every call returns an int status: HAD_OK (0) or a negative HAD_ERR_*.
+ *   Nothing is thrown across the ABI.  had_last_error() returns a
+ *   thread-local message describing the last failure on the calling thread.
+ * - A failing host call leaves every handle exactly as it was.
+ * - The library never allocates device memory.  The caller owns every device
+ *   buffer (inputs, outputs, pools, workspaces) and every host handle it
+ *   creates.  Device pointers are plain addresses from the caller's
+ *   allocator (e.g. torch); "stream" is a hipStream_t passed as void*
+ *   (NULL = the default stream).  Device calls only enqueue work on that
+ *   stream: no hidden synchronisation, no host<->device copies.
+ * - bf16 tensors are IEEE bfloat16 bit patterns; all tensors are dense,
+ *   row-major, in the layout written next to each argument.
+ * - Device-side index checks: every kernel checks page ids against
+ *   num_pages and slot ids against n_slots and skips (never dereferences) an
+ *   out-of-range id.  If the optional d_err pointer (device int32) is not
+ *   NULL the kernel ORs a HAD_DERR_* bit into it; the caller reads it when
+ *   convenient (no device->host round trip is forced).
+ */
+#ifndef HAD_H
+#define HAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HAD_ABI_VERSION 1
+
+enum {
+  HAD_OK = 0,
+  HAD_ERR_INVALID_ARG = -1,       /* null pointer, negative size, bad value      */
+  HAD_ERR_UNSUPPORTED_SHAPE = -2, /* shape outside what the kernels implement    */
+  HAD_ERR_OUT_OF_PAGES = -3,      /* free list cannot satisfy a reservation      */
+  HAD_ERR_OUT_OF_SLOTS = -4,      /* no free state slot                          */
+  HAD_ERR_BAD_SEQ = -5,           /* unknown or freed sequence id                */
+  HAD_ERR_WORKSPACE_TOO_SMALL = -6,
+  HAD_ERR_HIP = -7,               /* a HIP runtime call failed                   */
+  HAD_ERR_BAD_SLOT = -8,          /* slot id out of range or not held            */
+  HAD_ERR_CAPACITY = -9,          /* max_seqs or max_pages_per_seq exceeded      */
+  HAD_ERR_RANGE = -10             /* length argument outside [0, current length] */
+};
+
+/* bits ORed into *d_err by kernels */
+enum {
+  HAD_DERR_PAGE = 1,    /* page id < 0 or >= num_pages for a position < seq_len */
+  HAD_DERR_SLOT = 2,    /* slot id >= n_slots, or out slot < 0                 */
+  HAD_DERR_SEQLEN = 4   /* seq_len < q_len (or T) or beyond max_pages*page_size */
+};
+
+int had_abi_version(void);
+const char *had_last_error(void);
+
+/* ======================================================================
+ * kv_page_table -- host side (C++; no GPU needed)
+ *
+ * Logical position p of sequence s lives in physical page
+ * page_table[s][p / page_size], row p % page_size.  Forked sequences alias
+ * the pages of their prefix (reference counts); the first write into a
+ * shared, partially filled last page copies it first (copy-on-write).  This
+ * is the engine's "logical cache in C++, physical tensors in Python" split
+ * (24-ai.news, optimisation list, hybrid prefix caching; zubnet.ai ¶2,
+ * copy-on-write of cached checkpoints).
+ *
+ * Allocation policy (deterministic, so results can be compared bit for bit):
+ * the free list starts as `free_order` (identity if NULL); allocation pops
+ * its LAST element; a page whose reference count drops to 0 is pushed at the
+ * end.  New sequence ids are the lowest unused id.
+ * ====================================================================== */
+typedef struct had_kvpt had_kvpt;
+
+/* num_pages physical pages of page_size tokens; up to max_seqs live
+ * sequences of up to max_pages_per_seq pages each.  free_order: host array
+ * of num_pages distinct ids in [0, num_pages) or NULL.  *out receives the
+ * handle (owned by the caller; release with had_kvpt_destroy). */
+int had_kvpt_create(int32_t num_pages, int32_t page_size, int32_t max_seqs,
+                    int32_t max_pages_per_seq, const int32_t *free_order,
+                    had_kvpt **out);
+int had_kvpt_destroy(had_kvpt *h);
+
+/* New empty sequence; *seq receives its id.  HAD_ERR_CAPACITY when
+ * max_seqs sequences are live. */
+int had_kvpt_seq_create(had_kvpt *h, int32_t *seq);
+
+/* New sequence sharing the first prefix_len tokens of src: it aliases the
+ * first ceil(prefix_len / page_size) pages (each gains a reference).
+ * HAD_ERR_RANGE if prefix_len > length of src. */
+int had_kvpt_seq_fork(had_kvpt *h, int32_t src, int32_t prefix_len, int32_t *seq);
+
+/* Grow seq by n_tokens (>= 0).  If the last page is partially filled and
+ * shared it is first replaced by a fresh page; the copy the caller must then
+ * perform on every layer's pools is reported as cow = {src, dst, valid}
+ * (valid = tokens already in the page) with *n_cow = 1, else *n_cow = 0.
+ * Then fresh pages are appended until the sequence covers its new length.
+ * Transactional: HAD_ERR_CAPACITY / HAD_ERR_OUT_OF_PAGES change nothing.
+ * cow: host int32[3]; n_cow: host int32. */
+int had_kvpt_reserve(had_kvpt *h, int32_t seq, int32_t n_tokens, int32_t *cow,
+                     int32_t *n_cow);
+
+/* Shrink seq to new_len (<= length): pages past ceil(new_len / page_size)
+ * are dropped, last first; a page that loses its last reference goes back to
+ * the free list.  Stale rows left in a kept page are masked by the length. */
+int had_kvpt_truncate(had_kvpt *h, int32_t seq, int32_t new_len);
+
+/* Truncate to 0 and release the id. */
+int had_kvpt_seq_free(had_kvpt *h, int32_t seq);
+
+int had_kvpt_seq_len(const had_kvpt *h, int32_t seq, int32_t *len);
+
+/* Write the page-table rows and lengths of n sequences:
+ * page_table host int32[n][max_pages] (unused entries = -1),
+ * seq_lens host int32[n].  HAD_ERR_INVALID_ARG if a sequence holds more
+ * than max_pages pages. */
+int had_kvpt_export(const had_kvpt *h, const int32_t *seqs, int32_t n,
+                    int32_t *page_table, int32_t max_pages, int32_t *seq_lens);
+
+/* Number of free pages and of pages with a reference. */
+int had_kvpt_stats(const had_kvpt *h, int32_t *n_free, int32_t *n_used);
+
+/* ----------------------------------------------------------------------
+ * State slots of the linear-attention (GDN) layers: reference-counted ids
+ * into a caller-owned float32 pool [n_slots][H][d_v][d_k].  A sequence's
+ * current state is addressed by index (current_input_indices, zubnet.ai ¶2):
+ * a cached checkpoint is shared by retaining its id and is never written;
+ * a step reads slot in_idx and writes a fresh slot out_idx (copy-on-write
+ * by index, no tensor copy).  Same free-list policy as the pages.
+ * ---------------------------------------------------------------------- */
+typedef struct had_slots had_slots;
+
+int had_slots_create(int32_t n_slots, const int32_t *free_order, had_slots **out);
+int had_slots_destroy(had_slots *h);
+int had_slots_acquire(had_slots *h, int32_t *slot);   /* refcount = 1 */
+int had_slots_retain(had_slots *h, int32_t slot);     /* HAD_ERR_BAD_SLOT if not held */
+int had_slots_release(had_slots *h, int32_t slot);    /* back to the free list at 0 */
+int had_slots_stats(const had_slots *h, int32_t *n_free, int32_t *n_used);
+
+/* Accept the first `accepted` of T verified draft tokens of seq (its length
+ * includes the T drafts).  KV: truncate to length - T + accepted.  State:
+ * *current_slot = in_slot if accepted == 0 else out_slots[accepted - 1];
+ * every other out slot is released in draft order, then in_slot is released
+ * if accepted > 0 and in_slot >= 0 (in_slot = -1 is the zero state).  All
+ * preconditions (distinct held out slots, in_slot held, 0 <= accepted <= T,
+ * length >= T) are checked first; on error nothing changes.  Rollback is an
+ * index update only: no device memory is touched (24-ai.news, "Mamba State
+ * Update": O(1) pointer update).  out_slots: host int32[T]. */
+int had_spec_rollback(had_kvpt *kv, had_slots *slots, int32_t seq, int32_t T,
+                      int32_t accepted, int32_t in_slot, const int32_t *out_slots,
+                      int32_t *current_slot);
+
+/* ======================================================================
+ * kv_page_table -- device helpers
+ * ====================================================================== */
+typedef struct {
+  int32_t num_pages;  /* pages in each pool                    */
+  int32_t H_kv;       /* KV heads                              */
+  int32_t page_size;  /* tokens per page (P)                   */
+  int32_t head_dim;   /* D                                     */
+} had_kv_layout;
+/* Pools: K and V, bf16 [num_pages][H_kv][page_size][head_dim] each, one
+ * pair per attention layer.  One (page, head) is a contiguous block of
+ * page_size * head_dim * 2 bytes. */
+
+/* Copy whole pages src[i] -> dst[i] (all heads) in both pools, i < n.
+ * src, dst: HOST int32 arrays (ids are checked on the host: HAD_ERR_INVALID_ARG
+ * when out of range or when a dst also appears as a src).  This is the device
+ * half of copy-on-write (the triple from had_kvpt_reserve). */
+int had_kv_copy_pages(const had_kv_layout *L, void *k_pool, void *v_pool,
+                      const int32_t *src, const int32_t *dst, int32_t n, void *stream);
+
+/* Raw append: write t_new tokens per sequence at positions
+ * seq_lens[s] - t_new + j (seq_lens already include them).
+ * k_new, v_new: device bf16 [n_seqs][t_new][H_kv][head_dim];
+ * d_page_table: device int32 [n_seqs][max_pages]; d_seq_lens: device int32. */
+int had_kv_append(const had_kv_layout *L, void *k_pool, void *v_pool,
+                  const int32_t *d_page_table, int32_t max_pages,
+                  const int32_t *d_seq_lens, const void *k_new, const void *v_new,
+                  int32_t n_seqs, int32_t t_new, int32_t *d_err, void *stream);
+
+/* ======================================================================
+ * qk_norm_rope_gate -- fused prologue of a full-attention layer
+ * (zubnet.ai ¶2: QK-RMSNorm + partial RoPE + gate split fused into one
+ * kernel with intermediates in registers).
+ *
+ * For each sequence s, new token j (position pos = seq_lens[s] - T + j) and
+ * head:
+ *   q    = RMSNorm(qg[s][j][hq][0][:]) * w_q,  gate = qg[s][j][hq][1][:]
+ *   k    = RMSNorm(k[s][j][h][:]) * w_k,       v passed through
+ *   RMSNorm(x) = x / sqrt(mean(x^2) + eps)     (fp32)
+ *   then the first rotary_dim dims of q and k are rotated, pairs
+ *   (i, i + rotary_dim/2), angle pos * rope_base^(-2i/rotary_dim) (fp64)
+ *   (RoFormer rotary embedding applied to a prefix of the head).
+ * Writes q_out, gate_out (bf16, round to nearest even) and k, v into the
+ * KV pools at the page slot of pos.
+ * ====================================================================== */
+typedef struct {
+  int32_t n_seqs, T, H_q, H_kv, head_dim, rotary_dim; /* head_dim in {64,128,256}, rotary_dim even, <= head_dim */
+  double rope_base;                                   /* e.g. 10000                                            */
+  float eps;                                          /* e.g. 1e-6                                             */
+  int32_t num_pages, page_size, max_pages;            /* pool pages, tokens per page, page_table row stride    */
+} had_qknrg_desc;
+
+typedef struct {
+  const void *qg;            /* bf16 [n_seqs][T][H_q][2][head_dim]  (q then gate)  */
+  const void *k;             /* bf16 [n_seqs][T][H_kv][head_dim]                   */
+  const void *v;             /* bf16 [n_seqs][T][H_kv][head_dim]                   */
+  const float *w_q, *w_k;    /* fp32 [head_dim]                                    */
+  const int32_t *page_table; /* int32 [n_seqs][max_pages]                          */
+  const int32_t *seq_lens;   /* int32 [n_seqs], lengths including the T new tokens */
+  void *k_pool, *v_pool;     /* bf16 pools (layout above), written                 */
+  void *q_out, *gate_out;    /* bf16 [n_seqs][T][H_q][head_dim], written           */
+  int32_t *d_err;            /* optional device flag word                          */
+} had_qknrg_ptrs;
+
+int had_qk_norm_rope_gate(const had_qknrg_desc *d, const had_qknrg_ptrs *p, void *stream);
+
+/* ======================================================================
+ * decode_attn -- split-K GQA decode attention over the paged KV cache
+ *
+ * For sequence s, query token j < q_len and query head hq (KV head
+ * h = hq / (H_q / H_kv)):  n = seq_lens[s] - q_len + j + 1 keys are visible
+ * (causal inside the draft), and
+ *   out[s][j][hq] = softmax_t(sm_scale * q . K[t]) @ V[t],  t < n,
+ * with K/V read through the page table.  Full-attention layers of the hybrid
+ * model (24-ai.news, model paragraph) at contexts up to 1M tokens
+ * (long-context table).
+ *
+ * Work is split over the context ("split-K"): work unit (s, h, split)
+ * covers pages [split*pps, (split+1)*pps) and writes an unnormalised partial
+ * (o, m, l) to the workspace; a second kernel merges the partials by
+ * log-sum-exp and writes bf16 (round to nearest even).  Query rows per KV
+ * head = q_len * (H_q / H_kv); below 16 rows a VALU kernel runs, at 16 or
+ * more a bf16 MFMA kernel.
+ *
+ * Workspace (caller-allocated device memory, >= had_decode_attn_workspace_bytes):
+ *   ws_o  fp32 [n_seqs][H_kv][num_splits][rows][head_dim]
+ *   ws_ml fp32 [n_seqs][H_kv][num_splits][rows][2]   (m, l)
+ * starting at the workspace base, ws_ml right after ws_o.  Row r = j * G + g
+ * is query j, head h * G + g.  m is in base-2 units: m = max over the split
+ * of sm_scale * log2(e) * q.k; l = sum of 2^(that - m); o = sum of
+ * 2^(that - m) * v.  An empty split has m = -inf, l = 0, o = 0.
+ * ====================================================================== */
+typedef struct {
+  int32_t n_seqs, q_len, H_q, H_kv, head_dim; /* head_dim in {64,128,256}; H_q % H_kv == 0           */
+  int32_t num_pages, page_size, max_pages;    /* pool pages; page_size in {16,32,64}; row stride      */
+  float sm_scale;                             /* usually 1/sqrt(head_dim)                            */
+  int32_t max_seq_len;                        /* host bound on every seq_lens[s]; 0 = max_pages*page_size */
+  int32_t num_splits;                         /* 0 = choose automatically                            */
+} had_attn_desc;
+
+typedef struct {
+  const void *q;             /* bf16 [n_seqs][q_len][H_q][head_dim]         */
+  const void *k_pool, *v_pool;
+  const int32_t *page_table; /* int32 [n_seqs][max_pages]                   */
+  const int32_t *seq_lens;   /* int32 [n_seqs] (include the q_len tokens)   */
+  void *workspace;
+  size_t workspace_bytes;
+  void *out;                 /* bf16 [n_seqs][q_len][H_q][head_dim]         */
+  int32_t *d_err;            /* optional                                    */
+} had_attn_ptrs;
+
+/* Split plan for desc: number of splits and pages per split. */
+int had_decode_attn_plan(const had_attn_desc *d, int32_t *num_splits, int32_t *pages_per_split);
+size_t had_decode_attn_workspace_bytes(const had_attn_desc *d);
+int had_decode_attn(const had_attn_desc *d, const had_attn_ptrs *p, void *stream);
+
+/* The merge step alone (runs inside had_decode_attn): reads num_splits
+ * partials in the workspace layout above and writes out. */
+int had_decode_attn_combine(const had_attn_desc *d, int32_t num_splits,
+                            const void *workspace, void *out, void *stream);
+
+/* ======================================================================
+ * gdn_state_update -- gated delta rule on slot-addressed states
+ *
+ * For sequence s and head h, with S (d_v x d_k) read from
+ * state_pool[in_idx[s]][h] (zero when in_idx[s] == -1), for t < T:
+ *   S <- alpha_t * S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *   o[s][t][h] = q_scale * S q_t,  S written to state_pool[out_idx[s][t]][h]
+ * (Gated DeltaNet layers of the hybrid model, 24-ai.news model paragraph;
+ * recurrence as in Yang, Kautz & Hatamizadeh, ICLR 2025; states addressed by
+ * index, zubnet.ai ¶2 and 24-ai.news "Mamba State Update").  fp32 state and
+ * arithmetic.  With T > 1 every token's state is a checkpoint (speculative
+ * verify); the caller picks the kept one by index (had_spec_rollback).
+ * Preconditions (not checked on device): no slot is written by two
+ * (s, t) pairs, and no slot written by the call is read by another sequence
+ * of the same call.  in_idx[s] == out_idx[s][0] is allowed only when T == 1.
+ * ====================================================================== */
+typedef struct {
+  int32_t n_seqs, T, H, d_k, d_v; /* d_k, d_v in {64, 128}; 1 <= T <= 8 */
+  int32_t n_slots;
+  float q_scale;                  /* 1 for the plain recurrence          */
+} had_gdn_desc;
+
+typedef struct {
+  float *state_pool;         /* fp32 [n_slots][H][d_v][d_k]              */
+  const int32_t *in_idx;     /* int32 [n_seqs]  (-1 = zero state)         */
+  const int32_t *out_idx;    /* int32 [n_seqs][T]                         */
+  const void *q, *k;         /* bf16 [n_seqs][T][H][d_k]                  */
+  const void *v;             /* bf16 [n_seqs][T][H][d_v]                  */
+  const float *alpha, *beta; /* fp32 [n_seqs][T][H]                       */
+  float *o;                  /* fp32 [n_seqs][T][H][d_v], written         */
+  int32_t *d_err;            /* optional                                  */
+} had_gdn_ptrs;
+
+int had_gdn_state_update(const had_gdn_desc *d, const had_gdn_ptrs *p, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HAD_H */

@@ -1,0 +1,145 @@
+"""GPU parity: split-K decode attention through the C ABI vs the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_attention_decode_amd as had
+import synth
+from oracle import attention as A
+from oracle import bf16
+from gpu_util import DEV, assert_attn_close, bits_of, paged_case, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(seed, lens, q_len, H_q, H_kv, D, P, num_splits=0, structured=False, max_seq_len=0):
+    q, kp, vp, pt, L = paged_case(seed, lens, q_len, H_q, H_kv, D, P, structured=structured)
+    print("case seed=%d lens=%s q_len=%d H_q=%d H_kv=%d D=%d P=%d splits=%d" % (seed, list(lens), q_len, H_q, H_kv,
+                                                                               D, P, num_splits), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L), num_splits=num_splits,
+                          max_seq_len=max_seq_len, d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref = A.paged_attention(bits_of(q), bits_of(kp), bits_of(vp), pt, L, P, 1.0 / np.sqrt(D))
+    return out, ref
+
+
+def test_tiny_config():
+    # 512 prior tokens + the decode token, page size 16, shuffled pages, 4 q heads / 1 KV head, D 64
+    out, ref = _run(100, [513], 1, 4, 1, 64, 16)
+    assert_attn_close(out, ref)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("P", [16, 64])
+def test_head_dims_and_page_sizes(D, P):
+    out, ref = _run(200 + D + P, [1, 77, 1000, 4099], 1, 8, 1, D, P)
+    assert_attn_close(out, ref)
+
+
+@pytest.mark.parametrize("G,q_len,H_kv", [(1, 1, 2), (4, 1, 2), (2, 3, 1), (3, 2, 2), (12, 1, 1), (4, 2, 1)])
+def test_row_counts_and_causal_draft(G, q_len, H_kv):
+    out, ref = _run(300 + G * 10 + q_len, [q_len, 190, 3001], q_len, G * H_kv, H_kv, 128, 32)
+    assert_attn_close(out, ref)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 300])
+def test_forced_split_counts_including_empty_splits(splits):
+    out, ref = _run(400 + splits, [2500, 17], 1, 8, 1, 256, 64, num_splits=splits)
+    assert_attn_close(out, ref)
+
+
+def test_structured_values_keep_output_order_one():
+    # V = N(0,1) + per-dim offset, q x 4 (peaky softmax): |o| = O(1) at long context
+    out, ref = _run(500, [50001], 1, 8, 1, 256, 64, structured=True)
+    assert np.abs(ref).max() > 0.2
+    assert_attn_close(out, ref)
+
+
+def test_one_token_context_returns_v_exactly():
+    q, kp, vp, pt, L = paged_case(600, [1, 1], 1, 8, 1, 256, 64)
+    out = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L))
+    torch.cuda.synchronize()
+    for s in range(2):
+        v = vp[pt[s, 0], 0, 0]
+        for hq in range(8):
+            assert torch.equal(out[s, 0, hq].cpu(), v)
+
+
+def test_identical_keys_give_mean_of_values():
+    lens = [700]
+    q, kp, vp, pt, L = paged_case(700, lens, 1, 8, 1, 128, 16)
+    key = synth.normal_bf16((128,), synth.seed_of(700, 99))
+    for p in pt[0][pt[0] >= 0]:
+        kp[p, 0] = key
+    out = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L))
+    torch.cuda.synchronize()
+    from oracle import paging
+    V = bf16.to_f64(paging.gather(bits_of(vp), pt[0], 700, 16))
+    mean = V[:, 0].mean(0)
+    got = bf16.to_f64(bits_of(out))[0, 0]
+    assert np.abs(got - mean[None]).max() <= 1e-2
+
+
+def test_shuffled_and_identity_page_tables_give_identical_bytes():
+    q, kp, vp, pt, L = paged_case(800, [3000], 1, 8, 1, 256, 64, extra_pages=0)
+    n = int(-(-3000 // 64))
+    # identity layout: page i holds logical page i
+    kp2 = kp.clone()
+    vp2 = vp.clone()
+    for i in range(n):
+        kp2[i] = kp[pt[0, i]]
+        vp2[i] = vp[pt[0, i]]
+    pt2 = pt.copy()
+    pt2[0, :n] = np.arange(n)
+    o1 = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L))
+    o2 = had.decode_attn(to_dev(q), to_dev(kp2), to_dev(vp2), to_dev(pt2), to_dev(L))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu(), o2.cpu())
+
+
+def test_out_of_range_page_id_sets_the_sentinel_without_fault():
+    q, kp, vp, pt, L = paged_case(900, [300], 1, 8, 1, 128, 16)
+    pt[0, 3] = kp.shape[0] + 5
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L), d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_PAGE
+    assert torch.isfinite(out.float()).all()
+
+
+def test_combine_alone_against_oracle_partials():
+    rng = np.random.default_rng(5)
+    q_len, H_q, H_kv, D, Lk = 2, 8, 2, 128, 300
+    q = rng.standard_normal((q_len, H_q, D))
+    K = rng.standard_normal((Lk, H_kv, D))
+    V = rng.standard_normal((Lk, H_kv, D))
+    bounds = [(0, 100), (100, 250), (250, 299), (299, 320), (320, 400)]   # last split empty for every query
+    o, m, l = A.split_partials(q, K, V, 0.1, bounds)
+    ref = A.lse_merge(o, m, l)
+    G, rows, ns = H_q // H_kv, q_len * (H_q // H_kv), len(bounds)
+    ws_o = np.zeros((1, H_kv, ns, rows, D), np.float32)
+    ws_ml = np.zeros((1, H_kv, ns, rows, 2), np.float32)
+    for si in range(ns):
+        for j in range(q_len):
+            for hq in range(H_q):
+                h, g = hq // G, hq % G
+                r = j * G + g
+                ws_o[0, h, si, r] = o[si, j, hq]
+                ws_ml[0, h, si, r, 0] = m[si, j, hq] * np.log2(np.e)   # base-2 units
+                ws_ml[0, h, si, r, 1] = l[si, j, hq]
+    ws = to_dev(np.concatenate([ws_o.ravel(), ws_ml.ravel()]))
+    desc = had.attn_desc((1, q_len, H_q, D), (4, H_kv, 16, D), 32)
+    out = torch.empty((1, q_len, H_q, D), dtype=torch.bfloat16, device=DEV)
+    had.decode_attn_combine(desc, ns, ws, out)
+    torch.cuda.synchronize()
+    assert_attn_close(out, ref[None])
+
+
+def test_bad_descriptor_is_rejected():
+    q, kp, vp, pt, L = paged_case(950, [10], 1, 6, 4, 128, 16)
+    with pytest.raises(had.HadError) as e:
+        had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L))
+    assert e.value.kind == "invalid"

@@ -1,0 +1,143 @@
+"""GPU parity: slot-addressed gated delta rule update vs the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_attention_decode_amd as had
+import synth
+from oracle import bf16, gdn
+from gpu_util import DEV, bits_of, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, S, T, H, dk, dv):
+    q = synth.l2_normalised_bf16((S, T, H, dk), synth.seed_of(seed, 1))
+    k = synth.l2_normalised_bf16((S, T, H, dk), synth.seed_of(seed, 2))
+    v = synth.normal_bf16((S, T, H, dv), synth.seed_of(seed, 3))
+    al = synth.uniform_f32((S, T, H), 0.9, 1.0, synth.seed_of(seed, 4))
+    be = synth.uniform_f32((S, T, H), 0.0, 1.0, synth.seed_of(seed, 5))
+    return q, k, v, al, be
+
+
+def _warm_pool(seed, n_slots, H, dk, dv):
+    """Initial states: the fp64 recurrence over 64 seeded warm-up tokens from 0."""
+    pool = np.zeros((n_slots, H, dv, dk), np.float32)
+    for sl in range(n_slots):
+        q, k, v, al, be = _inputs(synth.seed_of(seed, 50, sl), 1, 64, H, dk, dv)
+        for h in range(H):
+            st, _ = gdn.sequential(np.zeros((dv, dk)), bf16.to_f64(bits_of(q)[0, :, h]), bf16.to_f64(bits_of(k)[0, :, h]),
+                                   bf16.to_f64(bits_of(v)[0, :, h]), al.numpy()[0, :, h].astype(np.float64),
+                                   be.numpy()[0, :, h].astype(np.float64))
+            pool[sl, h] = st[-1].astype(np.float32)
+    return pool
+
+
+def _rel_fro(a, b):
+    return np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-30)
+
+
+def _run_and_check(seed, S, T, H, dk, dv, n_slots, in_idx, out_idx):
+    pool = _warm_pool(seed, n_slots, H, dk, dv)
+    q, k, v, al, be = _inputs(seed, S, T, H, dk, dv)
+    print("case seed=%d S=%d T=%d H=%d dk=%d dv=%d in=%s out=%s" % (seed, S, T, H, dk, dv, in_idx, out_idx),
+          flush=True)
+    pd = to_dev(pool)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o = had.gdn_state_update(pd, to_dev(np.asarray(in_idx, np.int32)), to_dev(np.asarray(out_idx, np.int32)),
+                             to_dev(q), to_dev(k), to_dev(v), to_dev(al), to_dev(be), d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    new_ref, o_ref = gdn.state_update(pool, np.asarray(in_idx), np.asarray(out_idx), bf16.to_f64(bits_of(q)),
+                                      bf16.to_f64(bits_of(k)), bf16.to_f64(bits_of(v)), al.numpy().astype(np.float64),
+                                      be.numpy().astype(np.float64))
+    got = pd.cpu().numpy()
+    written = set(np.asarray(out_idx).ravel().tolist())
+    for sl in range(n_slots):
+        if sl in written:
+            for h in range(H):
+                assert _rel_fro(got[sl, h].astype(np.float64), new_ref[sl, h].astype(np.float64)) <= 1e-4
+        else:
+            assert np.array_equal(got[sl], pool[sl])   # untouched slots keep their bytes
+    oc = o.cpu().numpy().astype(np.float64)
+    for s in range(S):
+        for t in range(T):
+            for h in range(H):
+                assert _rel_fro(oc[s, t, h], o_ref[s, t, h]) <= 1e-4
+
+
+def test_tiny_config_single_head():
+    _run_and_check(1, 1, 1, 1, 64, 64, 8, [3], [[6]])
+
+
+def test_agentic_shape_8_heads_128():
+    _run_and_check(2, 1, 1, 8, 128, 128, 4, [1], [[2]])
+
+
+def test_speculative_checkpoints_t4():
+    _run_and_check(3, 1, 4, 8, 128, 128, 8, [5], [[0, 7, 2, 3]])
+
+
+def test_batch_with_shared_input_slot_and_zero_state():
+    # two sequences read the same cached checkpoint (copy-on-write by index),
+    # a third starts from the zero state
+    _run_and_check(4, 3, 1, 2, 128, 64, 10, [4, 4, -1], [[1], [2], [9]])
+
+
+def test_in_place_single_token():
+    _run_and_check(5, 1, 1, 2, 64, 128, 3, [1], [[1]])
+
+
+def test_beta_zero_alpha_one_is_bit_exact_identity():
+    H, dk, dv = 4, 128, 128
+    pool = _warm_pool(6, 2, H, dk, dv)
+    q, k, v, _, _ = _inputs(6, 1, 3, H, dk, dv)
+    pd = to_dev(pool)
+    ones = torch.ones((1, 3, H), dtype=torch.float32)
+    zeros = torch.zeros((1, 3, H), dtype=torch.float32)
+    had.gdn_state_update(pd, to_dev(np.array([0], np.int32)), to_dev(np.array([[1, 1, 1]], np.int32)), to_dev(q),
+                         to_dev(k), to_dev(v), to_dev(ones), to_dev(zeros))
+    torch.cuda.synchronize()
+    assert np.array_equal(pd.cpu().numpy()[1], pool[0])
+
+
+def test_bad_slot_sets_sentinel():
+    H, dk, dv = 1, 64, 64
+    pool = np.zeros((2, H, dv, dk), np.float32)
+    q, k, v, al, be = _inputs(7, 1, 1, H, dk, dv)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pd = to_dev(pool)
+    had.gdn_state_update(pd, to_dev(np.array([5], np.int32)), to_dev(np.array([[9]], np.int32)), to_dev(q), to_dev(k),
+                         to_dev(v), to_dev(al), to_dev(be), d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_SLOT
+    assert np.array_equal(pd.cpu().numpy(), pool)
+
+
+def test_800_token_chain_drift():
+    # free-running 800-step chain on the GPU (ping-pong between two slots)
+    # against the fp64 recurrence: relative error <= 1e-3 at every step
+    H, dk, dv, n = 8, 128, 128, 800
+    pool = _warm_pool(8, 2, H, dk, dv)
+    q, k, v, al, be = _inputs(8, 1, n, H, dk, dv)
+    pd = to_dev(pool)
+    qd, kd, vd, ad, bd = to_dev(q), to_dev(k), to_dev(v), to_dev(al), to_dev(be)
+    hist = torch.empty((n, H, dv, dk), dtype=torch.float32, device=DEV)
+    for t in range(n):
+        src, dst = t % 2, (t + 1) % 2
+        had.gdn_state_update(pd, to_dev(np.array([src], np.int32)), to_dev(np.array([[dst]], np.int32)),
+                             qd[:, t:t + 1].contiguous(), kd[:, t:t + 1].contiguous(), vd[:, t:t + 1].contiguous(),
+                             ad[:, t:t + 1].contiguous(), bd[:, t:t + 1].contiguous())
+        hist[t].copy_(pd[dst])
+    torch.cuda.synchronize()
+    qf, kf, vf = bf16.to_f64(bits_of(q))[0], bf16.to_f64(bits_of(k))[0], bf16.to_f64(bits_of(v))[0]
+    af, bfv = al.numpy()[0].astype(np.float64), be.numpy()[0].astype(np.float64)
+    hh = hist.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for h in range(H):
+        st, _ = gdn.sequential(pool[0, h].astype(np.float64), qf[:, h], kf[:, h], vf[:, h], af[:, h], bfv[:, h])
+        for t in range(n):
+            worst = max(worst, _rel_fro(hh[t, h], st[t]))
+    print("worst relative state error over the chain: %.3g" % worst)
+    assert worst <= 1e-3

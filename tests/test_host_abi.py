@@ -1,0 +1,146 @@
+"""C ABI library: symbols, and the C++ page-table / slot manager against the
+oracle's integer model, bit for bit (CPU only: no GPU compute is called)."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import hybrid_attention_decode_amd as had
+from hybrid_attention_decode_amd import HadError, PageTable, SlotPool
+from oracle import speculative
+from oracle.paging import ModelError, PageTableModel, SlotPoolModel
+import scenario
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "had.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(had_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = had.lib()
+    declared = _declared()
+    assert len(declared) >= 25
+    for name in declared:
+        assert hasattr(L, name), name
+    assert declared == had.exported_symbols()
+    assert had.abi_version() == 1
+
+
+def test_scenario_on_the_cpp_manager():
+    cfg, order, ops = scenario.load("page_table_scenario.txt")
+    pt = PageTable(*cfg, free_order=order)
+    scenario.run(pt, ops, HadError)
+
+
+def _call(obj, name, *args):
+    try:
+        return ("ok", getattr(obj, name)(*args))
+    except (HadError, ModelError) as e:
+        return ("err", e.kind)
+
+
+def test_fuzz_cpp_manager_matches_model_bit_exact():
+    rng = np.random.default_rng(11)
+    for trial in range(12):
+        P = int(rng.choice([1, 4, 16, 64]))
+        N = int(rng.integers(8, 80))
+        max_seqs = int(rng.integers(2, 8))
+        max_pages = int(rng.integers(2, 16))
+        order = rng.permutation(N)
+        m = PageTableModel(N, P, max_seqs, max_pages, free_order=list(order))
+        c = PageTable(N, P, max_seqs, max_pages, free_order=order)
+        for step in range(400):
+            op = int(rng.integers(0, 7))
+            sid = int(rng.integers(-1, max_seqs + 1))
+            n = int(rng.integers(0, 3 * P + 2))
+            if op == 0:
+                a, b = _call(m, "seq_create"), _call(c, "seq_create")
+            elif op == 1:
+                a, b = _call(m, "seq_fork", sid, n), _call(c, "seq_fork", sid, n)
+            elif op in (2, 3):
+                a, b = _call(m, "reserve", sid, n), _call(c, "reserve", sid, n)
+            elif op == 4:
+                L = m.seqs[sid]["len"] if sid in m.seqs else 0
+                k = int(rng.integers(0, L + 2))
+                a, b = _call(m, "truncate", sid, k), _call(c, "truncate", sid, k)
+            elif op == 5:
+                a, b = _call(m, "seq_free", sid), _call(c, "seq_free", sid)
+            else:
+                a, b = _call(m, "stats"), _call(c, "stats")
+            assert a == b, (trial, step, op, a, b)
+            live = sorted(m.seqs)
+            pm, lm = m.export(live, max_pages)
+            pc, lc = c.export(live, max_pages)
+            assert np.array_equal(pm, pc) and np.array_equal(lm, lc)
+            assert m.stats() == c.stats()
+
+
+def test_fuzz_slots_and_rollback_match_model():
+    rng = np.random.default_rng(12)
+    for trial in range(10):
+        n_slots = 16
+        order = rng.permutation(n_slots)
+        ms, cs = SlotPoolModel(n_slots, list(order)), SlotPool(n_slots, order)
+        mp, cp = PageTableModel(64, 4, 4, 32, list(range(64))), PageTable(64, 4, 4, 32)
+        sm, sc = mp.seq_create(), cp.seq_create()
+        assert sm == sc
+        mp.reserve(sm, 9)
+        cp.reserve(sc, 9)
+        for step in range(200):
+            op = int(rng.integers(0, 4))
+            if op == 0:
+                a, b = _call(ms, "acquire"), _call(cs, "acquire")
+            elif op == 1:
+                x = int(rng.integers(-1, n_slots + 1))
+                a, b = _call(ms, "retain", x), _call(cs, "retain", x)
+            elif op == 2:
+                x = int(rng.integers(-1, n_slots + 1))
+                a, b = _call(ms, "release", x), _call(cs, "release", x)
+            else:
+                T = int(rng.integers(1, 5))
+                acc = int(rng.integers(0, T + 2))
+                held = [s for s in range(n_slots) if ms.ref[s] > 0]
+                if len(held) < T + 1:
+                    continue
+                pick = list(rng.choice(held, T + 1, replace=False))
+                in_slot = int(pick[0]) if rng.random() < 0.8 else -1
+                outs = [int(x) for x in pick[1:]]
+                if rng.random() < 0.1:
+                    outs[0] = outs[-1]  # invalid: repeated
+                mp.reserve(sm, T)
+                cp.reserve(sc, T)
+                try:
+                    a = ("ok", speculative.rollback(mp, ms, sm, T, acc, in_slot, outs))
+                except ModelError as e:
+                    a = ("err", e.kind)
+                try:
+                    b = ("ok", had.spec_rollback(cp, cs, sc, T, acc, in_slot, outs))
+                except HadError as e:
+                    b = ("err", e.kind)
+            assert a == b, (trial, step, a, b)
+            assert ms.stats() == cs.stats()
+            assert mp.export([sm], 32)[0].tolist() == cp.export([sc], 32)[0].tolist()
+            assert mp.export([sm], 32)[1].tolist() == cp.export([sc], 32)[1].tolist()
+
+
+def test_error_paths_leave_handles_unchanged():
+    pt = PageTable(4, 4, 2, 2)
+    s = pt.seq_create()
+    pt.reserve(s, 5)
+    before = (pt.export([s], 2), pt.stats())
+    for bad in (lambda: pt.reserve(s, 4), lambda: pt.truncate(s, 6), lambda: pt.seq_fork(s, 9),
+                lambda: pt.reserve(9, 1), lambda: pt.export([s], 1)):
+        with pytest.raises(HadError):
+            bad()
+    after = (pt.export([s], 2), pt.stats())
+    assert np.array_equal(before[0][0], after[0][0]) and before[1] == after[1]
+    with pytest.raises(HadError) as e:
+        PageTable(4, 4, 2, 2, free_order=[0, 1, 1, 3])
+    assert e.value.kind == "invalid"
+    assert "free_order" in str(e.value)
