@@ -1,0 +1,426 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the hybrid-attention decode path on one MI355X.
+
+Workload (long-context sweep): one sequence decoding at contexts 128K, 256K
+and 1M tokens through a 48-layer hybrid stack -- 12 full-attention layers
+(8 query heads / 1 KV head, head_dim 256, partial RoPE on 64 dims, bf16 KV in
+64-token pages drawn from a randomly permuted pool) and 36 Gated DeltaNet
+layers (8 heads, d_k = d_v = 128, fp32 state), layers 4i..4i+2 GDN and 4i+3
+attention.  Synthetic seeded inputs; values do not affect timing.
+
+One step = one decode token through the whole stack:
+  host   C++ page-table reserve of the new token (+ pinned async H2D of the
+         length and, on a page boundary, of the new page-table entry)
+  device replay of a captured HIP graph of the 48 layers:
+         GDN layer       had_gdn_state_update  (slot ping-pong by index)
+         attention layer had_qk_norm_rope_gate -> had_decode_attn
+                         (split-K partial + combine)
+
+Prints one JSON line (stdout).  Progress goes to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s + achieved HBM GB/s (% of peak) at 128K/256K/1M ctx, 1 GPU"
+PEAK_HBM_GBPS = 8000.0
+P, H_Q, H_KV, D, R = 64, 8, 1, 256, 64
+N_ATTN, N_GDN = 12, 36
+GDN_H, DK, DV = 8, 128, 128
+KV_BYTES_PER_TOKEN = 2 * H_KV * D * 2          # K and V rows, bf16
+GDN_BYTES_PER_LAYER = 2 * GDN_H * DK * DV * 4  # state read + write, fp32
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_valu_d256_longctx_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "hybrid_attention_decode_amd", "csrc", "kernels", "attn_valu.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_step(L):
+    return N_ATTN * L * KV_BYTES_PER_TOKEN + N_GDN * GDN_BYTES_PER_LAYER
+
+
+class LongContextStack:
+    """Device state of the 48-layer stack for one sequence at context L0."""
+
+    def __init__(self, L0, n_tokens, seed=0):
+        import torch
+
+        import hybrid_attention_decode_amd as had
+        import synth
+
+        self.torch, self.had = torch, had
+        dev = "cuda"
+        self.L0 = L0
+        self.total = L0 + n_tokens
+        self.max_pages = -(-self.total // P) + 1
+        self.num_pages = self.max_pages + 4
+        order = synth.permutation(self.num_pages, synth.seed_of(seed, 1))
+        self.pt = had.PageTable(self.num_pages, P, 1, self.max_pages, free_order=order)
+        self.seq = self.pt.seq_create()
+        self.pt.reserve(self.seq, L0)
+        table, lens = self.pt.export([self.seq], self.max_pages)
+        self.pt_dev = torch.from_numpy(table).to(dev)
+        self.lens_dev = torch.from_numpy(lens).to(dev)
+        self.len = L0
+        # pinned staging, one entry per step so no buffer is rewritten while a copy is pending
+        self.lens_pin = torch.empty(n_tokens + 1, dtype=torch.int32, pin_memory=True)
+        self.page_pin = torch.empty(n_tokens + 1, dtype=torch.int32, pin_memory=True)
+
+        g = torch.Generator(device=dev)
+        self.attn = []
+        for i in range(N_ATTN):
+            g.manual_seed(synth.seed_of(seed, 100, i))
+            lay = dict(
+                k_pool=torch.randn((self.num_pages, H_KV, P, D), generator=g, device=dev, dtype=torch.bfloat16),
+                v_pool=torch.randn((self.num_pages, H_KV, P, D), generator=g, device=dev, dtype=torch.bfloat16),
+                qg=torch.randn((1, 1, H_Q, 2, D), generator=g, device=dev, dtype=torch.bfloat16),
+                k=torch.randn((1, 1, H_KV, D), generator=g, device=dev, dtype=torch.bfloat16),
+                v=torch.randn((1, 1, H_KV, D), generator=g, device=dev, dtype=torch.bfloat16),
+                w_q=torch.rand((D,), generator=g, device=dev) + 0.5,
+                w_k=torch.rand((D,), generator=g, device=dev) + 0.5,
+                q_out=torch.empty((1, 1, H_Q, D), device=dev, dtype=torch.bfloat16),
+                gate=torch.empty((1, 1, H_Q, D), device=dev, dtype=torch.bfloat16),
+                out=torch.empty((1, 1, H_Q, D), device=dev, dtype=torch.bfloat16),
+            )
+            self.attn.append(lay)
+        self.desc = had.attn_desc((1, 1, H_Q, D), (self.num_pages, H_KV, P, D), self.max_pages,
+                                  max_seq_len=self.total)
+        self.n_splits, self.pps = had.decode_attn_plan(self.desc)
+        self.ws = torch.empty(had.decode_attn_workspace_bytes(self.desc), dtype=torch.uint8, device=dev)
+        self.gdn = []
+        for i in range(N_GDN):
+            g.manual_seed(synth.seed_of(seed, 200, i))
+            q = torch.randn((1, 1, GDN_H, DK), generator=g, device=dev, dtype=torch.float64)
+            k = torch.randn((1, 1, GDN_H, DK), generator=g, device=dev, dtype=torch.float64)
+            lay = dict(
+                pool=torch.randn((2, GDN_H, DV, DK), generator=g, device=dev) * 0.05,
+                q=(q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
+                k=(k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
+                v=torch.randn((1, 1, GDN_H, DV), generator=g, device=dev, dtype=torch.bfloat16),
+                alpha=torch.rand((1, 1, GDN_H), generator=g, device=dev) * 0.1 + 0.9,
+                beta=torch.rand((1, 1, GDN_H), generator=g, device=dev),
+                o=torch.empty((1, 1, GDN_H, DV), device=dev),
+            )
+            self.gdn.append(lay)
+        # slot ping-pong by index: even steps read slot 0 and write slot 1, odd steps the reverse
+        self.in_idx = [torch.tensor([0], dtype=torch.int32, device=dev), torch.tensor([1], dtype=torch.int32, device=dev)]
+        self.out_idx = [torch.tensor([[1]], dtype=torch.int32, device=dev), torch.tensor([[0]], dtype=torch.int32, device=dev)]
+        self.graphs = None
+
+    # --- the per-layer calls ---------------------------------------------------
+    def attn_layer(self, i):
+        a = self.attn[i]
+        self.had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
+                                   a["k_pool"], a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
+        self.had.decode_attn(a["q_out"], a["k_pool"], a["v_pool"], self.pt_dev, self.lens_dev,
+                             max_seq_len=self.total, workspace=self.ws, out=a["out"])
+
+    def gdn_layer(self, i, parity):
+        g = self.gdn[i]
+        self.had.gdn_state_update(g["pool"], self.in_idx[parity], self.out_idx[parity], g["q"], g["k"], g["v"],
+                                  g["alpha"], g["beta"], o=g["o"])
+
+    def layers(self, parity):
+        ia = ig = 0
+        for l in range(N_ATTN + N_GDN):
+            if l % 4 == 3:
+                self.attn_layer(ia)
+                ia += 1
+            else:
+                self.gdn_layer(ig, parity)
+                ig += 1
+
+    def capture(self):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.layers(0)
+            self.layers(1)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graphs = []
+        for par in (0, 1):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                self.layers(par)
+            self.graphs.append(gr)
+        torch.cuda.synchronize()
+
+    # --- one decode step ---------------------------------------------------------
+    def step(self, t):
+        cow = self.pt.reserve(self.seq, 1)            # host: C++ page-table manager
+        assert cow is None                            # one unshared sequence: never copies
+        self.len += 1
+        pos = self.len - 1
+        if pos % P == 0:                              # a new page was allocated for this token
+            table, _ = self.pt.export([self.seq], self.max_pages)
+            self.page_pin[t] = int(table[0, pos // P])
+            self.pt_dev[0, pos // P].copy_(self.page_pin[t], non_blocking=True)
+        self.lens_pin[t] = self.len
+        self.lens_dev.copy_(self.lens_pin[t:t + 1], non_blocking=True)
+        self.graphs[t % 2].replay()
+
+
+def time_graph(torch, fn, reps):
+    """Average duration of one call of fn, from a captured batch of `reps` calls."""
+    gr = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        for r in range(reps):
+            fn(r)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps  # microseconds
+
+
+def run_context(L0, steps, warmup, kernel_reps, seed=0):
+    import torch
+
+    import hybrid_attention_decode_amd as had
+
+    t0 = time.time()
+    st = LongContextStack(L0, steps + warmup + 2, seed)
+    st.capture()
+    log("ctx %d: setup %.1fs (splits=%d, pages/split=%d)" % (L0, time.time() - t0, st.n_splits, st.pps))
+    for t in range(warmup):
+        st.step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    len_start = st.len
+    e0.record()
+    for t in range(warmup, warmup + steps):
+        st.step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the same 48-layer graph replayed back to back without the host-side
+    # bookkeeping and copies (device time of a step)
+    e0.record()
+    for t in range(steps):
+        st.graphs[t % 2].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    mean_len = len_start + (steps + 1) / 2.0
+    step_bytes = algorithmic_bytes_per_step(mean_len)
+    log("ctx %d: %.4f ms/step, %.1f steps/s" % (L0, ms, 1e3 / ms))
+
+    # per kernel class, captured back-to-back batches rotating over the layers
+    L = st.len
+    ws = st.ws
+    n = max(1, kernel_reps)
+
+    def partial(r):
+        a = st.attn[r % N_ATTN]
+        had.decode_attn_partial(a["q_out"], a["k_pool"], a["v_pool"], st.pt_dev, st.lens_dev, ws,
+                                max_seq_len=st.total)
+
+    def combine(r):
+        had.decode_attn_combine(st.desc, st.n_splits, ws, st.attn[r % N_ATTN]["out"])
+
+    def prologue(r):
+        a = st.attn[r % N_ATTN]
+        had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], st.pt_dev, st.lens_dev, a["k_pool"],
+                              a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
+
+    def gdn(r):
+        st.gdn_layer(r % N_GDN, r % 2)
+
+    us = {
+        "attn_partial": time_graph(torch, partial, n * N_ATTN),
+        "attn_combine": time_graph(torch, combine, n * N_ATTN),
+        "prologue": time_graph(torch, prologue, n * N_ATTN),
+        "gdn_update": time_graph(torch, gdn, max(2, n) * N_GDN),
+    }
+    attn_bytes = L * KV_BYTES_PER_TOKEN
+    res = dict(
+        context=L0, steps=steps, warmup=warmup, ms_per_step=ms, steps_per_s=1e3 / ms, graph_only_ms_per_step=graph_ms,
+        mean_context_timed=mean_len, algorithmic_bytes_per_step=step_bytes,
+        hbm_gbps=step_bytes / (ms * 1e-3) / 1e9, hbm_frac=step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        us_per_layer={k: round(v, 3) for k, v in us.items()},
+        attn_us_per_layer=round(us["attn_partial"] + us["attn_combine"] + us["prologue"], 3),
+        attn_partial_gbps=attn_bytes / (us["attn_partial"] * 1e-6) / 1e9,
+        attn_partial_bytes_per_launch=attn_bytes, attn_partial_context=L,
+        num_splits=st.n_splits, pages_per_split=st.pps,
+    )
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_calibration(nbytes=1 << 30):
+    """A plain device copy of known size, for scaling the PMC byte counters."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: %d bytes read, %d bytes written" % (nbytes, nbytes))
+
+
+def roofline(res):
+    r = dict(bound="hbm", achieved=round(res["attn_partial_gbps"], 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+             frac=round(res["attn_partial_gbps"] / PEAK_HBM_GBPS, 4), traffic=None,
+             kernel="attn_valu_kernel<256>", bytes_per_launch=res["attn_partial_bytes_per_launch"],
+             context=res["attn_partial_context"])
+    try:
+        with open(PMC_SUMMARY) as f:
+            pmc = json.load(f)
+        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if pmc.get("kernel_source_sha256") == src_hash and pmc.get("context") == res["context"]:
+            r["traffic"] = pmc.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return r
+
+
+def cpu_baseline(L0, min_seconds=10.0, max_blocks=1000, seed=0):
+    """The fp64 oracle timed on one block of the stack (1 prologue + 1 attention
+    layer + 3 GDN layers) at context L0, repeated for >= min_seconds; scaled x12
+    to a full 48-layer step."""
+    import torch
+
+    import synth
+    from oracle import attention as A
+    from oracle import bf16, gdn
+    from oracle import prologue as Pr
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas = 1
+    rng = np.random.default_rng(seed)
+    n_pages = -(-(L0 + 1) // P)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.seed_of(seed, 900))
+    kp = torch.randn((n_pages, H_KV, P, D), generator=g, device="cuda", dtype=torch.bfloat16)
+    vp = torch.randn((n_pages, H_KV, P, D), generator=g, device="cuda", dtype=torch.bfloat16)
+    kb, vb = synth.bits(kp), synth.bits(vp)
+    table = rng.permutation(n_pages).astype(np.int32)[None]
+    lens = np.array([L0 + 1], np.int32)
+    qg = rng.standard_normal((1, H_Q, 2, D))
+    kn, vn = rng.standard_normal((1, H_KV, D)), rng.standard_normal((1, H_KV, D))
+    w = rng.random(D) + 0.5
+    pool = (rng.standard_normal((2, GDN_H, DV, DK)) * 0.05).astype(np.float32)
+    gq = rng.standard_normal((1, 1, GDN_H, DK))
+    gk = rng.standard_normal((1, 1, GDN_H, DK))
+    gk /= np.linalg.norm(gk, axis=-1, keepdims=True)
+    gv = rng.standard_normal((1, 1, GDN_H, DV))
+    ga, gb = rng.uniform(0.9, 1, (1, 1, GDN_H)), rng.uniform(0, 1, (1, 1, GDN_H))
+    qb = bf16.from_f64(rng.standard_normal((1, 1, H_Q, D)))
+    blocks = 0
+    t0 = time.perf_counter()
+    while blocks < max_blocks:
+        Pr.qk_norm_rope_gate(qg, kn, vn, w, w, np.array([L0]), R)
+        A.paged_attention(qb, kb, vb, table, lens, P, 1 / 16.0)
+        for _ in range(3):
+            gdn.state_update(pool, np.array([0]), np.array([[1]]), gq, gk, gv, ga, gb)
+        blocks += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    per_step = el / blocks * (N_ATTN + N_GDN) / 4
+    return dict(value=round(1.0 / per_step, 6), unit="steps/s", cores=int(blas), kind="oracle",
+                sample="%d block(s) of 1 prologue + 1 attention layer (ctx %d) + 3 GDN layers in %.1f s, "
+                       "scaled x12 to the 48-layer step" % (blocks, L0 + 1, el))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ctx", type=int, default=131072, help="context of the headline value")
+    ap.add_argument("--sweep", default="262144,1048576", help="further contexts measured in the same run")
+    ap.add_argument("--kernel-reps", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (scales PMC byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the multi-GPU split of this path is a design note, not a code path)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import hybrid_attention_decode_amd as had
+
+    had.lib()
+    if args.copy_calibration:
+        copy_calibration()
+    head = run_context(args.ctx, args.steps, args.warmup, args.kernel_reps)
+    sweep = []
+    for c in [int(x) for x in args.sweep.split(",") if x.strip()]:
+        sweep.append(run_context(c, args.steps, args.warmup, args.kernel_reps))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host ...")
+        cpu = cpu_baseline(args.ctx, args.cpu_seconds)
+        log("oracle: %s" % cpu)
+    out = {
+        "metric": METRIC,
+        "value": round(head["steps_per_s"], 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "long-context decode: 1 sequence, %d-token context, %d decode steps timed, 48-layer hybrid "
+                        "stack (12 full-attention: 8 q / 1 KV heads, head_dim 256, partial RoPE 64, bf16 KV in "
+                        "64-token permuted pages; 36 Gated DeltaNet: 8 heads, 128x128 fp32 state)"
+                        % (args.ctx, args.steps),
+            "context": args.ctx,
+            "parallelism": "none (1 GPU, one GPU's head share)",
+        },
+        "hbm_gbps": round(head["hbm_gbps"], 1),
+        "hbm_frac_of_peak": round(head["hbm_frac"], 4),
+        "us_per_layer": head["us_per_layer"],
+        "graph_only_ms_per_step": round(head["graph_only_ms_per_step"], 5),
+        "num_splits": head["num_splits"],
+        "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
+        "roofline": roofline(head),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

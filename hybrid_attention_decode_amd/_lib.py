@@ -107,6 +107,7 @@ _SIGS = {
     "had_decode_attn_plan": ([ctypes.POINTER(AttnDesc), _pi32, _pi32], ctypes.c_int),
     "had_decode_attn_workspace_bytes": ([ctypes.POINTER(AttnDesc)], ctypes.c_size_t),
     "had_decode_attn": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
+    "had_decode_attn_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
     "had_decode_attn_combine": ([ctypes.POINTER(AttnDesc), _i32, _p, _p, _p], ctypes.c_int),
     "had_gdn_state_update": ([ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnPtrs), _p], ctypes.c_int),
 }
@@ -375,6 +376,20 @@ def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_
                     workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"))
     _check(lib().had_decode_attn(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
     return out
+
+
+def decode_attn_partial(q, k_pool, v_pool, page_table, seq_lens, workspace, sm_scale=None, max_seq_len=0,
+                        num_splits=0, d_err=None):
+    """Split-K partial kernel only: writes (o, m, l) partials to ``workspace``.
+    Returns the descriptor (for decode_attn_combine)."""
+    torch = _torch()
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits)
+    ptrs = AttnPtrs(_dev(q, torch.bfloat16, "q"), _dev(k_pool, torch.bfloat16, "k_pool"),
+                    _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
+                    _dev(seq_lens, torch.int32, "seq_lens"), _dev(workspace, torch.uint8, "workspace"),
+                    workspace.numel(), None, _opt(d_err, "d_err"))
+    _check(lib().had_decode_attn_partial(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
+    return desc
 
 
 def decode_attn_combine(desc, num_splits, workspace, out):

@@ -16,8 +16,8 @@ using had::fail;
 
 namespace {
 
-constexpr int kTargetUnits = 512;  // two 4-wave workgroups per CU on 256 CUs
-constexpr int kMinTilesPerUnit = 16;
+constexpr int kTargetUnits = 256;     // one 8-wave workgroup per CU on 256 CUs
+constexpr int kMinTilesPerUnit = 32;  // at least 4 tiles of 8 tokens per wave
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -45,29 +45,32 @@ int check_desc(const had_attn_desc* d) {
   return HAD_OK;
 }
 
-int plan(const had_attn_desc* d, int* ns_out, int* pps_out) {
+// Split plan over the pages a sequence can reach (max_seq_len, a host bound,
+// so the plan does not depend on device data).  Split i owns pages
+// [i*n/ns, (i+1)*n/ns): balanced to within one page.
+int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   const int64_t max_len = d->max_seq_len > 0 ? d->max_seq_len : static_cast<int64_t>(d->max_pages) * d->page_size;
   const int64_t n_pages = std::max<int64_t>(1, ceil_div(max_len, d->page_size));
-  int64_t pps;
+  int64_t ns;
   if (d->num_splits > 0) {
-    pps = ceil_div(n_pages, d->num_splits);
+    ns = d->num_splits;
   } else {
     const int64_t units = static_cast<int64_t>(d->n_seqs) * d->H_kv;
     const int64_t want = std::max<int64_t>(1, ceil_div(kTargetUnits, units));
     const int64_t min_pps = ceil_div(kMinTilesPerUnit, d->page_size / 8);
-    pps = std::max<int64_t>(min_pps, ceil_div(n_pages, want));
+    ns = std::max<int64_t>(1, std::min<int64_t>(want, n_pages / min_pps));
+    ns = std::max<int64_t>(ns, ceil_div(n_pages, had::kMaxPagesPerSplit));
   }
-  pps = std::max<int64_t>(pps, ceil_div(n_pages, 1 << 20));
-  if (pps > had::kMaxPagesPerSplit) {
-    if (d->num_splits > 0)
-      return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %d splits leave %lld pages per split (max %d)",
-                  d->num_splits, static_cast<long long>(pps), had::kMaxPagesPerSplit);
-    pps = had::kMaxPagesPerSplit;
-  }
-  pps = std::min<int64_t>(pps, n_pages);
-  const int64_t ns = d->num_splits > 0 ? d->num_splits : ceil_div(n_pages, pps);
+  const int64_t pps = ceil_div(n_pages, ns);
+  if (pps > had::kMaxPagesPerSplit)
+    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %lld splits leave %lld pages per split (max %d)",
+                static_cast<long long>(ns), static_cast<long long>(pps), had::kMaxPagesPerSplit);
+  if (ns > had::kMaxSplits)
+    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %lld splits (max %d)", static_cast<long long>(ns),
+                had::kMaxSplits);
   *ns_out = static_cast<int>(ns);
   *pps_out = static_cast<int>(pps);
+  if (n_pages_out) *n_pages_out = static_cast<int>(n_pages);
   return HAD_OK;
 }
 
@@ -85,7 +88,7 @@ int had_decode_attn_plan(const had_attn_desc* d, int32_t* num_splits, int32_t* p
   int st = check_desc(d);
   if (st != HAD_OK) return st;
   int ns, pps;
-  st = plan(d, &ns, &pps);
+  st = plan(d, &ns, &pps, nullptr);
   if (st != HAD_OK) return st;
   *num_splits = ns;
   *pages_per_split = pps;
@@ -95,19 +98,19 @@ int had_decode_attn_plan(const had_attn_desc* d, int32_t* num_splits, int32_t* p
 size_t had_decode_attn_workspace_bytes(const had_attn_desc* d) {
   if (check_desc(d) != HAD_OK) return 0;
   int ns, pps;
-  if (plan(d, &ns, &pps) != HAD_OK) return 0;
+  if (plan(d, &ns, &pps, nullptr) != HAD_OK) return 0;
   return ws_bytes(d, ns);
 }
 
-int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream) {
+static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* stream, had::ValuArgs* out_args) {
   int st = check_desc(d);
   if (st != HAD_OK) return st;
-  if (!p || !p->q || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace || !p->out)
+  if (!p || !p->q || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn: NULL pointer in ptrs");
   if (!aligned16(p->q) || !aligned16(p->k_pool) || !aligned16(p->v_pool) || !aligned16(p->workspace))
     return fail(HAD_ERR_INVALID_ARG, "decode_attn: q, pools and workspace must be 16-byte aligned");
-  int ns, pps;
-  st = plan(d, &ns, &pps);
+  int ns, pps, n_plan;
+  st = plan(d, &ns, &pps, &n_plan);
   if (st != HAD_OK) return st;
   const size_t need = ws_bytes(d, ns);
   if (p->workspace_bytes < need)
@@ -135,6 +138,7 @@ int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream
   a.max_pages = d->max_pages;
   a.num_splits = ns;
   a.pps = pps;
+  a.n_pages_plan = n_plan;
   a.scale_log2 = d->sm_scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -150,19 +154,32 @@ int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream
     }
   }
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn: partial kernel launch: %s", hipGetErrorString(e));
+  if (out_args) *out_args = a;
+  return HAD_OK;
+}
 
+int had_decode_attn_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* stream) {
+  const int st = launch_partial(d, p, stream, nullptr);
+  return st == HAD_OK ? had::ok() : st;
+}
+
+int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream) {
+  if (p && !p->out) return fail(HAD_ERR_INVALID_ARG, "decode_attn: out is NULL");
+  had::ValuArgs a{};
+  int st = launch_partial(d, p, stream, &a);
+  if (st != HAD_OK) return st;
   had::CombineArgs c{};
   c.ws_o = a.ws_o;
   c.ws_ml = a.ws_ml;
   c.out = static_cast<uint16_t*>(p->out);
-  c.n_seqs = d->n_seqs;
-  c.q_len = d->q_len;
-  c.H_q = d->H_q;
-  c.H_kv = d->H_kv;
-  c.G = G;
-  c.rows = rows;
-  c.num_splits = ns;
-  e = had::launch_attn_combine(c, d->head_dim, s);
+  c.n_seqs = a.n_seqs;
+  c.q_len = a.q_len;
+  c.H_q = a.H_q;
+  c.H_kv = a.H_kv;
+  c.G = a.G;
+  c.rows = a.rows;
+  c.num_splits = a.num_splits;
+  const hipError_t e = had::launch_attn_combine(c, d->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn: combine launch: %s", hipGetErrorString(e));
   return had::ok();
 }
@@ -171,8 +188,9 @@ int had_decode_attn_combine(const had_attn_desc* d, int32_t num_splits, const vo
                             void* stream) {
   int st = check_desc(d);
   if (st != HAD_OK) return st;
-  if (!workspace || !out || num_splits < 1)
-    return fail(HAD_ERR_INVALID_ARG, "decode_attn_combine: bad argument (num_splits=%d)", num_splits);
+  if (!workspace || !out || num_splits < 1 || num_splits > had::kMaxSplits)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_combine: bad argument (num_splits=%d, max %d)", num_splits,
+                had::kMaxSplits);
   const int G = d->H_q / d->H_kv;
   const int rows = d->q_len * G;
   had::CombineArgs c{};

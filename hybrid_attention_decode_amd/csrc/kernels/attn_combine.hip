@@ -5,13 +5,14 @@
 //   M = max_i m_i,  w_i = 2^(m_i - M),  out = sum_i w_i o_i / sum_i w_i l_i,
 // rounded to bf16 (nearest even).  Splits with m = -inf carry weight 0; a
 // row with no visible key at all (sum of weights 0) is written as zeros.
-// This is the log-sum-exp merge that makes the split over the context exact
-// up to rounding (the split-K step of the decode path; long contexts up to
-// 1M tokens, 24-ai.news long-context table).
+// This log-sum-exp merge makes the split over the context exact up to
+// rounding (long contexts up to 1M tokens, 24-ai.news long-context table).
 //
-// One 64-lane wave per (row, 64-wide slice of head_dim): lanes read the
-// split maxima 64 at a time, then stream the partials with one coalesced
-// 256-byte row per split.
+// The merge reads every partial once (rows x splits x head_dim fp32) and is
+// bound by memory latency, not bandwidth: one 8-wave block per row issues
+// all of its partial loads (float4 per lane, up to 256 splits per pass)
+// before it touches any of them, reads the maxima in the same round trip,
+// and reduces across waves through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,69 +22,112 @@
 namespace had {
 namespace {
 
-__global__ __launch_bounds__(64) void attn_combine_kernel(CombineArgs a, int D) {
-  __shared__ float wsh[64];
-  const int lane = threadIdx.x;
-  const int dblk = blockIdx.x;        // 64-wide slice of head_dim
-  const int row = blockIdx.y;         // j * G + g
-  const int sh_ = blockIdx.z;         // s * H_kv + h
-  const int s = sh_ / a.H_kv, h = sh_ % a.H_kv;
+constexpr int kWaves = 8;
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_combine_kernel(CombineArgs a) {
+  constexpr int LS = D / 4;          // lanes per split row (float4 each)
+  constexpr int SPW = 64 / LS;       // split rows per wave per load
+  constexpr int U = 32 / SPW;        // loads per lane per pass
+  constexpr int PASS = kWaves * SPW * U;  // splits per pass (256)
+  __shared__ float wsh[PASS];
+  __shared__ float4 red[kWaves][LS];
+  __shared__ float scal[kWaves];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane / LS, dl = lane % LS;
+  const int row = blockIdx.x;
+  const int unit = blockIdx.y;  // s * H_kv + h
   const int ns = a.num_splits;
-  const size_t unit0 = static_cast<size_t>(sh_) * ns;
+  const size_t base = static_cast<size_t>(unit) * ns;
   const float* ml = a.ws_ml;
-  const int d = dblk * 64 + lane;
+  const size_t ostride = static_cast<size_t>(a.rows) * D;  // floats between consecutive splits
+  const float4* o4 = reinterpret_cast<const float4*>(a.ws_o + (base * a.rows + row) * D);
 
-  // pass 1: row maximum over the splits
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float M = -INFINITY;
-  for (int i = lane; i < ns; i += 64) M = fmaxf(M, ml[((unit0 + i) * a.rows + row) * 2]);
+  float lsum = 0.f;
+  for (int p0 = 0; p0 < ns; p0 += PASS) {
+    // issue every load of this pass first
+    float4 ov[U];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor_f(M, off));
-  const float Ms = (M == -INFINITY) ? 0.f : M;
-
-  // pass 2: weighted sums, 64 splits at a time (weights via LDS broadcast)
-  float acc = 0.f, lsum = 0.f;
-  for (int i0 = 0; i0 < ns; i0 += 64) {
-    const int i = i0 + lane;
-    float w = 0.f;
-    if (i < ns) {
-      const float mi = ml[((unit0 + i) * a.rows + row) * 2];
-      w = (mi == -INFINITY) ? 0.f : exp2f(mi - Ms);
-      lsum += w * ml[((unit0 + i) * a.rows + row) * 2 + 1];
+    for (int u = 0; u < U; ++u) {
+      const int i = p0 + (u * kWaves + wave) * SPW + sub;
+      ov[u] = (i < ns) ? o4[i * (ostride / 4) + dl] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mi = -INFINITY, li = 0.f;
+    const int my = p0 + tid;  // this thread's split for the maxima (PASS <= blockDim)
+    if (tid < PASS && my < ns) {
+      mi = ml[((base + my) * a.rows + row) * 2];
+      li = ml[((base + my) * a.rows + row) * 2 + 1];
+    }
+    // block maximum of this pass, merged into the running maximum
+    float mw = mi;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mw = fmaxf(mw, shfl_xor_f(mw, off));
+    if (lane == 0) scal[wave] = mw;
+    __syncthreads();
+    float mp = scal[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mp = fmaxf(mp, scal[w]);
+    const float M_new = fmaxf(M, mp);
+    const float Ms = (M_new == -INFINITY) ? 0.f : M_new;
+    const float rescale = (M == -INFINITY) ? 0.f : exp2f(M - Ms);
+    acc.x *= rescale; acc.y *= rescale; acc.z *= rescale; acc.w *= rescale;
+    lsum *= rescale;
+    M = M_new;
+    if (tid < PASS && my < ns) {
+      const float w = (mi == -INFINITY) ? 0.f : exp2f(mi - Ms);
+      wsh[tid] = w;
+      lsum += w * li;
     }
     __syncthreads();
-    wsh[lane] = w;
-    __syncthreads();
-    const int n = min(64, ns - i0);
-    if (d < D) {
-      const float* op = a.ws_o + ((unit0 + i0) * a.rows + row) * D + d;
-      const size_t stride = static_cast<size_t>(a.rows) * D;
-      int k = 0;
-      for (; k + 4 <= n; k += 4) {
-        const float o0 = op[(k + 0) * stride], o1 = op[(k + 1) * stride];
-        const float o2 = op[(k + 2) * stride], o3 = op[(k + 3) * stride];
-        acc += wsh[k] * o0;
-        acc += wsh[k + 1] * o1;
-        acc += wsh[k + 2] * o2;
-        acc += wsh[k + 3] * o3;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int il = (u * kWaves + wave) * SPW + sub;
+      if (p0 + il < ns) {
+        const float w = wsh[il];
+        acc.x += w * ov[u].x; acc.y += w * ov[u].y; acc.z += w * ov[u].z; acc.w += w * ov[u].w;
       }
-      for (; k < n; ++k) acc += wsh[k] * op[k * stride];
     }
+    __syncthreads();
   }
+  // sum over the SPW sub-rows of a wave, then over the waves
+#pragma unroll
+  for (int off = LS; off < 64; off <<= 1) {
+    acc.x += shfl_xor_f(acc.x, off); acc.y += shfl_xor_f(acc.y, off);
+    acc.z += shfl_xor_f(acc.z, off); acc.w += shfl_xor_f(acc.w, off);
+  }
+  if (sub == 0) red[wave][dl] = acc;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lsum += shfl_xor_f(lsum, off);
-
-  if (d < D) {
+  if (lane == 0) scal[wave] = lsum;
+  __syncthreads();
+  if (tid < LS) {
+    float4 t = red[0][tid];
+    float l = scal[0];
+    for (int w = 1; w < kWaves; ++w) {
+      t.x += red[w][tid].x; t.y += red[w][tid].y; t.z += red[w][tid].z; t.w += red[w][tid].w;
+      l += scal[w];
+    }
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const int s = unit / a.H_kv, h = unit % a.H_kv;
     const int jq = row / a.G, g = row % a.G;
-    const float y = (lsum > 0.f) ? acc / lsum : 0.f;
-    a.out[((static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g) * D + d] = f32_to_bf16(y);
+    uint16_t* op = a.out + ((static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g) * D + 4 * tid;
+    const uint32_t lo = pack_bf16x2(t.x * inv, t.y * inv), hi = pack_bf16x2(t.z * inv, t.w * inv);
+    *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
   }
 }
 
 }  // namespace
 
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream) {
-  dim3 grid((head_dim + 63) / 64, a.rows, a.n_seqs * a.H_kv);
-  hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(64), 0, stream, a, head_dim);
+  const dim3 grid(a.rows, a.n_seqs * a.H_kv);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(64 * kWaves), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(64 * kWaves), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(attn_combine_kernel<256>, grid, dim3(64 * kWaves), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@ namespace had {
 // Largest page range one split-K work unit may own (its page ids are staged
 // in LDS).
 constexpr int kMaxPagesPerSplit = 512;
+// Largest number of splits the merge kernel accepts per (sequence, KV head).
+constexpr int kMaxSplits = 4096;
 
 struct ValuArgs {
   const uint16_t* q;
@@ -23,6 +25,7 @@ struct ValuArgs {
   int32_t* d_err;
   int n_seqs, q_len, H_q, H_kv, G, rows, row_base;
   int num_pages, page_size, max_pages, num_splits, pps;
+  int n_pages_plan;  // pages the split plan covers; split i owns [i*n/ns, (i+1)*n/ns)
   float scale_log2;
 };
 

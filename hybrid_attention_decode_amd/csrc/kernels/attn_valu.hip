@@ -8,8 +8,9 @@
 // (zubnet.ai TokenSpeed article, second paragraph), contexts to 1M tokens
 // (24-ai.news long-context table).
 //
-// gfx950 mapping (one workgroup = 4 waves, each wave streams its own tiles
-// of 8 tokens; the workgroup owns a contiguous range of pages):
+// gfx950 mapping (one workgroup = 8 waves, two per SIMD, each wave streams
+// its own tiles of 8 tokens; the workgroup owns a contiguous, balanced range
+// of pages, one workgroup per CU):
 //  * QK: a tile step covers TPS tokens with LPT lanes per token; lane j of a
 //    token loads 16-byte chunks j, j+LPT of the K row (coalesced 128-bit
 //    loads straight into registers) and accumulates all 8 rows with
@@ -24,7 +25,7 @@
 //    pairs of two tokens are broadcast through LDS and v pairs are formed
 //    with v_perm_b32, so every MAC is a bf16 dot2.
 //  * K/V of a wave's next two tiles are in flight while it computes one.
-//  * The 4 waves' partials are merged through LDS before the single store.
+//  * The 8 waves' partials are merged through LDS before the single store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,7 +36,7 @@ namespace had {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRows = 8;  // rows handled per launch (padded with zero queries)
 constexpr int kTT = 8;    // tokens per tile
 
@@ -92,7 +93,7 @@ __device__ __forceinline__ void load_tile(Tile<D>& T, const ValuArgs& a, const L
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_valu_kernel(ValuArgs a) {
+__global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
   using C = Cfg<D>;
   __shared__ Lds sh;
   const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -102,22 +103,28 @@ __global__ __launch_bounds__(256, 2) void attn_valu_kernel(ValuArgs a) {
   const int P = a.page_size;
   const int tpp = P / kTT;
 
+  // page ids of this split -> LDS; they are fetched before the length is
+  // known (every row of the page table is max_pages wide) so the two loads
+  // overlap.  Checked ids; -1 marks an invalid one.
+  const int pg0 = static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
+  const int pg1_plan = static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
+  for (int i = threadIdx.x; i < pg1_plan - pg0; i += blockDim.x) {
+    int pid = a.page_table[static_cast<size_t>(s) * a.max_pages + pg0 + i];
+    sh.pages[i] = pid;
+  }
   const int L = a.seq_lens[s];
   const bool bad_len = L < a.q_len || L > a.max_pages * P;
   if (bad_len && threadIdx.x == 0) set_err(a.d_err, HAD_DERR_SEQLEN);
   const int n_pages = bad_len ? 0 : (L + P - 1) / P;
-  const int pg0 = sp * a.pps;
-  const int pg1 = min(pg0 + a.pps, n_pages);
+  const int pg1 = min(pg1_plan, n_pages);
   const int npg = max(pg1 - pg0, 0);
-
-  // page ids of this split -> LDS (checked; -1 marks an invalid id)
-  for (int i = threadIdx.x; i < npg; i += 256) {
-    int pid = a.page_table[static_cast<size_t>(s) * a.max_pages + pg0 + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+    const int pid = sh.pages[i];
     if (pid < 0 || pid >= a.num_pages) {
       set_err(a.d_err, HAD_DERR_PAGE);
-      pid = -1;
+      sh.pages[i] = -1;
     }
-    sh.pages[i] = pid;
   }
 
   // q rows in lane order: slot r holds row (r ^ sigma(j8)) of this launch
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void attn_valu_kernel(ValuArgs a) {
 
   // ---- merge the 4 waves and store the split's partial
   const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.num_splits + sp;
-  for (int idx = threadIdx.x; idx < kRows * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < kRows * D; idx += blockDim.x) {
     const int r = idx / D, d = idx % D;
     const int row = a.row_base + r;
     if (row >= a.rows) continue;
@@ -331,13 +338,13 @@ __global__ __launch_bounds__(256, 2) void attn_valu_kernel(ValuArgs a) {
 hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      hipLaunchKernelGGL(attn_valu_kernel<64>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_valu_kernel<64>, grid, dim3(64 * kWaves), 0, stream, a);
       break;
     case 128:
-      hipLaunchKernelGGL(attn_valu_kernel<128>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_valu_kernel<128>, grid, dim3(64 * kWaves), 0, stream, a);
       break;
     case 256:
-      hipLaunchKernelGGL(attn_valu_kernel<256>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_valu_kernel<256>, grid, dim3(64 * kWaves), 0, stream, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -290,8 +290,13 @@ int had_decode_attn_plan(const had_attn_desc *d, int32_t *num_splits, int32_t *p
 size_t had_decode_attn_workspace_bytes(const had_attn_desc *d);
 int had_decode_attn(const had_attn_desc *d, const had_attn_ptrs *p, void *stream);
 
-/* The merge step alone (runs inside had_decode_attn): reads num_splits
- * partials in the workspace layout above and writes out. */
+/* The two halves of had_decode_attn, for callers that move or inspect the
+ * partials between them (e.g. a context-parallel split of one sequence over
+ * several devices exchanges the (o, m, l) partials before merging).
+ * had_decode_attn_partial writes the workspace only (p->out is ignored);
+ * had_decode_attn_combine reads num_splits partials in the workspace layout
+ * above and writes out. */
+int had_decode_attn_partial(const had_attn_desc *d, const had_attn_ptrs *p, void *stream);
 int had_decode_attn_combine(const had_attn_desc *d, int32_t num_splits,
                             const void *workspace, void *out, void *stream);
 
