@@ -29,6 +29,7 @@ _STATUS = {
     -10: "range",
 }
 DERR_PAGE, DERR_SLOT, DERR_SEQLEN = 1, 2, 4
+ATTN_DETERMINISTIC = 1
 
 
 class HadError(RuntimeError):
@@ -63,7 +64,7 @@ class QknrgPtrs(ctypes.Structure):
 class AttnDesc(ctypes.Structure):
     _fields_ = [("n_seqs", _i32), ("q_len", _i32), ("H_q", _i32), ("H_kv", _i32), ("head_dim", _i32),
                 ("num_pages", _i32), ("page_size", _i32), ("max_pages", _i32), ("sm_scale", ctypes.c_float),
-                ("max_seq_len", _i32), ("num_splits", _i32)]
+                ("max_seq_len", _i32), ("num_splits", _i32), ("flags", _i32)]
 
 
 class AttnPtrs(ctypes.Structure):
@@ -336,14 +337,15 @@ def qk_norm_rope_gate(qg, k, v, w_q, w_k, page_table, seq_lens, k_pool, v_pool, 
     return q_out, gate_out
 
 
-def attn_desc(q_shape, k_pool_shape, max_pages, sm_scale=None, max_seq_len=0, num_splits=0):
+def attn_desc(q_shape, k_pool_shape, max_pages, sm_scale=None, max_seq_len=0, num_splits=0, deterministic=False):
     S, q_len, H_q, D = q_shape
     N, H_kv, P, D2 = k_pool_shape
     if D != D2:
         raise ValueError("q and pool head_dim differ")
     if sm_scale is None:
         sm_scale = 1.0 / float(np.sqrt(D))
-    return AttnDesc(S, q_len, H_q, H_kv, D, N, P, max_pages, float(sm_scale), int(max_seq_len), int(num_splits))
+    return AttnDesc(S, q_len, H_q, H_kv, D, N, P, max_pages, float(sm_scale), int(max_seq_len), int(num_splits),
+                    ATTN_DETERMINISTIC if deterministic else 0)
 
 
 def decode_attn_plan(desc):
@@ -361,10 +363,10 @@ def decode_attn_workspace_bytes(desc):
 
 
 def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_len=0, num_splits=0,
-                workspace=None, out=None, d_err=None):
+                workspace=None, out=None, d_err=None, deterministic=False):
     """q [S, q_len, H_q, D] bf16 -> out [S, q_len, H_q, D] bf16."""
     torch = _torch()
-    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits)
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits, deterministic)
     need = decode_attn_workspace_bytes(desc)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -379,11 +381,11 @@ def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_
 
 
 def decode_attn_partial(q, k_pool, v_pool, page_table, seq_lens, workspace, sm_scale=None, max_seq_len=0,
-                        num_splits=0, d_err=None):
+                        num_splits=0, d_err=None, deterministic=False):
     """Split-K partial kernel only: writes (o, m, l) partials to ``workspace``.
     Returns the descriptor (for decode_attn_combine)."""
     torch = _torch()
-    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits)
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits, deterministic)
     ptrs = AttnPtrs(_dev(q, torch.bfloat16, "q"), _dev(k_pool, torch.bfloat16, "k_pool"),
                     _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
                     _dev(seq_lens, torch.int32, "seq_lens"), _dev(workspace, torch.uint8, "workspace"),

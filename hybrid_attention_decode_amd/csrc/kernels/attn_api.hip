@@ -40,6 +40,7 @@ int check_desc(const had_attn_desc* d) {
     return fail(HAD_ERR_INVALID_ARG, "decode_attn: max_seq_len %d outside [0, max_pages*page_size=%lld]",
                 d->max_seq_len, static_cast<long long>(cap));
   if (d->num_splits < 0) return fail(HAD_ERR_INVALID_ARG, "decode_attn: num_splits %d < 0", d->num_splits);
+  if (d->flags & ~HAD_ATTN_DETERMINISTIC) return fail(HAD_ERR_INVALID_ARG, "decode_attn: unknown flags 0x%x", d->flags);
   const int rows = d->q_len * (d->H_q / d->H_kv);
   if (rows > 256) return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %d query rows per KV head > 256", rows);
   return HAD_OK;
@@ -139,6 +140,7 @@ static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* 
   a.num_splits = ns;
   a.pps = pps;
   a.n_pages_plan = n_plan;
+  a.deterministic = (d->flags & HAD_ATTN_DETERMINISTIC) ? 1 : 0;
   a.scale_log2 = d->sm_scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -26,6 +26,7 @@ struct ValuArgs {
   int n_seqs, q_len, H_q, H_kv, G, rows, row_base;
   int num_pages, page_size, max_pages, num_splits, pps;
   int n_pages_plan;  // pages the split plan covers; split i owns [i*n/ns, (i+1)*n/ns)
+  int deterministic;  // fixed tile stride per wave instead of dynamic claims
   float scale_log2;
 };
 

@@ -24,7 +24,8 @@
 //  * PV: lanes own 4 consecutive d of V rows (coalesced 64-bit loads); p
 //    pairs of two tokens are broadcast through LDS and v pairs are formed
 //    with v_perm_b32, so every MAC is a bf16 dot2.
-//  * K/V of a wave's next two tiles are in flight while it computes one.
+//  * K/V of a wave's next two tiles are in flight while it computes one;
+//    tiles after the first two are claimed from an LDS counter.
 //  * The 8 waves' partials are merged through LDS before the single store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,6 +40,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kRows = 8;  // rows handled per launch (padded with zero queries)
 constexpr int kTT = 8;    // tokens per tile
+static_assert(kMaxPagesPerSplit <= 64 * kWaves, "one page-table entry per thread");
 
 template <int D>
 struct Cfg {
@@ -65,21 +67,23 @@ struct Tile {
 };
 
 struct Lds {
+  uint2 q[kRows][64];                // query block (bf16), rows in launch order
   float o[kWaves][kRows][256];      // per-wave partial outputs for the merge
   float ml[kWaves][kRows][2];       // per-wave (m, l)
   uint32_t p[kWaves][4][kRows];     // bf16 p pairs: [pair][row]
   float alpha[kWaves][kRows];       // per-row rescale factor of the current tile
   int32_t pages[kMaxPagesPerSplit];  // page ids of the workgroup's range (-1 = invalid)
+  int next;                          // next tile to claim
+  int err;                           // HAD_DERR bits seen by the workgroup
 };
 
+// K and V of one 8-token tile: page `pid`, tile `tip` inside the page.
 template <int D>
-__device__ __forceinline__ void load_tile(Tile<D>& T, const ValuArgs& a, const Lds& sh, int tile, int pg0, int tpp,
-                                          int h, int tg, int j, int tgv, int dl) {
+__device__ __forceinline__ void load_tile_at(Tile<D>& T, const ValuArgs& a, int pid, int tip, int h, int tg, int j,
+                                             int tgv, int dl) {
   using C = Cfg<D>;
-  const int pid_raw = sh.pages[tile / tpp - pg0];
-  const int pid = __builtin_amdgcn_readfirstlane(pid_raw < 0 ? 0 : pid_raw);
-  const int off = (tile % tpp) * kTT;
-  const size_t base = ((static_cast<size_t>(pid) * a.H_kv + h) * a.page_size + off) * D;
+  const int pu = __builtin_amdgcn_readfirstlane(pid);
+  const size_t base = ((static_cast<size_t>(pu) * a.H_kv + h) * a.page_size + tip * kTT) * D;
   const uint16_t* kb = a.k_pool + base;
   const uint16_t* vb = a.v_pool + base;
 #pragma unroll
@@ -97,61 +101,98 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
   using C = Cfg<D>;
   __shared__ Lds sh;
   const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
   const int tg = lane / C::LPT, j = lane % C::LPT, j8 = j & 7;
   const int tgv = lane / (D / C::DPL), dl = lane % (D / C::DPL);
   const int P = a.page_size;
   const int tpp = P / kTT;
 
-  // page ids of this split -> LDS; they are fetched before the length is
-  // known (every row of the page table is max_pages wide) so the two loads
-  // overlap.  Checked ids; -1 marks an invalid one.
+  // Every global load below is unconditional (addresses clamped to valid
+  // memory, results masked afterwards): loads under divergent or uniform
+  // branches make the compiler's wait-count bookkeeping fall back to
+  // "wait for everything", which would serialise the K/V prefetch.
+  //
+  // This split owns pages [pg0, pg1_plan) of the plan (balanced to within one
+  // page); tiles are numbered from the split's first token.
   const int pg0 = static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
   const int pg1_plan = static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
-  for (int i = threadIdx.x; i < pg1_plan - pg0; i += blockDim.x) {
-    int pid = a.page_table[static_cast<size_t>(s) * a.max_pages + pg0 + i];
-    sh.pages[i] = pid;
+  const int npg_plan = pg1_plan - pg0;
+  const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
+
+  // One page-table entry per thread (a split owns at most
+  // kMaxPagesPerSplit = blockDim pages), then the query block.
+  const int pt_val = pt_row[min(pg0 + static_cast<int>(threadIdx.x), a.max_pages - 1)];
+
+  // The kRows x D query block of this launch -> LDS, one 8-byte piece per
+  // thread (rows past `rows` are zero).  Loading it per wave instead would
+  // send every wave of the GPU to the same few L2 lines at kernel start.
+  {
+    constexpr int PER_ROW = D / 4;  // 8-byte pieces per row
+    const int r = threadIdx.x / PER_ROW, c4 = threadIdx.x % PER_ROW;
+    if (r < kRows) {
+      const int row = a.row_base + r;
+      const bool valid = row < a.rows;
+      const int rc = valid ? row : 0;
+      const uint2 v = *reinterpret_cast<const uint2*>(
+          a.q + ((static_cast<size_t>(s) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D + c4 * 4);
+      sh.q[r][c4] = valid ? v : make_uint2(0u, 0u);
+    }
   }
+  const int my_row = a.row_base + sigma(j8);
+
   const int L = a.seq_lens[s];
   const bool bad_len = L < a.q_len || L > a.max_pages * P;
-  if (bad_len && threadIdx.x == 0) set_err(a.d_err, HAD_DERR_SEQLEN);
   const int n_pages = bad_len ? 0 : (L + P - 1) / P;
-  const int pg1 = min(pg1_plan, n_pages);
-  const int npg = max(pg1 - pg0, 0);
-  __syncthreads();
-  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
-    const int pid = sh.pages[i];
-    if (pid < 0 || pid >= a.num_pages) {
-      set_err(a.d_err, HAD_DERR_PAGE);
-      sh.pages[i] = -1;
-    }
+  const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
+  const int ntiles = npg * tpp;
+  int errs = (bad_len && threadIdx.x == 0) ? HAD_DERR_SEQLEN : 0;
+  if (threadIdx.x == 0) {
+    sh.next = 2 * kWaves;
+    sh.err = 0;
   }
-
-  // q rows in lane order: slot r holds row (r ^ sigma(j8)) of this launch
-  uint32_t qr[kRows][C::CH * 4];
-  int my_row = a.row_base + sigma(j8);
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int row = a.row_base + (r ^ sigma(j8));
-#pragma unroll
-    for (int c = 0; c < C::CH; ++c) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < a.rows) {
-        const int jq = row / a.G, g = row % a.G;
-        const uint16_t* qp = a.q + ((static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g) * D;
-        v = *reinterpret_cast<const uint4*>(qp + (j + c * C::LPT) * 8);
-      }
-      qr[r][c * 4 + 0] = v.x;
-      qr[r][c * 4 + 1] = v.y;
-      qr[r][c * 4 + 2] = v.z;
-      qr[r][c * 4 + 3] = v.w;
-    }
+  // checked page ids of the split -> LDS (-1 marks an invalid id)
+  if (static_cast<int>(threadIdx.x) < npg_plan) {
+    const bool ok = pt_val >= 0 && pt_val < a.num_pages;
+    if (!ok && static_cast<int>(threadIdx.x) < npg) errs |= HAD_DERR_PAGE;
+    sh.pages[threadIdx.x] = ok ? pt_val : -1;
   }
   // visible-key limit of this lane's QK row (causal inside the draft)
   const int lim = (my_row < a.rows) ? (L - a.q_len + my_row / a.G + 1) : L;
   const int lim_min = L - a.q_len + 1;  // every row sees positions below this
 
   __syncthreads();
+
+  // The first two tiles of this wave: page ids read straight from the
+  // page-table row (scalar loads), issued right after the barrier.  (Issued
+  // before it they delay the small loads the barrier waits for by more than
+  // they gain.)  A tile past the length or the split is loaded for nothing
+  // and never used.
+  Tile<D> buf[2];
+  int tcur[2] = {wave, wave + kWaves};
+  // (issue order pinned: all of buffer 0, then all of buffer 1, the order
+  // the loop refills them in, so the wait counts inside the loop stay exact)
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int pid = pt_row[min(pg0 + tcur[b] / tpp, a.max_pages - 1)];
+    load_tile_at<D>(buf[b], a, (pid < 0 || pid >= a.num_pages) ? 0 : pid, tcur[b] % tpp, h, tg, j, tgv, dl);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // q rows in lane order: slot r holds row (r ^ sigma(j8)) of this launch
+  uint32_t qr[kRows][C::CH * 4];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(&sh.q[r ^ sigma(j8)][0]);
+#pragma unroll
+    for (int c = 0; c < C::CH; ++c) {
+      const uint4 v = qrow[j + c * C::LPT];
+      qr[r][c * 4 + 0] = v.x;
+      qr[r][c * 4 + 1] = v.y;
+      qr[r][c * 4 + 2] = v.z;
+      qr[r][c * 4 + 3] = v.w;
+    }
+  }
 
   float o[kRows][C::DPL];
 #pragma unroll
@@ -160,131 +201,149 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
     for (int d = 0; d < C::DPL; ++d) o[r][d] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int t_begin = pg0 * tpp, t_end = pg0 * tpp + npg * tpp;
-  // this wave's tiles: t_begin + wave + kWaves * i
-  const int my_first = t_begin + wave;
-  const int n_my = (t_end > my_first) ? (t_end - my_first + kWaves - 1) / kWaves : 0;
+  // Tiles are claimed dynamically: the first two per wave are fixed above,
+  // later ones come from an LDS counter, so the two waves sharing a SIMD
+  // (which the issue arbiter does not serve equally) finish together.  In
+  // deterministic mode wave w takes tiles w + 2*kWaves*i and w + kWaves +
+  // 2*kWaves*i instead.  Claims grow monotonically, so tcur[0] < tcur[1]
+  // always: the loop runs while both buffers hold a tile (its only exit test
+  // is at the top -- with exits between the two halves the compiler's wait
+  // counts at the loop head fall back to waiting for every load), and at
+  // most one tile is left for buffer 0 after it.
+  auto process = [&](Tile<D>& T, const int tile) __attribute__((always_inline)) {
+    const int pg = pg0 + tile / tpp;
+    const int pos0 = pg * P + (tile % tpp) * kTT;  // logical position of the tile's token 0
+    const bool tile_ok = sh.pages[pg - pg0] >= 0;
 
-  Tile<D> buf[2];
-  if (n_my > 0) load_tile<D>(buf[0], a, sh, my_first, pg0, tpp, h, tg, j, tgv, dl);
-  if (n_my > 1) load_tile<D>(buf[1], a, sh, my_first + kWaves, pg0, tpp, h, tg, j, tgv, dl);
-
-  for (int it = 0; it < n_my; it += 2) {
+    // ---- scores
+    float sc[C::TS];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int ii = it + b;
-      if (ii >= n_my) break;
-      const int tile = my_first + ii * kWaves;
-      Tile<D>& T = buf[b];
-      const int pos0 = (tile / tpp) * P + (tile % tpp) * kTT;  // logical position of the tile's token 0
-      const bool tile_ok = sh.pages[tile / tpp - pg0] >= 0;
-
-      // ---- scores
-      float sc[C::TS];
+    for (int i = 0; i < C::TS; ++i) {
+      float acc[kRows];
 #pragma unroll
-      for (int i = 0; i < C::TS; ++i) {
-        float acc[kRows];
+      for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
+      for (int c = 0; c < C::CH; ++c) {
+        const uint32_t kw[4] = {T.k[i][c].x, T.k[i][c].y, T.k[i][c].z, T.k[i][c].w};
 #pragma unroll
-        for (int c = 0; c < C::CH; ++c) {
-          const uint32_t kw[4] = {T.k[i][c].x, T.k[i][c].y, T.k[i][c].z, T.k[i][c].w};
+        for (int w = 0; w < 4; ++w)
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-#pragma unroll
-            for (int r = 0; r < kRows; ++r) acc[r] = dot2_bf16(qr[r][c * 4 + w], kw[w], acc[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += dpp<DPP_ROW_HALF_MIRROR>(acc[r + 4]);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) acc[r] += dpp<DPP_QUAD_XOR2>(acc[r + 2]);
-        acc[0] += dpp<DPP_QUAD_XOR1>(acc[1]);
-        if (C::LPT == 16) acc[0] += dpp<DPP_ROW_ROR8>(acc[0]);
-        sc[i] = acc[0] * a.scale_log2;
-      }
-      // the next-but-one tile reuses these K registers
-      const bool masked = !tile_ok || (pos0 + kTT > lim_min);
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < C::TS; ++i) {
-          const int pos = pos0 + i * C::TPS + tg;
-          if (!tile_ok || pos >= lim) sc[i] = -INFINITY;
-        }
-      }
-
-      // ---- online softmax (rows are lane-uniform within groups of LPT)
-      float mt = sc[0];
-#pragma unroll
-      for (int i = 1; i < C::TS; ++i) mt = fmaxf(mt, sc[i]);
-      if (C::LPT == 8) mt = fmaxf(mt, dpp<DPP_ROW_ROR8>(mt));
-      mt = fmaxf(mt, shfl_xor_f(mt, 16));
-      mt = fmaxf(mt, shfl_xor_f(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_sub = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_sub);
-      float lsum = 0.f;
-      uint16_t pb[C::TS];
-#pragma unroll
-      for (int i = 0; i < C::TS; ++i) {
-        pb[i] = f32_to_bf16(exp2f(sc[i] - m_sub));
-        lsum += bf16_to_f32(pb[i]);
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-
-      // ---- publish p pairs and alpha to the wave's LDS slice
-      if (C::LPT == 8 || j < 8) {
-        uint16_t* pw = reinterpret_cast<uint16_t*>(&sh.p[wave][0][0]);
-#pragma unroll
-        for (int i = 0; i < C::TS; ++i) {
-          const int t = i * C::TPS + tg;  // token within the tile
-          const int g = t % C::TG, vi = t / C::TG;
-          const int pair = (vi >> 1) * C::TG + g, half = vi & 1;
-          pw[(pair * kRows + sigma(j8)) * 2 + half] = pb[i];
-        }
-        if (tg == 0) sh.alpha[wave][sigma(j8)] = alpha;
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-
-      // ---- rescale and accumulate P V
-      const float4 a0 = *reinterpret_cast<const float4*>(&sh.alpha[wave][0]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&sh.alpha[wave][4]);
-      const float al[kRows] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      bool need = false;
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) need |= al[r] != 1.f;
-      if (need) {
-#pragma unroll
-        for (int r = 0; r < kRows; ++r)
-#pragma unroll
-          for (int d = 0; d < C::DPL; ++d) o[r][d] *= al[r];
-      }
-      if (masked) {  // never multiply stale or unchecked rows: zero invalid V
-#pragma unroll
-        for (int i = 0; i < C::VPL; ++i) {
-          const int pos = pos0 + tgv + C::TG * i;
-          if (!tile_ok || pos >= L) T.v[i] = make_uint2(0, 0);
-        }
+          for (int r = 0; r < kRows; ++r) acc[r] = dot2_bf16(qr[r][c * 4 + w], kw[w], acc[r]);
       }
 #pragma unroll
-      for (int k = 0; k < C::NPAIR; ++k) {
-        const uint4 p0 = *reinterpret_cast<const uint4*>(&sh.p[wave][k * C::TG + tgv][0]);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(&sh.p[wave][k * C::TG + tgv][4]);
-        const uint32_t pr[kRows] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        const uint2 va = T.v[2 * k], vb = T.v[2 * k + 1];
-        const uint32_t vp[4] = {perm_b32(vb.x, va.x, 0x05040100u), perm_b32(vb.x, va.x, 0x07060302u),
-                                perm_b32(vb.y, va.y, 0x05040100u), perm_b32(vb.y, va.y, 0x07060302u)};
+      for (int r = 0; r < 4; ++r) acc[r] += dpp<DPP_ROW_HALF_MIRROR>(acc[r + 4]);
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) o[r][d] = dot2_bf16(pr[r], vp[d], o[r][d]);
-      }
-      __builtin_amdgcn_wave_barrier();
-
-      if (ii + 2 < n_my) load_tile<D>(T, a, sh, tile + 2 * kWaves, pg0, tpp, h, tg, j, tgv, dl);
+      for (int r = 0; r < 2; ++r) acc[r] += dpp<DPP_QUAD_XOR2>(acc[r + 2]);
+      acc[0] += dpp<DPP_QUAD_XOR1>(acc[1]);
+      if (C::LPT == 16) acc[0] += dpp<DPP_ROW_ROR8>(acc[0]);
+      sc[i] = acc[0] * a.scale_log2;
     }
+    const bool masked = !tile_ok || (pos0 + kTT > lim_min);
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < C::TS; ++i) {
+        const int pos = pos0 + i * C::TPS + tg;
+        if (!tile_ok || pos >= lim) sc[i] = -INFINITY;
+      }
+    }
+
+    // ---- online softmax (rows are lane-uniform within groups of LPT)
+    float mt = sc[0];
+#pragma unroll
+    for (int i = 1; i < C::TS; ++i) mt = fmaxf(mt, sc[i]);
+    if (C::LPT == 8) mt = fmaxf(mt, dpp<DPP_ROW_ROR8>(mt));
+    mt = fmaxf(mt, shfl_xor_f(mt, 16));
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_sub = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_sub);
+    float lsum = 0.f;
+    uint16_t pb[C::TS];
+#pragma unroll
+    for (int i = 0; i < C::TS; ++i) {
+      pb[i] = f32_to_bf16(exp2f(sc[i] - m_sub));
+      lsum += bf16_to_f32(pb[i]);
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+
+    // ---- publish p pairs and alpha to the wave's LDS slice
+    if (C::LPT == 8 || j < 8) {
+      uint16_t* pw = reinterpret_cast<uint16_t*>(&sh.p[wave][0][0]);
+#pragma unroll
+      for (int i = 0; i < C::TS; ++i) {
+        const int t = i * C::TPS + tg;  // token within the tile
+        const int g = t % C::TG, vi = t / C::TG;
+        const int pair = (vi >> 1) * C::TG + g, half = vi & 1;
+        pw[(pair * kRows + sigma(j8)) * 2 + half] = pb[i];
+      }
+      if (tg == 0) sh.alpha[wave][sigma(j8)] = alpha;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // ---- rescale and accumulate P V
+    const float4 a0 = *reinterpret_cast<const float4*>(&sh.alpha[wave][0]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&sh.alpha[wave][4]);
+    const float al[kRows] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    bool need = false;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) need |= al[r] != 1.f;
+    if (need) {
+#pragma unroll
+      for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int d = 0; d < C::DPL; ++d) o[r][d] *= al[r];
+    }
+    // never multiply stale or unchecked rows: zero V past the length or in
+    // an invalid page (selects, not a branch: a branch that rewrites load
+    // destinations spoils the compiler's wait counts for the other buffer)
+    const int vlim = tile_ok ? L - pos0 : 0;
+#pragma unroll
+    for (int i = 0; i < C::VPL; ++i) {
+      const bool keep = tgv + C::TG * i < vlim;
+      T.v[i].x = keep ? T.v[i].x : 0u;
+      T.v[i].y = keep ? T.v[i].y : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < C::NPAIR; ++k) {
+      const uint4 p0 = *reinterpret_cast<const uint4*>(&sh.p[wave][k * C::TG + tgv][0]);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(&sh.p[wave][k * C::TG + tgv][4]);
+      const uint32_t pr[kRows] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      const uint2 va = T.v[2 * k], vb = T.v[2 * k + 1];
+      const uint32_t vp[4] = {perm_b32(vb.x, va.x, 0x05040100u), perm_b32(vb.x, va.x, 0x07060302u),
+                              perm_b32(vb.y, va.y, 0x05040100u), perm_b32(vb.y, va.y, 0x07060302u)};
+#pragma unroll
+      for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[r][d] = dot2_bf16(pr[r], vp[d], o[r][d]);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+  };
+  auto refill = [&](Tile<D>& T, int& tc) __attribute__((always_inline)) {
+    // claim the next tile for this buffer and start its loads; past the end
+    // the loads re-read the last tile (never used)
+    int nxt = tc + 2 * kWaves;
+    if (!a.deterministic) {
+      if (lane == 0) nxt = atomicAdd(&sh.next, 1);
+      nxt = __builtin_amdgcn_readfirstlane(nxt);
+    }
+    tc = nxt;
+    const int nc = min(nxt, ntiles - 1);
+    const int pid = sh.pages[nc / tpp];
+    load_tile_at<D>(T, a, pid < 0 ? 0 : pid, nc % tpp, h, tg, j, tgv, dl);
+    // keep the refill here: the scheduler would otherwise sink it below the
+    // wait for the other buffer, halving the prefetch distance
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  while (tcur[1] < ntiles) {
+    process(buf[0], tcur[0]);
+    refill(buf[0], tcur[0]);
+    process(buf[1], tcur[1]);
+    refill(buf[1], tcur[1]);
   }
+  if (tcur[0] < ntiles) process(buf[0], tcur[0]);
 
   // ---- wave totals: l over token groups, o over PV token groups
   if (C::LPT == 8) l_run += dpp<DPP_ROW_ROR8>(l_run);
@@ -306,9 +365,11 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
     sh.ml[wave][sigma(j8)][0] = m_run;
     sh.ml[wave][sigma(j8)][1] = l_run;
   }
+  if (errs) atomicOr(&sh.err, errs);
   __syncthreads();
+  if (threadIdx.x == 0 && sh.err) set_err(a.d_err, sh.err);
 
-  // ---- merge the 4 waves and store the split's partial
+  // ---- merge the waves and store the split's partial
   const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.num_splits + sp;
   for (int idx = threadIdx.x; idx < kRows * D; idx += blockDim.x) {
     const int r = idx / D, d = idx % D;

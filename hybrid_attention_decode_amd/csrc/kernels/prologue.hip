@@ -4,6 +4,7 @@
 // intermediates never leave registers (zubnet.ai TokenSpeed article, second
 // paragraph); here one wave owns one head of one token and the only other
 // storage touched is a 1 KB LDS row used to fetch the rotation partner.
+// Grid: (token, group of 4 heads), 4 waves per block.
 //
 //   q    = RMSNorm(qg[.., 0, :]) * w_q,   gate = qg[.., 1, :]
 //   k    = RMSNorm(k) * w_k,              v unchanged
@@ -11,8 +12,8 @@
 //   dims d < R rotate in pairs (i, i + R/2), angle pos * base^(-2i/R):
 //     y_i' = y_i cos - y_{i+R/2} sin,  y_{i+R/2}' = y_{i+R/2} cos + y_i sin
 //   (RMSNorm: Zhang & Sennrich 2019; rotary embedding: Su et al., RoFormer
-//   2021, applied to a prefix of the head), angles and their sines and
-//   cosines in fp64, pos = seq_lens[s] - T + j.
+//   2021, applied to a prefix of the head), angles in fp64 (reduced to
+//   [-pi, pi] before an fp32 sine/cosine), pos = seq_lens[s] - T + j.
 // Outputs are rounded to bf16 (nearest even); gate and v are copied bit for
 // bit.
 #include <hip/hip_runtime.h>
@@ -59,14 +60,18 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   int pid = -1;
   if (pos_ok) pid = a.page_table[static_cast<size_t>(s) * a.max_pages + pos / a.P];
   const bool page_ok = pos_ok && pid >= 0 && pid < a.num_pages;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && blockIdx.y == 0) {
     if (!pos_ok) set_err(a.d_err, HAD_DERR_SEQLEN);
     else if (!page_ok) set_err(a.d_err, HAD_DERR_PAGE);
   }
   const size_t tok = static_cast<size_t>(s) * a.T + j;
 
-  // rotation angle of this lane's pair index (i = d mod R/2 for d < R)
+  // rotation angle of this lane's pair index (i = d mod R/2 for d < R):
+  // theta = pos * base^(-2i/R) in fp64 (at pos ~ 1e6 an fp32 product would
+  // be off by ~0.06 rad), reduced to [-pi, pi] in fp64, then sine and cosine
+  // of the small reduced angle in fp32.
   const int half = a.R / 2;
+  const double log2_base = log2(a.base);
   float cs[E], sn[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) {
@@ -75,15 +80,17 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     sn[m] = 0.f;
     if (d < a.R) {
       const int i = d % half;
-      const double inv_freq = pow(a.base, -2.0 * i / a.R);
-      double sd, cd;
-      sincos(static_cast<double>(pos) * inv_freq, &sd, &cd);
-      cs[m] = static_cast<float>(cd);
-      sn[m] = static_cast<float>(sd);
+      const double inv_freq = exp2(-2.0 * i / a.R * log2_base);
+      const double theta = static_cast<double>(pos) * inv_freq;
+      const double two_pi = 6.283185307179586476925286766559;
+      const double red = theta - two_pi * rint(theta / two_pi);
+      sincosf(static_cast<float>(red), &sn[m], &cs[m]);
     }
   }
 
-  for (int hh = wave; hh < a.H_q + a.H_kv; hh += kWaves) {
+  {
+    const int hh = blockIdx.y * kWaves + wave;  // one head per wave
+    if (hh >= a.H_q + a.H_kv) return;
     const bool is_q = hh < a.H_q;
     const int h = is_q ? hh : hh - a.H_q;
     const uint16_t* src = is_q ? a.qg + (tok * a.H_q + h) * 2 * D : a.k + (tok * a.H_kv + h) * D;
@@ -180,7 +187,7 @@ extern "C" int had_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_pt
   a.max_pages = d->max_pages;
   a.base = d->rope_base;
   a.eps = d->eps;
-  const dim3 grid(d->n_seqs * d->T), block(256);
+  const dim3 grid(d->n_seqs * d->T, (d->H_q + d->H_kv + 3) / 4), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (d->head_dim) {
     case 64: hipLaunchKernelGGL(had::prologue_kernel<64>, grid, block, 0, s, a); break;

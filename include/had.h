@@ -272,7 +272,15 @@ typedef struct {
   float sm_scale;                             /* usually 1/sqrt(head_dim)                            */
   int32_t max_seq_len;                        /* host bound on every seq_lens[s]; 0 = max_pages*page_size */
   int32_t num_splits;                         /* 0 = choose automatically                            */
+  int32_t flags;                              /* HAD_ATTN_* bits                                     */
 } had_attn_desc;
+
+/* Work inside a split is handed to the waves dynamically by default, which
+ * balances waves that share a SIMD but makes the fp32 summation order (and
+ * so the last bits of the output) depend on timing.  With this flag every
+ * wave takes a fixed stride of tiles: the output bits are a function of the
+ * inputs and the split plan only. */
+#define HAD_ATTN_DETERMINISTIC 1
 
 typedef struct {
   const void *q;             /* bf16 [n_seqs][q_len][H_q][head_dim]         */

@@ -13,13 +13,13 @@ from gpu_util import DEV, assert_attn_close, bits_of, paged_case, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(seed, lens, q_len, H_q, H_kv, D, P, num_splits=0, structured=False, max_seq_len=0):
+def _run(seed, lens, q_len, H_q, H_kv, D, P, num_splits=0, structured=False, max_seq_len=0, deterministic=False):
     q, kp, vp, pt, L = paged_case(seed, lens, q_len, H_q, H_kv, D, P, structured=structured)
     print("case seed=%d lens=%s q_len=%d H_q=%d H_kv=%d D=%d P=%d splits=%d" % (seed, list(lens), q_len, H_q, H_kv,
                                                                                D, P, num_splits), flush=True)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     out = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L), num_splits=num_splits,
-                          max_seq_len=max_seq_len, d_err=err)
+                          max_seq_len=max_seq_len, d_err=err, deterministic=deterministic)
     torch.cuda.synchronize()
     assert err.item() == 0
     ref = A.paged_attention(bits_of(q), bits_of(kp), bits_of(vp), pt, L, P, 1.0 / np.sqrt(D))
@@ -34,8 +34,9 @@ def test_tiny_config():
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("P", [16, 64])
-def test_head_dims_and_page_sizes(D, P):
-    out, ref = _run(200 + D + P, [1, 77, 1000, 4099], 1, 8, 1, D, P)
+@pytest.mark.parametrize("det", [False, True])
+def test_head_dims_and_page_sizes(D, P, det):
+    out, ref = _run(200 + D + P, [1, 77, 1000, 4099], 1, 8, 1, D, P, deterministic=det)
     assert_attn_close(out, ref)
 
 
@@ -84,6 +85,7 @@ def test_identical_keys_give_mean_of_values():
 
 
 def test_shuffled_and_identity_page_tables_give_identical_bytes():
+    # deterministic mode: output bits depend on the inputs and the split plan only
     q, kp, vp, pt, L = paged_case(800, [3000], 1, 8, 1, 256, 64, extra_pages=0)
     n = int(-(-3000 // 64))
     # identity layout: page i holds logical page i
@@ -94,10 +96,14 @@ def test_shuffled_and_identity_page_tables_give_identical_bytes():
         vp2[i] = vp[pt[0, i]]
     pt2 = pt.copy()
     pt2[0, :n] = np.arange(n)
-    o1 = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L))
-    o2 = had.decode_attn(to_dev(q), to_dev(kp2), to_dev(vp2), to_dev(pt2), to_dev(L))
+    o1 = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L), deterministic=True)
+    o2 = had.decode_attn(to_dev(q), to_dev(kp2), to_dev(vp2), to_dev(pt2), to_dev(L), deterministic=True)
+    o3 = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L))   # dynamic tile claims
     torch.cuda.synchronize()
     assert torch.equal(o1.cpu(), o2.cpu())
+    # the dynamic schedule only changes the fp32 summation order
+    diff = (o1.float() - o3.float()).abs().max().item()
+    assert diff <= 2e-3, diff
 
 
 def test_out_of_range_page_id_sets_the_sentinel_without_fault():
