@@ -149,3 +149,27 @@ def test_bad_descriptor_is_rejected():
     with pytest.raises(had.HadError) as e:
         had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L))
     assert e.value.kind == "invalid"
+
+
+@pytest.mark.parametrize("G,q_len,H_kv,D,P", [
+    (16, 4, 1, 256, 64),   # speculative verify: 16 q heads / 1 KV head x 4 drafts = 64 rows
+    (16, 1, 1, 128, 16),   # 16 rows, one token
+    (8, 2, 2, 64, 64),     # 16 rows per KV head, two KV heads
+    (4, 5, 1, 256, 16),    # 20 rows (padded to 64)
+    (20, 4, 1, 128, 64),   # 80 rows: two row blocks
+])
+def test_mfma_path_rows_at_least_16(G, q_len, H_kv, D, P):
+    out, ref = _run(1000 + G * 7 + q_len, [q_len, 97, 2050, 6000], q_len, G * H_kv, H_kv, D, P)
+    assert_attn_close(out, ref)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 700])
+def test_mfma_path_forced_splits(splits):
+    out, ref = _run(1100 + splits, [4100, 33], 4, 16, 1, 256, 64, num_splits=splits)
+    assert_attn_close(out, ref)
+
+
+def test_mfma_path_structured_values():
+    out, ref = _run(1200, [30000], 4, 16, 1, 256, 64, structured=True)
+    assert np.abs(ref).max() > 0.2
+    assert_attn_close(out, ref)
