@@ -271,6 +271,403 @@ def run_context(L0, steps, warmup, kernel_reps, seed=0):
     return res
 
 
+class Stack:
+    """The 48-layer hybrid stack for n_seqs sequences with T new tokens per step.
+
+    Per-step control (sequence lengths, GDN input slot per sequence, GDN output
+    slot per (sequence, token)) lives in one device int32 block that the host
+    refreshes with a single pinned async copy before each graph replay; the
+    page table is patched entry by entry when the host manager hands out a
+    new page.
+    """
+
+    def __init__(self, n_seqs, T, H_q, num_pages, max_pages, max_seq_len, n_slots, n_steps, seed):
+        import torch
+
+        import hybrid_attention_decode_amd as had
+        import synth
+
+        self.torch, self.had = torch, had
+        dev = "cuda"
+        self.n, self.T, self.H_q = n_seqs, T, H_q
+        self.num_pages, self.max_pages, self.max_seq_len = num_pages, max_pages, max_seq_len
+        n = n_seqs
+        self.ctrl_len = 2 * n + n * T
+        self.ctrl = torch.zeros(self.ctrl_len, dtype=torch.int32, device=dev)
+        self.lens_dev = self.ctrl[:n]
+        self.in_dev = self.ctrl[n:2 * n]
+        self.out_dev = self.ctrl[2 * n:].view(n, T)
+        self.ctrl_pin = torch.empty((n_steps + 4, self.ctrl_len), dtype=torch.int32, pin_memory=True)
+        self.pt_dev = torch.full((n, max_pages), -1, dtype=torch.int32, device=dev)
+        self.pt_pin = torch.empty(n_steps * n * (T // P + 2) + 16, dtype=torch.int32, pin_memory=True)
+        self.pt_pin_at = 0
+        g = torch.Generator(device=dev)
+        self.attn = []
+        for i in range(N_ATTN):
+            g.manual_seed(synth.seed_of(seed, 100, i))
+            self.attn.append(dict(
+                k_pool=torch.randn((num_pages, H_KV, P, D), generator=g, device=dev, dtype=torch.bfloat16),
+                v_pool=torch.randn((num_pages, H_KV, P, D), generator=g, device=dev, dtype=torch.bfloat16),
+                qg=torch.randn((n, T, H_q, 2, D), generator=g, device=dev, dtype=torch.bfloat16),
+                k=torch.randn((n, T, H_KV, D), generator=g, device=dev, dtype=torch.bfloat16),
+                v=torch.randn((n, T, H_KV, D), generator=g, device=dev, dtype=torch.bfloat16),
+                w_q=torch.rand((D,), generator=g, device=dev) + 0.5,
+                w_k=torch.rand((D,), generator=g, device=dev) + 0.5,
+                q_out=torch.empty((n, T, H_q, D), device=dev, dtype=torch.bfloat16),
+                gate=torch.empty((n, T, H_q, D), device=dev, dtype=torch.bfloat16),
+                out=torch.empty((n, T, H_q, D), device=dev, dtype=torch.bfloat16)))
+        self.desc = had.attn_desc((n, T, H_q, D), (num_pages, H_KV, P, D), max_pages, max_seq_len=max_seq_len)
+        self.n_splits, self.pps = had.decode_attn_plan(self.desc)
+        self.ws = torch.empty(had.decode_attn_workspace_bytes(self.desc), dtype=torch.uint8, device=dev)
+        self.gdn = []
+        for i in range(N_GDN):
+            g.manual_seed(synth.seed_of(seed, 200, i))
+            q = torch.randn((n, T, GDN_H, DK), generator=g, device=dev, dtype=torch.float64)
+            k = torch.randn((n, T, GDN_H, DK), generator=g, device=dev, dtype=torch.float64)
+            self.gdn.append(dict(
+                pool=torch.randn((n_slots, GDN_H, DV, DK), generator=g, device=dev) * 0.05,
+                q=(q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
+                k=(k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
+                v=torch.randn((n, T, GDN_H, DV), generator=g, device=dev, dtype=torch.bfloat16),
+                alpha=torch.rand((n, T, GDN_H), generator=g, device=dev) * 0.1 + 0.9,
+                beta=torch.rand((n, T, GDN_H), generator=g, device=dev),
+                o=torch.empty((n, T, GDN_H, DV), device=dev)))
+        self.graph = None
+
+    def attn_layer(self, i):
+        a = self.attn[i]
+        self.had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
+                                   a["k_pool"], a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
+        self.had.decode_attn(a["q_out"], a["k_pool"], a["v_pool"], self.pt_dev, self.lens_dev,
+                             max_seq_len=self.max_seq_len, workspace=self.ws, out=a["out"])
+
+    def gdn_layer(self, i):
+        g = self.gdn[i]
+        self.had.gdn_state_update(g["pool"], self.in_dev, self.out_dev, g["q"], g["k"], g["v"], g["alpha"],
+                                  g["beta"], o=g["o"])
+
+    def layers(self):
+        ia = ig = 0
+        for l in range(N_ATTN + N_GDN):
+            if l % 4 == 3:
+                self.attn_layer(ia)
+                ia += 1
+            else:
+                self.gdn_layer(ig)
+                ig += 1
+
+    def capture(self):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.layers()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.layers()
+        torch.cuda.synchronize()
+
+    def set_page(self, s, idx, pid):
+        """Patch one device page-table entry (pinned staging, never reused)."""
+        self.pt_pin[self.pt_pin_at] = int(pid)
+        self.pt_dev[s, idx].copy_(self.pt_pin[self.pt_pin_at], non_blocking=True)
+        self.pt_pin_at += 1
+
+    def push_ctrl(self, t, lens, in_idx, out_idx):
+        row = self.ctrl_pin[t]
+        n = self.n
+        row[:n] = torch_int(lens)
+        row[n:2 * n] = torch_int(in_idx)
+        row[2 * n:] = torch_int(out_idx).reshape(-1)
+        self.ctrl.copy_(row, non_blocking=True)
+
+
+def torch_int(x):
+    import torch
+
+    return torch.as_tensor(np.asarray(x, dtype=np.int32).reshape(-1))
+
+
+def stack_kernel_us(st, kernel_reps):
+    """Per-kernel-class averages from captured back-to-back batches."""
+    import torch
+
+    had = st.had
+    n = max(1, kernel_reps)
+
+    def partial(r):
+        a = st.attn[r % N_ATTN]
+        had.decode_attn_partial(a["q_out"], a["k_pool"], a["v_pool"], st.pt_dev, st.lens_dev, st.ws,
+                                max_seq_len=st.max_seq_len)
+
+    def combine(r):
+        had.decode_attn_combine(st.desc, st.n_splits, st.ws, st.attn[r % N_ATTN]["out"])
+
+    def prologue(r):
+        a = st.attn[r % N_ATTN]
+        had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], st.pt_dev, st.lens_dev, a["k_pool"],
+                              a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
+
+    def gdn(r):
+        st.gdn_layer(r % N_GDN)
+
+    return {
+        "attn_partial": round(time_graph(torch, partial, n * N_ATTN), 3),
+        "attn_combine": round(time_graph(torch, combine, n * N_ATTN), 3),
+        "prologue": round(time_graph(torch, prologue, n * N_ATTN), 3),
+        "gdn_update": round(time_graph(torch, gdn, max(2, n) * N_GDN), 3),
+    }
+
+
+def run_speculative(L0=262144, steps=256, warmup=10, kernel_reps=4, T=4, G=16, seed=5):
+    """Speculative verify: T drafts per step, GQA group G (G*T query rows per KV
+    head, MFMA path), GDN checkpoint per draft token into fresh slots, accepted
+    length ~ U{0..T} (seeded), rollback by index."""
+    import torch
+
+    import hybrid_attention_decode_amd as had
+    import synth
+
+    n_steps = steps + warmup
+    max_len = L0 + (n_steps + 2) * T
+    max_pages = -(-max_len // P) + 1
+    num_pages = max_pages + 8
+    n_slots = 2 * T + 2
+    st = Stack(1, T, G, num_pages, max_pages, max_len, n_slots, n_steps, seed)
+    pt = had.PageTable(num_pages, P, 1, max_pages, free_order=synth.permutation(num_pages, synth.seed_of(seed, 1)))
+    slots = had.SlotPool(n_slots, free_order=synth.permutation(n_slots, synth.seed_of(seed, 2)))
+    seq = pt.seq_create()
+    pt.reserve(seq, L0)
+    table, _ = pt.export([seq], max_pages)
+    st.pt_dev.copy_(torch.from_numpy(table))
+    cur = slots.acquire()
+    accepted = synth.integers(0, T, n_steps, synth.seed_of(seed, 3))
+    L = L0
+
+    def step(t):
+        nonlocal cur, L
+        outs = [slots.acquire() for _ in range(T)]
+        held = -(-L // P)
+        assert pt.reserve(seq, T) is None
+        if -(-(L + T) // P) > held:                    # pages handed out for the drafts
+            row = pt.export([seq], max_pages)[0][0]
+            for idx in range(held, -(-(L + T) // P)):
+                st.set_page(0, idx, row[idx])
+        st.push_ctrl(t, [L + T], [cur], [outs])
+        st.graph.replay()
+        a = int(accepted[t])
+        cur = had.spec_rollback(pt, slots, seq, T, a, cur, outs)
+        L += a
+
+    st.push_ctrl(0, [L + T], [cur], [[cur] * T])
+    st.capture()
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L_start = L
+    e0.record()
+    for t in range(warmup, n_steps):
+        step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    acc_mean = float(np.mean(accepted[warmup:n_steps]))
+    mean_len = (L_start + L) / 2.0 + T
+    step_bytes = N_ATTN * mean_len * KV_BYTES_PER_TOKEN + N_GDN * (1 + T) * GDN_BYTES_PER_LAYER // 2
+    us = stack_kernel_us(st, kernel_reps)
+    res = dict(workload="speculative verify: 1 sequence at %d-token context, %d drafts per step, GQA group %d "
+                        "(%d query rows per KV head, MFMA path), GDN checkpoint per draft, accepted ~ U{0..%d}, "
+                        "rollback by index" % (L0, T, G, G * T, T),
+               steps=steps, warmup=warmup, ms_per_step=round(ms, 5), steps_per_s=round(1e3 / ms, 3),
+               accepted_per_step=round(acc_mean, 4), accepted_tokens_per_s=round(acc_mean * 1e3 / ms, 2),
+               algorithmic_bytes_per_step=int(step_bytes),
+               hbm_gbps=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+               attn_partial_gbps=round(L * KV_BYTES_PER_TOKEN / (us["attn_partial"] * 1e-6) / 1e9, 1),
+               us_per_layer=us, num_splits=st.n_splits)
+    log("speculative: %.1f steps/s, %.2f accepted/step, partial %.1f us" % (1e3 / ms, acc_mean, us["attn_partial"]))
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6):
+    """Agentic multi-turn: 50,000-token first turn, then `turns` turns of
+    `turn_len` decode steps; at each turn boundary the current GDN state slot
+    is kept as a cached checkpoint (retained) and the next step reads it and
+    writes a fresh slot."""
+    import torch
+
+    import hybrid_attention_decode_amd as had
+    import synth
+
+    n_steps = turns * turn_len
+    max_len = first_turn + n_steps + 1
+    max_pages = -(-max_len // P) + 1
+    num_pages = max_pages + 8
+    n_slots = turns + 4
+    st = Stack(1, 1, H_Q, num_pages, max_pages, max_len, n_slots, n_steps, seed)
+    pt = had.PageTable(num_pages, P, 1, max_pages, free_order=synth.permutation(num_pages, synth.seed_of(seed, 1)))
+    slots = had.SlotPool(n_slots, free_order=synth.permutation(n_slots, synth.seed_of(seed, 2)))
+    seq = pt.seq_create()
+    pt.reserve(seq, first_turn)
+    table, _ = pt.export([seq], max_pages)
+    st.pt_dev.copy_(torch.from_numpy(table))
+    cur = slots.acquire()
+    L = first_turn
+    checkpoints = []
+
+    def step(t):
+        nonlocal cur, L
+        if t > 0 and t % turn_len == 0:            # turn boundary: keep the state as a checkpoint
+            slots.retain(cur)
+            checkpoints.append(cur)
+        out = slots.acquire()
+        assert pt.reserve(seq, 1) is None
+        L += 1
+        if (L - 1) % P == 0:
+            st.set_page(0, (L - 1) // P, pt.export([seq], max_pages)[0][0, (L - 1) // P])
+        st.push_ctrl(t, [L], [cur], [[out]])
+        st.graph.replay()
+        slots.release(cur)
+        cur = out
+
+    st.push_ctrl(0, [L + 1], [cur], [[cur]])
+    st.capture()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(turns + 1)]
+    e0.record()
+    for t in range(n_steps):
+        if t % turn_len == 0:
+            ev[t // turn_len].record()
+        step(t)
+    ev[turns].record()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_steps
+    per_turn = [ev[i].elapsed_time(ev[i + 1]) / turn_len for i in range(turns)]
+    mean_len = first_turn + (n_steps + 1) / 2.0
+    step_bytes = algorithmic_bytes_per_step(mean_len)
+    us = stack_kernel_us(st, kernel_reps)
+    res = dict(workload="agentic multi-turn: %d-token first turn, %d turns x %d decode steps (context %d -> %d), "
+                        "checkpoint slot kept at every turn boundary" % (first_turn, turns, turn_len, first_turn + 1,
+                                                                         first_turn + n_steps),
+               steps=n_steps, ms_per_step=round(ms, 5), steps_per_s=round(1e3 / ms, 3),
+               first_turn_steps_per_s=round(1e3 / per_turn[0], 2), last_turn_steps_per_s=round(1e3 / per_turn[-1], 2),
+               checkpoints_kept=len(checkpoints), algorithmic_bytes_per_step=int(step_bytes),
+               hbm_gbps=round(step_bytes / (ms * 1e-3) / 1e9, 1), us_per_layer_at_end=us)
+    log("agentic: %.1f steps/s over %d steps" % (1e3 / ms, n_steps))
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warmup=10, kernel_reps=4, seed=7):
+    """Prefix-shared concurrency: n_seqs sequences fork one prefix (page
+    aliasing, copy-on-write of the shared partial page on first append), private
+    suffixes ~ U{0..max_suffix}, GDN input slots drawn as a permutation
+    (sequences without a suffix read the shared prefix checkpoint)."""
+    import torch
+
+    import hybrid_attention_decode_amd as had
+    import synth
+
+    n_steps = steps + warmup
+    suffix = synth.integers(0, max_suffix, n_seqs, synth.seed_of(seed, 4))
+    max_len = prefix + int(suffix.max()) + n_steps + 2
+    max_pages = -(-max_len // P) + 1
+    prefix_pages = -(-prefix // P)
+    num_pages = prefix_pages + sum(-(-(int(x) + n_steps + P) // P) + 1 for x in suffix) + 16
+    n_slots = 64
+    st = Stack(n_seqs, 1, H_Q, num_pages, max_pages, max_len, n_slots, n_steps, seed)
+    pt = had.PageTable(num_pages, P, n_seqs + 1, max_pages,
+                       free_order=synth.permutation(num_pages, synth.seed_of(seed, 1)))
+    root = pt.seq_create()
+    pt.reserve(root, prefix)                                  # the cached prefix
+    seqs = [pt.seq_fork(root, prefix) for _ in range(n_seqs)]
+    n_cow = 0
+
+    def cow(trip):
+        nonlocal n_cow
+        if trip is None:
+            return False
+        for a in st.attn:
+            had.kv_copy_pages(a["k_pool"], a["v_pool"], [trip[0]], [trip[1]])
+        n_cow += 1
+        return True
+
+    for i, sq in enumerate(seqs):                             # private suffixes (raw append)
+        if suffix[i] > 0:
+            cow(pt.reserve(sq, int(suffix[i])))
+    table, lens = pt.export(seqs, max_pages)
+    st.pt_dev.copy_(torch.from_numpy(table))
+    slot_order = synth.permutation(n_slots, synth.seed_of(seed, 2))
+    slots = had.SlotPool(n_slots, free_order=slot_order)
+    shared = slots.acquire()                                  # prefix checkpoint
+    cur = []
+    for i in range(n_seqs):
+        if suffix[i] == 0:
+            slots.retain(shared)
+            cur.append(shared)
+        else:
+            cur.append(slots.acquire())
+    Ls = [int(x) for x in lens]
+
+    def step(t):
+        outs = [slots.acquire() for _ in range(n_seqs)]
+        for i, sq in enumerate(seqs):
+            pos = Ls[i]
+            copied = cow(pt.reserve(sq, 1))
+            Ls[i] += 1
+            if copied or pos % P == 0:                  # the token's page entry changed
+                st.set_page(i, pos // P, pt.export([sq], max_pages)[0][0, pos // P])
+        st.push_ctrl(t, Ls, cur, [[o] for o in outs])
+        st.graph.replay()
+        for i in range(n_seqs):
+            slots.release(cur[i])
+            cur[i] = outs[i]
+
+    tmp = [slots.acquire() for _ in range(n_seqs)]            # distinct slots for the capture run
+    st.push_ctrl(0, [x + 1 for x in Ls], cur, [[o] for o in tmp])
+    st.capture()
+    for o in tmp:
+        slots.release(o)
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L0s = list(Ls)
+    e0.record()
+    for t in range(warmup, n_steps):
+        step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    mean_lens = [(a + b) / 2.0 for a, b in zip(L0s, Ls)]
+    logical = N_ATTN * sum(mean_lens) * KV_BYTES_PER_TOKEN + N_GDN * n_seqs * GDN_BYTES_PER_LAYER
+    unique = N_ATTN * (prefix + sum(m - prefix for m in mean_lens)) * KV_BYTES_PER_TOKEN + \
+        N_GDN * n_seqs * GDN_BYTES_PER_LAYER
+    us = stack_kernel_us(st, kernel_reps)
+    res = dict(workload="prefix-shared: %d sequences fork a %d-token prefix (copy-on-write on the first divergent "
+                        "page), private suffixes ~ U{0..%d}, %d GDN slots, one token per sequence per step"
+                        % (n_seqs, prefix, max_suffix, n_slots),
+               steps=steps, warmup=warmup, ms_per_step=round(ms, 5), steps_per_s=round(1e3 / ms, 3),
+               tokens_per_s=round(n_seqs * 1e3 / ms, 2), cow_copies=n_cow,
+               logical_bytes_per_step=int(logical), unique_bytes_per_step=int(unique),
+               logical_gbps=round(logical / (ms * 1e-3) / 1e9, 1), unique_gbps=round(unique / (ms * 1e-3) / 1e9, 1),
+               us_per_layer=us, num_splits=st.n_splits)
+    log("prefix-shared: %.1f steps/s (%.0f tokens/s), %d CoW copies" % (1e3 / ms, n_seqs * 1e3 / ms, n_cow))
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes=1 << 30):
     """A plain device copy of known size, for scaling the PMC byte counters."""
     import torch
@@ -362,6 +759,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workloads", default="speculative,agentic,prefix",
+                    help="further workloads reported beside the headline (comma list, '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (scales PMC byte counters)")
     args = ap.parse_args()
@@ -384,6 +783,15 @@ def main():
     sweep = []
     for c in [int(x) for x in args.sweep.split(",") if x.strip()]:
         sweep.append(run_context(c, args.steps, args.warmup, args.kernel_reps))
+    extra = {}
+    wl = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    if "speculative" in wl:
+        extra["speculative"] = run_speculative(steps=args.steps, warmup=args.warmup, kernel_reps=args.kernel_reps)
+    if "agentic" in wl:
+        extra["agentic"] = run_agentic(kernel_reps=args.kernel_reps)
+    if "prefix" in wl:
+        extra["prefix_shared"] = run_prefix_shared(steps=args.steps, warmup=args.warmup,
+                                                   kernel_reps=args.kernel_reps)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
@@ -416,6 +824,7 @@ def main():
         "graph_only_ms_per_step": round(head["graph_only_ms_per_step"], 5),
         "num_splits": head["num_splits"],
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
+        "workloads": extra,
         "roofline": roofline(head),
         "cpu_baseline": cpu,
     }
