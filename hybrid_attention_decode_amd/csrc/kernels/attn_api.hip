@@ -56,12 +56,13 @@ int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   if (d->num_splits > 0) {
     ns = d->num_splits;
   } else {
-    // VALU path: one 8-wave workgroup per CU; MFMA path (>= 16 rows): two
-    // 4-wave workgroups per CU, each at least 4 tiles of 32 tokens
+    // one 8-wave workgroup per CU on either path; a VALU unit covers at
+    // least 4 tiles of 8 tokens per wave, an MFMA unit (>= 16 rows) at least
+    // 4 iterations of 64 tokens
     const bool mfma = d->q_len * (d->H_q / d->H_kv) >= 16;
     const int64_t units = static_cast<int64_t>(d->n_seqs) * d->H_kv;
-    const int64_t want = std::max<int64_t>(1, ceil_div(mfma ? 2 * kTargetUnits : kTargetUnits, units));
-    const int64_t min_pps = mfma ? ceil_div(128, d->page_size) : ceil_div(kMinTilesPerUnit, d->page_size / 8);
+    const int64_t want = std::max<int64_t>(1, ceil_div(kTargetUnits, units));
+    const int64_t min_pps = mfma ? ceil_div(256, d->page_size) : ceil_div(kMinTilesPerUnit, d->page_size / 8);
     ns = std::max<int64_t>(1, std::min<int64_t>(want, n_pages / min_pps));
     ns = std::max<int64_t>(ns, ceil_div(n_pages, had::kMaxPagesPerSplit));
   }

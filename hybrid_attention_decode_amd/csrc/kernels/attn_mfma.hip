@@ -7,19 +7,26 @@
 // (sequence, KV head), softmax(sm_scale q K^T) V over the split's tokens,
 // causal inside the draft, written as unnormalised (o, m, l) in base 2.
 //
-// gfx950 mapping (one workgroup = 4 waves, wave w owns query rows
-// 16w .. 16w+15 of the launch; tiles of 32 tokens):
-//  * K and V tiles are staged once per workgroup: global -> registers
-//    (prefetched one tile ahead) -> LDS, double-buffered.  K keeps its
-//    row-major layout with the 16-byte chunks XOR-swizzled by token (so 16
-//    lanes reading 16 tokens hit 16 different bank groups); V is written
-//    d-major (transposed) for the PV operand.
-//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows, B = q rows held
-//    in registers): the C layout leaves each lane 8 token scores of ONE query
-//    row, which is exactly the B operand P^T of O^T = V^T P^T once the 32
-//    tokens are taken in the order tau(g, i) = 4g + i (i < 4), 16 + 4g + i-4
-//    (i >= 4) -- so P never goes through LDS, and the online-softmax
-//    rescale of a lane's O^T accumulators uses the lane's own row state.
+// gfx950 mapping.  One workgroup of 8 waves per split, two teams of 4 waves;
+// each iteration stages 64 tokens of K and V in LDS and team t works on
+// tokens 32t .. 32t+31 of them, wave w of a team owning query rows
+// 16(w mod 4) .. +15 of the launch.  The teams keep separate softmax states
+// and are merged through LDS once at the end, so a split writes one partial
+// however many tokens it covers.
+//  * Staging: global -> registers -> LDS with two register stages in flight
+//    (tiles i+1 and i+2 load while tile i is computed) and two LDS buffers,
+//    one barrier per iteration.  A thread moves one 16-byte chunk column of
+//    TPT consecutive tokens, so its TPT V chunks transpose in registers
+//    (v_perm) into TPT-wide runs of each d-row and go to LDS as 8-byte
+//    writes; K keeps its row-major layout with 16-byte chunks XOR-swizzled
+//    by token row.
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = q
+//    rows held in registers): the C layout leaves each lane 8 token scores
+//    of ONE query row, which is exactly the B operand P^T of O^T = V^T P^T
+//    once the 32 tokens are taken in the order tau(g, i) = 4g + i (i < 4),
+//    16 + 4g + i-4 (i >= 4) -- so P never goes through LDS, and the
+//    online-softmax rescale of a lane's O^T accumulators uses the lane's own
+//    row state (skipped when no row maximum of the wave moved).
 //  * Row maxima and sums combine the 4 lanes of a row with two bpermutes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,41 +39,67 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // staging registers (first-class vectors)
 
-constexpr int kMWaves = 4;
-constexpr int kMRows = 16 * kMWaves;  // query rows per launch
-constexpr int kMTT = 32;              // tokens per tile
+constexpr int kMWaves = 8;                 // two teams of four waves
+constexpr int kMRows = 64;                 // query rows per launch (16 per wave of a team)
+constexpr int kMTeamTok = 32;              // tokens per team per iteration
+constexpr int kMTile = 2 * kMTeamTok;      // tokens staged per iteration
 
 template <int D>
 struct MCfg {
   static constexpr int KS = D / 32;              // QK k-steps (32 d each)
   static constexpr int MB = D / 16;              // PV output blocks (16 d each)
   static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  static constexpr int CPT = kMTT * CPR / 256;   // chunks per thread per tile (K, and again V)
+  static constexpr int TPT = CPR / 8;            // consecutive tokens per staging thread (4, 2, 1)
+  static constexpr int GPT = kMTeamTok / TPT;    // token groups per team
+  static constexpr int CPW = 64 / GPT;           // chunk columns per staging wave
   static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
-  static constexpr int VTP = kMTT + 4;           // bf16 per d-row of the transposed V tile (padded)
-  static_assert(CPT >= 1, "unsupported head_dim");
+  static constexpr int VTP = kMTeamTok + 4;      // bf16 pitch of a transposed V row (padded)
+  static constexpr int OP = D + 4;               // float pitch of a team-merge row (padded)
+  static_assert(CPW * 4 == CPR, "staging map must cover every chunk column");
+};
+
+template <int D>
+struct MTiles {
+  u32x4_t k[2][kMTile * MCfg<D>::CPR];
+  uint16_t vt[2][2][D * MCfg<D>::VTP];  // [buffer][team][d][token]
+};
+
+template <int D>
+struct MMerge {
+  float o[4][16][MCfg<D>::OP];
+  float ml[4][16][2];
 };
 
 template <int D>
 struct MLds {
-  uint4 k[2][kMTT * MCfg<D>::CPR];
-  uint16_t vt[2][D * MCfg<D>::VTP];
+  union {
+    MTiles<D> t;
+    MMerge<D> m;
+  } u;
   int32_t pages[kMaxPagesPerSplit];
   int err;
 };
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// chunk-column swizzle of K row r: x ^ (x >> 2) is one-to-one on 4 bits, so
+// the 16 rows one MFMA operand read touches land in 16 different 16-byte
+// bank groups, and so do the rows 4 apart that one staging store touches
+__device__ __forceinline__ int kswz(int r, int mask) { return (r ^ (r >> 2)) & mask; }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(ValuArgs a) {
+__global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   using C = MCfg<D>;
+  constexpr int TPT = C::TPT;
   __shared__ MLds<D> sh;
   const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
+  const int team = wave >> 2, rb = wave & 3;
   const int P = a.page_size;
 
   const int pg0 = static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
@@ -79,68 +112,95 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(ValuArgs a) {
   const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
   const int tok0 = pg0 * P;
   const int tok_end = npg > 0 ? min((pg0 + npg) * P, L) : tok0;  // this split's tokens: [tok0, tok_end)
-  const int n_tiles = (tok_end - tok0 + kMTT - 1) / kMTT;
+  const int n_it = (tok_end - tok0 + kMTile - 1) / kMTile;
 
   int errs = (bad_len && tid == 0) ? HAD_DERR_SEQLEN : 0;
   if (tid == 0) sh.err = 0;
-  for (int i = tid; i < npg_plan; i += blockDim.x) {
-    const int pid = pt_row[pg0 + i];
+  // page ids of the split (entry 0 always written, so the clamped loads of an
+  // empty split still read a valid page); bad ids become -1 and read page 0
+  for (int i = tid; i < max(npg_plan, 1); i += blockDim.x) {
+    const int pid = i < npg_plan ? pt_row[pg0 + i] : -1;
     const bool ok = pid >= 0 && pid < a.num_pages;
     if (!ok && i < npg) errs |= HAD_DERR_PAGE;
     sh.pages[i] = ok ? pid : -1;
   }
 
   // q rows of this wave as the B operand of S^T = K Q^T: lane (r16, g) holds
-  // row 16*wave + r16, dims 32*ks + 8g .. +8 (zero for padding rows)
-  const int row = a.row_base + 16 * wave + r16;
+  // row 16*rb + r16, dims 32*ks + 8g .. +8 (zero for padding rows)
+  const int row = a.row_base + 16 * rb + r16;
   const bool row_ok = row < a.rows;
-  uint4 qb[C::KS];
+  const bool wave_active = a.row_base + 16 * rb < a.rows;  // uniform: any row of this wave real
+  u32x4_t qb[C::KS];
   {
     const int rc = row_ok ? row : 0;
     const uint16_t* qp = a.q + ((static_cast<size_t>(s) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * ks + 8 * g);
-      qb[ks] = row_ok ? v : make_uint4(0u, 0u, 0u, 0u);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g);
+      qb[ks] = row_ok ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
   const int lim = row_ok ? (L - a.q_len + row / a.G + 1) : L;  // visible keys of this lane's row
 
+  // staging map: wave w moves tokens of team w/4, chunk columns
+  // CPW*(w%4) .. +CPW; lane -> (token group lu, chunk column lc)
+  const int lu = lane % C::GPT;
+  const int lc = (wave & 3) * C::CPW + lane / C::GPT;
+  const int ltok = (wave >> 2) * kMTeamTok + lu * TPT;  // first tile row of the group
+  const int last_tok = max(tok_end - 1, tok0);
+  const int last_pg = max(npg - 1, 0);
+
   __syncthreads();
 
-  // ---- K/V staging: thread tid moves chunks id = tid + 256*i of the tile
-  uint4 kreg[C::CPT], vreg[C::CPT];
-  auto load_regs = [&](int tile) __attribute__((always_inline)) {
+  // every staging load is unconditional: tokens past the split clamp to its
+  // last token, so the addresses stay in bounds and the compiler can count
+  // the loads in flight exactly
+  auto load = [&](u32x4_t (&kr)[TPT], u32x4_t (&vr)[TPT], int it) __attribute__((always_inline)) {
+    const int t0 = min(tok0 + it * kMTile + ltok, last_tok);
+    int pid = sh.pages[min(t0 / P - pg0, last_pg)];
+    pid = pid < 0 ? 0 : pid;
+    const uint16_t* kb = a.k_pool + (static_cast<size_t>(pid) * a.H_kv + h) * P * D + lc * 8;
+    const uint16_t* vb = a.v_pool + (static_cast<size_t>(pid) * a.H_kv + h) * P * D + lc * 8;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int id = tid + 256 * i;
-      const int tt = id / C::CPR, c = id % C::CPR;
-      const int tok = min(tok0 + tile * kMTT + tt, max(tok_end - 1, tok0));
-      int pid = sh.pages[min(tok / P - pg0, max(npg - 1, 0))];
-      pid = pid < 0 ? 0 : pid;
-      const size_t off = ((static_cast<size_t>(pid) * a.H_kv + h) * P + tok % P) * D + c * 8;
-      kreg[i] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-      vreg[i] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+    for (int i = 0; i < TPT; ++i) {
+      const int t = min(t0 + i, last_tok) % P;  // the group never leaves its page (P % TPT == 0)
+      kr[i] = *reinterpret_cast<const u32x4_t*>(kb + t * D);
+      vr[i] = *reinterpret_cast<const u32x4_t*>(vb + t * D);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto store_lds = [&](int tile, int b) __attribute__((always_inline)) {
+
+  auto stage = [&](const u32x4_t (&kr)[TPT], const u32x4_t (&vr)[TPT], int it, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int id = tid + 256 * i;
-      const int tt = id / C::CPR, c = id % C::CPR;
-      const int tok = tok0 + tile * kMTT + tt;
-      const bool tok_ok = tok < tok_end && sh.pages[min(tok / P - pg0, max(npg - 1, 0))] >= 0;
-      sh.k[b][tt * C::CPR + (c ^ (tt & C::SWZ))] = kreg[i];
-      // V transposed; rows that must not count (past the split, past the
-      // length, unchecked page) are written as zeros so stale bits never meet
-      // a zero probability
-      const uint4 v = tok_ok ? vreg[i] : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint16_t* vt = &sh.vt[b][(8 * c) * C::VTP + tt];
+    for (int i = 0; i < TPT; ++i) {
+      const int r = ltok + i;
+      sh.u.t.k[b][r * C::CPR + (lc ^ kswz(r, C::SWZ))] = kr[i];
+    }
+    // V rows that must not count (past the split, unchecked page) are
+    // staged as zeros so stale bits never meet a zero probability
+    const int tg = tok0 + it * kMTile + ltok;
+    const bool pg_ok = tg < tok_end && sh.pages[min(tg / P - pg0, last_pg)] >= 0;
+    u32x4_t v[TPT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(2 * e) * C::VTP] = static_cast<uint16_t>(w[e] & 0xffffu);
-        vt[(2 * e + 1) * C::VTP] = static_cast<uint16_t>(w[e] >> 16);
+    for (int i = 0; i < TPT; ++i) v[i] = (pg_ok && tg + i < tok_end) ? vr[i] : u32x4_t{0u, 0u, 0u, 0u};
+    uint16_t* vt = &sh.u.t.vt[b][ltok / kMTeamTok][(8 * lc) * C::VTP + lu * TPT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // word j holds d = 8 lc + 2j (low half) and 8 lc + 2j + 1 (high half)
+      uint16_t* lo_row = vt + (2 * j) * C::VTP;
+      uint16_t* hi_row = vt + (2 * j + 1) * C::VTP;
+      if constexpr (TPT == 4) {
+        const uint32_t l01 = perm_b32(v[1][j], v[0][j], 0x05040100u);
+        const uint32_t l23 = perm_b32(v[3][j], v[2][j], 0x05040100u);
+        const uint32_t h01 = perm_b32(v[1][j], v[0][j], 0x07060302u);
+        const uint32_t h23 = perm_b32(v[3][j], v[2][j], 0x07060302u);
+        *reinterpret_cast<uint2*>(lo_row) = make_uint2(l01, l23);
+        *reinterpret_cast<uint2*>(hi_row) = make_uint2(h01, h23);
+      } else if constexpr (TPT == 2) {
+        *reinterpret_cast<uint32_t*>(lo_row) = perm_b32(v[1][j], v[0][j], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(hi_row) = perm_b32(v[1][j], v[0][j], 0x07060302u);
+      } else {
+        *lo_row = static_cast<uint16_t>(v[0][j] & 0xffffu);
+        *hi_row = static_cast<uint16_t>(v[0][j] >> 16);
       }
     }
   };
@@ -150,30 +210,27 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(ValuArgs a) {
   for (int mb = 0; mb < C::MB; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (n_tiles > 0) load_regs(0);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int b = tile & 1;
-    store_lds(tile, b);
-    if (tile + 1 < n_tiles) load_regs(tile + 1);
-    __syncthreads();
-
-    // ---- S^T for the 32 tokens: two 16-token blocks, KS k-steps each
+  auto compute = [&](int it, int b) __attribute__((always_inline)) {
+    if (!wave_active) return;
+    const u32x4_t* kt = sh.u.t.k[b];
+    const uint16_t* vt = sh.u.t.vt[b][team];
+    // ---- S^T for the team's 32 tokens: two 16-token blocks, KS k-steps each
     float sc[8];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const int tt = 16 * tb + r16;  // A-operand row = token
+      const int r = team * kMTeamTok + 16 * tb + r16;  // A-operand row = token
+      const int sw = kswz(r, C::SWZ);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const int c = 4 * ks + g;
-        const uint4 kv = sh.k[b][tt * C::CPR + (c ^ (tt & C::SWZ))];
+        const u32x4_t kv = kt[r * C::CPR + ((4 * ks + g) ^ sw)];
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qb[ks]), acc, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * tb + i] = acc[i] * a.scale_log2;
     }
-    // tokens of slot i: tau(g, i) = 4g + i and 16 + 4g + i
-    const int pos0 = tok0 + tile * kMTT;
+    // tokens of slot i: tau(g, i) = 4g + i and 16 + 4g + i - 4
+    const int pos0 = tok0 + it * kMTile + team * kMTeamTok;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int pos = pos0 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
@@ -197,36 +254,82 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(ValuArgs a) {
       lsum += bf16_lo(pw[i]) + bf16_hi(pw[i]);
     }
     l_run = l_run * alpha + lsum;
+    if (__any(m_new != m_run)) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) o[mb] = o[mb] * alpha;
+    }
     m_run = m_new;
-    const uint4 pb = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    const u32x4_t pb = {pw[0], pw[1], pw[2], pw[3]};
 
     // ---- O^T += V^T P^T over the 32 tokens, one MFMA per 16 output dims
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
-      const uint16_t* vrow = &sh.vt[b][(16 * mb + r16) * C::VTP];
+      const uint16_t* vrow = vt + (16 * mb + r16) * C::VTP;
       const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
       const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-      const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      o[mb] = o[mb] * alpha;
+      const u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
       o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), o[mb], 0, 0, 0);
     }
+  };
+
+  // ---- main loop: register stages A (even tiles) and B (odd tiles), LDS
+  // buffer 0 for A and 1 for B; the loop exits only at its header
+  u32x4_t kA[TPT], vA[TPT], kB[TPT], vB[TPT];
+  load(kA, vA, 0);
+  load(kB, vB, 1);
+  int it = 0;
+  while (it + 1 < n_it) {
+    stage(kA, vA, it, 0);
+    load(kA, vA, it + 2);
+    __syncthreads();
+    compute(it, 0);
+    stage(kB, vB, it + 1, 1);
+    load(kB, vB, it + 3);
+    __syncthreads();
+    compute(it + 1, 1);
+    it += 2;
+  }
+  if (it < n_it) {
+    stage(kA, vA, it, 0);
+    __syncthreads();
+    compute(it, 0);
   }
 
-  // ---- row totals and the partial store (no cross-wave merge: waves own rows)
+  // ---- row totals, then team 1 hands its state to team 0 through LDS
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
   if (errs) atomicOr(&sh.err, errs);
+  __syncthreads();  // the tile buffers are free from here on
+  if (team == 1 && wave_active) {
+    float* orow = sh.u.m.o[rb][r16];
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+      *reinterpret_cast<float4*>(orow + 16 * mb + 4 * g) = make_float4(o[mb][0], o[mb][1], o[mb][2], o[mb][3]);
+    if (g == 0) {
+      sh.u.m.ml[rb][r16][0] = m_run;
+      sh.u.m.ml[rb][r16][1] = l_run;
+    }
+  }
   __syncthreads();
   if (tid == 0 && sh.err) set_err(a.d_err, sh.err);
-  if (row_ok) {
+  if (team == 0 && row_ok) {
+    const float m1 = sh.u.m.ml[rb][r16][0], l1 = sh.u.m.ml[rb][r16][1];
+    const float M = fmaxf(m_run, m1);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    const float w0 = exp2f(m_run - Ms), w1 = exp2f(m1 - Ms);
+    const float* orow = sh.u.m.o[rb][r16];
     const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.num_splits + sp;
     float* op = a.ws_o + (unit * a.rows + row) * D;
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-      *reinterpret_cast<float4*>(op + 16 * mb + 4 * g) = make_float4(o[mb][0], o[mb][1], o[mb][2], o[mb][3]);
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const float4 o1 = *reinterpret_cast<const float4*>(orow + 16 * mb + 4 * g);
+      *reinterpret_cast<float4*>(op + 16 * mb + 4 * g) =
+          make_float4(o[mb][0] * w0 + o1.x * w1, o[mb][1] * w0 + o1.y * w1, o[mb][2] * w0 + o1.z * w1,
+                      o[mb][3] * w0 + o1.w * w1);
+    }
     if (g == 0) {
-      a.ws_ml[(unit * a.rows + row) * 2 + 0] = m_run;
-      a.ws_ml[(unit * a.rows + row) * 2 + 1] = l_run;
+      a.ws_ml[(unit * a.rows + row) * 2 + 0] = M;
+      a.ws_ml[(unit * a.rows + row) * 2 + 1] = l_run * w0 + l1 * w1;
     }
   }
 }
@@ -239,9 +342,9 @@ hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipSt
   for (int rb = 0; rb < a.rows && e == hipSuccess; rb += kMRows) {
     a.row_base = rb;
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL(attn_mfma_kernel<256>, grid, dim3(256), 0, stream, a); break;
+      case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(64 * kMWaves), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(64 * kMWaves), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(attn_mfma_kernel<256>, grid, dim3(64 * kMWaves), 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();
