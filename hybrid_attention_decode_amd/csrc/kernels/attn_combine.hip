@@ -9,10 +9,11 @@
 // rounding (long contexts up to 1M tokens, 24-ai.news long-context table).
 //
 // The merge reads every partial once (rows x splits x head_dim fp32) and is
-// bound by memory latency, not bandwidth: one 8-wave block per row issues
-// all of its partial loads (float4 per lane, up to 256 splits per pass)
-// before it touches any of them, reads the maxima in the same round trip,
-// and reduces across waves through LDS.
+// bound by memory latency and by how many CUs pull the partials, not by
+// HBM bandwidth: one 4-wave block per (row, 32-dim slice) -- 8 blocks per
+// row at head_dim 256 -- issues all of its partial loads (float4 per lane,
+// up to 256 splits per pass) before it touches any of them, reads the
+// maxima in the same round trip, and reduces across waves through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,41 +23,43 @@
 namespace had {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
+constexpr int kDC = 32;                      // output dims per block
+constexpr int kLS = kDC / 4;                 // lanes per split row (float4 each)
+constexpr int kSPW = 64 / kLS;               // split rows per wave per load
+constexpr int kU = 8;                        // loads per lane per pass
+constexpr int kPass = kWaves * kSPW * kU;    // splits per pass (256)
+static_assert(kPass <= 64 * kWaves, "one maximum per thread per pass");
 
-template <int D>
-__global__ __launch_bounds__(512) void attn_combine_kernel(CombineArgs a) {
-  constexpr int LS = D / 4;          // lanes per split row (float4 each)
-  constexpr int SPW = 64 / LS;       // split rows per wave per load
-  constexpr int U = 32 / SPW;        // loads per lane per pass
-  constexpr int PASS = kWaves * SPW * U;  // splits per pass (256)
-  __shared__ float wsh[PASS];
-  __shared__ float4 red[kWaves][LS];
+__global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a, int D) {
+  __shared__ float wsh[kPass];
+  __shared__ float4 red[kWaves][kLS];
   __shared__ float scal[kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int sub = lane / LS, dl = lane % LS;
+  const int sub = lane / kLS, dl = lane % kLS;
   const int row = blockIdx.x;
-  const int unit = blockIdx.y;  // s * H_kv + h
+  const int d0 = blockIdx.y * kDC;
+  const int unit = blockIdx.z;  // s * H_kv + h
   const int ns = a.num_splits;
   const size_t base = static_cast<size_t>(unit) * ns;
   const float* ml = a.ws_ml;
-  const size_t ostride = static_cast<size_t>(a.rows) * D;  // floats between consecutive splits
-  const float4* o4 = reinterpret_cast<const float4*>(a.ws_o + (base * a.rows + row) * D);
+  const size_t ostride4 = static_cast<size_t>(a.rows) * D / 4;  // float4s between consecutive splits
+  const float4* o4 = reinterpret_cast<const float4*>(a.ws_o + (base * a.rows + row) * D + d0);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float M = -INFINITY;
   float lsum = 0.f;
-  for (int p0 = 0; p0 < ns; p0 += PASS) {
+  for (int p0 = 0; p0 < ns; p0 += kPass) {
     // issue every load of this pass first
-    float4 ov[U];
+    float4 ov[kU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = p0 + (u * kWaves + wave) * SPW + sub;
-      ov[u] = (i < ns) ? o4[i * (ostride / 4) + dl] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < kU; ++u) {
+      const int i = p0 + (u * kWaves + wave) * kSPW + sub;
+      ov[u] = (i < ns) ? o4[i * ostride4 + dl] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float mi = -INFINITY, li = 0.f;
-    const int my = p0 + tid;  // this thread's split for the maxima (PASS <= blockDim)
-    if (tid < PASS && my < ns) {
+    const int my = p0 + tid;  // this thread's split for the maxima
+    if (tid < kPass && my < ns) {
       mi = ml[((base + my) * a.rows + row) * 2];
       li = ml[((base + my) * a.rows + row) * 2 + 1];
     }
@@ -75,15 +78,15 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineArgs a) {
     acc.x *= rescale; acc.y *= rescale; acc.z *= rescale; acc.w *= rescale;
     lsum *= rescale;
     M = M_new;
-    if (tid < PASS && my < ns) {
+    if (tid < kPass && my < ns) {
       const float w = (mi == -INFINITY) ? 0.f : exp2f(mi - Ms);
       wsh[tid] = w;
       lsum += w * li;
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int il = (u * kWaves + wave) * SPW + sub;
+    for (int u = 0; u < kU; ++u) {
+      const int il = (u * kWaves + wave) * kSPW + sub;
       if (p0 + il < ns) {
         const float w = wsh[il];
         acc.x += w * ov[u].x; acc.y += w * ov[u].y; acc.z += w * ov[u].z; acc.w += w * ov[u].w;
@@ -91,9 +94,9 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineArgs a) {
     }
     __syncthreads();
   }
-  // sum over the SPW sub-rows of a wave, then over the waves
+  // sum over the split sub-rows of a wave, then over the waves
 #pragma unroll
-  for (int off = LS; off < 64; off <<= 1) {
+  for (int off = kLS; off < 64; off <<= 1) {
     acc.x += shfl_xor_f(acc.x, off); acc.y += shfl_xor_f(acc.y, off);
     acc.z += shfl_xor_f(acc.z, off); acc.w += shfl_xor_f(acc.w, off);
   }
@@ -102,9 +105,10 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineArgs a) {
   for (int off = 32; off >= 1; off >>= 1) lsum += shfl_xor_f(lsum, off);
   if (lane == 0) scal[wave] = lsum;
   __syncthreads();
-  if (tid < LS) {
+  if (tid < kLS) {
     float4 t = red[0][tid];
     float l = scal[0];
+#pragma unroll
     for (int w = 1; w < kWaves; ++w) {
       t.x += red[w][tid].x; t.y += red[w][tid].y; t.z += red[w][tid].z; t.w += red[w][tid].w;
       l += scal[w];
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineArgs a) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     const int s = unit / a.H_kv, h = unit % a.H_kv;
     const int jq = row / a.G, g = row % a.G;
-    uint16_t* op = a.out + ((static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g) * D + 4 * tid;
+    uint16_t* op = a.out + ((static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g) * D + d0 + 4 * tid;
     const uint32_t lo = pack_bf16x2(t.x * inv, t.y * inv), hi = pack_bf16x2(t.z * inv, t.w * inv);
     *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
   }
@@ -121,13 +125,9 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineArgs a) {
 }  // namespace
 
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid(a.rows, a.n_seqs * a.H_kv);
-  switch (head_dim) {
-    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(64 * kWaves), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(64 * kWaves), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(attn_combine_kernel<256>, grid, dim3(64 * kWaves), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return hipErrorInvalidValue;
+  const dim3 grid(a.rows, head_dim / kDC, a.n_seqs * a.H_kv);
+  hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(64 * kWaves), 0, stream, a, head_dim);
   return hipGetLastError();
 }
 
