@@ -59,6 +59,32 @@ def sequential(S0, q, k, v, alpha, beta, q_scale=1.0):
     return states, outs
 
 
+def sequential_heads(S0, q, k, v, alpha, beta, q_scale=1.0):
+    """All heads of one sequence over T tokens, in the rank-one form.
+
+    S (I - beta k k^T) = S - beta (S k) k^T, so each token costs O(d_v d_k)
+    per head instead of the dense product's O(d_v d_k^2); the result is the
+    same recurrence as ``step`` (pinned against it to 1e-12).  S0 [H, d_v,
+    d_k]; q, k [T, H, d_k]; v [T, H, d_v]; alpha, beta [T, H].  Returns
+    (final state [H, d_v, d_k], outputs [T, H, d_v]); intermediate states are
+    not kept, so a long chain stays cheap in memory.
+    """
+    S = np.array(S0, np.float64, copy=True)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    beta = np.asarray(beta, np.float64)
+    T = q.shape[0]
+    outs = np.empty((T,) + v.shape[1:])
+    for t in range(T):
+        Sk = np.einsum("hvk,hk->hv", S, k[t])
+        S = alpha[t][:, None, None] * (S - beta[t][:, None, None] * Sk[:, :, None] * k[t][:, None, :]) \
+            + beta[t][:, None, None] * v[t][:, :, None] * k[t][:, None, :]
+        outs[t] = q_scale * np.einsum("hvk,hk->hv", S, q[t])
+    return S, outs
+
+
 def chunked(S0, q, k, v, alpha, beta, chunk, q_scale=1.0):
     """The same recurrence evaluated chunk by chunk (WY / UT form).
 

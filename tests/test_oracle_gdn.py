@@ -138,3 +138,32 @@ def test_state_update_slots_and_checkpoints():
     new2, _ = gdn.state_update(pool, np.array([3]), np.array([[3]]), q[:1, :1], k[:1, :1], v[:1, :1], al[:1, :1], be[:1, :1])
     st, _ = gdn.sequential(pool[3, 0].astype(np.float64), q[0, :1, 0], k[0, :1, 0], v[0, :1, 0], al[0, :1, 0], be[0, :1, 0])
     assert np.array_equal(new2[3, 0], st[0].astype(np.float32))
+
+
+def test_rank_one_heads_match_dense_definition():
+    # several heads, ragged magnitudes, q_scale != 1: the rank-one form used
+    # for long chains equals the dense per-head recurrence
+    rng = np.random.default_rng(7)
+    H, T, dv, dk = 3, 9, 5, 6
+    S0 = rng.standard_normal((H, dv, dk))
+    q, k = rng.standard_normal((T, H, dk)), _unit(rng, T * H, dk).reshape(T, H, dk) * 1.3
+    v = rng.standard_normal((T, H, dv))
+    al, be = rng.uniform(0.8, 1.0, (T, H)), rng.uniform(0.0, 1.0, (T, H))
+    S, o = gdn.sequential_heads(S0, q, k, v, al, be, q_scale=0.7)
+    for h in range(H):
+        st, oh = gdn.sequential(S0[h], q[:, h], k[:, h], v[:, h], al[:, h], be[:, h], q_scale=0.7)
+        np.testing.assert_allclose(S[h], st[-1], atol=1e-12)
+        np.testing.assert_allclose(o[:, h], oh, atol=1e-12)
+
+
+def test_rank_one_heads_reproduce_hand_worked_2x2():
+    g = _golden()
+    f = lambda xs: np.array([float(x) for x in xs])
+    S0 = f(g["S0"][0]).reshape(1, 2, 2)
+    t1, t2 = g["token1"][0], g["token2"][0]
+    k = np.stack([f(t1[1:3]), f(t2[1:3])])[:, None, :]
+    v = np.stack([f(t1[4:6]), f(t2[4:6])])[:, None, :]
+    al = np.array([[float(t1[7])], [float(t2[7])]])
+    be = np.array([[float(t1[9])], [float(t2[9])]])
+    S, _ = gdn.sequential_heads(S0, np.zeros((2, 1, 2)), k, v, al, be)
+    np.testing.assert_allclose(S[0], f(g["S2"][0]).reshape(2, 2), atol=1e-14)
