@@ -13,8 +13,9 @@ One step = one decode token through the whole stack:
          length and, on a page boundary, of the new page-table entry)
   device replay of a captured HIP graph of the 48 layers:
          GDN layer       had_gdn_state_update  (slot ping-pong by index)
-         attention layer had_qk_norm_rope_gate -> had_decode_attn
-                         (split-K partial + combine)
+         attention layer had_decode_attn_layer: the prologue (QK-RMSNorm,
+                         partial RoPE, gate split, K/V append) runs inside the
+                         split-K partial kernel, then the combine kernel
 
 Prints one JSON line (stdout).  Progress goes to stderr.
 """
@@ -121,10 +122,9 @@ class LongContextStack:
     # --- the per-layer calls ---------------------------------------------------
     def attn_layer(self, i):
         a = self.attn[i]
-        self.had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
-                                   a["k_pool"], a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
-        self.had.decode_attn(a["q_out"], a["k_pool"], a["v_pool"], self.pt_dev, self.lens_dev,
-                             max_seq_len=self.total, workspace=self.ws, out=a["out"])
+        self.had.decode_attn_layer(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
+                                   a["k_pool"], a["v_pool"], R, max_seq_len=self.total, workspace=self.ws,
+                                   out=a["out"], gate_out=a["gate"])
 
     def gdn_layer(self, i, parity):
         g = self.gdn[i]
@@ -232,18 +232,14 @@ def run_context(L0, steps, warmup, kernel_reps, seed=0):
     ws = st.ws
     n = max(1, kernel_reps)
 
-    def partial(r):
+    def partial(r):  # the fused kernel: prologue + split-K partials
         a = st.attn[r % N_ATTN]
-        had.decode_attn_partial(a["q_out"], a["k_pool"], a["v_pool"], st.pt_dev, st.lens_dev, ws,
-                                max_seq_len=st.total)
+        had.decode_attn_layer(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], st.pt_dev, st.lens_dev, a["k_pool"],
+                              a["v_pool"], R, max_seq_len=st.total, workspace=ws, gate_out=a["gate"],
+                              out=a["out"], partial_only=True)
 
     def combine(r):
         had.decode_attn_combine(st.desc, st.n_splits, ws, st.attn[r % N_ATTN]["out"])
-
-    def prologue(r):
-        a = st.attn[r % N_ATTN]
-        had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], st.pt_dev, st.lens_dev, a["k_pool"],
-                              a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
 
     def gdn(r):
         st.gdn_layer(r % N_GDN, r % 2)
@@ -251,7 +247,6 @@ def run_context(L0, steps, warmup, kernel_reps, seed=0):
     us = {
         "attn_partial": time_graph(torch, partial, n * N_ATTN),
         "attn_combine": time_graph(torch, combine, n * N_ATTN),
-        "prologue": time_graph(torch, prologue, n * N_ATTN),
         "gdn_update": time_graph(torch, gdn, max(2, n) * N_GDN),
     }
     attn_bytes = L * KV_BYTES_PER_TOKEN
@@ -260,7 +255,7 @@ def run_context(L0, steps, warmup, kernel_reps, seed=0):
         mean_context_timed=mean_len, algorithmic_bytes_per_step=step_bytes,
         hbm_gbps=step_bytes / (ms * 1e-3) / 1e9, hbm_frac=step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         us_per_layer={k: round(v, 3) for k, v in us.items()},
-        attn_us_per_layer=round(us["attn_partial"] + us["attn_combine"] + us["prologue"], 3),
+        attn_us_per_layer=round(us["attn_partial"] + us["attn_combine"], 3),
         attn_partial_gbps=attn_bytes / (us["attn_partial"] * 1e-6) / 1e9,
         attn_partial_bytes_per_launch=attn_bytes, attn_partial_context=L,
         num_splits=st.n_splits, pages_per_split=st.pps,
@@ -336,10 +331,9 @@ class Stack:
 
     def attn_layer(self, i):
         a = self.attn[i]
-        self.had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
-                                   a["k_pool"], a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
-        self.had.decode_attn(a["q_out"], a["k_pool"], a["v_pool"], self.pt_dev, self.lens_dev,
-                             max_seq_len=self.max_seq_len, workspace=self.ws, out=a["out"])
+        self.had.decode_attn_layer(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
+                                   a["k_pool"], a["v_pool"], R, max_seq_len=self.max_seq_len, workspace=self.ws,
+                                   out=a["out"], gate_out=a["gate"])
 
     def gdn_layer(self, i):
         g = self.gdn[i]
@@ -397,18 +391,14 @@ def stack_kernel_us(st, kernel_reps):
     had = st.had
     n = max(1, kernel_reps)
 
-    def partial(r):
+    def partial(r):  # the fused kernel: prologue + split-K partials
         a = st.attn[r % N_ATTN]
-        had.decode_attn_partial(a["q_out"], a["k_pool"], a["v_pool"], st.pt_dev, st.lens_dev, st.ws,
-                                max_seq_len=st.max_seq_len)
+        had.decode_attn_layer(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], st.pt_dev, st.lens_dev, a["k_pool"],
+                              a["v_pool"], R, max_seq_len=st.max_seq_len, workspace=st.ws, gate_out=a["gate"],
+                              out=a["out"], partial_only=True)
 
     def combine(r):
         had.decode_attn_combine(st.desc, st.n_splits, st.ws, st.attn[r % N_ATTN]["out"])
-
-    def prologue(r):
-        a = st.attn[r % N_ATTN]
-        had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], st.pt_dev, st.lens_dev, a["k_pool"],
-                              a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
 
     def gdn(r):
         st.gdn_layer(r % N_GDN)
@@ -416,7 +406,6 @@ def stack_kernel_us(st, kernel_reps):
     return {
         "attn_partial": round(time_graph(torch, partial, n * N_ATTN), 3),
         "attn_combine": round(time_graph(torch, combine, n * N_ATTN), 3),
-        "prologue": round(time_graph(torch, prologue, n * N_ATTN), 3),
         "gdn_update": round(time_graph(torch, gdn, max(2, n) * N_GDN), 3),
     }
 
@@ -684,7 +673,7 @@ def copy_calibration(nbytes=1 << 30):
 def roofline(res):
     r = dict(bound="hbm", achieved=round(res["attn_partial_gbps"], 1), peak=PEAK_HBM_GBPS, unit="GB/s",
              frac=round(res["attn_partial_gbps"] / PEAK_HBM_GBPS, 4), traffic=None,
-             kernel="attn_valu_kernel<256>", bytes_per_launch=res["attn_partial_bytes_per_launch"],
+             kernel="attn_valu_kernel<256, true> (prologue fused)", bytes_per_launch=res["attn_partial_bytes_per_launch"],
              context=res["attn_partial_context"])
     try:
         with open(PMC_SUMMARY) as f:

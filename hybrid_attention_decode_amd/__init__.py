@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     attn_desc,
     decode_attn,
     decode_attn_combine,
+    decode_attn_layer,
     decode_attn_partial,
     decode_attn_plan,
     decode_attn_workspace_bytes,

@@ -110,6 +110,10 @@ _SIGS = {
     "had_decode_attn": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
     "had_decode_attn_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
     "had_decode_attn_combine": ([ctypes.POINTER(AttnDesc), _i32, _p, _p, _p], ctypes.c_int),
+    "had_decode_attn_layer": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc), ctypes.POINTER(QknrgPtrs), _p,
+                               ctypes.c_size_t, _p, _p], ctypes.c_int),
+    "had_decode_attn_layer_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc),
+                                       ctypes.POINTER(QknrgPtrs), _p, ctypes.c_size_t, _p], ctypes.c_int),
     "had_gdn_state_update": ([ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnPtrs), _p], ctypes.c_int),
 }
 
@@ -378,6 +382,44 @@ def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_
                     workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"))
     _check(lib().had_decode_attn(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
     return out
+
+
+def decode_attn_layer(qg, k, v, w_q, w_k, page_table, seq_lens, k_pool, v_pool, rotary_dim, rope_base=10000.0,
+                      eps=1e-6, sm_scale=None, max_seq_len=0, num_splits=0, workspace=None, out=None, gate_out=None,
+                      q_out=None, d_err=None, deterministic=False, partial_only=False):
+    """qk_norm_rope_gate + decode_attn in one pass (the prologue runs inside
+    the attention kernel).  qg [S, T, H_q, 2, D]; k, v [S, T, H_kv, D].
+    Returns (out, gate_out) [S, T, H_q, D]; q_out is written when given.
+    partial_only: stop after the partials (workspace), out is not written."""
+    torch = _torch()
+    S, T, H_q, two, D = qg.shape
+    H_kv = k.shape[2]
+    desc = attn_desc((S, T, H_q, D), k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits,
+                     deterministic)
+    pdesc = QknrgDesc(S, T, H_q, H_kv, D, rotary_dim, float(rope_base), float(eps), k_pool.shape[0], k_pool.shape[2],
+                      page_table.shape[1])
+    need = decode_attn_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qg.device)
+    if out is None:
+        out = torch.empty((S, T, H_q, D), dtype=torch.bfloat16, device=qg.device)
+    if gate_out is None:
+        gate_out = torch.empty((S, T, H_q, D), dtype=torch.bfloat16, device=qg.device)
+    ptrs = QknrgPtrs(_dev(qg, torch.bfloat16, "qg"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+                     _dev(w_q, torch.float32, "w_q"), _dev(w_k, torch.float32, "w_k"),
+                     _dev(page_table, torch.int32, "page_table"), _dev(seq_lens, torch.int32, "seq_lens"),
+                     _dev(k_pool, torch.bfloat16, "k_pool"), _dev(v_pool, torch.bfloat16, "v_pool"),
+                     None if q_out is None else _dev(q_out, torch.bfloat16, "q_out"),
+                     _dev(gate_out, torch.bfloat16, "gate_out"), _opt(d_err, "d_err"))
+    if partial_only:
+        _check(lib().had_decode_attn_layer_partial(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(ptrs),
+                                                   _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                                   _stream()))
+    else:
+        _check(lib().had_decode_attn_layer(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(ptrs),
+                                           _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                           _dev(out, torch.bfloat16, "out"), _stream()))
+    return out, gate_out
 
 
 def decode_attn_partial(q, k_pool, v_pool, page_table, seq_lens, workspace, sm_scale=None, max_seq_len=0,

@@ -79,9 +79,18 @@ int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   return HAD_OK;
 }
 
-size_t ws_bytes(const had_attn_desc* d, int ns) {
+size_t ws_partials_bytes(const had_attn_desc* d, int ns) {
   const size_t rows = static_cast<size_t>(d->q_len) * (d->H_q / d->H_kv);
   return static_cast<size_t>(d->n_seqs) * d->H_kv * ns * rows * (d->head_dim + 2) * sizeof(float);
+}
+
+// partials, then (256-byte aligned) a bf16 q block [n_seqs][q_len][H_q][D]
+// that had_decode_attn_layer uses when the prologue runs as its own kernel
+size_t ws_q_offset(const had_attn_desc* d, int ns) { return (ws_partials_bytes(d, ns) + 255) & ~size_t(255); }
+
+size_t ws_bytes(const had_attn_desc* d, int ns) {
+  return ws_q_offset(d, ns) +
+         static_cast<size_t>(d->n_seqs) * d->q_len * d->H_q * d->head_dim * sizeof(uint16_t);
 }
 
 }  // namespace
@@ -107,12 +116,14 @@ size_t had_decode_attn_workspace_bytes(const had_attn_desc* d) {
   return ws_bytes(d, ns);
 }
 
-static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* stream, had::ValuArgs* out_args) {
+// fused != nullptr: the prologue runs inside the partial kernel (p->q unused)
+static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* stream, had::ValuArgs* out_args,
+                          const had::FusedArgs* fused = nullptr) {
   int st = check_desc(d);
   if (st != HAD_OK) return st;
-  if (!p || !p->q || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace)
+  if (!p || (!p->q && !fused) || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn: NULL pointer in ptrs");
-  if (!aligned16(p->q) || !aligned16(p->k_pool) || !aligned16(p->v_pool) || !aligned16(p->workspace))
+  if ((!fused && !aligned16(p->q)) || !aligned16(p->k_pool) || !aligned16(p->v_pool) || !aligned16(p->workspace))
     return fail(HAD_ERR_INVALID_ARG, "decode_attn: q, pools and workspace must be 16-byte aligned");
   int ns, pps, n_plan;
   st = plan(d, &ns, &pps, &n_plan);
@@ -151,12 +162,14 @@ static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* 
   const dim3 grid(ns, d->H_kv, d->n_seqs);
   hipError_t e = hipSuccess;
   if (rows >= 16) {
+    if (fused) return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: the fused prologue runs below 16 rows only");
     a.row_base = 0;
     e = had::launch_attn_mfma(a, d->head_dim, grid, s);
   } else {
     for (int rb = 0; rb < rows && e == hipSuccess; rb += 8) {
       a.row_base = rb;
-      e = had::launch_attn_valu(a, d->head_dim, grid, s);
+      e = fused ? had::launch_attn_valu_fused(a, *fused, d->head_dim, grid, s)
+                : had::launch_attn_valu(a, d->head_dim, grid, s);
     }
   }
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn: partial kernel launch: %s", hipGetErrorString(e));
@@ -169,15 +182,11 @@ int had_decode_attn_partial(const had_attn_desc* d, const had_attn_ptrs* p, void
   return st == HAD_OK ? had::ok() : st;
 }
 
-int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream) {
-  if (p && !p->out) return fail(HAD_ERR_INVALID_ARG, "decode_attn: out is NULL");
-  had::ValuArgs a{};
-  int st = launch_partial(d, p, stream, &a);
-  if (st != HAD_OK) return st;
+static int launch_combine_after(const had_attn_desc* d, const had::ValuArgs& a, void* out, void* stream) {
   had::CombineArgs c{};
   c.ws_o = a.ws_o;
   c.ws_ml = a.ws_ml;
-  c.out = static_cast<uint16_t*>(p->out);
+  c.out = static_cast<uint16_t*>(out);
   c.n_seqs = a.n_seqs;
   c.q_len = a.q_len;
   c.H_q = a.H_q;
@@ -188,6 +197,90 @@ int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream
   const hipError_t e = had::launch_attn_combine(c, d->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn: combine launch: %s", hipGetErrorString(e));
   return had::ok();
+}
+
+int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream) {
+  if (p && !p->out) return fail(HAD_ERR_INVALID_ARG, "decode_attn: out is NULL");
+  had::ValuArgs a{};
+  const int st = launch_partial(d, p, stream, &a);
+  if (st != HAD_OK) return st;
+  return launch_combine_after(d, a, p->out, stream);
+}
+
+static int launch_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd, const had_qknrg_ptrs* pp,
+                                void* workspace, size_t workspace_bytes, void* stream, had::ValuArgs* out_args) {
+  int st = check_desc(d);
+  if (st != HAD_OK) return st;
+  if (!pd || !pp) return fail(HAD_ERR_INVALID_ARG, "decode_attn_layer: NULL argument");
+  if (pd->n_seqs != d->n_seqs || pd->T != d->q_len || pd->H_q != d->H_q || pd->H_kv != d->H_kv ||
+      pd->head_dim != d->head_dim || pd->num_pages != d->num_pages || pd->page_size != d->page_size ||
+      pd->max_pages != d->max_pages)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_layer: prologue and attention descriptors disagree");
+  if (d->q_len > 8)
+    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn_layer: q_len %d > 8 new tokens", d->q_len);
+  if (pd->rotary_dim < 0 || pd->rotary_dim > pd->head_dim || pd->rotary_dim % 2 != 0)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_layer: rotary_dim %d must be even and <= head_dim", pd->rotary_dim);
+  if (!(pd->rope_base > 0.0) || !(pd->eps >= 0.f))
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_layer: rope_base must be > 0 and eps >= 0");
+  if (!pp->qg || !pp->k || !pp->v || !pp->w_q || !pp->w_k || !pp->page_table || !pp->seq_lens || !pp->k_pool ||
+      !pp->v_pool || !pp->gate_out)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_layer: NULL pointer in prologue ptrs");
+  had::FusedArgs f{};
+  f.qg = static_cast<const uint16_t*>(pp->qg);
+  f.k_new = static_cast<const uint16_t*>(pp->k);
+  f.v_new = static_cast<const uint16_t*>(pp->v);
+  f.w_q = pp->w_q;
+  f.w_k = pp->w_k;
+  f.k_pool = static_cast<uint16_t*>(pp->k_pool);
+  f.v_pool = static_cast<uint16_t*>(pp->v_pool);
+  f.gate_out = static_cast<uint16_t*>(pp->gate_out);
+  f.q_out = static_cast<uint16_t*>(pp->q_out);
+  f.rope_base = pd->rope_base;
+  f.eps = pd->eps;
+  f.R = pd->rotary_dim;
+  had_attn_ptrs p{};
+  p.q = nullptr;
+  p.k_pool = pp->k_pool;
+  p.v_pool = pp->v_pool;
+  p.page_table = pp->page_table;
+  p.seq_lens = pp->seq_lens;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
+  p.out = nullptr;
+  p.d_err = pp->d_err;
+  if (d->q_len * (d->H_q / d->H_kv) < 16) return launch_partial(d, &p, stream, out_args, &f);
+  // 16 or more rows (MFMA path): every work unit would redo all of its
+  // rows' prologue, so the prologue runs once as its own kernel and writes
+  // q to the caller's q_out or to the workspace's q block
+  int ns, pps;
+  st = plan(d, &ns, &pps, nullptr);
+  if (st != HAD_OK) return st;
+  if (workspace_bytes < ws_bytes(d, ns))
+    return fail(HAD_ERR_WORKSPACE_TOO_SMALL, "decode_attn_layer: workspace %zu bytes < %zu", workspace_bytes,
+                ws_bytes(d, ns));
+  had_qknrg_ptrs pq = *pp;
+  if (!pq.q_out) pq.q_out = static_cast<char*>(workspace) + ws_q_offset(d, ns);
+  st = had_qk_norm_rope_gate(pd, &pq, stream);
+  if (st != HAD_OK) return st;
+  p.q = pq.q_out;
+  return launch_partial(d, &p, stream, out_args);
+}
+
+int had_decode_attn_layer(const had_attn_desc* d, const had_qknrg_desc* pd, const had_qknrg_ptrs* pp, void* workspace,
+                          size_t workspace_bytes, void* out, void* stream) {
+  if (!out) return fail(HAD_ERR_INVALID_ARG, "decode_attn_layer: out is NULL");
+  had::ValuArgs a{};
+  int st = launch_layer_partial(d, pd, pp, workspace, workspace_bytes, stream, &a);
+  if (st != HAD_OK) return st;
+  st = launch_combine_after(d, a, out, stream);
+  return st == HAD_OK ? had::ok() : st;
+}
+
+int had_decode_attn_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd, const had_qknrg_ptrs* pp,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  had::ValuArgs a{};
+  const int st = launch_layer_partial(d, pd, pp, workspace, workspace_bytes, stream, &a);
+  return st == HAD_OK ? had::ok() : st;
 }
 
 int had_decode_attn_combine(const had_attn_desc* d, int32_t num_splits, const void* workspace, void* out,

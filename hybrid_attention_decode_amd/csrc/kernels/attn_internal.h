@@ -30,6 +30,27 @@ struct ValuArgs {
   float scale_log2;
 };
 
+// Inputs of the prologue when the VALU attention kernel runs it inline (the
+// fused layer entry point, below 16 query rows per KV head): every
+// workgroup normalises and rotates its own query rows; the workgroup whose
+// split holds the last position also normalises and rotates the new keys,
+// writes the new K/V rows to the pools and adds the new tokens to its
+// partial from on-chip copies.
+struct FusedArgs {
+  const uint16_t* qg;     // [n_seqs][q_len][H_q][2][D]: q, then gate
+  const uint16_t* k_new;  // [n_seqs][q_len][H_kv][D] before norm / rotation
+  const uint16_t* v_new;  // [n_seqs][q_len][H_kv][D]
+  const float* w_q;
+  const float* w_k;
+  uint16_t* k_pool;       // the pools again, writable
+  uint16_t* v_pool;
+  uint16_t* gate_out;     // [n_seqs][q_len][H_q][D]
+  uint16_t* q_out;        // optional, same layout
+  double rope_base;
+  float eps;
+  int R;                  // rotary dims
+};
+
 struct CombineArgs {
   const float* ws_o;
   const float* ws_ml;
@@ -38,6 +59,7 @@ struct CombineArgs {
 };
 
 hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
+hipError_t launch_attn_valu_fused(const ValuArgs& a, const FusedArgs& f, int head_dim, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_mfma(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 

@@ -32,6 +32,7 @@
 
 #include "attn_internal.h"
 #include "kcommon.h"
+#include "prologue_math.h"
 
 namespace had {
 
@@ -68,10 +69,12 @@ struct Tile {
 
 struct Lds {
   uint2 q[kRows][64];                // query block (bf16), rows in launch order
-  float o[kWaves][kRows][256];      // per-wave partial outputs for the merge
-  float ml[kWaves][kRows][2];       // per-wave (m, l)
+  float o[kWaves + 1][kRows][256];  // per-wave partial outputs for the merge (+ the new tokens' when fused)
+  float ml[kWaves + 1][kRows][2];   // per-wave (m, l)
+  uint16_t knew[kRows][256];         // fused: the new tokens' K rows (bf16, normalised and rotated)
+  uint16_t vnew[kRows][256];         // fused: the new tokens' V rows
   uint32_t p[kWaves][4][kRows];     // bf16 p pairs: [pair][row]
-  float alpha[kWaves][kRows];       // per-row rescale factor of the current tile
+  float alpha[kWaves + 1][kRows];   // per-row rescale factor of the current tile; merge weights
   int32_t pages[kMaxPagesPerSplit];  // page ids of the workgroup's range (-1 = invalid)
   int next;                          // next tile to claim
   int err;                           // HAD_DERR bits seen by the workgroup
@@ -96,8 +99,8 @@ __device__ __forceinline__ void load_tile_at(Tile<D>& T, const ValuArgs& a, int 
     T.v[i] = *reinterpret_cast<const uint2*>(vb + (tgv + C::TG * i) * D + dl * C::DPL);
 }
 
-template <int D>
-__global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
+template <int D, bool FUSED>
+__global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs f) {
   using C = Cfg<D>;
   __shared__ Lds sh;
   const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -120,33 +123,116 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
   const int npg_plan = pg1_plan - pg0;
   const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
 
-  // One page-table entry per thread (a split owns at most
-  // kMaxPagesPerSplit = blockDim pages), then the query block.
+  // Start-up order.  Vector loads retire in issue order, so the small loads
+  // go out first: one page-table entry per thread (a split owns at most
+  // kMaxPagesPerSplit = blockDim pages) and one 8-byte piece of the kRows x D
+  // query block per thread (loading q per wave instead would send every wave
+  // of the GPU to the same few L2 lines at kernel start).  Then the first two
+  // K/V tiles of this wave, whose page ids come from scalar loads, so they
+  // are in flight while the small loads are consumed and the workgroup
+  // synchronises.
   const int pt_val = pt_row[min(pg0 + static_cast<int>(threadIdx.x), a.max_pages - 1)];
+  // fused: wave w owns query row w of the launch (and, in the workgroup that
+  // holds the last position, the new token w's key row): raw rows first
+  constexpr int E = D / 64;
+  const int f_row = min(a.row_base + wave, a.rows - 1);
+  const int f_j = f_row / a.G, f_hq = h * a.G + f_row % a.G;
+  const int f_t = min(wave, a.q_len - 1);
+  RowIn<D> f_qin, f_kin;
+  uint16_t f_vraw[E];
+  if constexpr (FUSED) {
+    row_load<D>(f_qin, f.qg + ((static_cast<size_t>(s) * a.q_len + f_j) * a.H_q + f_hq) * 2 * D, f.w_q, lane);
+    const size_t kr = ((static_cast<size_t>(s) * a.q_len + f_t) * a.H_kv + h) * D;
+    row_load<D>(f_kin, f.k_new + kr, f.w_k, lane);
+#pragma unroll
+    for (int m = 0; m < E; ++m) f_vraw[m] = f.v_new[kr + lane + 64 * m];
+  }
+  constexpr int PER_ROW = D / 4;  // 8-byte q pieces per row
+  const int q_r = threadIdx.x / PER_ROW, q_c4 = threadIdx.x % PER_ROW;
+  const int q_row = a.row_base + min(q_r, kRows - 1);
+  uint2 q_piece = make_uint2(0u, 0u);
+  if constexpr (!FUSED)
+    q_piece = *reinterpret_cast<const uint2*>(
+        a.q + ((static_cast<size_t>(s) * a.q_len + (q_row < a.rows ? q_row : 0) / a.G) * a.H_q + h * a.G +
+               (q_row < a.rows ? q_row : 0) % a.G) * D + q_c4 * 4);
 
-  // The kRows x D query block of this launch -> LDS, one 8-byte piece per
-  // thread (rows past `rows` are zero).  Loading it per wave instead would
-  // send every wave of the GPU to the same few L2 lines at kernel start.
-  {
-    constexpr int PER_ROW = D / 4;  // 8-byte pieces per row
-    const int r = threadIdx.x / PER_ROW, c4 = threadIdx.x % PER_ROW;
-    if (r < kRows) {
-      const int row = a.row_base + r;
-      const bool valid = row < a.rows;
-      const int rc = valid ? row : 0;
-      const uint2 v = *reinterpret_cast<const uint2*>(
-          a.q + ((static_cast<size_t>(s) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D + c4 * 4);
-      sh.q[r][c4] = valid ? v : make_uint2(0u, 0u);
+  // The first two tiles of this wave.  A tile past the length or the split
+  // is loaded for nothing and never used.  (Issue order pinned: all of
+  // buffer 0, then all of buffer 1, the order the loop refills them in, so
+  // the wait counts inside the loop stay exact.)
+  Tile<D> buf[2];
+  int tcur[2] = {wave, wave + kWaves};
+  // both page ids in one scalar round trip (the fences keep the two loads
+  // adjacent: left to itself the scheduler waits for the first before it
+  // computes the second address)
+  const int pix0 = min(pg0 + tcur[0] / tpp, a.max_pages - 1), pix1 = min(pg0 + tcur[1] / tpp, a.max_pages - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  int pid0[2] = {pt_row[pix0], pt_row[pix1]};
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) pid0[b] = (pid0[b] < 0 || pid0[b] >= a.num_pages) ? 0 : pid0[b];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    load_tile_at<D>(buf[b], a, pid0[b], tcur[b] % tpp, h, tg, j, tgv, dl);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  const int L = a.seq_lens[s];  // (a scalar load: it does not queue behind the tiles)
+
+  const bool bad_len = L < a.q_len || L > a.max_pages * P;
+  // fused: the workgroup whose split holds the last position owns the new tokens
+  const bool own = FUSED && !bad_len && (L - 1) / P >= pg0 && (L - 1) / P < pg1_plan;
+  int errs = (bad_len && threadIdx.x == 0) ? HAD_DERR_SEQLEN : 0;
+
+  // query block -> LDS (rows past `rows` are zero)
+  if constexpr (FUSED) {
+    uint16_t* qrow = reinterpret_cast<uint16_t*>(&sh.q[wave][0]);
+    float* xrow = &sh.o[wave][0][0];
+    if (a.row_base + wave < a.rows) {
+      uint16_t y[E];
+      row_norm_rope<D>(f_qin, L - a.q_len + f_j, f.R, f.rope_base, f.eps, xrow, lane, y);
+      const size_t orow = ((static_cast<size_t>(s) * a.q_len + f_j) * a.H_q + f_hq) * D;
+      const uint16_t* gate = f.qg + ((static_cast<size_t>(s) * a.q_len + f_j) * a.H_q + f_hq) * 2 * D + D;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        qrow[lane + 64 * m] = y[m];
+        if (sp == 0) {
+          f.gate_out[orow + lane + 64 * m] = gate[lane + 64 * m];
+          if (f.q_out) f.q_out[orow + lane + 64 * m] = y[m];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < E; ++m) qrow[lane + 64 * m] = 0;
     }
+    if (own && wave < a.q_len) {
+      // the new token `wave`: normalised, rotated key into the pool and LDS
+      const int pos = L - a.q_len + wave;
+      uint16_t y[E];
+      row_norm_rope<D>(f_kin, pos, f.R, f.rope_base, f.eps, xrow, lane, y);
+      const int pid = pt_row[pos / P];
+      const bool ok = pid >= 0 && pid < a.num_pages;
+      const size_t dst = ((static_cast<size_t>(ok ? pid : 0) * a.H_kv + h) * P + pos % P) * D;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        sh.knew[wave][lane + 64 * m] = y[m];
+        sh.vnew[wave][lane + 64 * m] = f_vraw[m];
+        if (ok) {
+          f.k_pool[dst + lane + 64 * m] = y[m];
+          f.v_pool[dst + lane + 64 * m] = f_vraw[m];
+        }
+      }
+      if (!ok && lane == 0) errs |= HAD_DERR_PAGE;
+    }
+  } else {
+    if (q_r < kRows) sh.q[q_r][q_c4] = (a.row_base + q_r < a.rows) ? q_piece : make_uint2(0u, 0u);
   }
   const int my_row = a.row_base + sigma(j8);
 
-  const int L = a.seq_lens[s];
-  const bool bad_len = L < a.q_len || L > a.max_pages * P;
   const int n_pages = bad_len ? 0 : (L + P - 1) / P;
   const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
   const int ntiles = npg * tpp;
-  int errs = (bad_len && threadIdx.x == 0) ? HAD_DERR_SEQLEN : 0;
   if (threadIdx.x == 0) {
     sh.next = 2 * kWaves;
     sh.err = 0;
@@ -157,27 +243,13 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
     if (!ok && static_cast<int>(threadIdx.x) < npg) errs |= HAD_DERR_PAGE;
     sh.pages[threadIdx.x] = ok ? pt_val : -1;
   }
-  // visible-key limit of this lane's QK row (causal inside the draft)
-  const int lim = (my_row < a.rows) ? (L - a.q_len + my_row / a.G + 1) : L;
-  const int lim_min = L - a.q_len + 1;  // every row sees positions below this
+  // visible-key limit of this lane's QK row (causal inside the draft); when
+  // fused the new tokens are left out here and added from LDS at the end
+  const int lim = FUSED ? L - a.q_len : (my_row < a.rows) ? (L - a.q_len + my_row / a.G + 1) : L;
+  const int lim_min = FUSED ? L - a.q_len : L - a.q_len + 1;  // every row sees positions below this
+  const int kv_end = FUSED ? L - a.q_len : L;                   // V rows at or past this are zeroed
 
   __syncthreads();
-
-  // The first two tiles of this wave: page ids read straight from the
-  // page-table row (scalar loads), issued right after the barrier.  (Issued
-  // before it they delay the small loads the barrier waits for by more than
-  // they gain.)  A tile past the length or the split is loaded for nothing
-  // and never used.
-  Tile<D> buf[2];
-  int tcur[2] = {wave, wave + kWaves};
-  // (issue order pinned: all of buffer 0, then all of buffer 1, the order
-  // the loop refills them in, so the wait counts inside the loop stay exact)
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int pid = pt_row[min(pg0 + tcur[b] / tpp, a.max_pages - 1)];
-    load_tile_at<D>(buf[b], a, (pid < 0 || pid >= a.num_pages) ? 0 : pid, tcur[b] % tpp, h, tg, j, tgv, dl);
-    __builtin_amdgcn_sched_barrier(0);
-  }
 
   // q rows in lane order: slot r holds row (r ^ sigma(j8)) of this launch
   uint32_t qr[kRows][C::CH * 4];
@@ -298,7 +370,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
     // never multiply stale or unchecked rows: zero V past the length or in
     // an invalid page (selects, not a branch: a branch that rewrites load
     // destinations spoils the compiler's wait counts for the other buffer)
-    const int vlim = tile_ok ? L - pos0 : 0;
+    const int vlim = tile_ok ? kv_end - pos0 : 0;
 #pragma unroll
     for (int i = 0; i < C::VPL; ++i) {
       const bool keep = tgv + C::TG * i < vlim;
@@ -365,50 +437,111 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a) {
     sh.ml[wave][sigma(j8)][0] = m_run;
     sh.ml[wave][sigma(j8)][1] = l_run;
   }
+  if constexpr (FUSED) {
+    // the new tokens' contribution (workgroup that owns them): wave w adds
+    // them for query row w from the LDS copies, causal inside the draft
+    if (own) {
+      const int r = wave, row = a.row_base + r;
+      float* orow = &sh.o[kWaves][r][0];
+      float mx = -INFINITY, lsum = 0.f, acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = 0.f;
+      if (row < a.rows) {
+        const int jq = row / a.G;  // this row's query token sees new tokens 0..jq
+        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(&sh.q[r][0]);
+        float qv[E], sc[kRows];
+#pragma unroll
+        for (int e = 0; e < E; ++e) qv[e] = bf16_to_f32(qrow[lane + 64 * e]);
+#pragma unroll
+        for (int t = 0; t < kRows; ++t) {
+          float dsum = 0.f;
+          if (t <= jq) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) dsum += qv[e] * bf16_to_f32(sh.knew[t][lane + 64 * e]);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) dsum += shfl_xor_f(dsum, off);
+          }
+          sc[t] = (t <= jq) ? dsum * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sc[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < kRows; ++t) {
+          if (t <= jq) {
+            const float pt = bf16_to_f32(f32_to_bf16(exp2f(sc[t] - mx)));
+            lsum += pt;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += pt * bf16_to_f32(sh.vnew[t][lane + 64 * e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) orow[lane + 64 * e] = acc[e];
+      if (lane == 0) {
+        sh.ml[kWaves][r][0] = mx;
+        sh.ml[kWaves][r][1] = lsum;
+      }
+    }
+  }
   if (errs) atomicOr(&sh.err, errs);
   __syncthreads();
   if (threadIdx.x == 0 && sh.err) set_err(a.d_err, sh.err);
+  const int n_parts = (FUSED && own) ? kWaves + 1 : kWaves;  // partials to merge
 
-  // ---- merge the waves and store the split's partial
+  // ---- merge the waves and store the split's partial: the per-row wave
+  // weights once (kRows threads), then one float4 of one row per thread
   const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.num_splits + sp;
-  for (int idx = threadIdx.x; idx < kRows * D; idx += blockDim.x) {
-    const int r = idx / D, d = idx % D;
-    const int row = a.row_base + r;
-    if (row >= a.rows) continue;
+  if (threadIdx.x < kRows) {
+    const int r = threadIdx.x;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][r][0]);
+    for (int w = 0; w < n_parts; ++w) M = fmaxf(M, sh.ml[w][r][0]);
     const float Ms = (M == -INFINITY) ? 0.f : M;
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    float lsum = 0.f;
+    for (int w = 0; w < n_parts; ++w) {
       const float wt = exp2f(sh.ml[w][r][0] - Ms);
-      acc += wt * sh.o[w][r][d];
+      sh.alpha[w][r] = wt;  // (the per-tile rescale slots are free now)
       lsum += wt * sh.ml[w][r][1];
     }
-    a.ws_o[(unit * a.rows + row) * D + d] = acc;
-    if (d == 0) {
+    const int row = a.row_base + r;
+    if (row < a.rows) {
       a.ws_ml[(unit * a.rows + row) * 2 + 0] = M;
       a.ws_ml[(unit * a.rows + row) * 2 + 1] = lsum;
     }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kRows * D / 4; idx += blockDim.x) {
+    const int r = idx / (D / 4), c4 = idx % (D / 4);
+    const int row = a.row_base + r;
+    if (row >= a.rows) continue;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int w = 0; w < n_parts; ++w) {
+      const float wt = sh.alpha[w][r];
+      const float4 o4 = *reinterpret_cast<const float4*>(&sh.o[w][r][4 * c4]);
+      acc.x += wt * o4.x; acc.y += wt * o4.y; acc.z += wt * o4.z; acc.w += wt * o4.w;
+    }
+    *reinterpret_cast<float4*>(&a.ws_o[(unit * a.rows + row) * D + 4 * c4]) = acc;
   }
 }
 
 }  // namespace
 
 hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream) {
+  const FusedArgs f{};
   switch (head_dim) {
-    case 64:
-      hipLaunchKernelGGL(attn_valu_kernel<64>, grid, dim3(64 * kWaves), 0, stream, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL(attn_valu_kernel<128>, grid, dim3(64 * kWaves), 0, stream, a);
-      break;
-    case 256:
-      hipLaunchKernelGGL(attn_valu_kernel<256>, grid, dim3(64 * kWaves), 0, stream, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: hipLaunchKernelGGL((attn_valu_kernel<64, false>), grid, dim3(64 * kWaves), 0, stream, a, f); break;
+    case 128: hipLaunchKernelGGL((attn_valu_kernel<128, false>), grid, dim3(64 * kWaves), 0, stream, a, f); break;
+    case 256: hipLaunchKernelGGL((attn_valu_kernel<256, false>), grid, dim3(64 * kWaves), 0, stream, a, f); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_valu_fused(const ValuArgs& a, const FusedArgs& f, int head_dim, dim3 grid, hipStream_t stream) {
+  if (a.q_len > kRows) return hipErrorInvalidValue;  // one new-token key row per wave
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((attn_valu_kernel<64, true>), grid, dim3(64 * kWaves), 0, stream, a, f); break;
+    case 128: hipLaunchKernelGGL((attn_valu_kernel<128, true>), grid, dim3(64 * kWaves), 0, stream, a, f); break;
+    case 256: hipLaunchKernelGGL((attn_valu_kernel<256, true>), grid, dim3(64 * kWaves), 0, stream, a, f); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

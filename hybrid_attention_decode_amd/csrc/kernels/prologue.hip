@@ -2,19 +2,10 @@
 // embedding + gate split, with the new K/V rows written straight into their
 // KV page slots.  The engine fuses these five steps into one kernel whose
 // intermediates never leave registers (zubnet.ai TokenSpeed article, second
-// paragraph); here one wave owns one head of one token and the only other
-// storage touched is a 1 KB LDS row used to fetch the rotation partner.
-// Grid: (token, group of 4 heads), 4 waves per block.
-//
-//   q    = RMSNorm(qg[.., 0, :]) * w_q,   gate = qg[.., 1, :]
-//   k    = RMSNorm(k) * w_k,              v unchanged
-//   RMSNorm(x) = x / sqrt(mean(x^2) + eps)                       (fp32)
-//   dims d < R rotate in pairs (i, i + R/2), angle pos * base^(-2i/R):
-//     y_i' = y_i cos - y_{i+R/2} sin,  y_{i+R/2}' = y_{i+R/2} cos + y_i sin
-//   (RMSNorm: Zhang & Sennrich 2019; rotary embedding: Su et al., RoFormer
-//   2021, applied to a prefix of the head), angles in fp64 (reduced to
-//   [-pi, pi] before an fp32 sine/cosine), pos = seq_lens[s] - T + j.
-// Outputs are rounded to bf16 (nearest even); gate and v are copied bit for
+// paragraph); here one wave owns one head of one token (the per-row
+// arithmetic is in prologue_math.h, shared with the attention kernels that
+// run the prologue inline).  Grid: (token, group of 4 heads), 4 waves per
+// block; positions pos = seq_lens[s] - T + j.  Gate and v are copied bit for
 // bit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -22,6 +13,7 @@
 #include "../host/status.h"
 #include "had.h"
 #include "kcommon.h"
+#include "prologue_math.h"
 
 using had::fail;
 
@@ -66,81 +58,31 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   }
   const size_t tok = static_cast<size_t>(s) * a.T + j;
 
-  // rotation angle of this lane's pair index (i = d mod R/2 for d < R):
-  // theta = pos * base^(-2i/R) in fp64 (at pos ~ 1e6 an fp32 product would
-  // be off by ~0.06 rad), reduced to [-pi, pi] in fp64, then sine and cosine
-  // of the small reduced angle in fp32.
-  const int half = a.R / 2;
-  const double log2_base = log2(a.base);
-  float cs[E], sn[E];
-#pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int d = lane + 64 * m;
-    cs[m] = 1.f;
-    sn[m] = 0.f;
-    if (d < a.R) {
-      const int i = d % half;
-      const double inv_freq = exp2(-2.0 * i / a.R * log2_base);
-      const double theta = static_cast<double>(pos) * inv_freq;
-      const double two_pi = 6.283185307179586476925286766559;
-      const double red = theta - two_pi * rint(theta / two_pi);
-      sincosf(static_cast<float>(red), &sn[m], &cs[m]);
-    }
-  }
-
-  {
-    const int hh = blockIdx.y * kWaves + wave;  // one head per wave
-    if (hh >= a.H_q + a.H_kv) return;
-    const bool is_q = hh < a.H_q;
-    const int h = is_q ? hh : hh - a.H_q;
-    const uint16_t* src = is_q ? a.qg + (tok * a.H_q + h) * 2 * D : a.k + (tok * a.H_kv + h) * D;
-    const float* w = is_q ? a.w_q : a.w_k;
-    float x[E];
-    float ss = 0.f;
+  const int hh = blockIdx.y * kWaves + wave;  // one head per wave
+  if (hh >= a.H_q + a.H_kv) return;
+  const bool is_q = hh < a.H_q;
+  const int h = is_q ? hh : hh - a.H_q;
+  const uint16_t* src = is_q ? a.qg + (tok * a.H_q + h) * 2 * D : a.k + (tok * a.H_kv + h) * D;
+  RowIn<D> in;
+  row_load<D>(in, src, is_q ? a.w_q : a.w_k, lane);
+  uint16_t y[E];
+  row_norm_rope<D>(in, pos, a.R, a.base, a.eps, row[wave], lane, y);
+  if (is_q) {
+    uint16_t* qo = a.q_out + (tok * a.H_q + h) * D;
+    uint16_t* go = a.gate_out + (tok * a.H_q + h) * D;
+    const uint16_t* gi = src + D;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      x[m] = bf16_to_f32(src[lane + 64 * m]);
-      ss += x[m] * x[m];
+      qo[lane + 64 * m] = y[m];
+      go[lane + 64 * m] = gi[lane + 64 * m];
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor_f(ss, off);
-    const float inv = 1.f / sqrtf(ss / static_cast<float>(D) + a.eps);
+  } else if (page_ok) {
+    const size_t dst = ((static_cast<size_t>(pid) * a.H_kv + h) * a.P + pos % a.P) * D;
+    const uint16_t* vi = a.v + (tok * a.H_kv + h) * D;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      x[m] = x[m] * inv * w[lane + 64 * m];
-      row[wave][lane + 64 * m] = x[m];
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    uint16_t y[E];
-#pragma unroll
-    for (int m = 0; m < E; ++m) {
-      const int d = lane + 64 * m;
-      float r = x[m];
-      if (d < a.R) {
-        const float other = row[wave][d < half ? d + half : d - half];
-        r = d < half ? x[m] * cs[m] - other * sn[m] : x[m] * cs[m] + other * sn[m];
-      }
-      y[m] = f32_to_bf16(r);
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (is_q) {
-      uint16_t* qo = a.q_out + (tok * a.H_q + h) * D;
-      uint16_t* go = a.gate_out + (tok * a.H_q + h) * D;
-      const uint16_t* gi = src + D;
-#pragma unroll
-      for (int m = 0; m < E; ++m) {
-        qo[lane + 64 * m] = y[m];
-        go[lane + 64 * m] = gi[lane + 64 * m];
-      }
-    } else if (page_ok) {
-      const size_t dst = ((static_cast<size_t>(pid) * a.H_kv + h) * a.P + pos % a.P) * D;
-      const uint16_t* vi = a.v + (tok * a.H_kv + h) * D;
-#pragma unroll
-      for (int m = 0; m < E; ++m) {
-        a.k_pool[dst + lane + 64 * m] = y[m];
-        a.v_pool[dst + lane + 64 * m] = vi[lane + 64 * m];
-      }
+      a.k_pool[dst + lane + 64 * m] = y[m];
+      a.v_pool[dst + lane + 64 * m] = vi[lane + 64 * m];
     }
   }
 }

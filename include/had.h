@@ -261,14 +261,16 @@ int had_qk_norm_rope_gate(const had_qknrg_desc *d, const had_qknrg_ptrs *p, void
  * Workspace (caller-allocated device memory, >= had_decode_attn_workspace_bytes):
  *   ws_o  fp32 [n_seqs][H_kv][num_splits][rows][head_dim]
  *   ws_ml fp32 [n_seqs][H_kv][num_splits][rows][2]   (m, l)
- * starting at the workspace base, ws_ml right after ws_o.  Row r = j * G + g
+ *   ws_q  bf16 [n_seqs][q_len][H_q][head_dim]         (had_decode_attn_layer only)
+ * starting at the workspace base, ws_ml right after ws_o, ws_q at the next
+ * 256-byte boundary.  Row r = j * G + g
  * is query j, head h * G + g.  m is in base-2 units: m = max over the split
  * of sm_scale * log2(e) * q.k; l = sum of 2^(that - m); o = sum of
  * 2^(that - m) * v.  An empty split has m = -inf, l = 0, o = 0.
  * ====================================================================== */
 typedef struct {
   int32_t n_seqs, q_len, H_q, H_kv, head_dim; /* head_dim in {64,128,256}; H_q % H_kv == 0           */
-  int32_t num_pages, page_size, max_pages;    /* pool pages; page_size in {16,32,64}; row stride      */
+  int32_t num_pages, page_size, max_pages;    /* pool pages; page_size a multiple of 8 in [8, 256]     */
   float sm_scale;                             /* usually 1/sqrt(head_dim)                            */
   int32_t max_seq_len;                        /* host bound on every seq_lens[s]; 0 = max_pages*page_size */
   int32_t num_splits;                         /* 0 = choose automatically                            */
@@ -307,6 +309,38 @@ int had_decode_attn(const had_attn_desc *d, const had_attn_ptrs *p, void *stream
 int had_decode_attn_partial(const had_attn_desc *d, const had_attn_ptrs *p, void *stream);
 int had_decode_attn_combine(const had_attn_desc *d, int32_t num_splits,
                             const void *workspace, void *out, void *stream);
+
+/* ======================================================================
+ * decode_attn_layer -- qk_norm_rope_gate and decode_attn in one pass
+ *
+ * Below 16 query rows per KV head the prologue of a full-attention layer
+ * runs inside the split-K partial kernel (the pages fuse the prologue's five
+ * steps into one kernel: zubnet.ai ¶2; here it is fused one step further,
+ * into the attention): every work unit normalises and rotates its own query
+ * rows, the unit whose split holds the last position normalises and rotates
+ * the T new keys, writes the new K/V rows to the pools and adds the new
+ * tokens to its partial from on-chip copies; then the usual merge writes
+ * out.  At 16 rows or more (the MFMA path) every unit would redo many rows'
+ * prologue, so it runs once as had_qk_norm_rope_gate, writing q to
+ * pp->q_out or, when that is NULL, to the workspace's ws_q block.
+ *
+ * Results: out as had_decode_attn with q = the q_out of had_qk_norm_rope_gate
+ * (same bits for q; the attention sums differ in order only); gate_out, the
+ * pools and (when non-NULL) q_out as had_qk_norm_rope_gate.
+ *
+ * d and pd describe the same layer (n_seqs, T = q_len, heads, head_dim, pool
+ * geometry must agree, else HAD_ERR_INVALID_ARG); pp supplies every pointer
+ * (pp->q_out may be NULL; pp->d_err is used for both halves); workspace as
+ * had_decode_attn (had_decode_attn_workspace_bytes(d)).  T <= 8
+ * (HAD_ERR_UNSUPPORTED_SHAPE otherwise).
+ * ====================================================================== */
+int had_decode_attn_layer(const had_attn_desc *d, const had_qknrg_desc *pd, const had_qknrg_ptrs *pp,
+                          void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* Its first half: the prologue and the partials only (workspace layout of
+ * had_decode_attn); had_decode_attn_combine finishes. */
+int had_decode_attn_layer_partial(const had_attn_desc *d, const had_qknrg_desc *pd, const had_qknrg_ptrs *pp,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* ======================================================================
  * gdn_state_update -- gated delta rule on slot-addressed states

@@ -1,0 +1,140 @@
+"""GPU parity: the fused attention layer (prologue inside the attention
+kernel) against the fp64 oracle, and against the two-call path."""
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_attention_decode_amd as had
+import synth
+from oracle import attention as A
+from oracle import bf16
+from oracle import paging as PG
+from oracle import prologue as Pr
+from gpu_util import DEV, assert_attn_close, bits_of, paged_case, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _within_one_ulp(got_bits, ref):
+    return np.all(np.abs(bf16.to_f64(got_bits) - ref) <= bf16.ulp(ref))
+
+
+def _inputs(seed, S, T, H_q, H_kv, D):
+    qg = synth.normal_bf16((S, T, H_q, 2, D), synth.seed_of(seed, 41))
+    k = synth.normal_bf16((S, T, H_kv, D), synth.seed_of(seed, 42))
+    v = synth.normal_bf16((S, T, H_kv, D), synth.seed_of(seed, 43))
+    w_q = synth.uniform_f32((D,), 0.5, 1.5, synth.seed_of(seed, 44))
+    w_k = synth.uniform_f32((D,), 0.5, 1.5, synth.seed_of(seed, 45))
+    return qg, k, v, w_q, w_k
+
+
+def _run(seed, lens, T, H_q, H_kv, D, R, P, num_splits=0, deterministic=False):
+    _, k_pool, v_pool, pt, L = paged_case(seed, lens, T, H_q, H_kv, D, P)
+    qg, k, v, w_q, w_k = _inputs(seed, len(lens), T, H_q, H_kv, D)
+    print("case seed=%d lens=%s T=%d H_q=%d H_kv=%d D=%d R=%d P=%d splits=%d" % (
+        seed, list(lens), T, H_q, H_kv, D, R, P, num_splits), flush=True)
+    kd, vd = to_dev(k_pool), to_dev(v_pool)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q_out = torch.empty((len(lens), T, H_q, D), dtype=torch.bfloat16, device=DEV)
+    out, gate = had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt),
+                                      to_dev(L), kd, vd, R, num_splits=num_splits, q_out=q_out, d_err=err,
+                                      deterministic=deterministic)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    return dict(k_pool=k_pool, v_pool=v_pool, pt=pt, L=L, qg=qg, k=k, v=v, w_q=w_q, w_k=w_k, kd=kd, vd=vd,
+                out=out, gate=gate, q_out=q_out, T=T, R=R, P=P, D=D)
+
+
+def _check_against_oracle(c):
+    T, R, P, D = c["T"], c["R"], c["P"], c["D"]
+    kb_in, vb_in = bits_of(c["k_pool"]), bits_of(c["v_pool"])
+    kb, vb = bits_of(c["kd"]), bits_of(c["vd"])
+    touched = np.zeros(kb.shape[:1] + kb.shape[2:3], bool)
+    for s, L in enumerate(c["L"]):
+        pos = np.arange(L - T, L)
+        q_ref, _, k_ref, v_ref = Pr.qk_norm_rope_gate(
+            bf16.to_f64(bits_of(c["qg"])[s]), bf16.to_f64(bits_of(c["k"])[s]), bf16.to_f64(bits_of(c["v"])[s]),
+            c["w_q"].numpy().astype(np.float64), c["w_k"].numpy().astype(np.float64), pos, R)
+        assert _within_one_ulp(bits_of(c["q_out"])[s], q_ref)
+        assert np.array_equal(bits_of(c["gate"])[s], bits_of(c["qg"])[s, :, :, 1])
+        for j, p in enumerate(pos):
+            page = c["pt"][s, p // P]
+            touched[page, p % P] = True
+            assert _within_one_ulp(kb[page, :, p % P], k_ref[j])
+            assert np.array_equal(vb[page, :, p % P], bits_of(c["v"])[s, j])
+        # attention over the prior context (pool input) + the oracle's new rows
+        K = bf16.to_f64(PG.gather(kb_in, c["pt"][s], L - T, P))
+        V = bf16.to_f64(PG.gather(vb_in, c["pt"][s], L - T, P))
+        K = np.concatenate([K, bf16.to_f64(bf16.from_f64(k_ref))])
+        V = np.concatenate([V, v_ref])
+        ref = A.attention(bf16.to_f64(bf16.from_f64(q_ref)), K, V, 1.0 / np.sqrt(D))
+        assert_attn_close(c["out"][s], ref)
+    # nothing else in the pools changed
+    for h in range(kb.shape[1]):
+        assert np.array_equal(kb[:, h][~touched], kb_in[:, h][~touched], equal_nan=True)
+        assert np.array_equal(vb[:, h][~touched], vb_in[:, h][~touched], equal_nan=True)
+
+
+@pytest.mark.parametrize("lens,T,H_q,H_kv,D,R,P", [
+    ([50001], 1, 8, 1, 256, 64, 64),          # the long-context layer shape (VALU, 8 rows)
+    ([130, 1000], 2, 4, 1, 128, 32, 16),      # 8 rows, two sequences
+    ([300], 3, 2, 1, 64, 16, 16),             # 6 rows
+    ([4], 4, 2, 1, 128, 128, 16),             # the whole context is the new tokens
+    ([7000], 4, 16, 1, 256, 64, 64),          # speculative verify shape (MFMA, 64 rows)
+    ([97], 1, 16, 1, 128, 128, 16),           # 16 rows, one token
+    ([2050, 513], 4, 8, 2, 64, 16, 64),       # 32 rows per KV head, two KV heads
+    ([600], 4, 20, 1, 128, 32, 32),           # 80 rows: two MFMA row blocks
+])
+def test_fused_layer_matches_oracle(lens, T, H_q, H_kv, D, R, P):
+    c = _run(2000 + sum(lens) % 997 + T, lens, T, H_q, H_kv, D, R, P)
+    _check_against_oracle(c)
+
+
+@pytest.mark.parametrize("H_q", [8, 16])
+def test_new_tokens_straddle_splits(H_q):
+    # one page per split and the 4 new tokens across a page boundary: two
+    # splits hold new positions, the one with the last position owns them
+    c = _run(2100 + H_q, [16 * 40 + 2], 4, H_q, 1, 128, 32, 16, num_splits=41)
+    _check_against_oracle(c)
+
+
+def test_fused_matches_two_call_path():
+    lens, T, H_q, H_kv, D, R, P = [3000, 70], 2, 4, 1, 256, 64, 64
+    c = _run(2200, lens, T, H_q, H_kv, D, R, P, deterministic=True)
+    kd2, vd2 = to_dev(c["k_pool"]), to_dev(c["v_pool"])
+    q2, g2 = had.qk_norm_rope_gate(to_dev(c["qg"]), to_dev(c["k"]), to_dev(c["v"]), to_dev(c["w_q"]),
+                                   to_dev(c["w_k"]), to_dev(c["pt"]), to_dev(c["L"]), kd2, vd2, R)
+    out2 = had.decode_attn(q2, kd2, vd2, to_dev(c["pt"]), to_dev(c["L"]), deterministic=True)
+    torch.cuda.synchronize()
+    # the prologue arithmetic is shared: q, gate and the written pools agree bit for bit
+    assert np.array_equal(bits_of(c["q_out"]), bits_of(q2))
+    assert np.array_equal(bits_of(c["gate"]), bits_of(g2))
+    assert np.array_equal(bits_of(c["kd"]), bits_of(kd2), equal_nan=True)
+    assert np.array_equal(bits_of(c["vd"]), bits_of(vd2), equal_nan=True)
+    # the attention differs only in the order of its sums
+    a, b = bf16.to_f64(bits_of(c["out"])), bf16.to_f64(bits_of(out2))
+    assert np.abs(a - b).max() <= 4e-3
+
+
+def test_bad_new_token_page_is_reported():
+    _, k_pool, v_pool, pt, L = paged_case(2300, [200], 1, 8, 1, 128, 16)
+    pt = pt.copy()
+    pt[0, 199 // 16] = 10 ** 6                     # the page of the new token: out of range
+    qg, k, v, w_q, w_k = _inputs(2300, 1, 1, 8, 1, 128)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("case bad new-token page", flush=True)
+    had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L),
+                          to_dev(k_pool), to_dev(v_pool), 32, d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_PAGE
+
+
+def test_disagreeing_descriptors_are_rejected():
+    qg, k, v, w_q, w_k = _inputs(2400, 1, 9, 8, 1, 64)
+    pool = torch.zeros((4, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(had.HadError) as e:
+        had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k),
+                              torch.zeros((1, 4), dtype=torch.int32, device=DEV),
+                              torch.tensor([20], dtype=torch.int32, device=DEV), pool, pool.clone(), 16)
+    assert e.value.kind == "unsupported_shape"          # T = 9 > 8
