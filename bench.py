@@ -329,8 +329,24 @@ class Stack:
                 o=torch.empty((n, T, GDN_H, DV), device=dev)))
         self.graph = None
 
+    def enable_cascade(self, prefix_pages_dev):
+        """Attention layers read the batch's shared prefix pages once for all
+        sequences (had_decode_attn_cascade) after a separate prologue."""
+        import torch
+
+        self.prefix_dev = prefix_pages_dev
+        nbytes = self.had.decode_attn_cascade_workspace_bytes(self.desc, prefix_pages_dev.numel())
+        self.cws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
     def attn_layer(self, i):
         a = self.attn[i]
+        if getattr(self, "prefix_dev", None) is not None:
+            self.had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
+                                       a["k_pool"], a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
+            self.had.decode_attn_cascade(a["q_out"], a["k_pool"], a["v_pool"], self.pt_dev, self.lens_dev,
+                                         self.prefix_dev, max_seq_len=self.max_seq_len, workspace=self.cws,
+                                         out=a["out"])
+            return
         self.had.decode_attn_layer(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
                                    a["k_pool"], a["v_pool"], R, max_seq_len=self.max_seq_len, workspace=self.ws,
                                    out=a["out"], gate_out=a["gate"])
@@ -403,6 +419,22 @@ def stack_kernel_us(st, kernel_reps):
     def gdn(r):
         st.gdn_layer(r % N_GDN)
 
+    if getattr(st, "prefix_dev", None) is not None:
+        def prologue(r):
+            a = st.attn[r % N_ATTN]
+            had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], st.pt_dev, st.lens_dev, a["k_pool"],
+                                  a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
+
+        def cascade(r):
+            a = st.attn[r % N_ATTN]
+            had.decode_attn_cascade(a["q_out"], a["k_pool"], a["v_pool"], st.pt_dev, st.lens_dev, st.prefix_dev,
+                                    max_seq_len=st.max_seq_len, workspace=st.cws, out=a["out"])
+
+        return {
+            "prologue": round(time_graph(torch, prologue, n * N_ATTN), 3),
+            "attn_cascade_prefix_suffix_combine": round(time_graph(torch, cascade, n * N_ATTN), 3),
+            "gdn_update": round(time_graph(torch, gdn, max(2, n) * N_GDN), 3),
+        }
     return {
         "attn_partial": round(time_graph(torch, partial, n * N_ATTN), 3),
         "attn_combine": round(time_graph(torch, combine, n * N_ATTN), 3),
@@ -556,11 +588,13 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
     return res
 
 
-def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warmup=10, kernel_reps=4, seed=7):
+def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warmup=10, kernel_reps=4, seed=7,
+                      cascade=True):
     """Prefix-shared concurrency: n_seqs sequences fork one prefix (page
     aliasing, copy-on-write of the shared partial page on first append), private
     suffixes ~ U{0..max_suffix}, GDN input slots drawn as a permutation
-    (sequences without a suffix read the shared prefix checkpoint)."""
+    (sequences without a suffix read the shared prefix checkpoint).  With
+    cascade, attention reads the prefix's whole pages once for all sequences."""
     import torch
 
     import hybrid_attention_decode_amd as had
@@ -595,6 +629,8 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
             cow(pt.reserve(sq, int(suffix[i])))
     table, lens = pt.export(seqs, max_pages)
     st.pt_dev.copy_(torch.from_numpy(table))
+    if cascade:                                               # the prefix's whole pages, shared by every fork
+        st.enable_cascade(torch.from_numpy(table[0, :prefix // P].copy()).to("cuda"))
     slot_order = synth.permutation(n_slots, synth.seed_of(seed, 2))
     slots = had.SlotPool(n_slots, free_order=slot_order)
     shared = slots.acquire()                                  # prefix checkpoint
@@ -643,14 +679,17 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
         N_GDN * n_seqs * GDN_BYTES_PER_LAYER
     us = stack_kernel_us(st, kernel_reps)
     res = dict(workload="prefix-shared: %d sequences fork a %d-token prefix (copy-on-write on the first divergent "
-                        "page), private suffixes ~ U{0..%d}, %d GDN slots, one token per sequence per step"
-                        % (n_seqs, prefix, max_suffix, n_slots),
+                        "page), private suffixes ~ U{0..%d}, %d GDN slots, one token per sequence per step; attention %s"
+                        % (n_seqs, prefix, max_suffix, n_slots,
+                           "reads the prefix's whole pages once for all sequences (cascade)" if cascade
+                           else "per sequence (fused prologue + split-K)"),
                steps=steps, warmup=warmup, ms_per_step=round(ms, 5), steps_per_s=round(1e3 / ms, 3),
                tokens_per_s=round(n_seqs * 1e3 / ms, 2), cow_copies=n_cow,
                logical_bytes_per_step=int(logical), unique_bytes_per_step=int(unique),
                logical_gbps=round(logical / (ms * 1e-3) / 1e9, 1), unique_gbps=round(unique / (ms * 1e-3) / 1e9, 1),
                us_per_layer=us, num_splits=st.n_splits)
-    log("prefix-shared: %.1f steps/s (%.0f tokens/s), %d CoW copies" % (1e3 / ms, n_seqs * 1e3 / ms, n_cow))
+    log("prefix-shared (%s): %.1f steps/s (%.0f tokens/s), %d CoW copies" % (
+        "cascade" if cascade else "per sequence", 1e3 / ms, n_seqs * 1e3 / ms, n_cow))
     del st
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -781,6 +820,9 @@ def main():
     if "prefix" in wl:
         extra["prefix_shared"] = run_prefix_shared(steps=args.steps, warmup=args.warmup,
                                                    kernel_reps=args.kernel_reps)
+        flat = run_prefix_shared(steps=args.steps, warmup=args.warmup, kernel_reps=args.kernel_reps, cascade=False)
+        extra["prefix_shared"]["per_sequence_path"] = {k: flat[k] for k in ("steps_per_s", "tokens_per_s",
+                                                                            "us_per_layer")}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")

@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     abi_version,
     attn_desc,
     decode_attn,
+    decode_attn_cascade,
+    decode_attn_cascade_workspace_bytes,
     decode_attn_combine,
     decode_attn_layer,
     decode_attn_partial,

@@ -72,6 +72,10 @@ class AttnPtrs(ctypes.Structure):
                 ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("out", _p), ("d_err", _p)]
 
 
+class AttnPrefix(ctypes.Structure):
+    _fields_ = [("prefix_pages", _i32), ("prefix_page_table", _p)]
+
+
 class GdnDesc(ctypes.Structure):
     _fields_ = [("n_seqs", _i32), ("T", _i32), ("H", _i32), ("d_k", _i32), ("d_v", _i32), ("n_slots", _i32),
                 ("q_scale", ctypes.c_float)]
@@ -110,6 +114,10 @@ _SIGS = {
     "had_decode_attn": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
     "had_decode_attn_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
     "had_decode_attn_combine": ([ctypes.POINTER(AttnDesc), _i32, _p, _p, _p], ctypes.c_int),
+    "had_decode_attn_cascade_workspace_bytes": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPrefix)],
+                                                ctypes.c_size_t),
+    "had_decode_attn_cascade": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPrefix), ctypes.POINTER(AttnPtrs), _p],
+                                ctypes.c_int),
     "had_decode_attn_layer": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc), ctypes.POINTER(QknrgPtrs), _p,
                                ctypes.c_size_t, _p, _p], ctypes.c_int),
     "had_decode_attn_layer_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc),
@@ -382,6 +390,34 @@ def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_
                     workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"))
     _check(lib().had_decode_attn(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
     return out
+
+
+def decode_attn_cascade(q, k_pool, v_pool, page_table, seq_lens, prefix_page_table, sm_scale=None, max_seq_len=0,
+                        workspace=None, out=None, d_err=None, deterministic=False):
+    """Decode attention for a batch whose sequences share their first
+    len(prefix_page_table) pages (read once for every sequence's rows).
+    q [S, q_len, H_q, D] bf16; prefix_page_table int32 [prefix_pages] on the device."""
+    torch = _torch()
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, 0, deterministic)
+    px = AttnPrefix(prefix_page_table.numel(), _dev(prefix_page_table, torch.int32, "prefix_page_table"))
+    need = lib().had_decode_attn_cascade_workspace_bytes(ctypes.byref(desc), ctypes.byref(px))
+    if need == 0:  # invalid descriptor or prefix: the call itself reports why
+        _check(lib().had_decode_attn_cascade(ctypes.byref(desc), ctypes.byref(px), None, _stream()))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    ptrs = AttnPtrs(_dev(q, torch.bfloat16, "q"), _dev(k_pool, torch.bfloat16, "k_pool"),
+                    _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
+                    _dev(seq_lens, torch.int32, "seq_lens"), _dev(workspace, torch.uint8, "workspace"),
+                    workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"))
+    _check(lib().had_decode_attn_cascade(ctypes.byref(desc), ctypes.byref(px), ctypes.byref(ptrs), _stream()))
+    return out
+
+
+def decode_attn_cascade_workspace_bytes(desc, prefix_pages):
+    px = AttnPrefix(prefix_pages, None)
+    return lib().had_decode_attn_cascade_workspace_bytes(ctypes.byref(desc), ctypes.byref(px))
 
 
 def decode_attn_layer(qg, k, v, w_q, w_k, page_table, seq_lens, k_pool, v_pool, rotary_dim, rope_base=10000.0,

@@ -157,6 +157,12 @@ static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* 
   a.n_pages_plan = n_plan;
   a.deterministic = (d->flags & HAD_ATTN_DETERMINISTIC) ? 1 : 0;
   a.scale_log2 = d->sm_scale * 1.4426950408889634f;
+  a.pg_begin = 0;
+  a.split_offset = 0;
+  a.ns_total = ns;
+  a.ws_rows = rows;
+  a.batch_rows = 0;
+  a.fixed_len = -1;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(ns, d->H_kv, d->n_seqs);
@@ -306,6 +312,130 @@ int had_decode_attn_combine(const had_attn_desc* d, int32_t num_splits, const vo
   hipError_t e = had::launch_attn_combine(c, d->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn_combine: launch: %s", hipGetErrorString(e));
   return had::ok();
+}
+
+// ---- shared-prefix (cascade) attention -----------------------------------
+// The batch's common prefix (prefix_pages whole pages, the same page ids at
+// the start of every sequence's page table) is read once for the query rows
+// of every sequence (MFMA kernel, rows of all sequences in one launch set);
+// each sequence's suffix is read by the usual kernel from page prefix_pages
+// on; both write partials into one workspace (prefix splits first) and the
+// ordinary combine merges them.  Same result as had_decode_attn.
+static int cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int* ns_p, int* ns_s, int* n_sfx) {
+  int st = check_desc(d);
+  if (st != HAD_OK) return st;
+  if (!px || px->prefix_pages < 1)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: prefix_pages must be >= 1");
+  const int64_t max_len = d->max_seq_len > 0 ? d->max_seq_len : static_cast<int64_t>(d->max_pages) * d->page_size;
+  const int64_t prefix_len = static_cast<int64_t>(px->prefix_pages) * d->page_size;
+  if (prefix_len + d->q_len > max_len || px->prefix_pages > d->max_pages)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: prefix of %d pages does not fit max_seq_len %lld",
+                px->prefix_pages, static_cast<long long>(max_len));
+  // prefix pass: one unit per KV head, rows of every sequence (MFMA)
+  had_attn_desc dp = *d;
+  dp.n_seqs = 1;
+  dp.q_len = d->q_len * 16;  // any row count >= 16 selects the MFMA plan
+  dp.max_seq_len = static_cast<int32_t>(prefix_len);
+  dp.num_splits = 0;
+  int pps;
+  st = plan(&dp, ns_p, &pps, nullptr);
+  if (st != HAD_OK) return st;
+  // suffix pass: the usual plan over the pages after the prefix
+  had_attn_desc ds = *d;
+  ds.max_seq_len = static_cast<int32_t>(max_len - prefix_len);
+  ds.num_splits = 0;
+  st = plan(&ds, ns_s, &pps, n_sfx);
+  if (st != HAD_OK) return st;
+  if (*ns_p + *ns_s > had::kMaxSplits)
+    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn_cascade: %d + %d splits (max %d)", *ns_p, *ns_s,
+                had::kMaxSplits);
+  return HAD_OK;
+}
+
+size_t had_decode_attn_cascade_workspace_bytes(const had_attn_desc* d, const had_attn_prefix* px) {
+  int ns_p, ns_s, n_sfx;
+  if (cascade_plan(d, px, &ns_p, &ns_s, &n_sfx) != HAD_OK) return 0;
+  return ws_partials_bytes(d, ns_p + ns_s);
+}
+
+int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, void* stream) {
+  int ns_p, ns_s, n_sfx;
+  int st = cascade_plan(d, px, &ns_p, &ns_s, &n_sfx);
+  if (st != HAD_OK) return st;
+  if (!p || !p->q || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace || !p->out ||
+      !px->prefix_page_table)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: NULL pointer in ptrs or prefix");
+  if (!aligned16(p->q) || !aligned16(p->k_pool) || !aligned16(p->v_pool) || !aligned16(p->workspace))
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: q, pools and workspace must be 16-byte aligned");
+  const int ns_total = ns_p + ns_s;
+  const size_t need = ws_partials_bytes(d, ns_total);
+  if (p->workspace_bytes < need)
+    return fail(HAD_ERR_WORKSPACE_TOO_SMALL, "decode_attn_cascade: workspace %zu bytes < %zu", p->workspace_bytes,
+                need);
+  const int G = d->H_q / d->H_kv;
+  const int rows = d->q_len * G;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  had::ValuArgs a{};
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.k_pool = static_cast<const uint16_t*>(p->k_pool);
+  a.v_pool = static_cast<const uint16_t*>(p->v_pool);
+  a.ws_o = static_cast<float*>(p->workspace);
+  a.ws_ml = a.ws_o + static_cast<size_t>(d->n_seqs) * d->H_kv * ns_total * rows * d->head_dim;
+  a.d_err = p->d_err;
+  a.q_len = d->q_len;
+  a.H_q = d->H_q;
+  a.H_kv = d->H_kv;
+  a.G = G;
+  a.num_pages = d->num_pages;
+  a.page_size = d->page_size;
+  a.deterministic = (d->flags & HAD_ATTN_DETERMINISTIC) ? 1 : 0;
+  a.scale_log2 = d->sm_scale * 1.4426950408889634f;
+  a.ns_total = ns_total;
+  a.ws_rows = rows;
+  // prefix pass: all sequences' rows, the prefix page list as page-table row 0
+  had::ValuArgs ap = a;
+  ap.page_table = px->prefix_page_table;
+  ap.seq_lens = p->seq_lens;  // unused (fixed_len)
+  ap.n_seqs = 1;
+  ap.rows = d->n_seqs * rows;
+  ap.max_pages = px->prefix_pages;
+  ap.num_splits = ns_p;
+  ap.pps = 0;
+  ap.n_pages_plan = px->prefix_pages;
+  ap.pg_begin = 0;
+  ap.split_offset = 0;
+  ap.batch_rows = rows;
+  ap.fixed_len = px->prefix_pages * d->page_size;
+  hipError_t e = had::launch_attn_mfma(ap, d->head_dim, dim3(ns_p, d->H_kv, 1), s);
+  if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn_cascade: prefix kernel launch: %s", hipGetErrorString(e));
+  // suffix pass: each sequence from page prefix_pages on
+  had::ValuArgs as = a;
+  as.page_table = p->page_table;
+  as.seq_lens = p->seq_lens;
+  as.n_seqs = d->n_seqs;
+  as.rows = rows;
+  as.max_pages = d->max_pages;
+  as.num_splits = ns_s;
+  as.pps = 0;
+  as.n_pages_plan = n_sfx;
+  as.pg_begin = px->prefix_pages;
+  as.split_offset = ns_p;
+  as.batch_rows = 0;
+  as.fixed_len = -1;
+  const dim3 grid(ns_s, d->H_kv, d->n_seqs);
+  if (rows >= 16) {
+    as.row_base = 0;
+    e = had::launch_attn_mfma(as, d->head_dim, grid, s);
+  } else {
+    for (int rb = 0; rb < rows && e == hipSuccess; rb += 8) {
+      as.row_base = rb;
+      e = had::launch_attn_valu(as, d->head_dim, grid, s);
+    }
+  }
+  if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn_cascade: suffix kernel launch: %s", hipGetErrorString(e));
+  had::ValuArgs am = as;
+  am.num_splits = ns_total;
+  return launch_combine_after(d, am, p->out, stream);
 }
 
 }  // extern "C"

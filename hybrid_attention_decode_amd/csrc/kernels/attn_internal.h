@@ -28,6 +28,15 @@ struct ValuArgs {
   int n_pages_plan;  // pages the split plan covers; split i owns [i*n/ns, (i+1)*n/ns)
   int deterministic;  // fixed tile stride per wave instead of dynamic claims
   float scale_log2;
+  // Shared-prefix (cascade) passes.  Defaults (0, 0, num_splits, rows, 0, -1)
+  // give the plain split-K launch.
+  int pg_begin;      // the plan covers page-table entries pg_begin .. pg_begin + n_pages_plan
+  int split_offset;  // partial of split sp goes to workspace split split_offset + sp ...
+  int ns_total;      // ... of ns_total per (sequence, KV head)
+  int ws_rows;       // query rows per (sequence, KV head) in the workspace
+  int batch_rows;    // MFMA prefix pass: > 0 = the launch's rows are those of all sequences
+                     // (row r belongs to sequence r / batch_rows); page table row 0 is the prefix
+  int fixed_len;     // >= 0: every row sees exactly this many tokens (the prefix), seq_lens unused
 };
 
 // Inputs of the prologue when the VALU attention kernel runs it inline (the

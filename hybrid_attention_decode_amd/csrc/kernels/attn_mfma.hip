@@ -89,7 +89,10 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 // bank groups, and so do the rows 4 apart that one staging store touches
 __device__ __forceinline__ int kswz(int r, int mask) { return (r ^ (r >> 2)) & mask; }
 
-template <int D>
+// R128: 128 query rows per launch, wave w owning rows 16w .. 16w+15 and
+// working through both 32-token halves of every staged tile itself (no team
+// merge); otherwise 64 rows, the two teams splitting the tile's tokens.
+template <int D, bool R128>
 __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   using C = MCfg<D>;
   constexpr int TPT = C::TPT;
@@ -99,15 +102,16 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int team = wave >> 2, rb = wave & 3;
+  const int team = R128 ? 0 : wave >> 2, rb = R128 ? wave : wave & 3;
   const int P = a.page_size;
 
-  const int pg0 = static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
-  const int pg1_plan = static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
+  const int pg0 = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
+  const int pg1_plan = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
   const int npg_plan = pg1_plan - pg0;
   const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
-  const int L = a.seq_lens[s];
-  const bool bad_len = L < a.q_len || L > a.max_pages * P;
+  const int L = a.fixed_len >= 0 ? a.fixed_len : a.seq_lens[s];
+  // (a suffix pass also needs every query to see the whole prefix before pg_begin)
+  const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P);
   const int n_pages = bad_len ? 0 : (L + P - 1) / P;
   const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
   const int tok0 = pg0 * P;
@@ -129,18 +133,24 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   // row 16*rb + r16, dims 32*ks + 8g .. +8 (zero for padding rows)
   const int row = a.row_base + 16 * rb + r16;
   const bool row_ok = row < a.rows;
+  // prefix pass: the launch's rows are those of every sequence of the batch
+  const int s_row = a.batch_rows > 0 ? (row_ok ? row : 0) / a.batch_rows : s;
+  const int rr = a.batch_rows > 0 ? (row_ok ? row : 0) % a.batch_rows : row;  // row within its sequence
   const bool wave_active = a.row_base + 16 * rb < a.rows;  // uniform: any row of this wave real
   u32x4_t qb[C::KS];
   {
-    const int rc = row_ok ? row : 0;
-    const uint16_t* qp = a.q + ((static_cast<size_t>(s) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D;
+    const int rc = row_ok ? rr : 0;
+    const uint16_t* qp = a.q + ((static_cast<size_t>(s_row) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g);
       qb[ks] = row_ok ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  const int lim = row_ok ? (L - a.q_len + row / a.G + 1) : L;  // visible keys of this lane's row
+  // visible keys of this lane's row (causal inside the draft; a prefix pass
+  // sees the whole prefix)
+  const int lim = (row_ok && a.fixed_len < 0) ? (L - a.q_len + rr / a.G + 1) : L;
+  const int vis_all = min(tok_end, a.fixed_len >= 0 ? L : L - a.q_len + 1);  // below this: every row, every split token
 
   // staging map: wave w moves tokens of team w/4, chunk columns
   // CPW*(w%4) .. +CPW; lane -> (token group lu, chunk column lc)
@@ -210,16 +220,15 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   for (int mb = 0; mb < C::MB; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto compute = [&](int it, int b) __attribute__((always_inline)) {
-    if (!wave_active) return;
+  auto compute_half = [&](int it, int b, int tm) __attribute__((always_inline)) {
     const u32x4_t* kt = sh.u.t.k[b];
-    const uint16_t* vt = sh.u.t.vt[b][team];
+    const uint16_t* vt = sh.u.t.vt[b][tm];
     // ---- S^T for the team's 32 tokens: two 16-token blocks, KS k-steps each
     float sc[8];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const int r = team * kMTeamTok + 16 * tb + r16;  // A-operand row = token
+      const int r = tm * kMTeamTok + 16 * tb + r16;  // A-operand row = token
       const int sw = kswz(r, C::SWZ);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -229,21 +238,28 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * tb + i] = acc[i] * a.scale_log2;
     }
-    // tokens of slot i: tau(g, i) = 4g + i and 16 + 4g + i - 4
-    const int pos0 = tok0 + it * kMTile + team * kMTeamTok;
+    // tokens of slot i: tau(g, i) = 4g + i and 16 + 4g + i - 4 (the mask is
+    // skipped for tiles every row sees in full)
+    const int pos0 = tok0 + it * kMTile + tm * kMTeamTok;
+    if (pos0 + kMTeamTok > vis_all) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pos = pos0 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
-      if (pos >= tok_end || pos >= lim) sc[i] = -INFINITY;
+      for (int i = 0; i < 8; ++i) {
+        const int pos = pos0 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
+        if (pos >= tok_end || pos >= lim) sc[i] = -INFINITY;
+      }
     }
 
-    // ---- online softmax for this lane's row (4 lanes per row: g = 0..3)
+    // ---- online softmax for this lane's row (4 lanes per row: g = 0..3).
+    // The reference m_run moves only when a score exceeds it by more than
+    // 2^8 (base 2), so p = 2^(s - m_run) <= 256 and the O^T rescale is rare;
+    // o, l and m stay consistent, which is all the merge needs.
     float mt = sc[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
     mt = fmaxf(mt, shfl_xor_f(mt, 16));
     mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
+    const bool move = mt > m_run + 8.f;
+    const float m_new = move ? mt : m_run;
     const float m_sub = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_sub);
     uint32_t pw[4];
@@ -254,7 +270,7 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
       lsum += bf16_lo(pw[i]) + bf16_hi(pw[i]);
     }
     l_run = l_run * alpha + lsum;
-    if (__any(m_new != m_run)) {
+    if (__any(move)) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) o[mb] = o[mb] * alpha;
     }
@@ -269,6 +285,15 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
       const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
       const u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
       o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), o[mb], 0, 0, 0);
+    }
+  };
+  auto compute = [&](int it, int b) __attribute__((always_inline)) {
+    if (!wave_active) return;
+    if constexpr (R128) {
+      compute_half(it, b, 0);
+      compute_half(it, b, 1);
+    } else {
+      compute_half(it, b, team);
     }
   };
 
@@ -299,6 +324,22 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
   if (errs) atomicOr(&sh.err, errs);
+  if constexpr (R128) {  // every wave owns its rows outright
+    __syncthreads();
+    if (tid == 0 && sh.err) set_err(a.d_err, sh.err);
+    if (row_ok) {
+      const size_t unit = (static_cast<size_t>(s_row) * a.H_kv + h) * a.ns_total + a.split_offset + sp;
+      float* op = a.ws_o + (unit * a.ws_rows + rr) * D;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+        *reinterpret_cast<float4*>(op + 16 * mb + 4 * g) = make_float4(o[mb][0], o[mb][1], o[mb][2], o[mb][3]);
+      if (g == 0) {
+        a.ws_ml[(unit * a.ws_rows + rr) * 2 + 0] = m_run;
+        a.ws_ml[(unit * a.ws_rows + rr) * 2 + 1] = l_run;
+      }
+    }
+    return;
+  }
   __syncthreads();  // the tile buffers are free from here on
   if (team == 1 && wave_active) {
     float* orow = sh.u.m.o[rb][r16];
@@ -318,8 +359,8 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
     const float Ms = (M == -INFINITY) ? 0.f : M;
     const float w0 = exp2f(m_run - Ms), w1 = exp2f(m1 - Ms);
     const float* orow = sh.u.m.o[rb][r16];
-    const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.num_splits + sp;
-    float* op = a.ws_o + (unit * a.rows + row) * D;
+    const size_t unit = (static_cast<size_t>(s_row) * a.H_kv + h) * a.ns_total + a.split_offset + sp;
+    float* op = a.ws_o + (unit * a.ws_rows + rr) * D;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       const float4 o1 = *reinterpret_cast<const float4*>(orow + 16 * mb + 4 * g);
@@ -328,8 +369,8 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
                       o[mb][3] * w0 + o1.w * w1);
     }
     if (g == 0) {
-      a.ws_ml[(unit * a.rows + row) * 2 + 0] = M;
-      a.ws_ml[(unit * a.rows + row) * 2 + 1] = l_run * w0 + l1 * w1;
+      a.ws_ml[(unit * a.ws_rows + rr) * 2 + 0] = M;
+      a.ws_ml[(unit * a.ws_rows + rr) * 2 + 1] = l_run * w0 + l1 * w1;
     }
   }
 }
@@ -339,12 +380,18 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
 hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipStream_t stream) {
   ValuArgs a = a_in;
   hipError_t e = hipSuccess;
-  for (int rb = 0; rb < a.rows && e == hipSuccess; rb += kMRows) {
+  // up to 64 rows: the token-split teams; more: 128 rows per launch
+  const bool r128 = a.rows > kMRows;
+  for (int rb = 0; rb < a.rows && e == hipSuccess; rb += r128 ? 2 * kMRows : kMRows) {
     a.row_base = rb;
-    switch (head_dim) {
-      case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(64 * kMWaves), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(64 * kMWaves), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL(attn_mfma_kernel<256>, grid, dim3(64 * kMWaves), 0, stream, a); break;
+    const dim3 blk(64 * kMWaves);
+    switch (head_dim * 2 + (r128 ? 1 : 0)) {
+      case 128: hipLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, blk, 0, stream, a); break;
+      case 129: hipLaunchKernelGGL((attn_mfma_kernel<64, true>), grid, blk, 0, stream, a); break;
+      case 256: hipLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, blk, 0, stream, a); break;
+      case 257: hipLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, blk, 0, stream, a); break;
+      case 512: hipLaunchKernelGGL((attn_mfma_kernel<256, false>), grid, blk, 0, stream, a); break;
+      case 513: hipLaunchKernelGGL((attn_mfma_kernel<256, true>), grid, blk, 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();

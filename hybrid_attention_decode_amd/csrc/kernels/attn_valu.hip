@@ -118,8 +118,8 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   //
   // This split owns pages [pg0, pg1_plan) of the plan (balanced to within one
   // page); tiles are numbered from the split's first token.
-  const int pg0 = static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
-  const int pg1_plan = static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
+  const int pg0 = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
+  const int pg1_plan = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
   const int npg_plan = pg1_plan - pg0;
   const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
 
@@ -180,7 +180,8 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
 
   const int L = a.seq_lens[s];  // (a scalar load: it does not queue behind the tiles)
 
-  const bool bad_len = L < a.q_len || L > a.max_pages * P;
+  // (a suffix pass also needs every query to see the whole prefix before pg_begin)
+  const bool bad_len = L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P;
   // fused: the workgroup whose split holds the last position owns the new tokens
   const bool own = FUSED && !bad_len && (L - 1) / P >= pg0 && (L - 1) / P < pg1_plan;
   int errs = (bad_len && threadIdx.x == 0) ? HAD_DERR_SEQLEN : 0;
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
 
   // ---- merge the waves and store the split's partial: the per-row wave
   // weights once (kRows threads), then one float4 of one row per thread
-  const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.num_splits + sp;
+  const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.ns_total + a.split_offset + sp;
   if (threadIdx.x < kRows) {
     const int r = threadIdx.x;
     float M = -INFINITY;
@@ -503,8 +504,8 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
     }
     const int row = a.row_base + r;
     if (row < a.rows) {
-      a.ws_ml[(unit * a.rows + row) * 2 + 0] = M;
-      a.ws_ml[(unit * a.rows + row) * 2 + 1] = lsum;
+      a.ws_ml[(unit * a.ws_rows + row) * 2 + 0] = M;
+      a.ws_ml[(unit * a.ws_rows + row) * 2 + 1] = lsum;
     }
   }
   __syncthreads();
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
       const float4 o4 = *reinterpret_cast<const float4*>(&sh.o[w][r][4 * c4]);
       acc.x += wt * o4.x; acc.y += wt * o4.y; acc.z += wt * o4.z; acc.w += wt * o4.w;
     }
-    *reinterpret_cast<float4*>(&a.ws_o[(unit * a.rows + row) * D + 4 * c4]) = acc;
+    *reinterpret_cast<float4*>(&a.ws_o[(unit * a.ws_rows + row) * D + 4 * c4]) = acc;
   }
 }
 

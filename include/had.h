@@ -311,6 +311,37 @@ int had_decode_attn_combine(const had_attn_desc *d, int32_t num_splits,
                             const void *workspace, void *out, void *stream);
 
 /* ======================================================================
+ * decode_attn_cascade -- decode attention for a batch sharing a prefix
+ *
+ * The sequences of a batch that forked one cached prefix (page aliasing:
+ * zubnet.ai ¶2 and 24-ai.news, hybrid prefix caching) share its pages; here
+ * those pages are streamed once for the query rows of every sequence (MFMA
+ * kernel: rows = n_seqs x q_len x H_q/H_kv per KV head) instead of once per
+ * sequence, each sequence's own pages after the prefix are streamed by the
+ * usual split-K kernel, and the ordinary merge combines both sets of
+ * partials.  Output: as had_decode_attn (same operation; the sums differ in
+ * order only).
+ *
+ * px->prefix_pages whole pages (>= 1) form the shared prefix; px's page list
+ * must equal the first prefix_pages entries of every sequence's page-table
+ * row (not checked), and every sequence must see the whole prefix:
+ * seq_lens[s] - q_len >= prefix_pages * page_size (HAD_DERR_SEQLEN in d_err
+ * otherwise).  A prefix page still being written (a shared partial page) is
+ * not part of it: such a page belongs to each sequence after copy-on-write.
+ * Workspace: >= had_decode_attn_cascade_workspace_bytes(d, px) bytes, layout
+ * of had_decode_attn's ws_o / ws_ml with the prefix splits first (returns 0
+ * for an invalid descriptor).
+ * ====================================================================== */
+typedef struct {
+  int32_t prefix_pages;              /* whole pages shared by every sequence (>= 1)  */
+  const int32_t *prefix_page_table;  /* device int32 [prefix_pages]: their ids, in order */
+} had_attn_prefix;
+
+size_t had_decode_attn_cascade_workspace_bytes(const had_attn_desc *d, const had_attn_prefix *px);
+int had_decode_attn_cascade(const had_attn_desc *d, const had_attn_prefix *px, const had_attn_ptrs *p,
+                            void *stream);
+
+/* ======================================================================
  * decode_attn_layer -- qk_norm_rope_gate and decode_attn in one pass
  *
  * Below 16 query rows per KV head the prologue of a full-attention layer

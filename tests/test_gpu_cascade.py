@@ -1,0 +1,108 @@
+"""GPU parity: shared-prefix (cascade) decode attention against the fp64
+oracle and against the per-sequence split-K path."""
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_attention_decode_amd as had
+import synth
+from oracle import attention as A
+from oracle import bf16
+from oracle import paging as PG
+from gpu_util import DEV, assert_attn_close, bits_of, nan_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(seed, n, prefix_len, suffixes, q_len, H_q, H_kv, D, P):
+    """n sequences forked from one prefix (the oracle's page-table model), each
+    with its own suffix + q_len new tokens; copy-on-write applied to the host
+    pools; rows past every length hold NaN."""
+    lens = [prefix_len + sfx + q_len for sfx in suffixes]
+    max_pages = max(-(-L // P) for L in lens) + 1
+    N = -(-prefix_len // P) + sum(-(-(sfx + q_len) // P) + 1 for sfx in suffixes) + 4
+    order = synth.permutation(N, synth.seed_of(seed, 0))
+    m = PG.PageTableModel(N, P, n + 1, max_pages, free_order=order)
+    root = m.seq_create()
+    m.reserve(root, prefix_len)
+    kd = synth.normal_bf16((N, H_kv, P, D), synth.seed_of(seed, 1))
+    vd = synth.normal_bf16((N, H_kv, P, D), synth.seed_of(seed, 2))
+    seqs = []
+    for i in range(n):
+        sq = m.seq_fork(root, prefix_len)
+        trip = m.reserve(sq, suffixes[i] + q_len)
+        if trip is not None:
+            kd[trip[1]] = kd[trip[0]]
+            vd[trip[1]] = vd[trip[0]]
+        seqs.append(sq)
+    table, L = m.export(seqs, max_pages)
+    # stale rows: NaN everywhere past each length in pages no sequence reads there
+    kb, vb = kd.clone(), vd.clone()
+    used = np.zeros((N, P), bool)
+    for i in range(n):
+        for t in range(int(L[i])):
+            used[table[i, t // P], t % P] = True
+    stale = torch.from_numpy(~used)
+    kb[stale.nonzero(as_tuple=True)[0], :, stale.nonzero(as_tuple=True)[1]] = float("nan")
+    vb[stale.nonzero(as_tuple=True)[0], :, stale.nonzero(as_tuple=True)[1]] = float("nan")
+    q = synth.normal_bf16((n, q_len, H_q, D), synth.seed_of(seed, 3))
+    prefix_pages = prefix_len // P
+    assert np.all(table[:, :prefix_pages] == table[0, :prefix_pages])
+    return q, kb, vb, table, L, table[0, :prefix_pages].copy()
+
+
+def _oracle(q, kb, vb, table, L, P, D):
+    kbits, vbits, qb = bits_of(kb), bits_of(vb), bf16.to_f64(bits_of(q))
+    out = []
+    for s in range(len(L)):
+        K = bf16.to_f64(PG.gather(kbits, table[s], int(L[s]), P))
+        V = bf16.to_f64(PG.gather(vbits, table[s], int(L[s]), P))
+        out.append(A.attention(qb[s], K, V, 1.0 / np.sqrt(D)))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("n,prefix_len,q_len,H_q,H_kv,D,P", [
+    (4, 1000, 1, 8, 1, 128, 16),     # 8 rows per sequence (VALU suffix), partial shared page copied
+    (3, 2048, 4, 16, 1, 256, 64),    # speculative shape: 64 rows per sequence (MFMA suffix)
+    (5, 700, 1, 4, 2, 64, 32),       # two KV heads
+    (16, 5000, 1, 8, 1, 256, 64),    # prefix-shared batch shape (smaller prefix)
+])
+def test_cascade_matches_oracle(n, prefix_len, q_len, H_q, H_kv, D, P):
+    seed = 3000 + n * 7 + prefix_len % 101
+    suffixes = [int(x) for x in synth.integers(0, 3 * P + 5, n, synth.seed_of(seed, 9))]
+    suffixes[0] = 0                                      # one sequence with no private token before the draft
+    q, kb, vb, table, L, prefix = _batch(seed, n, prefix_len, suffixes, q_len, H_q, H_kv, D, P)
+    print("case n=%d prefix=%d q_len=%d H_q=%d H_kv=%d D=%d P=%d suffixes=%s" % (
+        n, prefix_len, q_len, H_q, H_kv, D, P, suffixes), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kd, vd, pt, Ld = to_dev(kb), to_dev(vb), to_dev(table), to_dev(L)
+    out = had.decode_attn_cascade(to_dev(q), kd, vd, pt, Ld, to_dev(prefix), d_err=err)
+    ref_path = had.decode_attn(to_dev(q), kd, vd, pt, Ld)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref = _oracle(q, kb, vb, table, L, P, D)
+    assert_attn_close(out, ref)
+    a, b = bf16.to_f64(bits_of(out)), bf16.to_f64(bits_of(ref_path))
+    assert np.abs(a - b).max() <= 4e-3
+
+
+def test_cascade_sequence_inside_prefix_is_reported():
+    n, prefix_len, P = 2, 512, 16
+    q, kb, vb, table, L, prefix = _batch(3100, n, prefix_len, [5, 0], 1, 8, 1, 128, P)
+    L = L.copy()
+    L[1] = prefix_len - 3                                # this sequence does not see the whole prefix
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("case cascade with a too-short sequence", flush=True)
+    had.decode_attn_cascade(to_dev(q), to_dev(kb), to_dev(vb), to_dev(table), to_dev(L), to_dev(prefix), d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_SEQLEN
+
+
+def test_cascade_rejects_bad_prefix():
+    q = torch.zeros((2, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    pool = torch.zeros((8, 1, 16, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(had.HadError):
+        had.decode_attn_cascade(q, pool, pool, torch.zeros((2, 4), dtype=torch.int32, device=DEV),
+                                torch.tensor([40, 40], dtype=torch.int32, device=DEV),
+                                torch.zeros(0, dtype=torch.int32, device=DEV))
