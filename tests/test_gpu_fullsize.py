@@ -220,9 +220,10 @@ def test_speculative_verify_rollback_256k():
 def test_prefix_shared_batch_copy_on_write():
     """16 sequences fork a 50,000-token prefix, take private suffixes of
     U{0..12288} tokens and decode one token each: shared pages are read
-    through every sequence's page table, the shared partial page is copied
-    on first write, and GDN states come from permuted slots (sequences with
-    no suffix read the shared prefix checkpoint)."""
+    through every sequence's page table (and, by the cascade path, once for
+    all sequences), the shared partial page is copied on first write, and
+    GDN states come from permuted slots (sequences with no suffix read the
+    shared prefix checkpoint)."""
     seed, n, prefix, H_q, n_slots = 500, 16, 50000, 8, 64
     suffix = synth.integers(0, 12288, n, synth.seed_of(seed, 2))
     suffix[3] = 0                                            # at least one sequence without a suffix
@@ -281,6 +282,9 @@ def test_prefix_shared_batch_copy_on_write():
     q_out, _ = had.qk_norm_rope_gate(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), pt_d, lens_d, kd, vd,
                                      R, BASE, EPS, d_err=err)
     out = had.decode_attn(q_out, kd, vd, pt_d, lens_d, max_seq_len=int(lens.max()), d_err=err)
+    # the same attention with the prefix's whole pages read once for all sequences
+    out_c = had.decode_attn_cascade(q_out, kd, vd, pt_d, lens_d, to_dev(mtable[0, :prefix // P].copy()),
+                                    max_seq_len=int(lens.max()), d_err=err)
     o = had.gdn_state_update(pool_d, to_dev(np.array(in_idx, np.int32)), to_dev(np.array(out_idx, np.int32)),
                              to_dev(gq), to_dev(gk), to_dev(gv), to_dev(gal), to_dev(gbe), d_err=err)
     torch.cuda.synchronize()
@@ -298,6 +302,7 @@ def test_prefix_shared_batch_copy_on_write():
         K, V = _context(kb_ref, vb_ref, mtable[i], L - 1)
         ref = A.attention(q_ref, np.concatenate([K, k_new]), np.concatenate([V, v_new]), scale)
         assert_attn_close(out[i], ref)
+        assert_attn_close(out_c[i], ref)
     new_pool, o_ref = gdn.state_update(pool0, np.array(in_idx), np.array(out_idx), _gdn_f64(gq), _gdn_f64(gk),
                                        _gdn_f64(gv), _gdn_f64(gal), _gdn_f64(gbe))
     got = pool_d.cpu().numpy()
