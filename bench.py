@@ -12,10 +12,15 @@ One step = one decode token through the whole stack:
   host   C++ page-table reserve of the new token (+ pinned async H2D of the
          length and, on a page boundary, of the new page-table entry)
   device replay of a captured HIP graph of the 48 layers:
-         GDN layer       had_gdn_state_update  (slot ping-pong by index)
+         GDN layer       had_gdn_state_update  (slot ping-pong by index;
+                         alpha = exp(g), beta = sigmoid(b) formed in-kernel
+                         from the raw gate values)
          attention layer had_decode_attn_layer: the prologue (QK-RMSNorm,
                          partial RoPE, gate split, K/V append) runs inside the
-                         split-K partial kernel, then the combine kernel
+                         split-K partial kernel, then the combine kernel, which
+                         applies the output gate sigmoid(gate)
+  Every kernel ORs its error bits into one device word, read once after the
+  timed region (no per-step device-to-host round trip).
 
 Prints one JSON line (stdout).  Progress goes to stderr.
 """
@@ -47,6 +52,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def check_sentinel(st):
+    """The one device-to-host read of the run's error word, after timing."""
+    e = int(st.err.item())
+    if e:
+        raise RuntimeError("a kernel reported error bits 0x%x during the run" % e)
+
+
 def algorithmic_bytes_per_step(L):
     return N_ATTN * L * KV_BYTES_PER_TOKEN + N_GDN * GDN_BYTES_PER_LAYER
 
@@ -76,6 +88,8 @@ class LongContextStack:
         self.len = L0
         # pinned staging, one entry per step so no buffer is rewritten while a copy is pending
         self.lens_pin = torch.empty(n_tokens + 1, dtype=torch.int32, pin_memory=True)
+        # device sentinel: every kernel ORs its error bits here; read once after the run
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.page_pin = torch.empty(n_tokens + 1, dtype=torch.int32, pin_memory=True)
 
         g = torch.Generator(device=dev)
@@ -109,8 +123,8 @@ class LongContextStack:
                 q=(q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
                 k=(k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
                 v=torch.randn((1, 1, GDN_H, DV), generator=g, device=dev, dtype=torch.bfloat16),
-                alpha=torch.rand((1, 1, GDN_H), generator=g, device=dev) * 0.1 + 0.9,
-                beta=torch.rand((1, 1, GDN_H), generator=g, device=dev),
+                g=-0.1 * torch.rand((1, 1, GDN_H), generator=g, device=dev),   # raw log decay
+                b=torch.randn((1, 1, GDN_H), generator=g, device=dev),           # raw write strength
                 o=torch.empty((1, 1, GDN_H, DV), device=dev),
             )
             self.gdn.append(lay)
@@ -124,12 +138,12 @@ class LongContextStack:
         a = self.attn[i]
         self.had.decode_attn_layer(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
                                    a["k_pool"], a["v_pool"], R, max_seq_len=self.total, workspace=self.ws,
-                                   out=a["out"], gate_out=a["gate"])
+                                   out=a["out"], gate_out=a["gate"], d_err=self.err, gated=True)
 
     def gdn_layer(self, i, parity):
         g = self.gdn[i]
         self.had.gdn_state_update(g["pool"], self.in_idx[parity], self.out_idx[parity], g["q"], g["k"], g["v"],
-                                  g["alpha"], g["beta"], o=g["o"])
+                                  g["g"], g["b"], o=g["o"], d_err=self.err, raw_gates=True)
 
     def layers(self, parity):
         ia = ig = 0
@@ -260,6 +274,7 @@ def run_context(L0, steps, warmup, kernel_reps, seed=0):
         attn_partial_bytes_per_launch=attn_bytes, attn_partial_context=L,
         num_splits=st.n_splits, pages_per_split=st.pps,
     )
+    check_sentinel(st)
     del st
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -289,6 +304,7 @@ class Stack:
         n = n_seqs
         self.ctrl_len = 2 * n + n * T
         self.ctrl = torch.zeros(self.ctrl_len, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)  # device sentinel, read after the run
         self.lens_dev = self.ctrl[:n]
         self.in_dev = self.ctrl[n:2 * n]
         self.out_dev = self.ctrl[2 * n:].view(n, T)
@@ -324,8 +340,8 @@ class Stack:
                 q=(q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
                 k=(k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16),
                 v=torch.randn((n, T, GDN_H, DV), generator=g, device=dev, dtype=torch.bfloat16),
-                alpha=torch.rand((n, T, GDN_H), generator=g, device=dev) * 0.1 + 0.9,
-                beta=torch.rand((n, T, GDN_H), generator=g, device=dev),
+                g=-0.1 * torch.rand((n, T, GDN_H), generator=g, device=dev),
+                b=torch.randn((n, T, GDN_H), generator=g, device=dev),
                 o=torch.empty((n, T, GDN_H, DV), device=dev)))
         self.graph = None
 
@@ -342,19 +358,20 @@ class Stack:
         a = self.attn[i]
         if getattr(self, "prefix_dev", None) is not None:
             self.had.qk_norm_rope_gate(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
-                                       a["k_pool"], a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"])
+                                       a["k_pool"], a["v_pool"], R, q_out=a["q_out"], gate_out=a["gate"],
+                                       d_err=self.err)
             self.had.decode_attn_cascade(a["q_out"], a["k_pool"], a["v_pool"], self.pt_dev, self.lens_dev,
                                          self.prefix_dev, max_seq_len=self.max_seq_len, workspace=self.cws,
-                                         out=a["out"])
+                                         out=a["out"], d_err=self.err, gate=a["gate"])
             return
         self.had.decode_attn_layer(a["qg"], a["k"], a["v"], a["w_q"], a["w_k"], self.pt_dev, self.lens_dev,
                                    a["k_pool"], a["v_pool"], R, max_seq_len=self.max_seq_len, workspace=self.ws,
-                                   out=a["out"], gate_out=a["gate"])
+                                   out=a["out"], gate_out=a["gate"], d_err=self.err, gated=True)
 
     def gdn_layer(self, i):
         g = self.gdn[i]
-        self.had.gdn_state_update(g["pool"], self.in_dev, self.out_dev, g["q"], g["k"], g["v"], g["alpha"],
-                                  g["beta"], o=g["o"])
+        self.had.gdn_state_update(g["pool"], self.in_dev, self.out_dev, g["q"], g["k"], g["v"], g["g"], g["b"],
+                                  o=g["o"], d_err=self.err, raw_gates=True)
 
     def layers(self):
         ia = ig = 0
@@ -428,7 +445,7 @@ def stack_kernel_us(st, kernel_reps):
         def cascade(r):
             a = st.attn[r % N_ATTN]
             had.decode_attn_cascade(a["q_out"], a["k_pool"], a["v_pool"], st.pt_dev, st.lens_dev, st.prefix_dev,
-                                    max_seq_len=st.max_seq_len, workspace=st.cws, out=a["out"])
+                                    max_seq_len=st.max_seq_len, workspace=st.cws, out=a["out"], gate=a["gate"])
 
         return {
             "prologue": round(time_graph(torch, prologue, n * N_ATTN), 3),
@@ -482,8 +499,13 @@ def run_speculative(L0=262144, steps=256, warmup=10, kernel_reps=4, T=4, G=16, s
         cur = had.spec_rollback(pt, slots, seq, T, a, cur, outs)
         L += a
 
-    st.push_ctrl(0, [L + T], [cur], [[cur] * T])
+    # the capture's eager run: the last T held positions stand in for drafts
+    # (every page it reads is mapped), checkpoints into distinct free slots
+    tmp = [slots.acquire() for _ in range(T)]
+    st.push_ctrl(0, [L], [cur], [tmp])
     st.capture()
+    for o in tmp:
+        slots.release(o)
     for t in range(warmup):
         step(t)
     torch.cuda.synchronize()
@@ -509,6 +531,7 @@ def run_speculative(L0=262144, steps=256, warmup=10, kernel_reps=4, T=4, G=16, s
                attn_partial_gbps=round(L * KV_BYTES_PER_TOKEN / (us["attn_partial"] * 1e-6) / 1e9, 1),
                us_per_layer=us, num_splits=st.n_splits)
     log("speculative: %.1f steps/s, %.2f accepted/step, partial %.1f us" % (1e3 / ms, acc_mean, us["attn_partial"]))
+    check_sentinel(st)
     del st
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -556,7 +579,7 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
         slots.release(cur)
         cur = out
 
-    st.push_ctrl(0, [L + 1], [cur], [[cur]])
+    st.push_ctrl(0, [L], [cur], [[cur]])   # capture's eager run: mapped pages only, in-place T = 1
     st.capture()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -582,6 +605,7 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
                checkpoints_kept=len(checkpoints), algorithmic_bytes_per_step=int(step_bytes),
                hbm_gbps=round(step_bytes / (ms * 1e-3) / 1e9, 1), us_per_layer_at_end=us)
     log("agentic: %.1f steps/s over %d steps" % (1e3 / ms, n_steps))
+    check_sentinel(st)
     del st
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -658,7 +682,9 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
             cur[i] = outs[i]
 
     tmp = [slots.acquire() for _ in range(n_seqs)]            # distinct slots for the capture run
-    st.push_ctrl(0, [x + 1 for x in Ls], cur, [[o] for o in tmp])
+    # its eager run reads mapped pages only (it rewrites each sequence's last held row
+    # with the synthetic new-token K/V; the values do not affect timing)
+    st.push_ctrl(0, Ls, cur, [[o] for o in tmp])
     st.capture()
     for o in tmp:
         slots.release(o)
@@ -690,6 +716,7 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
                us_per_layer=us, num_splits=st.n_splits)
     log("prefix-shared (%s): %.1f steps/s (%.0f tokens/s), %d CoW copies" % (
         "cascade" if cascade else "per sequence", 1e3 / ms, n_seqs * 1e3 / ms, n_cow))
+    check_sentinel(st)
     del st
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

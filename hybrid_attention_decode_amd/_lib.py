@@ -30,6 +30,8 @@ _STATUS = {
 }
 DERR_PAGE, DERR_SLOT, DERR_SEQLEN = 1, 2, 4
 ATTN_DETERMINISTIC = 1
+ATTN_GATED_OUTPUT = 4
+GDN_RAW_GATES = 1
 
 
 class HadError(RuntimeError):
@@ -69,7 +71,7 @@ class AttnDesc(ctypes.Structure):
 
 class AttnPtrs(ctypes.Structure):
     _fields_ = [("q", _p), ("k_pool", _p), ("v_pool", _p), ("page_table", _p), ("seq_lens", _p),
-                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("out", _p), ("d_err", _p)]
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("out", _p), ("d_err", _p), ("gate", _p)]
 
 
 class AttnPrefix(ctypes.Structure):
@@ -78,7 +80,7 @@ class AttnPrefix(ctypes.Structure):
 
 class GdnDesc(ctypes.Structure):
     _fields_ = [("n_seqs", _i32), ("T", _i32), ("H", _i32), ("d_k", _i32), ("d_v", _i32), ("n_slots", _i32),
-                ("q_scale", ctypes.c_float)]
+                ("q_scale", ctypes.c_float), ("flags", _i32)]
 
 
 class GdnPtrs(ctypes.Structure):
@@ -349,7 +351,8 @@ def qk_norm_rope_gate(qg, k, v, w_q, w_k, page_table, seq_lens, k_pool, v_pool, 
     return q_out, gate_out
 
 
-def attn_desc(q_shape, k_pool_shape, max_pages, sm_scale=None, max_seq_len=0, num_splits=0, deterministic=False):
+def attn_desc(q_shape, k_pool_shape, max_pages, sm_scale=None, max_seq_len=0, num_splits=0, deterministic=False,
+              gated=False):
     S, q_len, H_q, D = q_shape
     N, H_kv, P, D2 = k_pool_shape
     if D != D2:
@@ -357,7 +360,7 @@ def attn_desc(q_shape, k_pool_shape, max_pages, sm_scale=None, max_seq_len=0, nu
     if sm_scale is None:
         sm_scale = 1.0 / float(np.sqrt(D))
     return AttnDesc(S, q_len, H_q, H_kv, D, N, P, max_pages, float(sm_scale), int(max_seq_len), int(num_splits),
-                    ATTN_DETERMINISTIC if deterministic else 0)
+                    (ATTN_DETERMINISTIC if deterministic else 0) | (ATTN_GATED_OUTPUT if gated else 0))
 
 
 def decode_attn_plan(desc):
@@ -375,10 +378,12 @@ def decode_attn_workspace_bytes(desc):
 
 
 def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_len=0, num_splits=0,
-                workspace=None, out=None, d_err=None, deterministic=False):
-    """q [S, q_len, H_q, D] bf16 -> out [S, q_len, H_q, D] bf16."""
+                workspace=None, out=None, d_err=None, deterministic=False, gate=None):
+    """q [S, q_len, H_q, D] bf16 -> out [S, q_len, H_q, D] bf16.
+    gate (same shape, bf16): when given, out is multiplied by sigmoid(gate)."""
     torch = _torch()
-    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits, deterministic)
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits, deterministic,
+                     gate is not None)
     need = decode_attn_workspace_bytes(desc)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -387,18 +392,21 @@ def decode_attn(q, k_pool, v_pool, page_table, seq_lens, sm_scale=None, max_seq_
     ptrs = AttnPtrs(_dev(q, torch.bfloat16, "q"), _dev(k_pool, torch.bfloat16, "k_pool"),
                     _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
                     _dev(seq_lens, torch.int32, "seq_lens"), _dev(workspace, torch.uint8, "workspace"),
-                    workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"))
+                    workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"),
+                    None if gate is None else _dev(gate, torch.bfloat16, "gate"))
     _check(lib().had_decode_attn(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
     return out
 
 
 def decode_attn_cascade(q, k_pool, v_pool, page_table, seq_lens, prefix_page_table, sm_scale=None, max_seq_len=0,
-                        workspace=None, out=None, d_err=None, deterministic=False):
+                        workspace=None, out=None, d_err=None, deterministic=False, gate=None):
     """Decode attention for a batch whose sequences share their first
     len(prefix_page_table) pages (read once for every sequence's rows).
-    q [S, q_len, H_q, D] bf16; prefix_page_table int32 [prefix_pages] on the device."""
+    q [S, q_len, H_q, D] bf16; prefix_page_table int32 [prefix_pages] on the device.
+    gate (like q): when given, out is multiplied by sigmoid(gate)."""
     torch = _torch()
-    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, 0, deterministic)
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, 0, deterministic,
+                     gate is not None)
     px = AttnPrefix(prefix_page_table.numel(), _dev(prefix_page_table, torch.int32, "prefix_page_table"))
     need = lib().had_decode_attn_cascade_workspace_bytes(ctypes.byref(desc), ctypes.byref(px))
     if need == 0:  # invalid descriptor or prefix: the call itself reports why
@@ -410,7 +418,8 @@ def decode_attn_cascade(q, k_pool, v_pool, page_table, seq_lens, prefix_page_tab
     ptrs = AttnPtrs(_dev(q, torch.bfloat16, "q"), _dev(k_pool, torch.bfloat16, "k_pool"),
                     _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
                     _dev(seq_lens, torch.int32, "seq_lens"), _dev(workspace, torch.uint8, "workspace"),
-                    workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"))
+                    workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"),
+                    None if gate is None else _dev(gate, torch.bfloat16, "gate"))
     _check(lib().had_decode_attn_cascade(ctypes.byref(desc), ctypes.byref(px), ctypes.byref(ptrs), _stream()))
     return out
 
@@ -422,16 +431,17 @@ def decode_attn_cascade_workspace_bytes(desc, prefix_pages):
 
 def decode_attn_layer(qg, k, v, w_q, w_k, page_table, seq_lens, k_pool, v_pool, rotary_dim, rope_base=10000.0,
                       eps=1e-6, sm_scale=None, max_seq_len=0, num_splits=0, workspace=None, out=None, gate_out=None,
-                      q_out=None, d_err=None, deterministic=False, partial_only=False):
+                      q_out=None, d_err=None, deterministic=False, partial_only=False, gated=False):
     """qk_norm_rope_gate + decode_attn in one pass (the prologue runs inside
     the attention kernel).  qg [S, T, H_q, 2, D]; k, v [S, T, H_kv, D].
     Returns (out, gate_out) [S, T, H_q, D]; q_out is written when given.
-    partial_only: stop after the partials (workspace), out is not written."""
+    partial_only: stop after the partials (workspace), out is not written.
+    gated: out is multiplied by sigmoid(gate) before its rounding."""
     torch = _torch()
     S, T, H_q, two, D = qg.shape
     H_kv = k.shape[2]
     desc = attn_desc((S, T, H_q, D), k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, num_splits,
-                     deterministic)
+                     deterministic, gated)
     pdesc = QknrgDesc(S, T, H_q, H_kv, D, rotary_dim, float(rope_base), float(eps), k_pool.shape[0], k_pool.shape[2],
                       page_table.shape[1])
     need = decode_attn_workspace_bytes(desc)
@@ -479,15 +489,17 @@ def decode_attn_combine(desc, num_splits, workspace, out):
     return out
 
 
-def gdn_state_update(state_pool, in_idx, out_idx, q, k, v, alpha, beta, o=None, q_scale=1.0, d_err=None):
+def gdn_state_update(state_pool, in_idx, out_idx, q, k, v, alpha, beta, o=None, q_scale=1.0, d_err=None,
+                     raw_gates=False):
     """state_pool [n_slots, H, d_v, d_k] fp32; q, k [S, T, H, d_k]; v [S, T, H, d_v] bf16;
-    alpha, beta [S, T, H] fp32; in_idx [S], out_idx [S, T] int32 -> o [S, T, H, d_v] fp32."""
+    alpha, beta [S, T, H] fp32; in_idx [S], out_idx [S, T] int32 -> o [S, T, H, d_v] fp32.
+    raw_gates: alpha, beta hold g and b; the kernel uses exp(g) and sigmoid(b)."""
     torch = _torch()
     n_slots, H, d_v, d_k = state_pool.shape
     S, T = out_idx.shape
     if o is None:
         o = torch.empty((S, T, H, d_v), dtype=torch.float32, device=state_pool.device)
-    desc = GdnDesc(S, T, H, d_k, d_v, n_slots, float(q_scale))
+    desc = GdnDesc(S, T, H, d_k, d_v, n_slots, float(q_scale), GDN_RAW_GATES if raw_gates else 0)
     ptrs = GdnPtrs(_dev(state_pool, torch.float32, "state_pool"), _dev(in_idx, torch.int32, "in_idx"),
                    _dev(out_idx, torch.int32, "out_idx"), _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
                    _dev(v, torch.bfloat16, "v"), _dev(alpha, torch.float32, "alpha"),

@@ -40,9 +40,17 @@ int check_desc(const had_attn_desc* d) {
     return fail(HAD_ERR_INVALID_ARG, "decode_attn: max_seq_len %d outside [0, max_pages*page_size=%lld]",
                 d->max_seq_len, static_cast<long long>(cap));
   if (d->num_splits < 0) return fail(HAD_ERR_INVALID_ARG, "decode_attn: num_splits %d < 0", d->num_splits);
-  if (d->flags & ~HAD_ATTN_DETERMINISTIC) return fail(HAD_ERR_INVALID_ARG, "decode_attn: unknown flags 0x%x", d->flags);
+  if (d->flags & ~(HAD_ATTN_DETERMINISTIC | HAD_ATTN_GATED_OUTPUT))
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn: unknown flags 0x%x", d->flags);
   const int rows = d->q_len * (d->H_q / d->H_kv);
   if (rows > 256) return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %d query rows per KV head > 256", rows);
+  return HAD_OK;
+}
+
+// The split entry points have no gate to apply at the merge.
+int no_gate(const had_attn_desc* d, const char* who) {
+  if (d && (d->flags & HAD_ATTN_GATED_OUTPUT))
+    return fail(HAD_ERR_INVALID_ARG, "%s: HAD_ATTN_GATED_OUTPUT is not available on this entry point", who);
   return HAD_OK;
 }
 
@@ -184,12 +192,20 @@ static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* 
 }
 
 int had_decode_attn_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* stream) {
+  if (no_gate(d, "decode_attn_partial") != HAD_OK) return HAD_ERR_INVALID_ARG;
   const int st = launch_partial(d, p, stream, nullptr);
   return st == HAD_OK ? had::ok() : st;
 }
 
-static int launch_combine_after(const had_attn_desc* d, const had::ValuArgs& a, void* out, void* stream) {
+// gate / gate_hstride: bf16 gate of head (s, j, hq) at gate + ((s*q_len + j)*H_q + hq)*gate_hstride,
+// applied when the descriptor asks for the gated output.
+static int launch_combine_after(const had_attn_desc* d, const had::ValuArgs& a, void* out, void* stream,
+                                const void* gate = nullptr, int gate_hstride = 0) {
   had::CombineArgs c{};
+  if (d->flags & HAD_ATTN_GATED_OUTPUT) {
+    c.gate = static_cast<const uint16_t*>(gate);
+    c.gate_hstride = gate_hstride;
+  }
   c.ws_o = a.ws_o;
   c.ws_ml = a.ws_ml;
   c.out = static_cast<uint16_t*>(out);
@@ -207,10 +223,12 @@ static int launch_combine_after(const had_attn_desc* d, const had::ValuArgs& a, 
 
 int had_decode_attn(const had_attn_desc* d, const had_attn_ptrs* p, void* stream) {
   if (p && !p->out) return fail(HAD_ERR_INVALID_ARG, "decode_attn: out is NULL");
+  if (d && p && (d->flags & HAD_ATTN_GATED_OUTPUT) && !p->gate)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn: HAD_ATTN_GATED_OUTPUT with a NULL gate");
   had::ValuArgs a{};
   const int st = launch_partial(d, p, stream, &a);
   if (st != HAD_OK) return st;
-  return launch_combine_after(d, a, p->out, stream);
+  return launch_combine_after(d, a, p->out, stream, p->gate, d->head_dim);
 }
 
 static int launch_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd, const had_qknrg_ptrs* pp,
@@ -278,12 +296,14 @@ int had_decode_attn_layer(const had_attn_desc* d, const had_qknrg_desc* pd, cons
   had::ValuArgs a{};
   int st = launch_layer_partial(d, pd, pp, workspace, workspace_bytes, stream, &a);
   if (st != HAD_OK) return st;
-  st = launch_combine_after(d, a, out, stream);
+  // the gate half of each head's (q, gate) pair in qg
+  st = launch_combine_after(d, a, out, stream, static_cast<const uint16_t*>(pp->qg) + d->head_dim, 2 * d->head_dim);
   return st == HAD_OK ? had::ok() : st;
 }
 
 int had_decode_attn_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd, const had_qknrg_ptrs* pp,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (no_gate(d, "decode_attn_layer_partial") != HAD_OK) return HAD_ERR_INVALID_ARG;
   had::ValuArgs a{};
   const int st = launch_layer_partial(d, pd, pp, workspace, workspace_bytes, stream, &a);
   return st == HAD_OK ? had::ok() : st;
@@ -293,6 +313,7 @@ int had_decode_attn_combine(const had_attn_desc* d, int32_t num_splits, const vo
                             void* stream) {
   int st = check_desc(d);
   if (st != HAD_OK) return st;
+  if (no_gate(d, "decode_attn_combine") != HAD_OK) return HAD_ERR_INVALID_ARG;
   if (!workspace || !out || num_splits < 1 || num_splits > had::kMaxSplits)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_combine: bad argument (num_splits=%d, max %d)", num_splits,
                 had::kMaxSplits);
@@ -359,6 +380,8 @@ size_t had_decode_attn_cascade_workspace_bytes(const had_attn_desc* d, const had
 }
 
 int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, void* stream) {
+  if (d && p && (d->flags & HAD_ATTN_GATED_OUTPUT) && !p->gate)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: HAD_ATTN_GATED_OUTPUT with a NULL gate");
   int ns_p, ns_s, n_sfx;
   int st = cascade_plan(d, px, &ns_p, &ns_s, &n_sfx);
   if (st != HAD_OK) return st;
@@ -435,7 +458,7 @@ int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, c
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn_cascade: suffix kernel launch: %s", hipGetErrorString(e));
   had::ValuArgs am = as;
   am.num_splits = ns_total;
-  return launch_combine_after(d, am, p->out, stream);
+  return launch_combine_after(d, am, p->out, stream, p->gate, d->head_dim);
 }
 
 }  // extern "C"

@@ -3,8 +3,10 @@
 // For query row r of (sequence s, KV head h) with partials (o_i, m_i, l_i)
 // from the splits i (m in base-2 units, o and l unnormalised):
 //   M = max_i m_i,  w_i = 2^(m_i - M),  out = sum_i w_i o_i / sum_i w_i l_i,
-// rounded to bf16 (nearest even).  Splits with m = -inf carry weight 0; a
-// row with no visible key at all (sum of weights 0) is written as zeros.
+// rounded to bf16 (nearest even) -- after an optional multiplication by
+// sigmoid(gate) (the gated attention output of the full-attention layers).
+// Splits with m = -inf carry weight 0; a row with no visible key at all (sum
+// of weights 0) is written as zeros.
 // This log-sum-exp merge makes the split over the context exact up to
 // rounding (long contexts up to 1M tokens, 24-ai.news long-context table).
 //
@@ -116,9 +118,17 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     const int s = unit / a.H_kv, h = unit % a.H_kv;
     const int jq = row / a.G, g = row % a.G;
-    uint16_t* op = a.out + ((static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g) * D + d0 + 4 * tid;
-    const uint32_t lo = pack_bf16x2(t.x * inv, t.y * inv), hi = pack_bf16x2(t.z * inv, t.w * inv);
-    *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
+    const size_t head = (static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g;
+    float4 r = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    if (a.gate) {  // gated output: sigmoid(gate) in fp32, before the rounding
+      const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + head * a.gate_hstride + d0 + 4 * tid);
+      r.x *= 1.f / (1.f + expf(-bf16_lo(gw.x)));
+      r.y *= 1.f / (1.f + expf(-bf16_hi(gw.x)));
+      r.z *= 1.f / (1.f + expf(-bf16_lo(gw.y)));
+      r.w *= 1.f / (1.f + expf(-bf16_hi(gw.y)));
+    }
+    uint16_t* op = a.out + head * D + d0 + 4 * tid;
+    *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
   }
 }
 

@@ -65,6 +65,10 @@ struct CombineArgs {
   const float* ws_ml;
   uint16_t* out;
   int n_seqs, q_len, H_q, H_kv, G, rows, num_splits;
+  // optional output gate: out *= sigmoid(gate), gate of (s, j, hq) at
+  // gate + ((s * q_len + j) * H_q + hq) * gate_hstride (the gate half of qg)
+  const uint16_t* gate;
+  int gate_hstride;
 };
 
 hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);

@@ -42,6 +42,7 @@ struct GdnArgs {
   int32_t* d_err;
   int T, H, d_v, n_slots;
   float q_scale;
+  int raw_gates;  // alpha / beta hold g and b: alpha = exp(g), beta = sigmoid(b)
 };
 
 __device__ __forceinline__ float sum8(float x) {
@@ -84,7 +85,11 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
     const size_t th = (static_cast<size_t>(s) * a.T + t) * a.H + h;
     const uint16_t* kp = a.k + th * DK;
     const uint16_t* qp = a.q + th * DK;
-    const float al = a.alpha[th], be = a.beta[th];
+    float al = a.alpha[th], be = a.beta[th];
+    if (a.raw_gates) {
+      al = expf(al);
+      be = 1.f / (1.f + expf(-be));
+    }
     const float vi = bf16_to_f32(a.v[th * a.d_v + row]);
     float kk[NC][4], qq[NC][4];
 #pragma unroll
@@ -133,6 +138,7 @@ extern "C" int had_gdn_state_update(const had_gdn_desc* d, const had_gdn_ptrs* p
                 d->H, d->n_slots);
   if ((d->d_k != 64 && d->d_k != 128) || (d->d_v != 64 && d->d_v != 128))
     return fail(HAD_ERR_UNSUPPORTED_SHAPE, "gdn_state_update: d_k=%d d_v=%d must be 64 or 128", d->d_k, d->d_v);
+  if (d->flags & ~HAD_GDN_RAW_GATES) return fail(HAD_ERR_INVALID_ARG, "gdn_state_update: unknown flags 0x%x", d->flags);
   if (!p->state_pool || !p->in_idx || !p->out_idx || !p->q || !p->k || !p->v || !p->alpha || !p->beta || !p->o)
     return fail(HAD_ERR_INVALID_ARG, "gdn_state_update: NULL pointer in ptrs");
   if ((reinterpret_cast<uintptr_t>(p->state_pool) & 15u) != 0 || (reinterpret_cast<uintptr_t>(p->q) & 7u) != 0 ||
@@ -151,6 +157,7 @@ extern "C" int had_gdn_state_update(const had_gdn_desc* d, const had_gdn_ptrs* p
   a.o = p->o;
   a.d_err = p->d_err;
   a.T = d->T;
+  a.raw_gates = (d->flags & HAD_GDN_RAW_GATES) ? 1 : 0;
   a.H = d->H;
   a.d_v = d->d_v;
   a.n_slots = d->n_slots;

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define HAD_ABI_VERSION 1
+#define HAD_ABI_VERSION 2
 
 enum {
   HAD_OK = 0,
@@ -284,6 +284,14 @@ typedef struct {
  * inputs and the split plan only. */
 #define HAD_ATTN_DETERMINISTIC 1
 
+/* The merge multiplies the attention output by sigmoid(gate) elementwise
+ * (fp32, before the bf16 rounding of out) -- the gated attention output of
+ * the hybrid model's full-attention layers.  had_decode_attn and
+ * had_decode_attn_cascade read the gate from had_attn_ptrs.gate (NULL is an
+ * error); had_decode_attn_layer takes the second half of qg; the split entry
+ * points (_partial, _combine, _layer_partial) reject the flag. */
+#define HAD_ATTN_GATED_OUTPUT 4
+
 typedef struct {
   const void *q;             /* bf16 [n_seqs][q_len][H_q][head_dim]         */
   const void *k_pool, *v_pool;
@@ -293,6 +301,9 @@ typedef struct {
   size_t workspace_bytes;
   void *out;                 /* bf16 [n_seqs][q_len][H_q][head_dim]         */
   int32_t *d_err;            /* optional                                    */
+  const void *gate;          /* bf16 [n_seqs][q_len][H_q][head_dim], read   *
+                              * with HAD_ATTN_GATED_OUTPUT only (the gate   *
+                              * that had_qk_norm_rope_gate splits off)      */
 } had_attn_ptrs;
 
 /* Split plan for desc: number of splits and pages per split. */
@@ -393,7 +404,13 @@ typedef struct {
   int32_t n_seqs, T, H, d_k, d_v; /* d_k, d_v in {64, 128}; 1 <= T <= 8 */
   int32_t n_slots;
   float q_scale;                  /* 1 for the plain recurrence          */
+  int32_t flags;                  /* HAD_GDN_* bits                      */
 } had_gdn_desc;
+
+/* alpha[] and beta[] hold the raw gate values g and b of each (token, head):
+ * the kernel forms alpha = exp(g) (g <= 0, the log decay) and
+ * beta = 1 / (1 + exp(-b)) in fp32 (the Gated DeltaNet parameterisation). */
+#define HAD_GDN_RAW_GATES 1
 
 typedef struct {
   float *state_pool;         /* fp32 [n_slots][H][d_v][d_k]              */

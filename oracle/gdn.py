@@ -34,6 +34,17 @@ of the float64 state.
 import numpy as np
 
 
+def gates_from_raw(g, b):
+    """Per-(token, head) gates from their raw values: alpha = exp(g) (g is the
+    log decay, g <= 0) and beta = 1 / (1 + exp(-b)), the parameterisation of
+    the Gated DeltaNet paper (decay in (0, 1], write strength in (0, 1)).
+    Reading (pages silent): the kernel receives g and b as they leave the
+    layer's projections."""
+    g = np.asarray(g, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.exp(g), 1.0 / (1.0 + np.exp(-b))
+
+
 def step(S, q, k, v, alpha, beta):
     """One token of the recurrence, dense form.  Returns (S_t, S_t q)."""
     d_k = k.shape[0]

@@ -17,11 +17,15 @@ The three steps are textbook operations:
   R dims only, with the "rotate-half" pairing (i, i + R/2), angle
   theta_i = pos * base**(-2i/R), i < R/2.
 * Gate split: the projection output of each query head holds q then gate.
+* Output gate: the attention output of a head is multiplied elementwise by
+  sigmoid(gate) (the gated attention output of the full-attention layers).
 
 Readings (pages silent): norm before rotation (the order of the name); the
 first R dims rotate and the rest pass through; base 10000 and eps 1e-6 by
 default; ``w`` is the final multiplier; qg layout [T, H_q, 2, D]; positions
-of the T new tokens are seq_len_before + j; v is passed through unchanged.
+of the T new tokens are seq_len_before + j; v is passed through unchanged;
+the gate the split produces is applied as sigmoid(gate) * attention output,
+per element of the head (the pages name the split, not where the gate acts).
 Angles are computed in float64.
 """
 
@@ -61,3 +65,10 @@ def qk_norm_rope_gate(qg, k, v, w_q, w_k, positions, rotary_dim, base=10000.0, e
     q_out = rope_partial(rmsnorm(q, w_q, eps), positions, rotary_dim, base)
     k_out = rope_partial(rmsnorm(k, w_k, eps), positions, rotary_dim, base)
     return q_out, gate, k_out, np.array(v, np.float64, copy=True)
+
+
+def output_gate(o, gate):
+    """o * sigmoid(gate), elementwise; o and gate [..., D]."""
+    o = np.asarray(o, np.float64)
+    gate = np.asarray(gate, np.float64)
+    return o / (1.0 + np.exp(-gate))

@@ -8,6 +8,7 @@ import hybrid_attention_decode_amd as had
 import synth
 from oracle import attention as A
 from oracle import bf16
+from oracle import prologue as Pr
 from gpu_util import DEV, assert_attn_close, bits_of, paged_case, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -173,3 +174,22 @@ def test_mfma_path_structured_values():
     out, ref = _run(1200, [30000], 4, 16, 1, 256, 64, structured=True)
     assert np.abs(ref).max() > 0.2
     assert_attn_close(out, ref)
+
+
+@pytest.mark.parametrize("lens,q_len,H_q,H_kv,D,P", [
+    ([40000], 1, 8, 1, 256, 64),      # VALU path
+    ([5000, 77], 4, 16, 1, 256, 64),  # MFMA path
+    ([999], 3, 4, 2, 64, 16),
+])
+def test_gated_output_against_oracle(lens, q_len, H_q, H_kv, D, P):
+    seed = 150 + sum(lens) % 89
+    q, kp, vp, pt, L = paged_case(seed, lens, q_len, H_q, H_kv, D, P)
+    gate = synth.normal_bf16(tuple(q.shape), synth.seed_of(seed, 77))
+    print("case gated seed=%d lens=%s q_len=%d H_q=%d H_kv=%d D=%d P=%d" % (seed, lens, q_len, H_q, H_kv, D, P),
+          flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L), d_err=err, gate=to_dev(gate))
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref = A.paged_attention(bits_of(q), bits_of(kp), bits_of(vp), pt, L, P, 1.0 / np.sqrt(D))
+    assert_attn_close(out, Pr.output_gate(ref, bf16.to_f64(bits_of(gate))))

@@ -10,6 +10,7 @@ import synth
 from oracle import attention as A
 from oracle import bf16
 from oracle import paging as PG
+from oracle import prologue as Pr
 from gpu_util import DEV, assert_attn_close, bits_of, nan_bf16, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -85,6 +86,22 @@ def test_cascade_matches_oracle(n, prefix_len, q_len, H_q, H_kv, D, P):
     assert_attn_close(out, ref)
     a, b = bf16.to_f64(bits_of(out)), bf16.to_f64(bits_of(ref_path))
     assert np.abs(a - b).max() <= 4e-3
+
+
+def test_cascade_gated_output():
+    n, prefix_len, q_len, H_q, H_kv, D, P = 6, 3000, 4, 16, 1, 256, 64
+    seed = 3200
+    suffixes = [int(x) for x in synth.integers(0, 3 * P + 5, n, synth.seed_of(seed, 9))]
+    q, kb, vb, table, L, prefix = _batch(seed, n, prefix_len, suffixes, q_len, H_q, H_kv, D, P)
+    gate = synth.normal_bf16(tuple(q.shape), synth.seed_of(seed, 8))
+    print("case gated cascade n=%d prefix=%d suffixes=%s" % (n, prefix_len, suffixes), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn_cascade(to_dev(q), to_dev(kb), to_dev(vb), to_dev(table), to_dev(L), to_dev(prefix),
+                                  d_err=err, gate=to_dev(gate))
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref = Pr.output_gate(_oracle(q, kb, vb, table, L, P, D), bf16.to_f64(bits_of(gate)))
+    assert_attn_close(out, ref)
 
 
 def test_cascade_sequence_inside_prefix_is_reported():

@@ -141,3 +141,45 @@ def test_800_token_chain_drift():
             worst = max(worst, _rel_fro(hh[t, h], st[t]))
     print("worst relative state error over the chain: %.3g" % worst)
     assert worst <= 1e-3
+
+
+def test_raw_gates_match_oracle_parameterisation():
+    # the kernel forms alpha = exp(g), beta = sigmoid(b) from raw values
+    seed, S, T, H, dk, dv, n_slots = 7, 2, 4, 8, 128, 128, 12
+    pool = _warm_pool(seed, n_slots, H, dk, dv)
+    q, k, v, _, _ = _inputs(seed, S, T, H, dk, dv)
+    g = -synth.uniform_f32((S, T, H), 0.0, 0.1, synth.seed_of(seed, 6))
+    b = synth.uniform_f32((S, T, H), -3.0, 3.0, synth.seed_of(seed, 7))
+    in_idx, out_idx = [4, 9], [[0, 1, 2, 3], [5, 6, 7, 8]]
+    print("case raw gates seed=%d S=%d T=%d" % (seed, S, T), flush=True)
+    pd = to_dev(pool)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o = had.gdn_state_update(pd, to_dev(np.asarray(in_idx, np.int32)), to_dev(np.asarray(out_idx, np.int32)),
+                             to_dev(q), to_dev(k), to_dev(v), to_dev(g), to_dev(b), d_err=err, raw_gates=True)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    al, be = gdn.gates_from_raw(g.numpy(), b.numpy())
+    new_ref, o_ref = gdn.state_update(pool, np.asarray(in_idx), np.asarray(out_idx), bf16.to_f64(bits_of(q)),
+                                      bf16.to_f64(bits_of(k)), bf16.to_f64(bits_of(v)), al, be)
+    got = pd.cpu().numpy()
+    for sl in sorted(set(np.asarray(out_idx).ravel().tolist())):
+        for h in range(H):
+            assert _rel_fro(got[sl, h].astype(np.float64), new_ref[sl, h].astype(np.float64)) <= 1e-4
+    oc = o.cpu().numpy().astype(np.float64)
+    for s in range(S):
+        for t in range(T):
+            for h in range(H):
+                assert _rel_fro(oc[s, t, h], o_ref[s, t, h]) <= 1e-4
+
+
+def test_unknown_gdn_flag_is_rejected():
+    pool = torch.zeros((2, 1, 64, 64), dtype=torch.float32, device=DEV)
+    x = torch.zeros((1, 1, 1, 64), dtype=torch.bfloat16, device=DEV)
+    a = torch.zeros((1, 1, 1), dtype=torch.float32, device=DEV)
+    desc = had._lib.GdnDesc(1, 1, 1, 64, 64, 2, 1.0, 8)
+    ptrs = had._lib.GdnPtrs(pool.data_ptr(), torch.zeros(1, dtype=torch.int32, device=DEV).data_ptr(),
+                            torch.ones((1, 1), dtype=torch.int32, device=DEV).data_ptr(), x.data_ptr(), x.data_ptr(),
+                            x.data_ptr(), a.data_ptr(), a.data_ptr(), torch.zeros((1, 1, 1, 64), device=DEV).data_ptr(),
+                            None)
+    import ctypes
+    assert had.lib().had_gdn_state_update(ctypes.byref(desc), ctypes.byref(ptrs), None) != 0

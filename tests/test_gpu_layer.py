@@ -29,21 +29,21 @@ def _inputs(seed, S, T, H_q, H_kv, D):
     return qg, k, v, w_q, w_k
 
 
-def _run(seed, lens, T, H_q, H_kv, D, R, P, num_splits=0, deterministic=False):
+def _run(seed, lens, T, H_q, H_kv, D, R, P, num_splits=0, deterministic=False, gated=False):
     _, k_pool, v_pool, pt, L = paged_case(seed, lens, T, H_q, H_kv, D, P)
     qg, k, v, w_q, w_k = _inputs(seed, len(lens), T, H_q, H_kv, D)
-    print("case seed=%d lens=%s T=%d H_q=%d H_kv=%d D=%d R=%d P=%d splits=%d" % (
-        seed, list(lens), T, H_q, H_kv, D, R, P, num_splits), flush=True)
+    print("case seed=%d lens=%s T=%d H_q=%d H_kv=%d D=%d R=%d P=%d splits=%d gated=%d" % (
+        seed, list(lens), T, H_q, H_kv, D, R, P, num_splits, gated), flush=True)
     kd, vd = to_dev(k_pool), to_dev(v_pool)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     q_out = torch.empty((len(lens), T, H_q, D), dtype=torch.bfloat16, device=DEV)
     out, gate = had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt),
                                       to_dev(L), kd, vd, R, num_splits=num_splits, q_out=q_out, d_err=err,
-                                      deterministic=deterministic)
+                                      deterministic=deterministic, gated=gated)
     torch.cuda.synchronize()
     assert err.item() == 0
     return dict(k_pool=k_pool, v_pool=v_pool, pt=pt, L=L, qg=qg, k=k, v=v, w_q=w_q, w_k=w_k, kd=kd, vd=vd,
-                out=out, gate=gate, q_out=q_out, T=T, R=R, P=P, D=D)
+                out=out, gate=gate, q_out=q_out, T=T, R=R, P=P, D=D, gated=gated)
 
 
 def _check_against_oracle(c):
@@ -69,6 +69,8 @@ def _check_against_oracle(c):
         K = np.concatenate([K, bf16.to_f64(bf16.from_f64(k_ref))])
         V = np.concatenate([V, v_ref])
         ref = A.attention(bf16.to_f64(bf16.from_f64(q_ref)), K, V, 1.0 / np.sqrt(D))
+        if c["gated"]:
+            ref = Pr.output_gate(ref, bf16.to_f64(bits_of(c["qg"])[s, :, :, 1]))
         assert_attn_close(c["out"][s], ref)
     # nothing else in the pools changed
     for h in range(kb.shape[1]):
@@ -97,6 +99,59 @@ def test_new_tokens_straddle_splits(H_q):
     # splits hold new positions, the one with the last position owns them
     c = _run(2100 + H_q, [16 * 40 + 2], 4, H_q, 1, 128, 32, 16, num_splits=41)
     _check_against_oracle(c)
+
+
+@pytest.mark.parametrize("lens,T,H_q,H_kv,D,R,P", [
+    ([50001], 1, 8, 1, 256, 64, 64),          # VALU path
+    ([7000, 300], 4, 16, 1, 256, 64, 64),     # MFMA path
+    ([900], 2, 8, 2, 128, 32, 16),            # two KV heads
+])
+def test_gated_output_matches_oracle(lens, T, H_q, H_kv, D, R, P):
+    c = _run(2500 + sum(lens) % 991 + T, lens, T, H_q, H_kv, D, R, P, gated=True)
+    _check_against_oracle(c)
+
+
+def test_gated_output_is_the_ungated_output_times_sigmoid():
+    lens, T, H_q, H_kv, D, R, P = [3000], 1, 8, 1, 256, 64, 64
+    a = _run(2600, lens, T, H_q, H_kv, D, R, P, deterministic=True)
+    b = _run(2600, lens, T, H_q, H_kv, D, R, P, deterministic=True, gated=True)
+    plain = bf16.to_f64(bits_of(a["out"]))
+    gate = bf16.to_f64(bits_of(a["qg"])[:, :, :, 1])
+    got = bf16.to_f64(bits_of(b["out"]))
+    # same fp32 partials; the gate multiplies before the one rounding, so the
+    # two differ by at most the ungated rounding (half an ulp) scaled, plus one
+    assert np.all(np.abs(got - Pr.output_gate(plain, gate)) <= bf16.ulp(plain) + bf16.ulp(got))
+
+
+def test_gated_flag_without_a_gate_is_rejected():
+    q = torch.zeros((1, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    pool = torch.zeros((4, 1, 16, 128), dtype=torch.bfloat16, device=DEV)
+    desc = had._lib.attn_desc(q.shape, pool.shape, 4, gated=True)
+    import ctypes
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    ptrs = had._lib.AttnPtrs(q.data_ptr(), pool.data_ptr(), pool.data_ptr(),
+                             torch.zeros((1, 4), dtype=torch.int32, device=DEV).data_ptr(),
+                             torch.tensor([20], dtype=torch.int32, device=DEV).data_ptr(), ws.data_ptr(), ws.numel(),
+                             torch.empty_like(q).data_ptr(), None, None)
+    assert had.lib().had_decode_attn(ctypes.byref(desc), ctypes.byref(ptrs), None) != 0
+    # the split halves have no gate to apply, with or without the pointer
+    ptrs.gate = q.data_ptr()
+    assert had.lib().had_decode_attn_partial(ctypes.byref(desc), ctypes.byref(ptrs), None) != 0
+    assert had.lib().had_decode_attn_combine(ctypes.byref(desc), 1, ws.data_ptr(), q.data_ptr(), None) != 0
+
+
+def test_gated_two_call_path_matches_gated_layer():
+    # prologue + decode_attn(gate=...) gives the fused layer's gated output
+    lens, T, H_q, H_kv, D, R, P = [2500, 90], 2, 8, 1, 256, 64, 64
+    c = _run(2700, lens, T, H_q, H_kv, D, R, P, deterministic=True, gated=True)
+    _check_against_oracle(c)
+    kd2, vd2 = to_dev(c["k_pool"]), to_dev(c["v_pool"])
+    q2, g2 = had.qk_norm_rope_gate(to_dev(c["qg"]), to_dev(c["k"]), to_dev(c["v"]), to_dev(c["w_q"]),
+                                   to_dev(c["w_k"]), to_dev(c["pt"]), to_dev(c["L"]), kd2, vd2, R)
+    out2 = had.decode_attn(q2, kd2, vd2, to_dev(c["pt"]), to_dev(c["L"]), deterministic=True, gate=g2)
+    torch.cuda.synchronize()
+    a, b = bf16.to_f64(bits_of(c["out"])), bf16.to_f64(bits_of(out2))
+    assert np.abs(a - b).max() <= 4e-3
 
 
 def test_fused_matches_two_call_path():

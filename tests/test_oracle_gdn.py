@@ -167,3 +167,25 @@ def test_rank_one_heads_reproduce_hand_worked_2x2():
     be = np.array([[float(t1[9])], [float(t2[9])]])
     S, _ = gdn.sequential_heads(S0, np.zeros((2, 1, 2)), k, v, al, be)
     np.testing.assert_allclose(S[0], f(g["S2"][0]).reshape(2, 2), atol=1e-14)
+
+
+def test_raw_gates_parameterisation():
+    from scipy.special import expit
+    rng = np.random.default_rng(21)
+    g = -np.abs(rng.standard_normal(50)) * 3
+    b = rng.standard_normal(50) * 4
+    al, be = gdn.gates_from_raw(g, b)
+    np.testing.assert_allclose(al, np.exp(g), rtol=1e-15)
+    np.testing.assert_allclose(be, expit(b), rtol=1e-14)
+    assert np.all((al > 0) & (al <= 1)) and np.all((be > 0) & (be < 1))
+    a0, b0 = gdn.gates_from_raw(0.0, 0.0)
+    assert a0 == 1.0 and b0 == 0.5
+    # a strongly negative b closes the write: the state decays by exp(sum g)
+    rng = np.random.default_rng(22)
+    S = rng.standard_normal((6, 6))
+    T = 5
+    gg = -rng.uniform(0, 0.2, T)
+    al, be = gdn.gates_from_raw(gg, np.full(T, -800.0))
+    assert np.all(be == 0.0)
+    states, _ = gdn.sequential(S, rng.standard_normal((T, 6)), _unit(rng, T, 6), rng.standard_normal((T, 6)), al, be)
+    np.testing.assert_allclose(states[-1], np.exp(gg.sum()) * S, rtol=1e-13)

@@ -90,3 +90,23 @@ def test_rope_frequencies_at_known_angles():
     np.testing.assert_allclose([r[0, 0, 0], r[0, 0, 32]], [np.cos(1.0), np.sin(1.0)], atol=1e-15)
     np.testing.assert_allclose([r[1, 0, 16], r[1, 0, 48]], [np.cos(1.0), np.sin(1.0)], atol=1e-14)
     assert np.count_nonzero(r[0]) == 2 and np.count_nonzero(r[1]) == 2
+
+
+def test_output_gate_special_values_and_symmetry():
+    rng = np.random.default_rng(9)
+    o = rng.standard_normal((3, 4, 32))
+    g = rng.standard_normal((3, 4, 32)) * 4
+    # sigmoid(0) = 1/2 exactly; sigmoid(x) + sigmoid(-x) = 1
+    np.testing.assert_array_equal(Pr.output_gate(o, np.zeros_like(o)), o / 2)
+    np.testing.assert_allclose(Pr.output_gate(o, g) + Pr.output_gate(o, -g), o, rtol=1e-14, atol=1e-15)
+    # saturation: a large gate passes the output, a very negative one closes it
+    np.testing.assert_allclose(Pr.output_gate(o, np.full_like(o, 60.0)), o, rtol=1e-15)
+    assert np.max(np.abs(Pr.output_gate(o, np.full_like(o, -60.0)))) < 1e-25
+    # agrees with the library's logistic function
+    from scipy.special import expit
+    np.testing.assert_allclose(Pr.output_gate(o, g), o * expit(g), rtol=1e-14)
+    # the gate acts per element, not per head (a swapped axis would fail)
+    g2 = g.copy()
+    g2[..., 0] = 30.0
+    assert np.allclose(Pr.output_gate(o, g2)[..., 0], o[..., 0])
+    assert np.allclose(Pr.output_gate(o, g2)[..., 1:], Pr.output_gate(o, g)[..., 1:])
