@@ -171,3 +171,32 @@ def state_update(pool, in_idx, out_idx, q, k, v, alpha, beta, q_scale=1.0):
             for t in range(T):
                 new_pool[out_idx[s, t], h] = states[t].astype(np.float32)
     return new_pool, o
+
+
+def prefill(pool, in_idx, out_idx, cu_seqlens, q, k, v, alpha, beta, q_scale=1.0):
+    """Slot-addressed prefill of a batch of variable-length sequences.
+
+    The operation a GDN layer performs on a prompt (the turn inputs and the
+    long first turn of the agentic workload): sequence s owns tokens
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed inputs, starts from
+    slot in_idx[s] (zero state for -1), runs the recurrence over all of its
+    tokens and writes only its final state, as float32, to slot out_idx[s].
+    A sequence with no token copies its input state.  Every input slot is
+    read as it was before the call.
+
+    pool float32 [n_slots, H, d_v, d_k]; q, k [N, H, d_k]; v [N, H, d_v];
+    alpha, beta [N, H] (float64 values).  Returns (new pool, o [N, H, d_v]).
+    """
+    pool = np.asarray(pool, np.float32)
+    new_pool = pool.copy()
+    H, d_v, d_k = pool.shape[1:]
+    o = np.empty((q.shape[0], H, d_v))
+    finals = []
+    for s in range(len(in_idx)):
+        a, b = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        S0 = np.zeros((H, d_v, d_k)) if in_idx[s] < 0 else pool[in_idx[s]].astype(np.float64)
+        S, o[a:b] = sequential_heads(S0, q[a:b], k[a:b], v[a:b], alpha[a:b], beta[a:b], q_scale)
+        finals.append(S)
+    for s, S in enumerate(finals):
+        new_pool[out_idx[s]] = S.astype(np.float32)
+    return new_pool, o

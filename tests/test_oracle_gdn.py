@@ -189,3 +189,52 @@ def test_raw_gates_parameterisation():
     assert np.all(be == 0.0)
     states, _ = gdn.sequential(S, rng.standard_normal((T, 6)), _unit(rng, T, 6), rng.standard_normal((T, 6)), al, be)
     np.testing.assert_allclose(states[-1], np.exp(gg.sum()) * S, rtol=1e-13)
+
+
+def _prefill_case(rng, lens, H, dk, dv, n_slots):
+    N = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q = _unit(rng, N * H, dk).reshape(N, H, dk)
+    k = _unit(rng, N * H, dk).reshape(N, H, dk)
+    v = rng.standard_normal((N, H, dv))
+    al = rng.uniform(0.85, 1.0, (N, H))
+    be = rng.uniform(0.0, 1.0, (N, H))
+    pool = rng.standard_normal((n_slots, H, dv, dk)).astype(np.float32)
+    return cu, q, k, v, al, be, pool
+
+
+def test_prefill_equals_the_chunked_form():
+    # an independently derived evaluation (WY/UT chunks, ragged last chunk)
+    rng = np.random.default_rng(31)
+    lens, H, dk, dv = [37, 0, 70, 5], 2, 8, 6
+    cu, q, k, v, al, be, pool = _prefill_case(rng, lens, H, dk, dv, 9)
+    in_idx, out_idx = np.array([3, 4, -1, 3]), np.array([0, 5, 4, 8])
+    new, o = gdn.prefill(pool, in_idx, out_idx, cu, q, k, v, al, be, q_scale=0.5)
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        for h in range(H):
+            S0 = np.zeros((dv, dk)) if in_idx[s] < 0 else pool[in_idx[s], h].astype(np.float64)
+            for C in (1, 16, 64):
+                S, oc = gdn.chunked(S0, q[a:b, h], k[a:b, h], v[a:b, h], al[a:b, h], be[a:b, h], C, q_scale=0.5)
+                np.testing.assert_allclose(o[a:b, h], oc, atol=1e-11)
+                np.testing.assert_allclose(new[out_idx[s], h], S.astype(np.float32), rtol=1e-6, atol=1e-6)
+
+
+def test_prefill_slot_semantics_and_closed_forms():
+    rng = np.random.default_rng(32)
+    lens, H, dk, dv = [0, 12, 9], 2, 4, 4
+    cu, q, k, v, al, be, pool = _prefill_case(rng, lens, H, dk, dv, 6)
+    be[cu[2]:cu[3]] = 0.0                                   # third sequence: no write, decay only
+    in_idx, out_idx = np.array([1, 2, 2]), np.array([3, 2, 5])  # second sequence updates its slot in place
+    new, o = gdn.prefill(pool, in_idx, out_idx, cu, q, k, v, al, be)
+    # an empty sequence copies its input state
+    assert np.array_equal(new[3], pool[1])
+    # beta = 0: S = prod(alpha) S0, o_t = gamma_t S0 q_t; the input is slot 2 as it was before the call
+    gam = np.cumprod(al[cu[2]:cu[3]], axis=0)
+    for h in range(H):
+        S0 = pool[2, h].astype(np.float64)
+        np.testing.assert_allclose(new[5, h], (gam[-1, h] * S0).astype(np.float32), rtol=1e-6)
+        np.testing.assert_allclose(o[cu[2]:cu[3], h], gam[:, h:h + 1] * (q[cu[2]:cu[3], h] @ S0.T), atol=1e-12)
+    # untouched slots keep their bytes
+    for sl in (0, 1, 4):
+        assert np.array_equal(new[sl], pool[sl])
+    assert not np.array_equal(new[2], pool[2])
