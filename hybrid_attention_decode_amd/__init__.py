@@ -24,6 +24,9 @@ from ._lib import (  # noqa: F401
     decode_attn_plan,
     decode_attn_workspace_bytes,
     exported_symbols,
+    gdn_prefill,
+    gdn_prefill_desc,
+    gdn_prefill_workspace_bytes,
     gdn_state_update,
     kv_append,
     kv_copy_pages,

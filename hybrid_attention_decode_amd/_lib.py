@@ -88,6 +88,17 @@ class GdnPtrs(ctypes.Structure):
                 ("alpha", _p), ("beta", _p), ("o", _p), ("d_err", _p)]
 
 
+class GdnPrefillDesc(ctypes.Structure):
+    _fields_ = [("n_seqs", _i32), ("H", _i32), ("d_k", _i32), ("d_v", _i32), ("n_slots", _i32), ("max_len", _i32),
+                ("q_scale", ctypes.c_float), ("flags", _i32)]
+
+
+class GdnPrefillPtrs(ctypes.Structure):
+    _fields_ = [("state_pool", _p), ("in_idx", _p), ("out_idx", _p), ("cu_seqlens", _p), ("q", _p), ("k", _p),
+                ("v", _p), ("alpha", _p), ("beta", _p), ("o", _p), ("workspace", _p),
+                ("workspace_bytes", ctypes.c_size_t), ("d_err", _p)]
+
+
 _SIGS = {
     "had_abi_version": ([], ctypes.c_int),
     "had_last_error": ([], ctypes.c_char_p),
@@ -125,6 +136,8 @@ _SIGS = {
     "had_decode_attn_layer_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc),
                                        ctypes.POINTER(QknrgPtrs), _p, ctypes.c_size_t, _p], ctypes.c_int),
     "had_gdn_state_update": ([ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnPtrs), _p], ctypes.c_int),
+    "had_gdn_prefill_workspace_bytes": ([ctypes.POINTER(GdnPrefillDesc)], ctypes.c_size_t),
+    "had_gdn_prefill": ([ctypes.POINTER(GdnPrefillDesc), ctypes.POINTER(GdnPrefillPtrs), _p], ctypes.c_int),
 }
 
 _lib = None
@@ -505,4 +518,45 @@ def gdn_state_update(state_pool, in_idx, out_idx, q, k, v, alpha, beta, o=None, 
                    _dev(v, torch.bfloat16, "v"), _dev(alpha, torch.float32, "alpha"),
                    _dev(beta, torch.float32, "beta"), _dev(o, torch.float32, "o"), _opt(d_err, "d_err"))
     _check(lib().had_gdn_state_update(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
+    return o
+
+
+def gdn_prefill_desc(state_shape, n_seqs, max_len, q_scale=1.0, raw_gates=False):
+    n_slots, H, d_v, d_k = state_shape
+    return GdnPrefillDesc(n_seqs, H, d_k, d_v, n_slots, int(max_len), float(q_scale),
+                          GDN_RAW_GATES if raw_gates else 0)
+
+
+def gdn_prefill_workspace_bytes(desc):
+    n = lib().had_gdn_prefill_workspace_bytes(ctypes.byref(desc))
+    if n == 0 and desc.max_len > 0:
+        _check(lib().had_gdn_prefill(ctypes.byref(desc), None, None))  # reports why the descriptor is invalid
+    return n
+
+
+def gdn_prefill(state_pool, in_idx, out_idx, cu_seqlens, q, k, v, alpha, beta, max_len=None, o=None, q_scale=1.0,
+                workspace=None, d_err=None, raw_gates=False):
+    """Whole prompts through the gated delta rule, chunk-parallel.
+    state_pool [n_slots, H, d_v, d_k] fp32; q, k [N, H, d_k], v [N, H, d_v] bf16 (sequences packed,
+    token offsets cu_seqlens int32 [n_seqs + 1] on the device); alpha, beta [N, H] fp32;
+    in_idx, out_idx int32 [n_seqs].  max_len bounds every sequence's length (default N).
+    Returns o [N, H, d_v] fp32; the final states land in slots out_idx."""
+    torch = _torch()
+    N, H, d_k = q.shape
+    n_seqs = cu_seqlens.numel() - 1
+    if max_len is None:
+        max_len = N
+    desc = gdn_prefill_desc(state_pool.shape, n_seqs, max_len, q_scale, raw_gates)
+    need = gdn_prefill_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((N, H, state_pool.shape[2]), dtype=torch.float32, device=q.device)
+    ptrs = GdnPrefillPtrs(_dev(state_pool, torch.float32, "state_pool"), _dev(in_idx, torch.int32, "in_idx"),
+                          _dev(out_idx, torch.int32, "out_idx"), _dev(cu_seqlens, torch.int32, "cu_seqlens"),
+                          _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+                          _dev(alpha, torch.float32, "alpha"), _dev(beta, torch.float32, "beta"),
+                          _dev(o, torch.float32, "o"), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                          _opt(d_err, "d_err"))
+    _check(lib().had_gdn_prefill(ctypes.byref(desc), ctypes.byref(ptrs), _stream()))
     return o

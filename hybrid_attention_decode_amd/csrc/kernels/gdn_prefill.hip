@@ -1,0 +1,596 @@
+// Gated delta rule over whole prompts, chunk-parallel (GDN prefill).
+//
+// For one (sequence, head), a chunk of C = 64 tokens starting from state S0
+// (d_v x d_k), with g_t = log alpha_t, lg_t = sum_{i<=t} g_i and
+// gamma_t = exp(lg_t) inside the chunk, the delta-rule inputs u_t
+// (S_t = alpha_t S_{t-1} + u_t k_t^T) satisfy
+//   (I + A) U = diag(beta) (V - diag(gamma) K S0^T),
+//   A[t][i] = beta_t exp(lg_t - lg_i) k_t.k_i  (i < t, else 0),
+// so with T = (I + A)^-1 (unit lower triangular)
+//   U  = U' - W S0^T,   U' = T diag(beta) V,   W = T diag(beta gamma) K,
+//   o  = diag(gamma) Q S0^T + Aqk U,   Aqk[t][i] = exp(lg_t - lg_i) q_t.k_i (i <= t),
+//   S_C = gamma_C S0 + (diag(gamma_C / gamma) U)^T K.
+// (WY / UT form of the delta rule: Yang et al., NeurIPS 2024, "Parallelizing
+// Linear Transformers with the Delta Rule over Sequence Length"; the gated
+// recurrence of the Gated DeltaNet paper, Yang, Kautz & Hatamizadeh, ICLR
+// 2025.  GDN layers of the hybrid model: 24-ai.news TokenSpeed article.)
+//
+// Two kernels:
+//  * prep, one workgroup per (sequence, chunk, head), all chunks at once:
+//    K K^T and K Q^T on MFMA, the triangular solve by forward substitution
+//    (one wave, lane j = column j of T, fp32), then U' and W on MFMA.  The
+//    results go to the workspace already in the register layout of the scan
+//    kernel's MFMA operands.
+//  * scan, one workgroup of 4 waves per (sequence, head, 16 rows of S): the
+//    state slice stays in registers across the chunks of the sequence; wave
+//    w owns the chunk's tokens 16w .. 16w+15 for U and o and the state
+//    columns 32w .. 32w+31 for the update.  Two barriers per chunk exchange
+//    U and the new state through LDS.
+// Products with a fp32 operand (the state, T, W, Aqk, U) use the split
+// x = hi + lo of both bf16 halves (hi*hi + hi*lo + lo*hi, or two terms when
+// the other operand is exact bf16), so each product keeps ~16 mantissa bits.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 operand layout: lane (r, g), r = lane % 16,
+// g = lane / 16, holds A[row r][k = 8g .. 8g+7] and B[k = 8g .. 8g+7][col r];
+// the result lane (r, g) holds C[rows 4g .. 4g+3][col r].  A contraction may
+// take its k index in any order both operands agree on: the scan kernel
+// contracts over d_k in the order sigma(ks, g, j) = 32 ks + 16 (j / 4) + 4 g
+// + j % 4 and over tokens in the same order tau(ks', g, j) -- the order in
+// which a result tile pair (16 x 16 tiles 2 ks and 2 ks + 1) leaves each
+// lane -- so results feed the next product without any reshuffle.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../host/status.h"
+#include "had.h"
+#include "kcommon.h"
+
+using had::fail;
+
+namespace had {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 64;  // tokens per chunk
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// x -> hi = bf16(x), lo = bf16(x - hi), both round to nearest even.
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+    hi[j] = h;
+    lo[j] = pack_bf16x2(x[2 * j] - bf16_lo(h), x[2 * j + 1] - bf16_hi(h));
+  }
+}
+
+__device__ __forceinline__ void cat8(f32x4_t a, f32x4_t b, float (&x)[8]) {
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+
+// Workspace block of one (sequence, chunk, head), in 16-byte units; every
+// array is [..][64 lanes] in the scan kernel's operand layout.
+template <int DK, int DV>
+struct PL {
+  static constexpr int KS = DK / 32;             // k-steps over d_k
+  static constexpr int DT = DK / 16;             // d_k tiles
+  static constexpr int VT = DV / 16;             // d_v tiles
+  static constexpr int W_HI = 0;                 // W, A operand: [t-tile][ks][lane], d_k in sigma order
+  static constexpr int W_LO = W_HI + 4 * KS * 64;
+  static constexpr int UP = W_LO + 4 * KS * 64;  // U', result layout: [t-tile][v-tile][lane] (4 floats)
+  static constexpr int A_HI = UP + 4 * VT * 64;  // Aqk, A operand: [t-tile][ks'][lane], tokens in tau order
+  static constexpr int A_LO = A_HI + 4 * 2 * 64;
+  static constexpr int KT = A_LO + 4 * 2 * 64;   // K^T, A operand: [d_k tile][ks'][lane], tokens in tau order
+  static constexpr int GAM = KT + DT * 2 * 64;   // 64 floats gamma_t, then 64 floats gamma_C / gamma_t
+  static constexpr int TOTAL = GAM + 2 * kC / 4;
+};
+
+struct PrefillArgs {
+  float* pool;
+  const int32_t* in_idx;
+  const int32_t* out_idx;
+  const int32_t* cu;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  u32x4_t* ws;
+  int32_t* d_err;
+  int n_seqs, H, n_slots, max_len, max_chunks, raw_gates;
+  float q_scale;
+};
+
+// One 16-byte piece of a bf16 row (zeros for rows past the chunk).
+__device__ __forceinline__ u32x4_t row16(const uint16_t* p, bool ok) {
+  u32x4_t r = {0u, 0u, 0u, 0u};
+  if (ok) r = *reinterpret_cast<const u32x4_t*>(p);
+  return r;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
+  using L = PL<DK, DV>;
+  constexpr int KS = L::KS, DT = L::DT, VT = L::VT;
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
+  if (tok0 < 0 || len < 0 || len > a.max_len) return;  // reported by the scan kernel
+  const int n = min(kC, len - c * kC);                  // tokens of this chunk
+  if (n <= 0) return;
+  const int base = tok0 + c * kC;
+  u32x4_t* ws = a.ws + (static_cast<size_t>(s * a.max_chunks + c) * a.H + h) * L::TOTAL;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const size_t rstride = static_cast<size_t>(a.H) * DK;  // between tokens of q / k
+
+  __shared__ float lgL[kC], betaL[kC];
+  __shared__ __align__(16) uint16_t ktL[DK][kC + 8];  // K^T [d][token]
+  __shared__ __align__(16) uint16_t vtL[DV][kC + 8];  // V^T [d][token]
+  __shared__ __align__(16) float amat[kC][kC + 4];    // A, then T diag(beta)
+  __shared__ __align__(16) float tbg[kC][kC + 4];     // T diag(beta gamma)
+
+  // gates: lg = inclusive prefix sum of log alpha (0 past the chunk), beta
+  if (wave == 0) {
+    float la = 0.f, be = 0.f;
+    if (lane < n) {
+      const size_t th = static_cast<size_t>(base + lane) * a.H + h;
+      const float al = a.alpha[th];
+      be = a.beta[th];
+      if (a.raw_gates) {
+        la = al;
+        be = 1.f / (1.f + expf(-be));
+      } else {
+        la = logf(al);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(la, off);
+      if (lane >= off) la += y;
+    }
+    lgL[lane] = la;
+    betaL[lane] = be;
+    const float lgC = __shfl(la, 63);
+    float* gw = reinterpret_cast<float*>(ws + L::GAM);
+    gw[lane] = expf(la);
+    gw[kC + lane] = expf(lgC - la);
+  }
+
+  // K^T and V^T into LDS: an item is (token pair p, 8 dims dc); two 16-byte
+  // rows transpose into 8 words of (token 2p, token 2p+1) at one dim
+  auto stage_t = [&](const uint16_t* src, size_t stride, int DD, uint16_t* dst) {
+    for (int it = threadIdx.x; it < 32 * (DD / 8); it += 256) {
+      const int p = it & 31, dc = it >> 5;
+      const int t0 = 2 * p, t1 = 2 * p + 1;
+      const u32x4_t x0 = row16(src + static_cast<size_t>(base + t0) * stride + 8 * dc, t0 < n);
+      const u32x4_t x1 = row16(src + static_cast<size_t>(base + t1) * stride + 8 * dc, t1 < n);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // dims 8dc + 2j (low halves) and 8dc + 2j + 1 (high halves)
+        *reinterpret_cast<uint32_t*>(dst + (8 * dc + 2 * j) * (kC + 8) + t0) = perm_b32(x1[j], x0[j], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(dst + (8 * dc + 2 * j + 1) * (kC + 8) + t0) = perm_b32(x1[j], x0[j], 0x07060302u);
+      }
+    }
+  };
+  stage_t(a.k + static_cast<size_t>(h) * DK, rstride, DK, &ktL[0][0]);
+  stage_t(a.v + static_cast<size_t>(h) * DV, static_cast<size_t>(a.H) * DV, DV, &vtL[0][0]);
+
+  // K rows of the four token tiles as MFMA operands (zero past the chunk)
+  u32x4_t kr[4][KS];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = 16 * tt + r16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kr[tt][ks] = row16(a.k + static_cast<size_t>(base + t) * rstride + h * DK + 32 * ks + 8 * g, t < n);
+  }
+  __syncthreads();
+
+  // A (strictly lower): wave w forms the tiles of token rows 16w .. 16w+15
+  {
+    u32x4_t kown[KS];
+    const int t = 16 * wave + r16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kown[ks] = row16(a.k + static_cast<size_t>(base + t) * rstride + h * DK + 32 * ks + 8 * g, t < n);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      if (nt > wave) break;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma(kown[ks], kr[nt][ks], acc);
+      const int i = 16 * nt + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * wave + 4 * g + r;
+        amat[tr][i] = i < tr ? betaL[tr] * expf(lgL[tr] - lgL[i]) * acc[r] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // T = (I + A)^-1 by forward substitution; lane j computes column j:
+    // T[t][j] = [t == j] - sum_{i<t} A[t][i] T[i][j]
+    float x[kC];
+#pragma unroll
+    for (int t = 0; t < kC; ++t) {
+      float acc[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i4 = 0; i4 < t; i4 += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(&amat[t][i4]);
+        acc[0] = fmaf(-av.x, x[i4], acc[0]);
+        if (i4 + 1 < t) acc[1] = fmaf(-av.y, x[i4 + 1], acc[1]);
+        if (i4 + 2 < t) acc[2] = fmaf(-av.z, x[i4 + 2], acc[2]);
+        if (i4 + 3 < t) acc[3] = fmaf(-av.w, x[i4 + 3], acc[3]);
+      }
+      x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+    const float bj = betaL[lane], bgj = bj * expf(lgL[lane]);
+#pragma unroll
+    for (int t = 0; t < kC; ++t) {
+      amat[t][lane] = x[t] * bj;  // the wave's reads of A are done: T diag(beta) takes its place
+      tbg[t][lane] = x[t] * bgj;
+    }
+  } else {
+    // Aqk for the scan kernel: tile (i-tile it, t-tile tt) of (K Q^T) leaves
+    // lane (t, g) holding i = 16 it + 4g + r, so tiles 2ks' and 2ks'+1 give
+    // the A operand of token step ks' in tau order
+    for (int tt = wave - 1; tt < 4; tt += 3) {
+      const int t = 16 * tt + r16;
+      u32x4_t qr[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qr[ks] = row16(a.q + static_cast<size_t>(base + t) * rstride + h * DK + 32 * ks + 8 * g, t < n);
+      float e[4][4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (it <= tt) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma(kr[it][ks], qr[ks], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * it + 4 * g + r;
+          e[it][r] = i <= t ? expf(lgL[t] - lgL[i]) * acc[r] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        const float x8[8] = {e[2 * kp][0], e[2 * kp][1], e[2 * kp][2], e[2 * kp][3],
+                             e[2 * kp + 1][0], e[2 * kp + 1][1], e[2 * kp + 1][2], e[2 * kp + 1][3]};
+        u32x4_t hi, lo;
+        split8(x8, hi, lo);
+        ws[L::A_HI + (tt * 2 + kp) * 64 + lane] = hi;
+        ws[L::A_LO + (tt * 2 + kp) * 64 + lane] = lo;
+      }
+    }
+    // K^T for the state update: lane (dk, g) of (d_k tile dt, token step
+    // ks') holds tokens 32ks' + 4g .. +3 and 32ks' + 16 + 4g .. +3
+    for (int b = wave - 1; b < DT * 2; b += 3) {
+      const int dt = b >> 1, kp = b & 1;
+      const uint16_t* row = &ktL[16 * dt + r16][32 * kp + 4 * g];
+      const uint2 x0 = *reinterpret_cast<const uint2*>(row);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(row + 16);
+      ws[L::KT + b * 64 + lane] = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+    }
+  }
+  __syncthreads();
+
+  // U' = T diag(beta) V and W = T diag(beta gamma) K for token rows 16w ..
+  {
+    const int t = 16 * wave + r16;
+    u32x4_t tbh[2], tbl[2], tgh[2], tgl[2];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      float x8[8];
+      cat8(*reinterpret_cast<const f32x4_t*>(&amat[t][32 * kp + 8 * g]),
+           *reinterpret_cast<const f32x4_t*>(&amat[t][32 * kp + 8 * g + 4]), x8);
+      split8(x8, tbh[kp], tbl[kp]);
+      cat8(*reinterpret_cast<const f32x4_t*>(&tbg[t][32 * kp + 8 * g]),
+           *reinterpret_cast<const f32x4_t*>(&tbg[t][32 * kp + 8 * g + 4]), x8);
+      split8(x8, tgh[kp], tgl[kp]);
+    }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&vtL[16 * vt + r16][32 * kp + 8 * g]);
+        acc = mfma(tbh[kp], b, acc);
+        acc = mfma(tbl[kp], b, acc);
+      }
+      ws[L::UP + (wave * VT + vt) * 64 + lane] = __builtin_bit_cast(u32x4_t, acc);
+    }
+    // W^T = K^T (T diag(beta gamma))^T: tile (d_k tile dt, t-tile w) leaves
+    // lane (t, g) holding d_k = 16 dt + 4g + r, so tiles 2ks and 2ks+1 give
+    // the A operand of d_k step ks in sigma order
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f32x4_t cw[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int dt = 2 * ks + e;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const u32x4_t am = *reinterpret_cast<const u32x4_t*>(&ktL[16 * dt + r16][32 * kp + 8 * g]);
+          acc = mfma(am, tgh[kp], acc);
+          acc = mfma(am, tgl[kp], acc);
+        }
+        cw[e] = acc;
+      }
+      float x8[8];
+      cat8(cw[0], cw[1], x8);
+      u32x4_t hi, lo;
+      split8(x8, hi, lo);
+      ws[L::W_HI + (wave * KS + ks) * 64 + lane] = hi;
+      ws[L::W_LO + (wave * KS + ks) * 64 + lane] = lo;
+    }
+  }
+}
+
+// Scan over the chunks of one (sequence, head) for state rows 16 vs .. +15.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
+  using L = PL<DK, DV>;
+  constexpr int KS = L::KS, VT = L::VT;
+  // block -> (unit = s * H + h, v-slice): the v-slices of one unit share the
+  // unit's workspace blocks, so they go to one XCD (blocks are dealt to the
+  // 8 XCDs round robin)
+  const int b = blockIdx.x;
+  const int unit = (b / 8 / VT) * 8 + b % 8, vs = (b / 8) % VT;
+  if (unit >= a.n_seqs * a.H) return;
+  const int s = unit / a.H, h = unit % a.H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+
+  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
+  const int in = a.in_idx[s], out = a.out_idx[s];
+  const bool bad_len = tok0 < 0 || len < 0 || len > a.max_len;
+  const bool bad_slot = in < -1 || in >= a.n_slots || out < 0 || out >= a.n_slots;
+  if (bad_len || bad_slot) {
+    if (threadIdx.x == 0 && vs == 0) set_err(a.d_err, (bad_len ? HAD_DERR_SEQLEN : 0) | (bad_slot ? HAD_DERR_SLOT : 0));
+    return;
+  }
+  const int n_chunks = (len + kC - 1) / kC;
+  const size_t slot_elems = static_cast<size_t>(a.H) * DV * DK;
+  const size_t row_off = (static_cast<size_t>(h) * DV + 16 * vs + r16) * DK;
+
+  __shared__ f32x4_t ubuf[4][64];         // U tiles of the chunk (result layout)
+  __shared__ u32x4_t sbuf[KS][2][64];     // new state as B operands (hi, lo) per d_k step
+
+  // state rows as B operands: lane (v, g) holds S[v][sigma(ks, g, j)]
+  u32x4_t shi[KS], slo[KS];
+  f32x4_t sown[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // fp32 columns of d_k step `wave`
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    f32x4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+    if (in >= 0) {
+      const float* src = a.pool + static_cast<size_t>(in) * slot_elems + row_off + 32 * ks + 4 * g;
+      p0 = *reinterpret_cast<const f32x4_t*>(src);
+      p1 = *reinterpret_cast<const f32x4_t*>(src + 16);
+    }
+    float x8[8];
+    cat8(p0, p1, x8);
+    split8(x8, shi[ks], slo[ks]);
+    if (ks == wave) {
+      sown[0] = p0;
+      sown[1] = p1;
+    }
+  }
+
+  const u32x4_t* blk0 = a.ws + static_cast<size_t>(s * a.max_chunks) * a.H * L::TOTAL + static_cast<size_t>(h) * L::TOTAL;
+  const size_t qstride = static_cast<size_t>(a.H) * DK;
+  for (int c = 0; c < n_chunks; ++c) {
+    const u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
+    const int n = min(kC, len - c * kC);
+    const int base = tok0 + c * kC;
+    const float* gw = reinterpret_cast<const float*>(blk + L::GAM);
+
+    u32x4_t whi[KS], wlo[KS], qa[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      whi[ks] = blk[L::W_HI + (wave * KS + ks) * 64 + lane];
+      wlo[ks] = blk[L::W_LO + (wave * KS + ks) * 64 + lane];
+    }
+    {
+      const int tq = min(16 * wave + r16, n - 1);  // rows past the chunk: any real row (their o is not stored)
+      const uint16_t* qp = a.q + static_cast<size_t>(base + tq) * qstride + h * DK;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint2 x0 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 4 * g);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 16 + 4 * g);
+        qa[ks] = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+      }
+    }
+    const f32x4_t up = __builtin_bit_cast(f32x4_t, blk[L::UP + (wave * VT + vs) * 64 + lane]);
+    u32x4_t ahi[2], alo[2];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      ahi[kp] = blk[L::A_HI + (wave * 2 + kp) * 64 + lane];
+      alo[kp] = blk[L::A_LO + (wave * 2 + kp) * 64 + lane];
+    }
+    u32x4_t kt[2][2];
+    if (wave < KS) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) kt[e][kp] = blk[L::KT + ((2 * wave + e) * 2 + kp) * 64 + lane];
+    }
+    const f32x4_t gam = *reinterpret_cast<const f32x4_t*>(gw + 16 * wave + 4 * g);
+    float rat[2][8];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      cat8(*reinterpret_cast<const f32x4_t*>(gw + kC + 32 * kp + 4 * g),
+           *reinterpret_cast<const f32x4_t*>(gw + kC + 32 * kp + 16 + 4 * g), rat[kp]);
+    }
+    const float gC = gw[kC - 1];
+
+    // U = U' - W S0^T and Y = Q S0^T for token rows 16w ..
+    f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = X;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      X = mfma(whi[ks], shi[ks], X);
+      Y = mfma(qa[ks], shi[ks], Y);
+      X = mfma(whi[ks], slo[ks], X);
+      Y = mfma(qa[ks], slo[ks], Y);
+      X = mfma(wlo[ks], shi[ks], X);
+    }
+    ubuf[wave][lane] = up - X;
+    __syncthreads();
+
+    // U (for o) and diag(gamma_C / gamma) U (for the state) as B operands over tokens in tau order
+    u32x4_t uh[2], ul[2], th[2], tl[2];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      float x8[8];
+      cat8(ubuf[2 * kp][lane], ubuf[2 * kp + 1][lane], x8);
+      split8(x8, uh[kp], ul[kp]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x8[j] *= rat[kp][j];
+      split8(x8, th[kp], tl[kp]);
+    }
+
+    // o = diag(gamma) Y + Aqk U (token step 1 holds only zeros for rows 0 .. 31)
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      if (kp == 1 && wave < 2) break;
+      O = mfma(ahi[kp], uh[kp], O);
+      O = mfma(ahi[kp], ul[kp], O);
+      O = mfma(alo[kp], uh[kp], O);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * g + r;
+      if (t < n)
+        a.o[(static_cast<size_t>(base + t) * a.H + h) * DV + 16 * vs + r16] = a.q_scale * fmaf(gam[r], Y[r], O[r]);
+    }
+
+    // S_C columns of d_k step `wave`: gamma_C S0 + K^T diag(gamma_C / gamma) U
+    if (wave < KS) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        f32x4_t acc = sown[e] * gC;
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          acc = mfma(kt[e][kp], th[kp], acc);
+          acc = mfma(kt[e][kp], tl[kp], acc);
+        }
+        sown[e] = acc;
+      }
+      float x8[8];
+      cat8(sown[0], sown[1], x8);
+      u32x4_t hi, lo;
+      split8(x8, hi, lo);
+      sbuf[wave][0][lane] = hi;
+      sbuf[wave][1][lane] = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      shi[ks] = sbuf[ks][0][lane];
+      slo[ks] = sbuf[ks][1][lane];
+    }
+  }
+
+  if (wave < KS) {
+    float* dst = a.pool + static_cast<size_t>(out) * slot_elems + row_off + 32 * wave + 4 * g;
+    *reinterpret_cast<f32x4_t*>(dst) = sown[0];
+    *reinterpret_cast<f32x4_t*>(dst + 16) = sown[1];
+  }
+}
+
+size_t block_bytes(int dk, int dv) {
+  if (dk == 128) return 16 * static_cast<size_t>(dv == 128 ? PL<128, 128>::TOTAL : PL<128, 64>::TOTAL);
+  return 16 * static_cast<size_t>(dv == 128 ? PL<64, 128>::TOTAL : PL<64, 64>::TOTAL);
+}
+
+int check(const had_gdn_prefill_desc* d) {
+  if (!d) return fail(HAD_ERR_INVALID_ARG, "gdn_prefill: desc is NULL");
+  if (d->n_seqs < 1 || d->H < 1 || d->n_slots < 1 || d->max_len < 0)
+    return fail(HAD_ERR_INVALID_ARG, "gdn_prefill: bad counts (n_seqs=%d H=%d n_slots=%d max_len=%d)", d->n_seqs,
+                d->H, d->n_slots, d->max_len);
+  if ((d->d_k != 64 && d->d_k != 128) || (d->d_v != 64 && d->d_v != 128))
+    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "gdn_prefill: d_k=%d d_v=%d (supported: 64, 128)", d->d_k, d->d_v);
+  if (d->flags & ~HAD_GDN_RAW_GATES) return fail(HAD_ERR_INVALID_ARG, "gdn_prefill: unknown flags 0x%x", d->flags);
+  return HAD_OK;
+}
+
+template <int DK, int DV>
+int launch(const had_gdn_prefill_desc* d, const PrefillArgs& a, hipStream_t st) {
+  if (a.max_chunks > 0) {
+    hipLaunchKernelGGL((gdn_prefill_prep_kernel<DK, DV>), dim3(a.max_chunks, d->H, d->n_seqs), dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: prep launch: %s", hipGetErrorString(e));
+  }
+  const int units = d->n_seqs * d->H;
+  const int blocks = (units + 7) / 8 * 8 * (DV / 16);
+  hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3(blocks), dim3(256), 0, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: scan launch: %s", hipGetErrorString(e));
+  return HAD_OK;
+}
+
+}  // namespace
+}  // namespace had
+
+extern "C" {
+
+size_t had_gdn_prefill_workspace_bytes(const had_gdn_prefill_desc* d) {
+  if (had::check(d) != HAD_OK) return 0;
+  const size_t chunks = static_cast<size_t>((d->max_len + had::kC - 1) / had::kC);
+  return static_cast<size_t>(d->n_seqs) * chunks * d->H * had::block_bytes(d->d_k, d->d_v);
+}
+
+int had_gdn_prefill(const had_gdn_prefill_desc* d, const had_gdn_prefill_ptrs* p, void* stream) {
+  int st = had::check(d);
+  if (st != HAD_OK) return st;
+  if (!p || !p->state_pool || !p->in_idx || !p->out_idx || !p->cu_seqlens || !p->q || !p->k || !p->v || !p->alpha ||
+      !p->beta || !p->o)
+    return fail(HAD_ERR_INVALID_ARG, "gdn_prefill: NULL pointer in ptrs");
+  const size_t need = had_gdn_prefill_workspace_bytes(d);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(HAD_ERR_WORKSPACE_TOO_SMALL, "gdn_prefill: workspace %zu bytes, need %zu", p->workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(p->workspace) | reinterpret_cast<uintptr_t>(p->state_pool) |
+       reinterpret_cast<uintptr_t>(p->q) | reinterpret_cast<uintptr_t>(p->k) | reinterpret_cast<uintptr_t>(p->v)) &
+      15u)
+    return fail(HAD_ERR_INVALID_ARG, "gdn_prefill: workspace, state_pool, q, k and v must be 16-byte aligned");
+  had::PrefillArgs a{};
+  a.pool = p->state_pool;
+  a.in_idx = p->in_idx;
+  a.out_idx = p->out_idx;
+  a.cu = p->cu_seqlens;
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.k = static_cast<const uint16_t*>(p->k);
+  a.v = static_cast<const uint16_t*>(p->v);
+  a.alpha = p->alpha;
+  a.beta = p->beta;
+  a.o = p->o;
+  a.ws = static_cast<had::u32x4_t*>(p->workspace);
+  a.d_err = p->d_err;
+  a.n_seqs = d->n_seqs;
+  a.H = d->H;
+  a.n_slots = d->n_slots;
+  a.max_len = d->max_len;
+  a.max_chunks = (d->max_len + had::kC - 1) / had::kC;
+  a.raw_gates = (d->flags & HAD_GDN_RAW_GATES) ? 1 : 0;
+  a.q_scale = d->q_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->d_k == 128 && d->d_v == 128) st = had::launch<128, 128>(d, a, s);
+  else if (d->d_k == 128) st = had::launch<128, 64>(d, a, s);
+  else if (d->d_v == 128) st = had::launch<64, 128>(d, a, s);
+  else st = had::launch<64, 64>(d, a, s);
+  return st == HAD_OK ? had::ok() : st;
+}
+
+}  // extern "C"

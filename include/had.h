@@ -425,6 +425,62 @@ typedef struct {
 
 int had_gdn_state_update(const had_gdn_desc *d, const had_gdn_ptrs *p, void *stream);
 
+/* ======================================================================
+ * gdn_prefill -- the same recurrence over whole prompts, chunk-parallel
+ *
+ * Sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed
+ * inputs; it starts from slot in_idx[s] (zero state for -1), runs the gated
+ * delta rule over all of its tokens (as had_gdn_state_update would, token
+ * by token), writes o for every token and its final state, fp32, to slot
+ * out_idx[s] only.  A sequence with no token copies its input state;
+ * in_idx[s] == out_idx[s] (in place) is allowed.  This is the GDN half of a
+ * prefill: the turn inputs and the long first turn of the agentic loop
+ * (24-ai.news TokenSpeed article, agentic workload; GDN layers and their
+ * state checkpoints: same article, model paragraph, and zubnet.ai ¶2).
+ *
+ * Evaluation: chunks of 64 tokens in the WY / UT form of the delta rule
+ * (Yang et al., NeurIPS 2024, "Parallelizing Linear Transformers with the
+ * Delta Rule over Sequence Length"; gated form in the Gated DeltaNet paper):
+ * a chunk-parallel kernel forms each chunk's triangular solve and
+ * state-independent products, then a scan kernel carries the state across
+ * the chunks of a sequence (MFMA; state kept in fp32, its matrix products
+ * in split bf16 pairs).  The result equals the token-by-token recurrence up
+ * to rounding (fp32 accumulation; relative error ~1e-5 per chunk).
+ *
+ * Shapes: d_k, d_v in {64, 128}; any H; 0 <= length <= max_len.
+ * Preconditions (not checked on device): no slot is written by two
+ * sequences, and no slot a sequence writes is read by another sequence.
+ * Device errors: HAD_DERR_SLOT (slot out of range: the sequence is skipped),
+ * HAD_DERR_SEQLEN (cu_seqlens not non-decreasing, or a length above
+ * max_len: skipped).
+ * ====================================================================== */
+typedef struct {
+  int32_t n_seqs, H, d_k, d_v;
+  int32_t n_slots;
+  int32_t max_len;           /* host bound on every sequence's length      */
+  float q_scale;
+  int32_t flags;             /* HAD_GDN_RAW_GATES                          */
+} had_gdn_prefill_desc;
+
+typedef struct {
+  float *state_pool;         /* fp32 [n_slots][H][d_v][d_k]                */
+  const int32_t *in_idx;     /* int32 [n_seqs] (-1 = zero state)           */
+  const int32_t *out_idx;    /* int32 [n_seqs]                             */
+  const int32_t *cu_seqlens; /* int32 [n_seqs + 1], device, token offsets  */
+  const void *q, *k;         /* bf16 [N][H][d_k], N = cu_seqlens[n_seqs]    */
+  const void *v;             /* bf16 [N][H][d_v]                           */
+  const float *alpha, *beta; /* fp32 [N][H] (raw g, b with RAW_GATES)      */
+  float *o;                  /* fp32 [N][H][d_v], written                  */
+  void *workspace;           /* had_gdn_prefill_workspace_bytes(d) bytes   */
+  size_t workspace_bytes;
+  int32_t *d_err;            /* optional                                   */
+} had_gdn_prefill_ptrs;
+
+/* Workspace: per (sequence, chunk of 64 tokens up to max_len, head) the
+ * chunk's solve results; 0 for an invalid descriptor. */
+size_t had_gdn_prefill_workspace_bytes(const had_gdn_prefill_desc *d);
+int had_gdn_prefill(const had_gdn_prefill_desc *d, const had_gdn_prefill_ptrs *p, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,11 @@ def normal_bf16_offset(shape, seed, device="cpu"):
     return (x + off).to(torch.bfloat16)
 
 
+def normal_f32(shape, seed, device="cpu"):
+    g = _gen(seed, device)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
 def uniform_f32(shape, lo, hi, seed, device="cpu"):
     g = _gen(seed, device)
     return torch.rand(shape, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
