@@ -15,7 +15,7 @@
 // recurrence of the Gated DeltaNet paper, Yang, Kautz & Hatamizadeh, ICLR
 // 2025.  GDN layers of the hybrid model: 24-ai.news TokenSpeed article.)
 //
-// Two kernels:
+// Three kernels:
 //  * prep, one workgroup per (sequence, chunk, head), all chunks at once:
 //    K K^T and K Q^T on MFMA, the triangular solve by forward substitution
 //    (one wave, lane j = column j of T, fp32), then U' and W on MFMA.  The
@@ -23,9 +23,13 @@
 //    kernel's MFMA operands.
 //  * scan, one workgroup of 4 waves per (sequence, head, 16 rows of S): the
 //    state slice stays in registers across the chunks of the sequence; wave
-//    w owns the chunk's tokens 16w .. 16w+15 for U and o and the state
-//    columns 32w .. 32w+31 for the update.  Two barriers per chunk exchange
-//    U and the new state through LDS.
+//    w owns the chunk's tokens 16w .. 16w+15 for U and the state columns
+//    32w .. 32w+31 for the update.  Two barriers per chunk exchange U and the
+//    new state through LDS.  Only W, K^T and U' are read on this sequential
+//    path (the per-chunk operand stream through each CU bounds it); it
+//    leaves U and each chunk's initial state in the workspace.
+//  * output, again one workgroup per (sequence, chunk, head), all chunks at
+//    once: o = q_scale (diag(gamma) Q S0^T + Aqk U).
 // Products with a fp32 operand (the state, T, W, Aqk, U) use the split
 // x = hi + lo of both bf16 halves (hi*hi + hi*lo + lo*hi, or two terms when
 // the other operand is exact bf16), so each product keeps ~16 mantissa bits.
@@ -85,12 +89,14 @@ struct PL {
   static constexpr int VT = DV / 16;             // d_v tiles
   static constexpr int W_HI = 0;                 // W, A operand: [t-tile][ks][lane], d_k in sigma order
   static constexpr int W_LO = W_HI + 4 * KS * 64;
-  static constexpr int UP = W_LO + 4 * KS * 64;  // U', result layout: [t-tile][v-tile][lane] (4 floats)
+  static constexpr int UP = W_LO + 4 * KS * 64;  // U' (U after the scan), result layout: [t-tile][v-tile][lane]
   static constexpr int A_HI = UP + 4 * VT * 64;  // Aqk, A operand: [t-tile][ks'][lane], tokens in tau order
   static constexpr int A_LO = A_HI + 4 * 2 * 64;
   static constexpr int KT = A_LO + 4 * 2 * 64;   // K^T, A operand: [d_k tile][ks'][lane], tokens in tau order
   static constexpr int GAM = KT + DT * 2 * 64;   // 64 floats gamma_t, then 64 floats gamma_C / gamma_t
-  static constexpr int TOTAL = GAM + 2 * kC / 4;
+  static constexpr int SC_HI = GAM + 2 * kC / 4; // chunk's initial state, B operand: [v-slice][ks][lane] (scan)
+  static constexpr int SC_LO = SC_HI + VT * KS * 64;
+  static constexpr int TOTAL = SC_LO + VT * KS * 64;
 };
 
 struct PrefillArgs {
@@ -220,18 +226,30 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
   if (wave == 0) {
     // T = (I + A)^-1 by forward substitution; lane j computes column j:
     // T[t][j] = [t == j] - sum_{i<t} A[t][i] T[i][j]
-    float x[kC];
-#pragma unroll
-    for (int t = 0; t < kC; ++t) {
-      float acc[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+    // Row t + 1 of A is read while row t is reduced (two register rows), so
+    // the LDS latency overlaps the arithmetic instead of following each read.
+    float x[kC], ra[kC], rb[kC];
+    auto load_row = [&](int t, float (&r)[kC]) {
 #pragma unroll
       for (int i4 = 0; i4 < t; i4 += 4) {
         const float4 av = *reinterpret_cast<const float4*>(&amat[t][i4]);
-        acc[0] = fmaf(-av.x, x[i4], acc[0]);
-        if (i4 + 1 < t) acc[1] = fmaf(-av.y, x[i4 + 1], acc[1]);
-        if (i4 + 2 < t) acc[2] = fmaf(-av.z, x[i4 + 2], acc[2]);
-        if (i4 + 3 < t) acc[3] = fmaf(-av.w, x[i4 + 3], acc[3]);
+        r[i4] = av.x;
+        r[i4 + 1] = av.y;
+        r[i4 + 2] = av.z;
+        r[i4 + 3] = av.w;
       }
+    };
+    x[0] = lane == 0 ? 1.f : 0.f;
+    load_row(1, ra);
+#pragma unroll
+    for (int t = 1; t < kC; ++t) {
+      float(&cur)[kC] = (t & 1) ? ra : rb;
+      float(&nxt)[kC] = (t & 1) ? rb : ra;
+      if (t + 1 < kC) load_row(t + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      float acc[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < t; ++i) acc[i & 3] = fmaf(-cur[i], x[i], acc[i & 3]);
       x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
     const float bj = betaL[lane], bgj = bj * expf(lgL[lane]);
@@ -339,7 +357,10 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
   }
 }
 
-// Scan over the chunks of one (sequence, head) for state rows 16 vs .. +15.
+// Scan over the chunks of one (sequence, head) for state rows 16 vs .. +15:
+// only what the state needs (W, K^T, U') is on this sequential path.  Per
+// chunk it leaves U (over U' in the workspace) and the chunk's initial
+// state (as B operands) for the output kernel.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   using L = PL<DK, DV>;
@@ -367,6 +388,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
 
   __shared__ f32x4_t ubuf[4][64];         // U tiles of the chunk (result layout)
   __shared__ u32x4_t sbuf[KS][2][64];     // new state as B operands (hi, lo) per d_k step
+  __shared__ __align__(16) float rbuf[kC];  // gamma_C / gamma_t of the chunk
 
   // state rows as B operands: lane (v, g) holds S[v][sigma(ks, g, j)]
   u32x4_t shi[KS], slo[KS];
@@ -388,105 +410,82 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
     }
   }
 
-  const u32x4_t* blk0 = a.ws + static_cast<size_t>(s * a.max_chunks) * a.H * L::TOTAL + static_cast<size_t>(h) * L::TOTAL;
-  const size_t qstride = static_cast<size_t>(a.H) * DK;
-  for (int c = 0; c < n_chunks; ++c) {
+  u32x4_t* blk0 = a.ws + static_cast<size_t>(s * a.max_chunks) * a.H * L::TOTAL + static_cast<size_t>(h) * L::TOTAL;
+  const int kw = wave < KS ? wave : 0;  // a wave that owns no d_k step (d_k 64) mirrors step 0 and discards it
+
+  // A chunk's operands, loaded one chunk ahead (none depends on the state).
+  // Every load is unconditional: a load under a branch would make the join
+  // wait for all loads in flight, the prefetch included.
+  struct Ops {
+    u32x4_t whi[KS], wlo[KS], kt[2][2];
+    f32x4_t up;
+    float rat, gC;
+  };
+  auto load = [&](int c, Ops& p) {
     const u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
-    const int n = min(kC, len - c * kC);
-    const int base = tok0 + c * kC;
     const float* gw = reinterpret_cast<const float*>(blk + L::GAM);
-
-    u32x4_t whi[KS], wlo[KS], qa[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      whi[ks] = blk[L::W_HI + (wave * KS + ks) * 64 + lane];
-      wlo[ks] = blk[L::W_LO + (wave * KS + ks) * 64 + lane];
+      p.whi[ks] = blk[L::W_HI + (wave * KS + ks) * 64 + lane];
+      p.wlo[ks] = blk[L::W_LO + (wave * KS + ks) * 64 + lane];
     }
-    {
-      const int tq = min(16 * wave + r16, n - 1);  // rows past the chunk: any real row (their o is not stored)
-      const uint16_t* qp = a.q + static_cast<size_t>(base + tq) * qstride + h * DK;
+    p.up = __builtin_bit_cast(f32x4_t, blk[L::UP + (wave * VT + vs) * 64 + lane]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint2 x0 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 4 * g);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 16 + 4 * g);
-        qa[ks] = u32x4_t{x0.x, x0.y, x1.x, x1.y};
-      }
-    }
-    const f32x4_t up = __builtin_bit_cast(f32x4_t, blk[L::UP + (wave * VT + vs) * 64 + lane]);
-    u32x4_t ahi[2], alo[2];
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      ahi[kp] = blk[L::A_HI + (wave * 2 + kp) * 64 + lane];
-      alo[kp] = blk[L::A_LO + (wave * 2 + kp) * 64 + lane];
-    }
-    u32x4_t kt[2][2];
+      for (int kp = 0; kp < 2; ++kp) p.kt[e][kp] = blk[L::KT + ((2 * kw + e) * 2 + kp) * 64 + lane];
+    p.rat = gw[kC + lane];
+    p.gC = gw[kC - 1];
+  };
+
+  auto step = [&](int c, const Ops& p) {
+    u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
+    // the chunk's initial state for the output kernel: this wave's d_k step
     if (wave < KS) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) kt[e][kp] = blk[L::KT + ((2 * wave + e) * 2 + kp) * 64 + lane];
+      blk[L::SC_HI + (vs * KS + wave) * 64 + lane] = shi[wave];
+      blk[L::SC_LO + (vs * KS + wave) * 64 + lane] = slo[wave];
     }
-    const f32x4_t gam = *reinterpret_cast<const f32x4_t*>(gw + 16 * wave + 4 * g);
-    float rat[2][8];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      cat8(*reinterpret_cast<const f32x4_t*>(gw + kC + 32 * kp + 4 * g),
-           *reinterpret_cast<const f32x4_t*>(gw + kC + 32 * kp + 16 + 4 * g), rat[kp]);
-    }
-    const float gC = gw[kC - 1];
-
-    // U = U' - W S0^T and Y = Q S0^T for token rows 16w ..
-    f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = X;
+    if (wave == 0) rbuf[lane] = p.rat;
+    // U = U' - W S0^T for token rows 16w .. (the split terms accumulate in
+    // separate chains)
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t X0 = z, X1 = z, X2 = z;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      X = mfma(whi[ks], shi[ks], X);
-      Y = mfma(qa[ks], shi[ks], Y);
-      X = mfma(whi[ks], slo[ks], X);
-      Y = mfma(qa[ks], slo[ks], Y);
-      X = mfma(wlo[ks], shi[ks], X);
+      X0 = mfma(p.whi[ks], shi[ks], X0);
+      X1 = mfma(p.whi[ks], slo[ks], X1);
+      X2 = mfma(p.wlo[ks], shi[ks], X2);
     }
-    ubuf[wave][lane] = up - X;
+    const f32x4_t U = p.up - (X0 + (X1 + X2));
+    ubuf[wave][lane] = U;
+    blk[L::UP + (wave * VT + vs) * 64 + lane] = __builtin_bit_cast(u32x4_t, U);  // U replaces U'
     __syncthreads();
 
-    // U (for o) and diag(gamma_C / gamma) U (for the state) as B operands over tokens in tau order
-    u32x4_t uh[2], ul[2], th[2], tl[2];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      float x8[8];
-      cat8(ubuf[2 * kp][lane], ubuf[2 * kp + 1][lane], x8);
-      split8(x8, uh[kp], ul[kp]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x8[j] *= rat[kp][j];
-      split8(x8, th[kp], tl[kp]);
-    }
-
-    // o = diag(gamma) Y + Aqk U (token step 1 holds only zeros for rows 0 .. 31)
-    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      if (kp == 1 && wave < 2) break;
-      O = mfma(ahi[kp], uh[kp], O);
-      O = mfma(ahi[kp], ul[kp], O);
-      O = mfma(alo[kp], uh[kp], O);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * g + r;
-      if (t < n)
-        a.o[(static_cast<size_t>(base + t) * a.H + h) * DV + 16 * vs + r16] = a.q_scale * fmaf(gam[r], Y[r], O[r]);
-    }
-
-    // S_C columns of d_k step `wave`: gamma_C S0 + K^T diag(gamma_C / gamma) U
+    // S_C columns of d_k step `wave`: gamma_C S0 + K^T diag(gamma_C / gamma) U,
+    // U over tokens in tau order as the B operand
     if (wave < KS) {
+      u32x4_t th[2], tl[2];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        float x8[8], r8[8];
+        cat8(ubuf[2 * kp][lane], ubuf[2 * kp + 1][lane], x8);
+        cat8(*reinterpret_cast<const f32x4_t*>(&rbuf[32 * kp + 4 * g]),
+             *reinterpret_cast<const f32x4_t*>(&rbuf[32 * kp + 16 + 4 * g]), r8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x8[j] *= r8[j];
+        split8(x8, th[kp], tl[kp]);
+      }
+      f32x4_t acc[2][2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        f32x4_t acc = sown[e] * gC;
+        acc[e][0] = sown[e] * p.gC;
+        acc[e][1] = z;
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          acc = mfma(kt[e][kp], th[kp], acc);
-          acc = mfma(kt[e][kp], tl[kp], acc);
+          acc[e][0] = mfma(p.kt[e][kp], th[kp], acc[e][0]);
+          acc[e][1] = mfma(p.kt[e][kp], tl[kp], acc[e][1]);
         }
-        sown[e] = acc;
+        sown[e] = acc[e][0] + acc[e][1];
       }
       float x8[8];
       cat8(sown[0], sown[1], x8);
@@ -501,12 +500,108 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
       shi[ks] = sbuf[ks][0][lane];
       slo[ks] = sbuf[ks][1][lane];
     }
+  };
+
+  // chunk c + 1's operands load while chunk c computes (two register sets;
+  // the last chunk reloads itself so that no load sits under a branch)
+  Ops pa, pb;
+  if (n_chunks > 0) load(0, pa);
+  for (int c = 0; c < n_chunks; c += 2) {
+    load(min(c + 1, n_chunks - 1), pb);
+    step(c, pa);
+    if (c + 1 >= n_chunks) break;
+    load(min(c + 2, n_chunks - 1), pa);
+    step(c + 1, pb);
   }
 
   if (wave < KS) {
     float* dst = a.pool + static_cast<size_t>(out) * slot_elems + row_off + 32 * wave + 4 * g;
     *reinterpret_cast<f32x4_t*>(dst) = sown[0];
     *reinterpret_cast<f32x4_t*>(dst + 16) = sown[1];
+  }
+}
+
+// Outputs of one (sequence, chunk, head), all chunks at once:
+//   o = q_scale (diag(gamma) Q S0^T + Aqk U)
+// with S0 the chunk's initial state and U as the scan kernel left them.
+// Wave w owns token rows 16w .. 16w+15; the state's B operands pass through
+// LDS once for the four waves.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
+  using L = PL<DK, DV>;
+  constexpr int KS = L::KS, VT = L::VT;
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
+  if (tok0 < 0 || len < 0 || len > a.max_len) return;
+  const int in = a.in_idx[s], out = a.out_idx[s];
+  if (in < -1 || in >= a.n_slots || out < 0 || out >= a.n_slots) return;  // the scan skipped it
+  const int n = min(kC, len - c * kC);
+  if (n <= 0) return;
+  const int base = tok0 + c * kC;
+  const u32x4_t* blk = a.ws + (static_cast<size_t>(s * a.max_chunks + c) * a.H + h) * L::TOTAL;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+
+  __shared__ u32x4_t sc[VT][KS][2][64];  // S0 B operands [v-slice][d_k step][hi, lo][lane]
+  for (int i = threadIdx.x; i < VT * KS * 64; i += 256) {
+    const int l = i & 63, k = i >> 6;  // k = vs * KS + ks
+    (&sc[0][0][0][0])[(k * 2) * 64 + l] = blk[L::SC_HI + k * 64 + l];
+    (&sc[0][0][0][0])[(k * 2 + 1) * 64 + l] = blk[L::SC_LO + k * 64 + l];
+  }
+  // Q rows 16w + r (rows past the chunk: any real row; their o is not stored), d_k in sigma order
+  u32x4_t qa[KS];
+  {
+    const int tq = min(16 * wave + r16, n - 1);
+    const uint16_t* qp = a.q + (static_cast<size_t>(base + tq) * a.H + h) * DK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint2 x0 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 4 * g);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 16 + 4 * g);
+      qa[ks] = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+    }
+  }
+  u32x4_t ahi[2], alo[2];
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    ahi[kp] = blk[L::A_HI + (wave * 2 + kp) * 64 + lane];
+    alo[kp] = blk[L::A_LO + (wave * 2 + kp) * 64 + lane];
+  }
+  const f32x4_t gam = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(blk + L::GAM) + 16 * wave + 4 * g);
+  __syncthreads();
+
+  const size_t o0 = (static_cast<size_t>(base) * a.H + h) * DV;
+  // rows past the chunk fall outside the buffer range and are dropped (the
+  // first such row is H * d_v floats past the last real one)
+  const __amdgpu_buffer_rsrc_t orsrc =
+      __builtin_amdgcn_make_buffer_rsrc(a.o + o0, 0, static_cast<int>(((n - 1) * a.H + 1) * DV * 4), 0x00020000);
+  const int nkp = wave < 2 ? 1 : 2;  // token step 1 holds only zeros for rows 0 .. 31
+#pragma unroll 2
+  for (int vs = 0; vs < VT; ++vs) {
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t Y0 = z, Y1 = z, O0 = z, O1 = z;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Y0 = mfma(qa[ks], sc[vs][ks][0][lane], Y0);
+      Y1 = mfma(qa[ks], sc[vs][ks][1][lane], Y1);
+    }
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      if (kp >= nkp) break;
+      // U over tokens in tau order: result tiles 2kp and 2kp + 1 of this lane
+      float x8[8];
+      cat8(__builtin_bit_cast(f32x4_t, blk[L::UP + ((2 * kp) * VT + vs) * 64 + lane]),
+           __builtin_bit_cast(f32x4_t, blk[L::UP + ((2 * kp + 1) * VT + vs) * 64 + lane]), x8);
+      u32x4_t uh, ul;
+      split8(x8, uh, ul);
+      O0 = mfma(ahi[kp], uh, O0);
+      O1 = mfma(ahi[kp], ul, O1);
+      O0 = mfma(alo[kp], uh, O0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * g + r;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.q_scale * fmaf(gam[r], Y0[r] + Y1[r], O0[r] + O1[r])),
+                                            orsrc, (t * a.H * DV + 16 * vs + r16) * 4, 0, 0);
+    }
   }
 }
 
@@ -536,8 +631,13 @@ int launch(const had_gdn_prefill_desc* d, const PrefillArgs& a, hipStream_t st) 
   const int units = d->n_seqs * d->H;
   const int blocks = (units + 7) / 8 * 8 * (DV / 16);
   hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3(blocks), dim3(256), 0, st, a);
-  const hipError_t e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: scan launch: %s", hipGetErrorString(e));
+  if (a.max_chunks > 0) {
+    hipLaunchKernelGGL((gdn_prefill_out_kernel<DK, DV>), dim3(a.max_chunks, d->H, d->n_seqs), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: output launch: %s", hipGetErrorString(e));
+  }
   return HAD_OK;
 }
 
