@@ -398,3 +398,37 @@ def test_agentic_schedule_turn_checkpoints():
         done = t_b
         for h in range(GH):
             assert _rel_fro(got_pool[slot, h].astype(np.float64), S[h]) <= 1e-3, (t_b, h)
+
+
+@pytest.mark.timeout(400)   # the fp64 oracle walks 50,000 tokens one by one (~40 s)
+def test_gdn_prefill_first_turn_50k():
+    # the agentic workload's 50,000-token first turn through one GDN layer
+    # (8 heads, d_k = d_v = 128) by the chunk-parallel prefill, against the
+    # token-by-token fp64 recurrence: the final state of every head and the
+    # outputs of a spread of tokens
+    N = 50000
+    q = synth.l2_normalised_bf16((N, GH, DK), synth.seed_of(910, 1))
+    k = synth.l2_normalised_bf16((N, GH, DK), synth.seed_of(910, 2))
+    v = synth.normal_bf16((N, GH, DV), synth.seed_of(910, 3))
+    g = -synth.uniform_f32((N, GH), 0.0, 0.1, synth.seed_of(910, 4))   # raw gates, as the model feeds them
+    b = synth.uniform_f32((N, GH), -3.0, 3.0, synth.seed_of(910, 5))
+    pool = torch.zeros((2, GH, DV, DK), dtype=torch.float32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    _say("case gdn prefill 50k first turn")
+    o = had.gdn_prefill(pool, to_dev(np.array([-1], np.int32)), to_dev(np.array([1], np.int32)),
+                        to_dev(np.array([0, N], np.int32)), to_dev(q), to_dev(k), to_dev(v), to_dev(g), to_dev(b),
+                        d_err=err, raw_gates=True)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    al, be = gdn.gates_from_raw(g.numpy(), b.numpy())
+    S, o_ref = gdn.sequential_heads(np.zeros((GH, DV, DK)), bf16.to_f64(bits_of(q)), bf16.to_f64(bits_of(k)),
+                                    bf16.to_f64(bits_of(v)), al, be)
+    got = pool[1].cpu().numpy().astype(np.float64)
+    for h in range(GH):
+        rel = np.linalg.norm(got[h] - S[h]) / np.linalg.norm(S[h])
+        assert rel <= 1e-4, (h, rel)
+    oc = o.cpu().numpy().astype(np.float64)
+    for t in list(range(0, N, 997)) + [N - 1]:
+        for h in range(GH):
+            rel = np.linalg.norm(oc[t, h] - o_ref[t, h]) / max(np.linalg.norm(o_ref[t, h]), 1e-30)
+            assert rel <= 1e-4, (t, h, rel)
