@@ -723,6 +723,55 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
     return res
 
 
+def run_gdn_prefill(lengths=(800, 50000), reps=10, seed=8):
+    """GDN half of a prefill: one sequence's prompt through one GDN layer (8
+    heads, d_k = d_v = 128, raw gates) by the chunk-parallel kernels -- the
+    agentic workload's 800-token turn inputs and its 50,000-token first
+    turn.  Per-kernel times come from a rocprofv3 kernel trace; here the
+    whole call is timed (graph of `reps` back-to-back calls)."""
+    import torch
+
+    import hybrid_attention_decode_amd as had
+    import synth
+
+    dev = "cuda"
+    res = {}
+    for N in lengths:
+        g = torch.Generator(device=dev)
+        g.manual_seed(synth.seed_of(seed, N))
+        q = torch.randn((N, GDN_H, DK), generator=g, device=dev, dtype=torch.float64)
+        k = torch.randn((N, GDN_H, DK), generator=g, device=dev, dtype=torch.float64)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v = torch.randn((N, GDN_H, DV), generator=g, device=dev, dtype=torch.bfloat16)
+        gg = -0.1 * torch.rand((N, GDN_H), generator=g, device=dev)
+        bb = torch.randn((N, GDN_H), generator=g, device=dev)
+        pool = torch.randn((2, GDN_H, DV, DK), generator=g, device=dev) * 0.05
+        cu = torch.tensor([0, N], dtype=torch.int32, device=dev)
+        i_in = torch.tensor([0], dtype=torch.int32, device=dev)
+        i_out = torch.tensor([1], dtype=torch.int32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        desc = had.gdn_prefill_desc(pool.shape, 1, N, raw_gates=True)
+        ws = torch.empty(had.gdn_prefill_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        o = torch.empty((N, GDN_H, DV), device=dev)
+
+        def call(r):
+            had.gdn_prefill(pool, i_in, i_out, cu, q, k, v, gg, bb, o=o, workspace=ws, d_err=err, raw_gates=True)
+
+        us = time_graph(torch, call, reps)
+        if int(err.item()):
+            raise RuntimeError("gdn_prefill reported error bits 0x%x" % int(err.item()))
+        chunks = -(-N // 64)
+        res[str(N)] = dict(tokens=N, us_per_layer=round(us, 2), tokens_per_s_per_layer=round(N / (us * 1e-6), 0),
+                           us_per_chunk=round(us / chunks, 3), workspace_mb=round(ws.numel() / 1e6, 1),
+                           gdn_layers_of_the_stack_ms=round(N_GDN * us * 1e-3, 3))
+        log("gdn prefill %d tokens: %.1f us per layer (%.3f us per 64-token chunk)" % (N, us, us / chunks))
+        del q, k, v, gg, bb, pool, ws, o
+        torch.cuda.empty_cache()
+    return dict(workload="GDN prefill of one prompt through one layer (8 heads, d_k = d_v = 128, raw gates): "
+                         "the 800-token turn input and the 50,000-token first turn of the agentic loop", **res)
+
+
 def copy_calibration(nbytes=1 << 30):
     """A plain device copy of known size, for scaling the PMC byte counters."""
     import torch
@@ -814,7 +863,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--workloads", default="speculative,agentic,prefix",
+    ap.add_argument("--workloads", default="speculative,agentic,prefix,prefill",
                     help="further workloads reported beside the headline (comma list, '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (scales PMC byte counters)")
@@ -851,6 +900,8 @@ def main():
         extra["prefix_shared"]["per_sequence_path"] = {k: flat[k] for k in ("steps_per_s", "tokens_per_s",
                                                                             "us_per_layer")}
     cpu = None
+    if "prefill" in wl:
+        extra["gdn_prefill"] = run_gdn_prefill()
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
         cpu = cpu_baseline(args.ctx, args.cpu_seconds)
