@@ -12,6 +12,7 @@ streams.
 from ._lib import (  # noqa: F401
     HadError,
     PageTable,
+    RadixCache,
     SlotPool,
     abi_version,
     attn_desc,

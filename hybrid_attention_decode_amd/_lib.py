@@ -112,6 +112,18 @@ _SIGS = {
     "had_kvpt_seq_len": ([_p, _i32, _pi32], ctypes.c_int),
     "had_kvpt_export": ([_p, _pi32, _i32, _pi32, _i32, _pi32], ctypes.c_int),
     "had_kvpt_stats": ([_p, _pi32, _pi32], ctypes.c_int),
+    "had_kvpt_info": ([_p, _pi32, _pi32], ctypes.c_int),
+    "had_kvpt_seq_create_from": ([_p, _pi32, _i32, _i32, _pi32], ctypes.c_int),
+    "had_kvpt_page_retain": ([_p, _i32], ctypes.c_int),
+    "had_kvpt_page_release": ([_p, _i32], ctypes.c_int),
+    "had_radix_create": ([_p, _p, ctypes.POINTER(_p)], ctypes.c_int),
+    "had_radix_destroy": ([_p], ctypes.c_int),
+    "had_radix_match": ([_p, _pi32, _i32, _pi32, _pi32, _pi32, _i32, _pi32], ctypes.c_int),
+    "had_radix_unlock": ([_p, _i32], ctypes.c_int),
+    "had_radix_insert": ([_p, _pi32, _i32, _pi32, _i32, _pi32], ctypes.c_int),
+    "had_radix_evict": ([_p, _i32, _i32, _pi32], ctypes.c_int),
+    "had_radix_stats": ([_p, _pi32, ctypes.POINTER(ctypes.c_int64), _pi32, ctypes.POINTER(ctypes.c_int64),
+                         ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
     "had_slots_create": ([_i32, _pi32, ctypes.POINTER(_p)], ctypes.c_int),
     "had_slots_destroy": ([_p], ctypes.c_int),
     "had_slots_acquire": ([_p, _pi32], ctypes.c_int),
@@ -244,6 +256,23 @@ class PageTable:
         _check(lib().had_kvpt_stats(self._h, ctypes.byref(f), ctypes.byref(u)))
         return f.value, u.value
 
+    def info(self):
+        n, ps = _i32(), _i32()
+        _check(lib().had_kvpt_info(self._h, ctypes.byref(n), ctypes.byref(ps)))
+        return n.value, ps.value
+
+    def seq_create_from(self, pages, length):
+        arr, ptr = _i32_array(pages)
+        out = _i32()
+        _check(lib().had_kvpt_seq_create_from(self._h, ptr, len(arr), length, ctypes.byref(out)))
+        return out.value
+
+    def page_retain(self, page):
+        _check(lib().had_kvpt_page_retain(self._h, page))
+
+    def page_release(self, page):
+        _check(lib().had_kvpt_page_release(self._h, page))
+
 
 class SlotPool:
     """Handle on the C++ state-slot pool (had_slots_*)."""
@@ -282,6 +311,65 @@ class SlotPool:
         f, u = _i32(), _i32()
         _check(lib().had_slots_stats(self._h, ctypes.byref(f), ctypes.byref(u)))
         return f.value, u.value
+
+
+class RadixCache:
+    """Hybrid prefix cache (had_radix_*): a radix tree over token ids whose
+    nodes hold KV pages and, where a state was saved, a GDN state slot.
+    Works on a PageTable and a SlotPool, which must outlive it."""
+
+    def __init__(self, pt, slots):
+        self._pt, self._slots = pt, slots  # keep the pools alive while the cache holds references
+        self._h = _p()
+        _check(lib().had_radix_create(pt._h, slots._h, ctypes.byref(self._h)))
+        self.page_size = pt.info()[1]
+
+    def close(self):
+        if self._h:
+            lib().had_radix_destroy(self._h)
+            self._h = _p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def match(self, tokens):
+        """Returns (matched_len, slot, pages, lock)."""
+        arr, ptr = _i32_array(tokens)
+        maxp = -(-len(arr) // self.page_size)
+        pages = np.full(max(maxp, 1), -1, dtype=np.int32)
+        m, sl, lk = _i32(), _i32(), _i32()
+        _check(lib().had_radix_match(self._h, ptr, len(arr), ctypes.byref(m), ctypes.byref(sl),
+                                     pages.ctypes.data_as(_pi32), len(pages), ctypes.byref(lk)))
+        return m.value, sl.value, pages[:-(-m.value // self.page_size)].tolist(), lk.value
+
+    def unlock(self, lock):
+        _check(lib().had_radix_unlock(self._h, lock))
+
+    def insert(self, tokens, pages, slot):
+        """Returns the number of tokens not cached before."""
+        arr, ptr = _i32_array(tokens)
+        parr, pptr = _i32_array(pages)
+        if len(parr) != -(-len(arr) // self.page_size):
+            raise ValueError("insert: %d pages for %d tokens" % (len(parr), len(arr)))
+        nt = _i32()
+        _check(lib().had_radix_insert(self._h, ptr, len(arr), pptr, slot, ctypes.byref(nt)))
+        return nt.value
+
+    def evict(self, min_free_pages, min_free_slots=0):
+        n = _i32()
+        _check(lib().had_radix_evict(self._h, min_free_pages, min_free_slots, ctypes.byref(n)))
+        return n.value
+
+    def stats(self):
+        nn, nc = _i32(), _i32()
+        toks, q, m = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().had_radix_stats(self._h, ctypes.byref(nn), ctypes.byref(toks), ctypes.byref(nc),
+                                     ctypes.byref(q), ctypes.byref(m)))
+        return dict(nodes=nn.value, cached_tokens=toks.value, checkpoints=nc.value, queried_tokens=q.value,
+                    matched_tokens=m.value)
 
 
 def spec_rollback(pt, slots, seq, T, accepted, in_slot, out_slots):

@@ -130,6 +130,42 @@ int had_kvpt_seq_fork(had_kvpt* h, int32_t src, int32_t prefix_len, int32_t* seq
   return had::ok();
 }
 
+int had_kvpt_seq_create_from(had_kvpt* h, const int32_t* pages, int32_t n_pages, int32_t len, int32_t* seq) {
+  if (!h || !seq || (n_pages > 0 && !pages)) return fail(HAD_ERR_INVALID_ARG, "seq_create_from: NULL argument");
+  if (len < 0 || n_pages != h->pages_for(len))
+    return fail(HAD_ERR_RANGE, "seq_create_from: %d pages do not cover exactly %d tokens", n_pages, len);
+  if (n_pages > h->max_pages)
+    return fail(HAD_ERR_CAPACITY, "seq_create_from: %d pages > max_pages_per_seq %d", n_pages, h->max_pages);
+  for (int32_t i = 0; i < n_pages; ++i)
+    if (pages[i] < 0 || pages[i] >= h->num_pages || h->ref[pages[i]] == 0)
+      return fail(HAD_ERR_INVALID_ARG, "seq_create_from: page %d is not a held page", pages[i]);
+  const int32_t id = h->new_id();
+  if (id < 0) return fail(HAD_ERR_CAPACITY, "seq_create_from: all %d sequence ids are live", h->max_seqs);
+  had_kvpt::Seq& d = h->seqs[id];
+  d.pages.assign(pages, pages + n_pages);
+  for (int32_t p : d.pages) ++h->ref[p];
+  d.len = len;
+  d.live = true;
+  *seq = id;
+  return had::ok();
+}
+
+int had_kvpt_page_retain(had_kvpt* h, int32_t page) {
+  if (!h) return fail(HAD_ERR_INVALID_ARG, "page_retain: NULL handle");
+  if (page < 0 || page >= h->num_pages || h->ref[page] == 0)
+    return fail(HAD_ERR_INVALID_ARG, "page_retain: page %d is not held", page);
+  ++h->ref[page];
+  return had::ok();
+}
+
+int had_kvpt_page_release(had_kvpt* h, int32_t page) {
+  if (!h) return fail(HAD_ERR_INVALID_ARG, "page_release: NULL handle");
+  if (page < 0 || page >= h->num_pages || h->ref[page] == 0)
+    return fail(HAD_ERR_INVALID_ARG, "page_release: page %d is not held", page);
+  if (--h->ref[page] == 0) h->free_list.push_back(page);
+  return had::ok();
+}
+
 int had_kvpt_reserve(had_kvpt* h, int32_t seq, int32_t n_tokens, int32_t* cow, int32_t* n_cow) {
   if (!h || !cow || !n_cow) return fail(HAD_ERR_INVALID_ARG, "reserve: NULL argument");
   had_kvpt::Seq* s = h->get(seq);
@@ -213,6 +249,13 @@ int had_kvpt_export(const had_kvpt* h, const int32_t* seqs, int32_t n, int32_t* 
     for (int32_t j = 0; j < max_pages; ++j) row[j] = j < np ? s->pages[j] : -1;
     seq_lens[i] = s->len;
   }
+  return had::ok();
+}
+
+int had_kvpt_info(const had_kvpt* h, int32_t* num_pages, int32_t* page_size) {
+  if (!h || !num_pages || !page_size) return fail(HAD_ERR_INVALID_ARG, "kvpt_info: NULL argument");
+  *num_pages = h->num_pages;
+  *page_size = h->page_size;
   return had::ok();
 }
 

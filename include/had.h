@@ -114,6 +114,18 @@ int had_kvpt_seq_create(had_kvpt *h, int32_t *seq);
  * HAD_ERR_RANGE if prefix_len > length of src. */
 int had_kvpt_seq_fork(had_kvpt *h, int32_t src, int32_t prefix_len, int32_t *seq);
 
+/* New sequence of length len aliasing the given held pages (each gains a
+ * reference): how a request starts from a cached prefix (had_radix_match).
+ * HAD_ERR_RANGE unless n_pages == ceil(len / page_size); HAD_ERR_INVALID_ARG
+ * if a page is out of range or has no reference.  pages: host int32[n_pages]. */
+int had_kvpt_seq_create_from(had_kvpt *h, const int32_t *pages, int32_t n_pages, int32_t len, int32_t *seq);
+
+/* One more / one less reference on a held page (a holder outside any
+ * sequence, such as the prefix cache).  HAD_ERR_INVALID_ARG if the page is
+ * out of range or has no reference; at 0 the page returns to the free list. */
+int had_kvpt_page_retain(had_kvpt *h, int32_t page);
+int had_kvpt_page_release(had_kvpt *h, int32_t page);
+
 /* Grow seq by n_tokens (>= 0).  If the last page is partially filled and
  * shared it is first replaced by a fresh page; the copy the caller must then
  * perform on every layer's pools is reported as cow = {src, dst, valid}
@@ -140,6 +152,9 @@ int had_kvpt_seq_len(const had_kvpt *h, int32_t seq, int32_t *len);
  * than max_pages pages. */
 int had_kvpt_export(const had_kvpt *h, const int32_t *seqs, int32_t n,
                     int32_t *page_table, int32_t max_pages, int32_t *seq_lens);
+
+/* The pool's page count and page size. */
+int had_kvpt_info(const had_kvpt *h, int32_t *num_pages, int32_t *page_size);
 
 /* Number of free pages and of pages with a reference. */
 int had_kvpt_stats(const had_kvpt *h, int32_t *n_free, int32_t *n_used);
@@ -173,6 +188,63 @@ int had_slots_stats(const had_slots *h, int32_t *n_free, int32_t *n_used);
 int had_spec_rollback(had_kvpt *kv, had_slots *slots, int32_t seq, int32_t T,
                       int32_t accepted, int32_t in_slot, const int32_t *out_slots,
                       int32_t *current_slot);
+
+/* ----------------------------------------------------------------------
+ * Hybrid prefix cache: a radix tree over token ids whose nodes hold the KV
+ * pages of their token span and, where a state was saved, a GDN state slot
+ * (the checkpoint of the recurrent layers at exactly that prefix length).
+ * This is the engine's radix-tree matching with Mamba-slot attachments over
+ * the C++ logical cache (24-ai.news TokenSpeed article, optimisation list,
+ * hybrid prefix caching; zubnet.ai ¶2: cached checkpoints reused without
+ * mutation by copy-on-write).  A hybrid model can resume only where both
+ * the KV and the recurrent state exist, so a match ends at the deepest
+ * node on the query's path that carries a slot.
+ *
+ * The cache holds its own references on pages (had_kvpt_page_retain) and
+ * slots (had_slots_retain); callers keep and release theirs as usual.
+ * Matched pages and slots are shared, never written by the cache's users:
+ * a request appends through had_kvpt_reserve (copy-on-write of a shared
+ * partial page) and writes its states to fresh slots.
+ * ---------------------------------------------------------------------- */
+typedef struct had_radix had_radix;
+
+/* The cache works on kv and slots, which must outlive it. */
+int had_radix_create(had_kvpt *kv, had_slots *slots, had_radix **out);
+/* Releases every page and slot reference the cache holds. */
+int had_radix_destroy(had_radix *r);
+
+/* Longest prefix of tokens[0..n) that is cached and ends at a checkpoint.
+ * *matched: its length (0 when none); *slot: its state slot (-1 for length
+ * 0: the zero state); pages: host int32[max_pages] receives the
+ * ceil(*matched / page_size) page ids holding the prefix's KV (valid rows:
+ * the first *matched positions; the caller may create a sequence on them
+ * with had_kvpt_seq_create_from).  *lock receives a handle that keeps the
+ * matched path from eviction until had_radix_unlock (-1 when *matched is 0).
+ * HAD_ERR_CAPACITY if max_pages is too small (nothing changes). */
+int had_radix_match(had_radix *r, const int32_t *tokens, int32_t n, int32_t *matched, int32_t *slot,
+                    int32_t *pages, int32_t max_pages, int32_t *lock);
+int had_radix_unlock(had_radix *r, int32_t lock);
+
+/* Cache tokens[0..n) with their pages (host int32[ceil(n / page_size)],
+ * every page held; the positions already cached keep the cache's pages) and
+ * slot (the state after token n-1; -1 for none).  The cache takes its own
+ * references on what it keeps.  *new_tokens (optional): tokens not cached
+ * before. */
+int had_radix_insert(had_radix *r, const int32_t *tokens, int32_t n, const int32_t *pages, int32_t slot,
+                     int32_t *new_tokens);
+
+/* Evict least-recently-used unlocked entries until the page pool has at
+ * least min_free_pages free pages and the slot pool min_free_slots free
+ * slots, or nothing evictable is left: leaves go first (their pages and
+ * slot), then checkpoints of inner nodes (their slot only).
+ * *n_evicted (optional): entries evicted. */
+int had_radix_evict(had_radix *r, int32_t min_free_pages, int32_t min_free_slots, int32_t *n_evicted);
+
+/* Nodes (root excluded), cached tokens, checkpoints, and the match
+ * counters: queried tokens and matched tokens over all had_radix_match
+ * calls (the cache hit rate is their ratio). */
+int had_radix_stats(const had_radix *r, int32_t *n_nodes, int64_t *cached_tokens, int32_t *n_checkpoints,
+                    int64_t *queried_tokens, int64_t *matched_tokens);
 
 /* ======================================================================
  * kv_page_table -- device helpers

@@ -24,6 +24,7 @@ attention   softmax decode attention over the gathered context, split
 prologue    RMSNorm + partial rotary embedding + gate split
 gdn         gated delta rule: sequential definition and chunkwise form
 speculative draft-verify bookkeeping and rollback by index
+radix       what a hybrid prefix-cache lookup returns (brute force)
 
 Parity status: every function here is pinned by the CPU tests under
 ``tests/test_oracle_*.py`` (closed forms, invariants, brute force, library
