@@ -540,9 +540,11 @@ def run_speculative(L0=262144, steps=256, warmup=10, kernel_reps=4, T=4, G=16, s
 
 def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6):
     """Agentic multi-turn: 50,000-token first turn, then `turns` turns of
-    `turn_len` decode steps; at each turn boundary the current GDN state slot
-    is kept as a cached checkpoint (retained) and the next step reads it and
-    writes a fresh slot."""
+    `turn_len` decode steps.  At each turn boundary the conversation so far
+    goes into the hybrid prefix cache (its pages and the current GDN state
+    slot as the checkpoint) and the next turn resumes from the cache's match
+    of the whole history; the next step reads the checkpoint slot and writes
+    a fresh one."""
     import torch
 
     import hybrid_attention_decode_amd as had
@@ -551,7 +553,7 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
     n_steps = turns * turn_len
     max_len = first_turn + n_steps + 1
     max_pages = -(-max_len // P) + 1
-    num_pages = max_pages + 8
+    num_pages = max_pages + turns + 8        # + the partial pages the cache keeps at turn boundaries
     n_slots = turns + 4
     st = Stack(1, 1, H_Q, num_pages, max_pages, max_len, n_slots, n_steps, seed)
     pt = had.PageTable(num_pages, P, 1, max_pages, free_order=synth.permutation(num_pages, synth.seed_of(seed, 1)))
@@ -563,16 +565,36 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
     cur = slots.acquire()
     L = first_turn
     checkpoints = []
+    cache = had.RadixCache(pt, slots)
+    tokens = np.zeros(max_len + 1, dtype=np.int32)                   # synthetic token ids of the conversation
+    tokens[:first_turn] = synth.integers(0, 150000, first_turn, synth.seed_of(seed, 3))
+    tok_rng = np.random.default_rng(synth.seed_of(seed, 4))
+    locks = []
+    host_us = []
+    n_cow = [0]
 
     def step(t):
         nonlocal cur, L
-        if t > 0 and t % turn_len == 0:            # turn boundary: keep the state as a checkpoint
-            slots.retain(cur)
+        if t > 0 and t % turn_len == 0:            # turn boundary: cache the conversation, resume from the cache
+            h0 = time.perf_counter()
+            row = pt.export([seq], max_pages)[0][0]
+            cache.insert(tokens[:L], row[:-(-L // P)], cur)
+            tokens[L] = tok_rng.integers(0, 150000)    # the next turn: the whole history plus its first new token
+            m, slot, pages, lock = cache.match(tokens[:L + 1])
+            if m != L or slot != cur or list(pages) != list(row[:-(-L // P)]):
+                raise RuntimeError("prefix cache did not return the cached conversation")
+            locks.append(lock)
+            host_us.append((time.perf_counter() - h0) * 1e6)
             checkpoints.append(cur)
+        tokens[L] = tok_rng.integers(0, 150000)
         out = slots.acquire()
-        assert pt.reserve(seq, 1) is None
+        trip = pt.reserve(seq, 1)
         L += 1
-        if (L - 1) % P == 0:
+        if trip is not None:                       # the cache shares the partial last page: copy it first
+            for a in st.attn:
+                had.kv_copy_pages(a["k_pool"], a["v_pool"], [trip[0]], [trip[1]])
+            n_cow[0] += 1
+        if trip is not None or (L - 1) % P == 0:
             st.set_page(0, (L - 1) // P, pt.export([seq], max_pages)[0][0, (L - 1) // P])
         st.push_ctrl(t, [L], [cur], [[out]])
         st.graph.replay()
@@ -597,14 +619,23 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
     mean_len = first_turn + (n_steps + 1) / 2.0
     step_bytes = algorithmic_bytes_per_step(mean_len)
     us = stack_kernel_us(st, kernel_reps)
-    res = dict(workload="agentic multi-turn: %d-token first turn, %d turns x %d decode steps (context %d -> %d), "
-                        "checkpoint slot kept at every turn boundary" % (first_turn, turns, turn_len, first_turn + 1,
-                                                                         first_turn + n_steps),
+    res = dict(workload="agentic multi-turn: %d-token first turn, %d turns x %d decode steps (context %d -> %d); at "
+                        "every turn boundary the conversation goes into the hybrid prefix cache (pages + GDN "
+                        "checkpoint slot) and the next turn resumes from its match" % (
+                            first_turn, turns, turn_len, first_turn + 1, first_turn + n_steps),
                steps=n_steps, ms_per_step=round(ms, 5), steps_per_s=round(1e3 / ms, 3),
                first_turn_steps_per_s=round(1e3 / per_turn[0], 2), last_turn_steps_per_s=round(1e3 / per_turn[-1], 2),
                checkpoints_kept=len(checkpoints), algorithmic_bytes_per_step=int(step_bytes),
                hbm_gbps=round(step_bytes / (ms * 1e-3) / 1e9, 1), us_per_layer_at_end=us)
-    log("agentic: %.1f steps/s over %d steps" % (1e3 / ms, n_steps))
+    cst = cache.stats()
+    res["prefix_cache"] = dict(turn_boundaries=len(host_us), hit_rate=round(cst["matched_tokens"] / cst["queried_tokens"], 5),
+                               nodes=cst["nodes"], checkpoints=cst["checkpoints"], cached_tokens=cst["cached_tokens"],
+                               host_us_per_boundary=round(float(np.mean(host_us)), 1), cow_copies=n_cow[0])
+    for lk in locks:
+        cache.unlock(lk)
+    cache.close()
+    log("agentic: %.1f steps/s over %d steps; prefix cache hit rate %.4f, %.0f us of host work per turn boundary"
+        % (1e3 / ms, n_steps, res["prefix_cache"]["hit_rate"], res["prefix_cache"]["host_us_per_boundary"]))
     check_sentinel(st)
     del st
     torch.cuda.synchronize()
