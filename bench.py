@@ -45,7 +45,18 @@ GDN_H, DK, DV = 8, 128, 128
 KV_BYTES_PER_TOKEN = 2 * H_KV * D * 2          # K and V rows, bf16
 GDN_BYTES_PER_LAYER = 2 * GDN_H * DK * DV * 4  # state read + write, fp32
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_valu_d256_longctx_pmc.json")
-KERNEL_SRC = os.path.join(ROOT, "hybrid_attention_decode_amd", "csrc", "kernels", "attn_valu.hip")
+KERNEL_DIR = os.path.join(ROOT, "hybrid_attention_decode_amd", "csrc", "kernels")
+# the partial kernel's source and the headers it includes: the PMC summary is
+# used only while they are unchanged
+KERNEL_SRCS = [os.path.join(KERNEL_DIR, f) for f in ("attn_valu.hip", "attn_internal.h", "prologue_math.h", "kcommon.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for fn in KERNEL_SRCS:
+        with open(fn, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -824,8 +835,7 @@ def roofline(res):
     try:
         with open(PMC_SUMMARY) as f:
             pmc = json.load(f)
-        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if pmc.get("kernel_source_sha256") == src_hash and pmc.get("context") == res["context"]:
+        if pmc.get("kernel_sources_sha256") == kernel_source_hash() and pmc.get("context") == res["context"]:
             r["traffic"] = pmc.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         pass
