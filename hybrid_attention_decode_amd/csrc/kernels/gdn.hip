@@ -11,7 +11,8 @@
 // writes another (zubnet.ai TokenSpeed article, second paragraph,
 // current_input_indices; 24-ai.news "Mamba State Update", O(1) pointer
 // update).  With T > 1 the state stays in registers across tokens and every
-// token's state is written as a checkpoint.
+// token's state is written as a checkpoint; all tokens' inputs are loaded
+// before the first is processed.
 //
 // Mapping: one wave per (s, h, block of 8 rows of S).  Lane (r, c) holds
 // row r's columns {4c + 32i .. 4c + 32i + 3}, so each row's 8 lanes read a
@@ -52,7 +53,12 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-template <int DK>
+// TM: compile-time bound on T.  Every token's inputs (q, k, v row, gates,
+// out slot) are loaded before the first token is processed -- tokens past T
+// reload the last one, so no load sits under a branch -- and the recurrence
+// then runs from registers; only the state store of each token waits on
+// the previous token.
+template <int DK, int TM>
 __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
   constexpr int NC = DK / 32;  // float4 column chunks per lane
   const int rb = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -63,41 +69,60 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
   const size_t row_off = static_cast<size_t>(h) * head_elems + static_cast<size_t>(row) * DK;
   const size_t slot_elems = static_cast<size_t>(a.H) * head_elems;
 
+  // token inputs first (independent of the state)
+  uint2 kw[TM][NC], qw[TM][NC];
+  float vi[TM], al[TM], be[TM];
+  int outs[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const int tt = min(t, a.T - 1);
+    const size_t th = (static_cast<size_t>(s) * a.T + tt) * a.H + h;
+    const uint16_t* kp = a.k + th * DK;
+    const uint16_t* qp = a.q + th * DK;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      kw[t][i] = *reinterpret_cast<const uint2*>(kp + 4 * c + 32 * i);
+      qw[t][i] = *reinterpret_cast<const uint2*>(qp + 4 * c + 32 * i);
+    }
+    vi[t] = bf16_to_f32(a.v[th * a.d_v + row]);
+    al[t] = a.alpha[th];
+    be[t] = a.beta[th];
+    outs[t] = a.out_idx[static_cast<size_t>(s) * a.T + tt];
+  }
+
   int in = a.in_idx[s];
   if (in < -1 || in >= a.n_slots) {
     if (lane == 0) set_err(a.d_err, HAD_DERR_SLOT);
     in = -1;
   }
   float S[NC][4];
-  if (in >= 0) {
-    const float* src = a.pool + static_cast<size_t>(in) * slot_elems + row_off;
+  {
+    // a clamped, unconditional load; the zero state (in = -1) is selected after it
+    const float* src = a.pool + static_cast<size_t>(max(in, 0)) * slot_elems + row_off;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const float4 t = *reinterpret_cast<const float4*>(src + 4 * c + 32 * i);
-      S[i][0] = t.x; S[i][1] = t.y; S[i][2] = t.z; S[i][3] = t.w;
+      const float4 t4 = *reinterpret_cast<const float4*>(src + 4 * c + 32 * i);
+      S[i][0] = in >= 0 ? t4.x : 0.f;
+      S[i][1] = in >= 0 ? t4.y : 0.f;
+      S[i][2] = in >= 0 ? t4.z : 0.f;
+      S[i][3] = in >= 0 ? t4.w : 0.f;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NC; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
   }
 
-  for (int t = 0; t < a.T; ++t) {
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t >= a.T) break;
     const size_t th = (static_cast<size_t>(s) * a.T + t) * a.H + h;
-    const uint16_t* kp = a.k + th * DK;
-    const uint16_t* qp = a.q + th * DK;
-    float al = a.alpha[th], be = a.beta[th];
+    float alt = al[t], bet = be[t];
     if (a.raw_gates) {
-      al = expf(al);
-      be = 1.f / (1.f + expf(-be));
+      alt = expf(alt);
+      bet = 1.f / (1.f + expf(-bet));
     }
-    const float vi = bf16_to_f32(a.v[th * a.d_v + row]);
     float kk[NC][4], qq[NC][4];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const uint2 kw = *reinterpret_cast<const uint2*>(kp + 4 * c + 32 * i);
-      const uint2 qw = *reinterpret_cast<const uint2*>(qp + 4 * c + 32 * i);
-      kk[i][0] = bf16_lo(kw.x); kk[i][1] = bf16_hi(kw.x); kk[i][2] = bf16_lo(kw.y); kk[i][3] = bf16_hi(kw.y);
-      qq[i][0] = bf16_lo(qw.x); qq[i][1] = bf16_hi(qw.x); qq[i][2] = bf16_lo(qw.y); qq[i][3] = bf16_hi(qw.y);
+      kk[i][0] = bf16_lo(kw[t][i].x); kk[i][1] = bf16_hi(kw[t][i].x); kk[i][2] = bf16_lo(kw[t][i].y); kk[i][3] = bf16_hi(kw[t][i].y);
+      qq[i][0] = bf16_lo(qw[t][i].x); qq[i][1] = bf16_hi(qw[t][i].x); qq[i][2] = bf16_lo(qw[t][i].y); qq[i][3] = bf16_hi(qw[t][i].y);
     }
     float sk = 0.f;
 #pragma unroll
@@ -105,18 +130,18 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sk = fmaf(S[i][e], kk[i][e], sk);
     sk = sum8(sk);
-    const float u = be * (vi - al * sk);
+    const float u = bet * (vi[t] - alt * sk);
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < NC; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        S[i][e] = fmaf(u, kk[i][e], al * S[i][e]);
+        S[i][e] = fmaf(u, kk[i][e], alt * S[i][e]);
         sq = fmaf(S[i][e], qq[i][e], sq);
       }
     sq = sum8(sq);
     if (c == 0) a.o[th * a.d_v + row] = a.q_scale * sq;
-    const int out = a.out_idx[static_cast<size_t>(s) * a.T + t];
+    const int out = outs[t];
     if (out < 0 || out >= a.n_slots) {
       if (lane == 0) set_err(a.d_err, HAD_DERR_SLOT);
       continue;
@@ -164,10 +189,16 @@ extern "C" int had_gdn_state_update(const had_gdn_desc* d, const had_gdn_ptrs* p
   a.q_scale = d->q_scale;
   const dim3 grid(d->d_v / 8, d->H, d->n_seqs);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d->d_k == 64)
-    hipLaunchKernelGGL(had::gdn_kernel<64>, grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(had::gdn_kernel<128>, grid, dim3(64), 0, s, a);
+  // the token bound the kernel is compiled for: 1, 4 or 8
+  if (d->d_k == 64) {
+    if (d->T == 1) hipLaunchKernelGGL((had::gdn_kernel<64, 1>), grid, dim3(64), 0, s, a);
+    else if (d->T <= 4) hipLaunchKernelGGL((had::gdn_kernel<64, 4>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((had::gdn_kernel<64, 8>), grid, dim3(64), 0, s, a);
+  } else {
+    if (d->T == 1) hipLaunchKernelGGL((had::gdn_kernel<128, 1>), grid, dim3(64), 0, s, a);
+    else if (d->T <= 4) hipLaunchKernelGGL((had::gdn_kernel<128, 4>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((had::gdn_kernel<128, 8>), grid, dim3(64), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_state_update: launch: %s", hipGetErrorString(e));
   return had::ok();
