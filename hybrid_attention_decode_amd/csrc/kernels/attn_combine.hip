@@ -47,6 +47,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
   const float* ml = a.ws_ml;
   const size_t ostride4 = static_cast<size_t>(a.rows) * D / 4;  // float4s between consecutive splits
   const float4* o4 = reinterpret_cast<const float4*>(a.ws_o + (base * a.rows + row) * D + d0);
+  const int s = unit / a.H_kv, h = unit % a.H_kv;
+  const int jq = row / a.G, g = row % a.G;
+  const size_t head = (static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g;
+  // the gate is read in the same round trip as the partials (unconditionally:
+  // without a gate the load reads the output row, and the value is unused)
+  const uint2 gw = *reinterpret_cast<const uint2*>(
+      a.gate ? a.gate + head * a.gate_hstride + d0 + 4 * (tid % kLS) : a.out + head * D + d0 + 4 * (tid % kLS));
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float M = -INFINITY;
@@ -116,12 +123,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
       l += scal[w];
     }
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    const int s = unit / a.H_kv, h = unit % a.H_kv;
-    const int jq = row / a.G, g = row % a.G;
-    const size_t head = (static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g;
     float4 r = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
     if (a.gate) {  // gated output: sigmoid(gate) in fp32, before the rounding
-      const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + head * a.gate_hstride + d0 + 4 * tid);
       r.x *= 1.f / (1.f + expf(-bf16_lo(gw.x)));
       r.y *= 1.f / (1.f + expf(-bf16_hi(gw.x)));
       r.z *= 1.f / (1.f + expf(-bf16_lo(gw.y)));
