@@ -193,3 +193,34 @@ def test_gated_output_against_oracle(lens, q_len, H_q, H_kv, D, P):
     assert err.item() == 0
     ref = A.paged_attention(bits_of(q), bits_of(kp), bits_of(vp), pt, L, P, 1.0 / np.sqrt(D))
     assert_attn_close(out, Pr.output_gate(ref, bf16.to_f64(bits_of(gate))))
+
+
+@pytest.mark.parametrize("G,q_len,D", [
+    (32, 8, 128),   # 256 query rows per KV head, the maximum: two 128-row launches
+    (51, 5, 64),    # 255 rows: the second launch ragged
+])
+def test_mfma_path_maximum_rows(G, q_len, D):
+    out, ref = _run(1300 + G, [q_len + 40, 1500], q_len, G, 1, D, 16)
+    assert_attn_close(out, ref)
+
+
+def test_one_split_at_the_page_limit():
+    # one split over exactly 512 pages (the per-split maximum) on both paths
+    out, ref = _run(1400, [512 * 16], 1, 8, 1, 64, 16, num_splits=1, max_seq_len=512 * 16)
+    assert_attn_close(out, ref)
+    out, ref = _run(1401, [512 * 16], 2, 16, 1, 64, 16, num_splits=1, max_seq_len=512 * 16)
+    assert_attn_close(out, ref)
+
+
+def test_rows_and_page_limits_are_rejected():
+    q = torch.zeros((1, 1, 257, 64), dtype=torch.bfloat16, device=DEV)     # 257 rows per KV head
+    pool = torch.zeros((4, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(had.HadError) as e:
+        had.decode_attn(q, pool, pool, torch.zeros((1, 4), dtype=torch.int32, device=DEV),
+                        torch.tensor([20], dtype=torch.int32, device=DEV))
+    assert e.value.kind == "unsupported_shape"
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device=DEV)
+    pool = torch.zeros((600, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(had.HadError):                                       # 513 pages in one split
+        had.decode_attn(q, pool, pool, torch.zeros((1, 600), dtype=torch.int32, device=DEV),
+                        torch.tensor([513 * 16], dtype=torch.int32, device=DEV), num_splits=1)
