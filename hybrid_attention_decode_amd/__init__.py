@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     decode_attn_plan,
     decode_attn_workspace_bytes,
     exported_symbols,
+    gdn_check_slots,
     gdn_prefill,
     gdn_prefill_desc,
     gdn_prefill_workspace_bytes,

@@ -148,6 +148,7 @@ _SIGS = {
     "had_decode_attn_layer_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc),
                                        ctypes.POINTER(QknrgPtrs), _p, ctypes.c_size_t, _p], ctypes.c_int),
     "had_gdn_state_update": ([ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnPtrs), _p], ctypes.c_int),
+    "had_gdn_check_slots": ([_i32, _i32, _i32, _pi32, _pi32, _i32], ctypes.c_int),
     "had_gdn_prefill_workspace_bytes": ([ctypes.POINTER(GdnPrefillDesc)], ctypes.c_size_t),
     "had_gdn_prefill": ([ctypes.POINTER(GdnPrefillDesc), ctypes.POINTER(GdnPrefillPtrs), _p], ctypes.c_int),
 }
@@ -590,6 +591,22 @@ def decode_attn_combine(desc, num_splits, workspace, out):
     return out
 
 
+def gdn_check_slots(n_slots, in_idx, out_idx, allow_in_place):
+    """Host check of the GDN slot preconditions (see had_gdn_check_slots);
+    in_idx [S], out_idx [S, T] as host arrays or tensors.  Raises HadError."""
+    if hasattr(in_idx, "cpu"):
+        in_idx, out_idx = in_idx.cpu().numpy(), out_idx.cpu().numpy()
+    ia, ip = _i32_array(np.asarray(in_idx).reshape(-1))
+    oa = np.asarray(out_idx, dtype=np.int32).reshape(len(ia), -1)
+    oa, op = _i32_array(oa)
+    _check(lib().had_gdn_check_slots(len(ia), oa.shape[1] if oa.ndim == 2 else 1, int(n_slots), ip, op,
+                                     1 if allow_in_place else 0))
+
+
+def _debug():
+    return os.environ.get("HAD_DEBUG") == "1"
+
+
 def gdn_state_update(state_pool, in_idx, out_idx, q, k, v, alpha, beta, o=None, q_scale=1.0, d_err=None,
                      raw_gates=False):
     """state_pool [n_slots, H, d_v, d_k] fp32; q, k [S, T, H, d_k]; v [S, T, H, d_v] bf16;
@@ -600,6 +617,8 @@ def gdn_state_update(state_pool, in_idx, out_idx, q, k, v, alpha, beta, o=None, 
     S, T = out_idx.shape
     if o is None:
         o = torch.empty((S, T, H, d_v), dtype=torch.float32, device=state_pool.device)
+    if _debug():
+        gdn_check_slots(n_slots, in_idx, out_idx, T == 1)
     desc = GdnDesc(S, T, H, d_k, d_v, n_slots, float(q_scale), GDN_RAW_GATES if raw_gates else 0)
     ptrs = GdnPtrs(_dev(state_pool, torch.float32, "state_pool"), _dev(in_idx, torch.int32, "in_idx"),
                    _dev(out_idx, torch.int32, "out_idx"), _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
@@ -634,6 +653,8 @@ def gdn_prefill(state_pool, in_idx, out_idx, cu_seqlens, q, k, v, alpha, beta, m
     n_seqs = cu_seqlens.numel() - 1
     if max_len is None:
         max_len = N
+    if _debug():
+        gdn_check_slots(state_pool.shape[0], in_idx, out_idx.reshape(-1, 1), True)
     desc = gdn_prefill_desc(state_pool.shape, n_seqs, max_len, q_scale, raw_gates)
     need = gdn_prefill_workspace_bytes(desc)
     if workspace is None:

@@ -322,6 +322,33 @@ int had_slots_stats(const had_slots* h, int32_t* n_free, int32_t* n_used) {
   return had::ok();
 }
 
+int had_gdn_check_slots(int32_t n_seqs, int32_t T, int32_t n_slots, const int32_t* in_idx, const int32_t* out_idx,
+                        int32_t allow_in_place) {
+  if (n_seqs < 0 || T < 1 || n_slots < 1 || (n_seqs > 0 && (!in_idx || !out_idx)))
+    return fail(HAD_ERR_INVALID_ARG, "gdn_check_slots: bad argument (n_seqs=%d T=%d n_slots=%d)", n_seqs, T, n_slots);
+  std::vector<int32_t> writer(n_slots, -1);  // sequence that writes each slot
+  for (int32_t s = 0; s < n_seqs; ++s) {
+    if (in_idx[s] < -1 || in_idx[s] >= n_slots)
+      return fail(HAD_ERR_BAD_SLOT, "gdn_check_slots: in_idx[%d] = %d outside [-1, %d)", s, in_idx[s], n_slots);
+    for (int32_t t = 0; t < T; ++t) {
+      const int32_t o = out_idx[static_cast<int64_t>(s) * T + t];
+      if (o < 0 || o >= n_slots)
+        return fail(HAD_ERR_BAD_SLOT, "gdn_check_slots: out_idx[%d][%d] = %d outside [0, %d)", s, t, o, n_slots);
+      if (writer[o] >= 0) return fail(HAD_ERR_BAD_SLOT, "gdn_check_slots: slot %d is written twice", o);
+      writer[o] = s;
+      if (o == in_idx[s] && !allow_in_place)
+        return fail(HAD_ERR_BAD_SLOT, "gdn_check_slots: sequence %d reads and writes slot %d", s, o);
+    }
+  }
+  for (int32_t s = 0; s < n_seqs; ++s) {
+    const int32_t i = in_idx[s];
+    if (i >= 0 && writer[i] >= 0 && writer[i] != s)
+      return fail(HAD_ERR_BAD_SLOT, "gdn_check_slots: slot %d is read by sequence %d and written by sequence %d", i, s,
+                  writer[i]);
+  }
+  return had::ok();
+}
+
 int had_spec_rollback(had_kvpt* kv, had_slots* slots, int32_t seq, int32_t T, int32_t accepted,
                       int32_t in_slot, const int32_t* out_slots, int32_t* current_slot) {
   if (!kv || !slots || !current_slot || (T > 0 && !out_slots) || T < 0)

@@ -497,6 +497,18 @@ typedef struct {
 
 int had_gdn_state_update(const had_gdn_desc *d, const had_gdn_ptrs *p, void *stream);
 
+/* Host check of the slot preconditions that the GDN kernels do not check
+ * on the device (two sequences racing on one slot is not visible there), on
+ * host copies of the index arrays: every id in range (in_idx >= -1), no
+ * slot written twice, no slot written by one sequence and read by another,
+ * and in_idx[s] equal to one of its own out slots only when allow_in_place
+ * (had_gdn_state_update with T == 1, had_gdn_prefill).  out_idx: host
+ * int32[n_seqs][T] (T = 1 for the prefill).  HAD_ERR_BAD_SLOT names the
+ * first violation.  A debugging aid: the binding runs it before every GDN
+ * call when the environment sets HAD_DEBUG=1. */
+int had_gdn_check_slots(int32_t n_seqs, int32_t T, int32_t n_slots, const int32_t *in_idx, const int32_t *out_idx,
+                        int32_t allow_in_place);
+
 /* ======================================================================
  * gdn_prefill -- the same recurrence over whole prompts, chunk-parallel
  *

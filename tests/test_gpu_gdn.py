@@ -183,3 +183,16 @@ def test_unknown_gdn_flag_is_rejected():
                             None)
     import ctypes
     assert had.lib().had_gdn_state_update(ctypes.byref(desc), ctypes.byref(ptrs), None) != 0
+
+
+def test_debug_mode_checks_slot_preconditions_on_the_host(monkeypatch):
+    monkeypatch.setenv("HAD_DEBUG", "1")
+    q, k, v, al, be = _inputs(8, 2, 1, 2, 64, 64)
+    pool = torch.zeros((4, 2, 64, 64), dtype=torch.float32, device=DEV)
+    print("case debug-mode slot checks", flush=True)
+    had.gdn_state_update(pool, to_dev(np.array([0, 1], np.int32)), to_dev(np.array([[2], [3]], np.int32)),
+                         to_dev(q), to_dev(k), to_dev(v), to_dev(al), to_dev(be))
+    torch.cuda.synchronize()
+    with pytest.raises(had.HadError):   # slot 2 written by sequence 0 and read by sequence 1: never launched
+        had.gdn_state_update(pool, to_dev(np.array([0, 2], np.int32)), to_dev(np.array([[2], [3]], np.int32)),
+                             to_dev(q), to_dev(k), to_dev(v), to_dev(al), to_dev(be))

@@ -144,3 +144,20 @@ def test_error_paths_leave_handles_unchanged():
         PageTable(4, 4, 2, 2, free_order=[0, 1, 1, 3])
     assert e.value.kind == "invalid"
     assert "free_order" in str(e.value)
+
+
+def test_gdn_slot_precondition_checker():
+    ok = [([0, 1], [[2], [3]], False), ([0, -1], [[0], [3]], True), ([4, 4], [[1, 2], [3, 0]], False),
+          ([-1], [[0, 1, 2, 3]], False)]
+    for in_idx, out_idx, inplace in ok:
+        had.gdn_check_slots(6, np.array(in_idx), np.array(out_idx), inplace)
+    bad = [([0, 1], [[2], [2]], False),        # one slot written twice
+           ([0, 2], [[2], [3]], False),        # written by sequence 0, read by sequence 1
+           ([0], [[0]], False),                # in place where not allowed
+           ([0], [[6]], True),                 # out of range
+           ([-2], [[1]], True),                # in out of range
+           ([1, 0], [[1, 2], [3, 4]], False)]  # a checkpoint slot that is the input: not in place
+    for in_idx, out_idx, inplace in bad:
+        with pytest.raises(HadError) as e:
+            had.gdn_check_slots(6, np.array(in_idx), np.array(out_idx), inplace)
+        assert e.value.kind == "bad_slot", (in_idx, out_idx)
