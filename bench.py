@@ -904,6 +904,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--seed", type=int, default=0, help="base seed of the synthetic inputs")
     ap.add_argument("--workloads", default="speculative,agentic,prefix,prefill",
                     help="further workloads reported beside the headline (comma list, '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -924,25 +925,27 @@ def main():
     had.lib()
     if args.copy_calibration:
         copy_calibration()
-    head = run_context(args.ctx, args.steps, args.warmup, args.kernel_reps)
+    head = run_context(args.ctx, args.steps, args.warmup, args.kernel_reps, seed=args.seed)
     sweep = []
     for c in [int(x) for x in args.sweep.split(",") if x.strip()]:
-        sweep.append(run_context(c, args.steps, args.warmup, args.kernel_reps))
+        sweep.append(run_context(c, args.steps, args.warmup, args.kernel_reps, seed=args.seed))
     extra = {}
     wl = [w.strip() for w in args.workloads.split(",") if w.strip()]
     if "speculative" in wl:
-        extra["speculative"] = run_speculative(steps=args.steps, warmup=args.warmup, kernel_reps=args.kernel_reps)
+        extra["speculative"] = run_speculative(steps=args.steps, warmup=args.warmup, kernel_reps=args.kernel_reps,
+                                               seed=5 + args.seed)
     if "agentic" in wl:
-        extra["agentic"] = run_agentic(kernel_reps=args.kernel_reps)
+        extra["agentic"] = run_agentic(kernel_reps=args.kernel_reps, seed=6 + args.seed)
     if "prefix" in wl:
         extra["prefix_shared"] = run_prefix_shared(steps=args.steps, warmup=args.warmup,
-                                                   kernel_reps=args.kernel_reps)
-        flat = run_prefix_shared(steps=args.steps, warmup=args.warmup, kernel_reps=args.kernel_reps, cascade=False)
+                                                   kernel_reps=args.kernel_reps, seed=7 + args.seed)
+        flat = run_prefix_shared(steps=args.steps, warmup=args.warmup, kernel_reps=args.kernel_reps, seed=7 + args.seed,
+                                 cascade=False)
         extra["prefix_shared"]["per_sequence_path"] = {k: flat[k] for k in ("steps_per_s", "tokens_per_s",
                                                                             "us_per_layer")}
     cpu = None
     if "prefill" in wl:
-        extra["gdn_prefill"] = run_gdn_prefill()
+        extra["gdn_prefill"] = run_gdn_prefill(seed=8 + args.seed)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
         cpu = cpu_baseline(args.ctx, args.cpu_seconds)
