@@ -646,13 +646,17 @@ def gdn_prefill(state_pool, in_idx, out_idx, cu_seqlens, q, k, v, alpha, beta, m
     """Whole prompts through the gated delta rule, chunk-parallel.
     state_pool [n_slots, H, d_v, d_k] fp32; q, k [N, H, d_k], v [N, H, d_v] bf16 (sequences packed,
     token offsets cu_seqlens int32 [n_seqs + 1] on the device); alpha, beta [N, H] fp32;
-    in_idx, out_idx int32 [n_seqs].  max_len bounds every sequence's length (default N).
+    in_idx, out_idx int32 [n_seqs].  max_len bounds every sequence's length; the
+    workspace holds n_seqs x ceil(max_len / 64) chunk blocks.  Default: the
+    longest sequence, read from cu_seqlens (a device-to-host copy; pass
+    max_len to avoid it, e.g. under graph capture).
     Returns o [N, H, d_v] fp32; the final states land in slots out_idx."""
     torch = _torch()
     N, H, d_k = q.shape
     n_seqs = cu_seqlens.numel() - 1
     if max_len is None:
-        max_len = N
+        cu = cu_seqlens.cpu().numpy().astype(np.int64)
+        max_len = int(max(1, (cu[1:] - cu[:-1]).max(initial=0)))
     if _debug():
         gdn_check_slots(state_pool.shape[0], in_idx, out_idx.reshape(-1, 1), True)
     desc = gdn_prefill_desc(state_pool.shape, n_seqs, max_len, q_scale, raw_gates)
