@@ -372,7 +372,9 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   const int unit = (b / 8 / VT) * 8 + b % 8, vs = (b / 8) % VT;
   if (unit >= a.n_seqs * a.H) return;
   const int s = unit / a.H, h = unit % a.H;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  // (wave is made uniform so that tests on it are scalar branches)
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
 
   const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
   const int in = a.in_idx[s], out = a.out_idx[s];
@@ -390,45 +392,59 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   __shared__ u32x4_t sbuf[KS][2][64];     // new state as B operands (hi, lo) per d_k step
   __shared__ __align__(16) float rbuf[kC];  // gamma_C / gamma_t of the chunk
 
-  // state rows as B operands: lane (v, g) holds S[v][sigma(ks, g, j)]
-  u32x4_t shi[KS], slo[KS];
-  f32x4_t sown[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // fp32 columns of d_k step `wave`
+  const int kw = wave < KS ? wave : 0;  // a wave that owns no d_k step (d_k 64) mirrors step 0 and discards it
+
+  // state rows as B operands: lane (v, g) holds S[v][sigma(ks, g, j)]; the
+  // wave's own d_k step also in fp32 (sown) and as its hi/lo pair (ohi, olo),
+  // so that no register array is indexed by the wave number (a dynamic
+  // index into registers compiles to a compare-and-select chain)
+  u32x4_t shi[KS], slo[KS], ohi, olo;
+  f32x4_t sown[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  {
+    const float* src = a.pool + static_cast<size_t>(max(in, 0)) * slot_elems + row_off + 4 * g;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    f32x4_t p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+    for (int ks = 0; ks < KS; ++ks) {
+      f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(src + 32 * ks);
+      f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(src + 32 * ks + 16);
+      if (in < 0) p0 = p1 = sown[0];
+      float x8[8];
+      cat8(p0, p1, x8);
+      split8(x8, shi[ks], slo[ks]);
+    }
     if (in >= 0) {
-      const float* src = a.pool + static_cast<size_t>(in) * slot_elems + row_off + 32 * ks + 4 * g;
-      p0 = *reinterpret_cast<const f32x4_t*>(src);
-      p1 = *reinterpret_cast<const f32x4_t*>(src + 16);
+      sown[0] = *reinterpret_cast<const f32x4_t*>(src + 32 * kw);
+      sown[1] = *reinterpret_cast<const f32x4_t*>(src + 32 * kw + 16);
     }
     float x8[8];
-    cat8(p0, p1, x8);
-    split8(x8, shi[ks], slo[ks]);
-    if (ks == wave) {
-      sown[0] = p0;
-      sown[1] = p1;
-    }
+    cat8(sown[0], sown[1], x8);
+    split8(x8, ohi, olo);
   }
 
   u32x4_t* blk0 = a.ws + static_cast<size_t>(s * a.max_chunks) * a.H * L::TOTAL + static_cast<size_t>(h) * L::TOTAL;
-  const int kw = wave < KS ? wave : 0;  // a wave that owns no d_k step (d_k 64) mirrors step 0 and discards it
 
   // A chunk's operands, loaded one chunk ahead (none depends on the state).
   // Every load is unconditional: a load under a branch would make the join
-  // wait for all loads in flight, the prefetch included.
+  // wait for all loads in flight, the prefetch included.  Vector-memory
+  // operations retire in issue order, and a store retires only when the
+  // write is acknowledged (slow once the workspace spills to HBM), so the
+  // step issues its stores after the next chunk's loads: waiting for those
+  // loads then never waits for a store of the same step.
   struct Ops {
     u32x4_t whi[KS], wlo[KS], kt[2][2];
     f32x4_t up;
     float rat, gC;
   };
-  auto load = [&](int c, Ops& p) {
+  auto load_w = [&](int c, Ops& p) {
     const u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
-    const float* gw = reinterpret_cast<const float*>(blk + L::GAM);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       p.whi[ks] = blk[L::W_HI + (wave * KS + ks) * 64 + lane];
       p.wlo[ks] = blk[L::W_LO + (wave * KS + ks) * 64 + lane];
     }
+  };
+  auto load_rest = [&](int c, Ops& p) {
+    const u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
+    const float* gw = reinterpret_cast<const float*>(blk + L::GAM);
     p.up = __builtin_bit_cast(f32x4_t, blk[L::UP + (wave * VT + vs) * 64 + lane]);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -438,16 +454,20 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
     p.gC = gw[kC - 1];
   };
 
-  auto step = [&](int c, const Ops& p) {
+  // the chunk's initial state for the output kernel: this wave's d_k step
+  // (chunk c + 1's is stored at the end of step c)
+  auto store_sc = [&](int c) {
     u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
-    // the chunk's initial state for the output kernel: this wave's d_k step
-    if (wave < KS) {
-      blk[L::SC_HI + (vs * KS + wave) * 64 + lane] = shi[wave];
-      blk[L::SC_LO + (vs * KS + wave) * 64 + lane] = slo[wave];
-    }
+    blk[L::SC_HI + (vs * KS + wave) * 64 + lane] = ohi;
+    blk[L::SC_LO + (vs * KS + wave) * 64 + lane] = olo;
+  };
+
+  // one chunk: c with operands p; the operands of chunk cn load into pn
+  auto step = [&](int c, const Ops& p, int cn, Ops& pn) {
+    u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
     if (wave == 0) rbuf[lane] = p.rat;
     // U = U' - W S0^T for token rows 16w .. (the split terms accumulate in
-    // separate chains)
+    // separate chains); chunk cn's operands load between the products
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
     f32x4_t X0 = z, X1 = z, X2 = z;
 #pragma unroll
@@ -456,6 +476,8 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
       X1 = mfma(p.whi[ks], slo[ks], X1);
       X2 = mfma(p.wlo[ks], shi[ks], X2);
     }
+    load_w(cn, pn);
+    load_rest(cn, pn);
     const f32x4_t U = p.up - (X0 + (X1 + X2));
     ubuf[wave][lane] = U;
     blk[L::UP + (wave * VT + vs) * 64 + lane] = __builtin_bit_cast(u32x4_t, U);  // U replaces U'
@@ -489,10 +511,10 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
       }
       float x8[8];
       cat8(sown[0], sown[1], x8);
-      u32x4_t hi, lo;
-      split8(x8, hi, lo);
-      sbuf[wave][0][lane] = hi;
-      sbuf[wave][1][lane] = lo;
+      split8(x8, ohi, olo);
+      sbuf[wave][0][lane] = ohi;
+      sbuf[wave][1][lane] = olo;
+      if (c + 1 < n_chunks) store_sc(c + 1);
     }
     __syncthreads();
 #pragma unroll
@@ -505,13 +527,15 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   // chunk c + 1's operands load while chunk c computes (two register sets;
   // the last chunk reloads itself so that no load sits under a branch)
   Ops pa, pb;
-  if (n_chunks > 0) load(0, pa);
+  if (n_chunks > 0) {
+    load_w(0, pa);
+    load_rest(0, pa);
+    if (wave < KS) store_sc(0);
+  }
   for (int c = 0; c < n_chunks; c += 2) {
-    load(min(c + 1, n_chunks - 1), pb);
-    step(c, pa);
+    step(c, pa, min(c + 1, n_chunks - 1), pb);
     if (c + 1 >= n_chunks) break;
-    load(min(c + 2, n_chunks - 1), pa);
-    step(c + 1, pb);
+    step(c + 1, pb, min(c + 2, n_chunks - 1), pa);
   }
 
   if (wave < KS) {
