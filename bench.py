@@ -798,7 +798,8 @@ def run_gdn_prefill(lengths=(800, 50000), reps=10, seed=8):
         o = torch.empty((N, GDN_H, DV), device=dev)
 
         def call(r):
-            had.gdn_prefill(pool, i_in, i_out, cu, q, k, v, gg, bb, o=o, workspace=ws, d_err=err, raw_gates=True)
+            had.gdn_prefill(pool, i_in, i_out, cu, q, k, v, gg, bb, max_len=N, o=o, workspace=ws, d_err=err,
+                            raw_gates=True)
 
         us = time_graph(torch, call, reps)
         if int(err.item()):

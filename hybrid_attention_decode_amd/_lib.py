@@ -655,6 +655,8 @@ def gdn_prefill(state_pool, in_idx, out_idx, cu_seqlens, q, k, v, alpha, beta, m
     N, H, d_k = q.shape
     n_seqs = cu_seqlens.numel() - 1
     if max_len is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise ValueError("gdn_prefill: pass max_len under graph capture (the default reads cu_seqlens to the host)")
         cu = cu_seqlens.cpu().numpy().astype(np.int64)
         max_len = int(max(1, (cu[1:] - cu[:-1]).max(initial=0)))
     if _debug():
