@@ -1,13 +1,14 @@
 // Hybrid prefix cache: radix tree over token ids with KV pages on every node
 // and GDN state slots (checkpoints) on the nodes where a state was saved.
 //
-// The engine matches cached prefixes in a radix tree whose nodes carry
-// Mamba-slot attachments, over its C++ logical cache, and reuses cached
-// states by copy-on-write (24-ai.news TokenSpeed article, optimisation list,
-// hybrid prefix caching; zubnet.ai TokenSpeed article, second paragraph).
-// A hybrid model resumes a request only where both the KV and the recurrent
-// state of the prefix exist, so a match ends at the deepest node of the
-// query's path that holds a slot.
+// Hybrid prefix caching (24-ai.news TokenSpeed article, optimisation list;
+// zubnet.ai TokenSpeed article, second paragraph): the host-side logical
+// cache keeps KV pages and saved recurrent states of past requests, and
+// shares both without ever writing them (a writer copies a shared page
+// first; a state slot is read by index and never overwritten).  A hybrid
+// model can resume a request only where both the KV and the recurrent state
+// of the prefix exist, so a match ends at the deepest node of the query's
+// path that holds a slot.
 //
 // Node layout: a node covers the token depths [start, end) of its edge and
 // holds the physical pages of the page indices [start / P, ceil(end / P)).

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
   const int n = min(kC, len - c * kC);                  // tokens of this chunk
   if (n <= 0) return;
   const int base = tok0 + c * kC;
-  u32x4_t* ws = a.ws + (static_cast<size_t>(s * a.max_chunks + c) * a.H + h) * L::TOTAL;
+  u32x4_t* ws = a.ws + ((static_cast<size_t>(s) * a.max_chunks + c) * a.H + h) * L::TOTAL;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const size_t rstride = static_cast<size_t>(a.H) * DK;  // between tokens of q / k
 
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
       f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(src + 32 * ks);
       f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(src + 32 * ks + 16);
-      if (in < 0) p0 = p1 = sown[0];
+      if (in < 0) p0 = p1 = f32x4_t{0.f, 0.f, 0.f, 0.f};  // no input slot: zero state
       float x8[8];
       cat8(p0, p1, x8);
       split8(x8, shi[ks], slo[ks]);
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
     split8(x8, ohi, olo);
   }
 
-  u32x4_t* blk0 = a.ws + static_cast<size_t>(s * a.max_chunks) * a.H * L::TOTAL + static_cast<size_t>(h) * L::TOTAL;
+  u32x4_t* blk0 = a.ws + static_cast<size_t>(s) * a.max_chunks * a.H * L::TOTAL + static_cast<size_t>(h) * L::TOTAL;
 
   // A chunk's operands, loaded one chunk ahead (none depends on the state).
   // Every load is unconditional: a load under a branch would make the join
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
   const int n = min(kC, len - c * kC);
   if (n <= 0) return;
   const int base = tok0 + c * kC;
-  const u32x4_t* blk = a.ws + (static_cast<size_t>(s * a.max_chunks + c) * a.H + h) * L::TOTAL;
+  const u32x4_t* blk = a.ws + ((static_cast<size_t>(s) * a.max_chunks + c) * a.H + h) * L::TOTAL;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
 
   __shared__ u32x4_t sc[VT][KS][2][64];  // S0 B operands [v-slice][d_k step][hi, lo][lane]
