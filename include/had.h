@@ -2,13 +2,18 @@
  * had.h -- C ABI of the hybrid-attention decode library (libhad.so), gfx950.
  *
  * One decode step of a hybrid model (full-attention layers interleaved with
- * Gated DeltaNet layers) as four groups of calls:
+ * Gated DeltaNet layers) as these groups of calls:
  *
- *   kv_page_table      host page-table / state-slot manager and two device
- *                      helpers that move KV rows (append, copy-on-write copy)
+ *   kv_page_table      host page-table / state-slot manager, speculative
+ *                      rollback, the hybrid prefix cache (radix tree), and
+ *                      two device helpers that move KV rows (append,
+ *                      copy-on-write copy)
  *   qk_norm_rope_gate  fused prologue of a full-attention layer
  *   decode_attn        split-K GQA decode attention over the paged KV cache
+ *                      (plus the shared-prefix "cascade" form and the layer
+ *                      entry point with the prologue fused in)
  *   gdn_state_update   gated delta rule update of slot-addressed states
+ *   gdn_prefill        the same recurrence over whole prompts, chunk-parallel
  *
  * Sources.  The system is the TokenSpeed inference engine described in a few
  * news articles: zubnet.ai (Spanish/French), second paragraph -- paged KV,
@@ -36,6 +41,12 @@
  *   stream: no hidden synchronisation, no host<->device copies.
  * - bf16 tensors are IEEE bfloat16 bit patterns; all tensors are dense,
  *   row-major, in the layout written next to each argument.
+ * - Alignment (the kernels load 8 or 16 bytes per lane): KV pools, q of the
+ *   attention calls, the new K/V rows of had_kv_append, every workspace, the
+ *   GDN state pools and the prefill's q, k, v must be 16-byte aligned, the
+ *   q and k of had_gdn_state_update 8-byte aligned; a misaligned pointer is
+ *   HAD_ERR_INVALID_ARG.  Allocator bases (hipMalloc, torch) always are;
+ *   only offset views can violate it.
  * - Device-side index checks: every kernel checks page ids against
  *   num_pages and slot ids against n_slots and skips (never dereferences) an
  *   out-of-range id.  If the optional d_err pointer (device int32) is not
@@ -192,13 +203,12 @@ int had_spec_rollback(had_kvpt *kv, had_slots *slots, int32_t seq, int32_t T,
 /* ----------------------------------------------------------------------
  * Hybrid prefix cache: a radix tree over token ids whose nodes hold the KV
  * pages of their token span and, where a state was saved, a GDN state slot
- * (the checkpoint of the recurrent layers at exactly that prefix length).
- * This is the engine's radix-tree matching with Mamba-slot attachments over
- * the C++ logical cache (24-ai.news TokenSpeed article, optimisation list,
- * hybrid prefix caching; zubnet.ai ¶2: cached checkpoints reused without
- * mutation by copy-on-write).  A hybrid model can resume only where both
- * the KV and the recurrent state exist, so a match ends at the deepest
- * node on the query's path that carries a slot.
+ * (the checkpoint of the recurrent layers at exactly that prefix length):
+ * the host-side half of hybrid prefix caching (24-ai.news TokenSpeed
+ * article, optimisation list; zubnet.ai ¶2, reuse of cached checkpoints
+ * without writing them).  A hybrid model can resume only where both the KV
+ * and the recurrent state exist, so a match ends at the deepest node on the
+ * query's path that carries a slot.
  *
  * The cache holds its own references on pages (had_kvpt_page_retain) and
  * slots (had_slots_retain); callers keep and release theirs as usual.
@@ -323,8 +333,10 @@ int had_qk_norm_rope_gate(const had_qknrg_desc *d, const had_qknrg_ptrs *p, void
  * model (24-ai.news, model paragraph) at contexts up to 1M tokens
  * (long-context table).
  *
- * Work is split over the context ("split-K"): work unit (s, h, split)
- * covers pages [split*pps, (split+1)*pps) and writes an unnormalised partial
+ * Work is split over the context ("split-K"): of the n pages that
+ * max_seq_len can reach, work unit (s, h, split i of ns) covers pages
+ * [i*n/ns, (i+1)*n/ns) (balanced to within one page; pages_per_split of the
+ * plan = ceil(n/ns)) and writes an unnormalised partial
  * (o, m, l) to the workspace; a second kernel merges the partials by
  * log-sum-exp and writes bf16 (round to nearest even).  Query rows per KV
  * head = q_len * (H_q / H_kv); below 16 rows a VALU kernel runs, at 16 or
@@ -378,7 +390,8 @@ typedef struct {
                               * that had_qk_norm_rope_gate splits off)      */
 } had_attn_ptrs;
 
-/* Split plan for desc: number of splits and pages per split. */
+/* Split plan for desc: number of splits and the largest page count of a
+ * split (both depend on the descriptor only, never on device data). */
 int had_decode_attn_plan(const had_attn_desc *d, int32_t *num_splits, int32_t *pages_per_split);
 size_t had_decode_attn_workspace_bytes(const had_attn_desc *d);
 int had_decode_attn(const had_attn_desc *d, const had_attn_ptrs *p, void *stream);
@@ -532,6 +545,8 @@ int had_gdn_check_slots(int32_t n_seqs, int32_t T, int32_t n_slots, const int32_
  * to rounding (fp32 accumulation; relative error ~1e-5 per chunk).
  *
  * Shapes: d_k, d_v in {64, 128}; any H; 0 <= length <= max_len.
+ * state_pool, q, k, v and the workspace must be 16-byte aligned
+ * (HAD_ERR_INVALID_ARG otherwise).
  * Preconditions (not checked on device): no slot is written by two
  * sequences, and no slot a sequence writes is read by another sequence.
  * Device errors: HAD_DERR_SLOT (slot out of range: the sequence is skipped),
