@@ -174,8 +174,9 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int t = min(t0 + i, last_tok) % P;  // the group never leaves its page (P % TPT == 0)
-      kr[i] = *reinterpret_cast<const u32x4_t*>(kb + t * D);
-      vr[i] = *reinterpret_cast<const u32x4_t*>(vb + t * D);
+      // non-temporal: the context streams through once per launch (as in the VALU kernel)
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + t * D));
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + t * D));
     }
     __builtin_amdgcn_sched_barrier(0);
   };

@@ -81,10 +81,17 @@ struct Lds {
 };
 
 // K and V of one 8-token tile: page `pid`, tile `tip` inside the page.
+// The loads carry the non-temporal hint: every K/V byte is read once per
+// launch, and streaming the context through the caches would evict what the
+// rest of the decode step reuses (recurrent states, page tables, the
+// partials the merge reads); measured on the 48-layer step it is also the
+// faster stream (1M context: 6.4 instead of 5.8 TB/s).
 template <int D>
 __device__ __forceinline__ void load_tile_at(Tile<D>& T, const ValuArgs& a, int pid, int tip, int h, int tg, int j,
                                              int tgv, int dl) {
   using C = Cfg<D>;
+  typedef uint32_t nt4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t nt2_t __attribute__((ext_vector_type(2)));
   const int pu = __builtin_amdgcn_readfirstlane(pid);
   const size_t base = ((static_cast<size_t>(pu) * a.H_kv + h) * a.page_size + tip * kTT) * D;
   const uint16_t* kb = a.k_pool + base;
@@ -92,11 +99,16 @@ __device__ __forceinline__ void load_tile_at(Tile<D>& T, const ValuArgs& a, int 
 #pragma unroll
   for (int i = 0; i < C::TS; ++i)
 #pragma unroll
-    for (int c = 0; c < C::CH; ++c)
-      T.k[i][c] = *reinterpret_cast<const uint4*>(kb + (i * C::TPS + tg) * D + (j + c * C::LPT) * 8);
+    for (int c = 0; c < C::CH; ++c) {
+      const nt4_t x = __builtin_nontemporal_load(
+          reinterpret_cast<const nt4_t*>(kb + (i * C::TPS + tg) * D + (j + c * C::LPT) * 8));
+      T.k[i][c] = make_uint4(x.x, x.y, x.z, x.w);
+    }
 #pragma unroll
-  for (int i = 0; i < C::VPL; ++i)
-    T.v[i] = *reinterpret_cast<const uint2*>(vb + (tgv + C::TG * i) * D + dl * C::DPL);
+  for (int i = 0; i < C::VPL; ++i) {
+    const nt2_t x = __builtin_nontemporal_load(reinterpret_cast<const nt2_t*>(vb + (tgv + C::TG * i) * D + dl * C::DPL));
+    T.v[i] = make_uint2(x.x, x.y);
+  }
 }
 
 template <int D, bool FUSED>
