@@ -641,12 +641,17 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
     cst = cache.stats()
     res["prefix_cache"] = dict(turn_boundaries=len(host_us), hit_rate=round(cst["matched_tokens"] / cst["queried_tokens"], 5),
                                nodes=cst["nodes"], checkpoints=cst["checkpoints"], cached_tokens=cst["cached_tokens"],
-                               host_us_per_boundary=round(float(np.mean(host_us)), 1), cow_copies=n_cow[0])
+                               host_us_per_boundary=round(float(np.mean(host_us)), 1),
+                               host_us_per_boundary_median=round(float(np.median(host_us)), 1),
+                               host_us_per_boundary_max=round(float(np.max(host_us)), 1), cow_copies=n_cow[0])
     for lk in locks:
         cache.unlock(lk)
     cache.close()
-    log("agentic: %.1f steps/s over %d steps; prefix cache hit rate %.4f, %.0f us of host work per turn boundary"
-        % (1e3 / ms, n_steps, res["prefix_cache"]["hit_rate"], res["prefix_cache"]["host_us_per_boundary"]))
+    log("agentic: %.1f steps/s over %d steps; prefix cache hit rate %.4f, host work per turn boundary %.0f us "
+        "(median %.0f, max %.0f)" % (1e3 / ms, n_steps, res["prefix_cache"]["hit_rate"],
+                                     res["prefix_cache"]["host_us_per_boundary"],
+                                     res["prefix_cache"]["host_us_per_boundary_median"],
+                                     res["prefix_cache"]["host_us_per_boundary_max"]))
     check_sentinel(st)
     del st
     torch.cuda.synchronize()

@@ -139,10 +139,10 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // go out first: one page-table entry per thread (a split owns at most
   // kMaxPagesPerSplit = blockDim pages) and one 8-byte piece of the kRows x D
   // query block per thread (loading q per wave instead would send every wave
-  // of the GPU to the same few L2 lines at kernel start).  Then the first two
-  // K/V tiles of this wave, whose page ids come from scalar loads, so they
-  // are in flight while the small loads are consumed and the workgroup
-  // synchronises.
+  // of the GPU to the same few L2 lines at kernel start).  Then the first
+  // K/V tile of this wave, whose page id comes from a scalar load, so it is
+  // in flight while the small loads are consumed; the second follows just
+  // before the workgroup synchronises.
   const int pt_val = pt_row[min(pg0 + static_cast<int>(threadIdx.x), a.max_pages - 1)];
   // fused: wave w owns query row w of the launch (and, in the workgroup that
   // holds the last position, the new token w's key row): raw rows first
@@ -169,9 +169,13 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
                (q_row < a.rows ? q_row : 0) % a.G) * D + q_c4 * 4);
 
   // The first two tiles of this wave.  A tile past the length or the split
-  // is loaded for nothing and never used.  (Issue order pinned: all of
-  // buffer 0, then all of buffer 1, the order the loop refills them in, so
-  // the wait counts inside the loop stay exact.)
+  // is loaded for nothing and never used.  Buffer 0 is requested here,
+  // buffer 1 just before the setup barrier: the small loads of the setup
+  // return behind whatever K/V requests the CUs issued before them, and with
+  // one tile per wave in the first burst (16 MB over the chip at head_dim
+  // 256) they come back sooner while the burst still keeps HBM busy.
+  // (Issue order: all of buffer 0, then all of buffer 1, the order the loop
+  // refills them in, so the wait counts inside the loop stay exact.)
   Tile<D> buf[2];
   int tcur[2] = {wave, wave + kWaves};
   // both page ids in one scalar round trip (the fences keep the two loads
@@ -184,11 +188,8 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
 #pragma unroll
   for (int b = 0; b < 2; ++b) pid0[b] = (pid0[b] < 0 || pid0[b] >= a.num_pages) ? 0 : pid0[b];
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    load_tile_at<D>(buf[b], a, pid0[b], tcur[b] % tpp, h, tg, j, tgv, dl);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  load_tile_at<D>(buf[0], a, pid0[0], tcur[0] % tpp, h, tg, j, tgv, dl);
+  __builtin_amdgcn_sched_barrier(0);
 
   const int L = a.seq_lens[s];  // (a scalar load: it does not queue behind the tiles)
 
@@ -262,6 +263,8 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   const int lim_min = FUSED ? L - a.q_len : L - a.q_len + 1;  // every row sees positions below this
   const int kv_end = FUSED ? L - a.q_len : L;                   // V rows at or past this are zeroed
 
+  load_tile_at<D>(buf[1], a, pid0[1], tcur[1] % tpp, h, tg, j, tgv, dl);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   // q rows in lane order: slot r holds row (r ^ sigma(j8)) of this launch
