@@ -90,7 +90,7 @@ class GdnPtrs(ctypes.Structure):
 
 class GdnPrefillDesc(ctypes.Structure):
     _fields_ = [("n_seqs", _i32), ("H", _i32), ("d_k", _i32), ("d_v", _i32), ("n_slots", _i32), ("max_len", _i32),
-                ("q_scale", ctypes.c_float), ("flags", _i32)]
+                ("q_scale", ctypes.c_float), ("flags", _i32), ("n_segments", _i32)]
 
 
 class GdnPrefillPtrs(ctypes.Structure):
@@ -628,10 +628,10 @@ def gdn_state_update(state_pool, in_idx, out_idx, q, k, v, alpha, beta, o=None, 
     return o
 
 
-def gdn_prefill_desc(state_shape, n_seqs, max_len, q_scale=1.0, raw_gates=False):
+def gdn_prefill_desc(state_shape, n_seqs, max_len, q_scale=1.0, raw_gates=False, n_segments=0):
     n_slots, H, d_v, d_k = state_shape
     return GdnPrefillDesc(n_seqs, H, d_k, d_v, n_slots, int(max_len), float(q_scale),
-                          GDN_RAW_GATES if raw_gates else 0)
+                          GDN_RAW_GATES if raw_gates else 0, int(n_segments))
 
 
 def gdn_prefill_workspace_bytes(desc):
@@ -642,14 +642,15 @@ def gdn_prefill_workspace_bytes(desc):
 
 
 def gdn_prefill(state_pool, in_idx, out_idx, cu_seqlens, q, k, v, alpha, beta, max_len=None, o=None, q_scale=1.0,
-                workspace=None, d_err=None, raw_gates=False):
+                workspace=None, d_err=None, raw_gates=False, n_segments=0):
     """Whole prompts through the gated delta rule, chunk-parallel.
     state_pool [n_slots, H, d_v, d_k] fp32; q, k [N, H, d_k], v [N, H, d_v] bf16 (sequences packed,
     token offsets cu_seqlens int32 [n_seqs + 1] on the device); alpha, beta [N, H] fp32;
     in_idx, out_idx int32 [n_seqs].  max_len bounds every sequence's length; the
     workspace holds n_seqs x ceil(max_len / 64) chunk blocks.  Default: the
     longest sequence, read from cu_seqlens (a device-to-host copy; pass
-    max_len to avoid it, e.g. under graph capture).
+    max_len to avoid it, e.g. under graph capture).  n_segments: scan
+    segments (0 = the library's choice; see had.h).
     Returns o [N, H, d_v] fp32; the final states land in slots out_idx."""
     torch = _torch()
     N, H, d_k = q.shape
@@ -661,7 +662,7 @@ def gdn_prefill(state_pool, in_idx, out_idx, cu_seqlens, q, k, v, alpha, beta, m
         max_len = int(max(1, (cu[1:] - cu[:-1]).max(initial=0)))
     if _debug():
         gdn_check_slots(state_pool.shape[0], in_idx, out_idx.reshape(-1, 1), True)
-    desc = gdn_prefill_desc(state_pool.shape, n_seqs, max_len, q_scale, raw_gates)
+    desc = gdn_prefill_desc(state_pool.shape, n_seqs, max_len, q_scale, raw_gates, n_segments)
     need = gdn_prefill_workspace_bytes(desc)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

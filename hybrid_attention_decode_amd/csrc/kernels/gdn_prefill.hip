@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../host/status.h"
 #include "had.h"
 #include "kcommon.h"
@@ -114,6 +116,24 @@ struct PrefillArgs {
   int32_t* d_err;
   int n_seqs, H, n_slots, max_len, max_chunks, raw_gates;
   float q_scale;
+  // segmented scan: the chunks of a sequence in n_segs runs of seg_chunks
+  // (the last may be shorter or empty); seg: per (sequence, segment, head)
+  // the fp32 blocks of SegL; phase 0 = one pass, 1 / 3 = the two scan
+  // passes of the segmented form (phase 2 is the link kernel)
+  float* seg;
+  int n_segs, seg_chunks, phase;
+};
+
+// Per (sequence, segment, head), fp32 [row][d_k] blocks of the segmented
+// scan: PI = the segment's transition (the state after the segment is
+// S_start PI + SE), SE = the state the segment reaches from zero, SS = the
+// state the segment starts from.
+template <int DK, int DV>
+struct SegL {
+  static constexpr size_t PI = 0;
+  static constexpr size_t SE = static_cast<size_t>(DK) * DK;
+  static constexpr size_t SS = SE + static_cast<size_t>(DV) * DK;
+  static constexpr size_t TOTAL = SS + static_cast<size_t>(DV) * DK;
 };
 
 // One 16-byte piece of a bf16 row (zeros for rows past the chunk).
@@ -361,17 +381,34 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
 // only what the state needs (W, K^T, U') is on this sequential path.  Per
 // chunk it leaves U (over U' in the workspace) and the chunk's initial
 // state (as B operands) for the output kernel.
+//
+// Segmented form (a long prompt with few heads: one pass would keep only
+// units x d_v/16 workgroups busy along a chain of every chunk).  With
+// S_{c+1} = S_c A_c + B_c per chunk, a run of chunks maps its start state
+// S to S PI + SE, PI = prod A_c (d_k x d_k) and SE the state reached from
+// zero.  Phase 1 scans every segment at once, twice over: the d_v state
+// rows from zero (giving SE) and the d_k rows of the identity with U' = 0
+// (giving PI), storing nothing per chunk; the link kernel chains the
+// segments' start states; phase 3 is the one-pass scan again, every segment
+// at once from its start state, storing U and the chunk states.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   using L = PL<DK, DV>;
-  constexpr int KS = L::KS, VT = L::VT;
-  // block -> (unit = s * H + h, v-slice): the v-slices of one unit share the
-  // unit's workspace blocks, so they go to one XCD (blocks are dealt to the
-  // 8 XCDs round robin)
+  using G = SegL<DK, DV>;
+  constexpr int KS = L::KS, VT = L::VT, DT = L::DT;
+  // block -> (item = (s * H + h) * n_segs + segment, slice): the slices of
+  // one item share the item's workspace blocks, so they go to one XCD
+  // (blocks are dealt to the 8 XCDs round robin).  Phase 1 has VT slices of
+  // state rows and DT of transition rows.
+  const int NSL = a.phase == 1 ? VT + DT : VT;
   const int b = blockIdx.x;
-  const int unit = (b / 8 / VT) * 8 + b % 8, vs = (b / 8) % VT;
-  if (unit >= a.n_seqs * a.H) return;
+  const int item = (b / 8 / NSL) * 8 + b % 8, vs = (b / 8) % NSL;
+  if (item >= a.n_seqs * a.H * a.n_segs) return;
+  const int seg = item % a.n_segs, unit = item / a.n_segs;
   const int s = unit / a.H, h = unit % a.H;
+  const bool pi_rows = vs >= VT;            // phase 1: rows of the transition
+  const int vsc = pi_rows ? VT - 1 : vs;    // (their U' loads read a real slice and are discarded)
+  const bool chunk_out = a.phase != 1;      // per-chunk U and states are stored
   // (wave is made uniform so that tests on it are scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
@@ -381,12 +418,17 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   const bool bad_len = tok0 < 0 || len < 0 || len > a.max_len;
   const bool bad_slot = in < -1 || in >= a.n_slots || out < 0 || out >= a.n_slots;
   if (bad_len || bad_slot) {
-    if (threadIdx.x == 0 && vs == 0) set_err(a.d_err, (bad_len ? HAD_DERR_SEQLEN : 0) | (bad_slot ? HAD_DERR_SLOT : 0));
+    if (threadIdx.x == 0 && vs == 0 && seg == 0)
+      set_err(a.d_err, (bad_len ? HAD_DERR_SEQLEN : 0) | (bad_slot ? HAD_DERR_SLOT : 0));
     return;
   }
+  // this block's chunks [c0, c1): the whole sequence, or its segment
   const int n_chunks = (len + kC - 1) / kC;
+  const int c0 = min(seg * a.seg_chunks, n_chunks);
+  const int c1 = a.n_segs > 1 ? min(c0 + a.seg_chunks, n_chunks) : n_chunks;
   const size_t slot_elems = static_cast<size_t>(a.H) * DV * DK;
-  const size_t row_off = (static_cast<size_t>(h) * DV + 16 * vs + r16) * DK;
+  const size_t row_off = (static_cast<size_t>(h) * DV + 16 * vsc + r16) * DK;
+  float* segb = a.seg + ((static_cast<size_t>(s) * a.n_segs + seg) * a.H + h) * G::TOTAL;
 
   __shared__ f32x4_t ubuf[4][64];         // U tiles of the chunk (result layout)
   __shared__ u32x4_t sbuf[KS][2][64];     // new state as B operands (hi, lo) per d_k step
@@ -401,20 +443,37 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   u32x4_t shi[KS], slo[KS], ohi, olo;
   f32x4_t sown[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   {
-    const float* src = a.pool + static_cast<size_t>(max(in, 0)) * slot_elems + row_off + 4 * g;
+    // start state: the input slot (one pass), zero or the identity rows
+    // (phase 1), the segment's start state (phase 3; the link kernel wrote
+    // every segment's, the first included)
+    const float* src = a.phase == 3 ? segb + G::SS + static_cast<size_t>(16 * vs + r16) * DK
+                                    : a.pool + static_cast<size_t>(max(in, 0)) * slot_elems + row_off;
+    const bool zero = a.phase == 0 && in < 0;
+    const int id_row = 16 * (vs - VT) + r16;  // phase 1, transition rows: row of the identity
+    // columns col0 .. +3 and col0 + 16 .. +3 of this lane's row
+    auto start = [&](int col0, f32x4_t& p0, f32x4_t& p1) {
+      if (a.phase == 1) {
+        const float on = pi_rows ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p0[j] = (col0 + j == id_row) ? on : 0.f;
+          p1[j] = (col0 + 16 + j == id_row) ? on : 0.f;
+        }
+      } else {
+        p0 = *reinterpret_cast<const f32x4_t*>(src + col0);
+        p1 = *reinterpret_cast<const f32x4_t*>(src + col0 + 16);
+        if (zero) p0 = p1 = f32x4_t{0.f, 0.f, 0.f, 0.f};  // no input slot: zero state
+      }
+    };
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(src + 32 * ks);
-      f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(src + 32 * ks + 16);
-      if (in < 0) p0 = p1 = f32x4_t{0.f, 0.f, 0.f, 0.f};  // no input slot: zero state
+      f32x4_t p0, p1;
+      start(32 * ks + 4 * g, p0, p1);
       float x8[8];
       cat8(p0, p1, x8);
       split8(x8, shi[ks], slo[ks]);
     }
-    if (in >= 0) {
-      sown[0] = *reinterpret_cast<const f32x4_t*>(src + 32 * kw);
-      sown[1] = *reinterpret_cast<const f32x4_t*>(src + 32 * kw + 16);
-    }
+    start(32 * kw + 4 * g, sown[0], sown[1]);
     float x8[8];
     cat8(sown[0], sown[1], x8);
     split8(x8, ohi, olo);
@@ -445,7 +504,8 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   auto load_rest = [&](int c, Ops& p) {
     const u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
     const float* gw = reinterpret_cast<const float*>(blk + L::GAM);
-    p.up = __builtin_bit_cast(f32x4_t, blk[L::UP + (wave * VT + vs) * 64 + lane]);
+    p.up = __builtin_bit_cast(f32x4_t, blk[L::UP + (wave * VT + vsc) * 64 + lane]);
+    if (pi_rows) p.up = f32x4_t{0.f, 0.f, 0.f, 0.f};  // the transition: U' = 0
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -480,7 +540,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
     load_rest(cn, pn);
     const f32x4_t U = p.up - (X0 + (X1 + X2));
     ubuf[wave][lane] = U;
-    blk[L::UP + (wave * VT + vs) * 64 + lane] = __builtin_bit_cast(u32x4_t, U);  // U replaces U'
+    if (chunk_out) blk[L::UP + (wave * VT + vs) * 64 + lane] = __builtin_bit_cast(u32x4_t, U);  // U replaces U'
     __syncthreads();
 
     // S_C columns of d_k step `wave`: gamma_C S0 + K^T diag(gamma_C / gamma) U,
@@ -514,7 +574,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
       split8(x8, ohi, olo);
       sbuf[wave][0][lane] = ohi;
       sbuf[wave][1][lane] = olo;
-      if (c + 1 < n_chunks) store_sc(c + 1);
+      if (chunk_out && c + 1 < c1) store_sc(c + 1);
     }
     __syncthreads();
 #pragma unroll
@@ -527,21 +587,73 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   // chunk c + 1's operands load while chunk c computes (two register sets;
   // the last chunk reloads itself so that no load sits under a branch)
   Ops pa, pb;
-  if (n_chunks > 0) {
-    load_w(0, pa);
-    load_rest(0, pa);
-    if (wave < KS) store_sc(0);
+  if (c1 > c0) {
+    load_w(c0, pa);
+    load_rest(c0, pa);
+    if (chunk_out && wave < KS) store_sc(c0);
   }
-  for (int c = 0; c < n_chunks; c += 2) {
-    step(c, pa, min(c + 1, n_chunks - 1), pb);
-    if (c + 1 >= n_chunks) break;
-    step(c + 1, pb, min(c + 2, n_chunks - 1), pa);
+  for (int c = c0; c < c1; c += 2) {
+    step(c, pa, min(c + 1, c1 - 1), pb);
+    if (c + 1 >= c1) break;
+    step(c + 1, pb, min(c + 2, c1 - 1), pa);
   }
 
-  if (wave < KS) {
-    float* dst = a.pool + static_cast<size_t>(out) * slot_elems + row_off + 32 * wave + 4 * g;
+  // end state: the output slot (one pass, and the last segment of phase 3),
+  // or the segment's SE / PI rows (phase 1)
+  if (wave < KS && !(a.phase == 3 && seg != a.n_segs - 1)) {
+    float* dst = a.phase == 1 ? segb + (pi_rows ? G::PI + static_cast<size_t>(16 * (vs - VT) + r16) * DK
+                                                : G::SE + static_cast<size_t>(16 * vs + r16) * DK) +
+                                    32 * wave + 4 * g
+                              : a.pool + static_cast<size_t>(out) * slot_elems + row_off + 32 * wave + 4 * g;
     *reinterpret_cast<f32x4_t*>(dst) = sown[0];
     *reinterpret_cast<f32x4_t*>(dst + 16) = sown[1];
+  }
+}
+
+// Segmented scan, phase 2: the start state of every segment,
+//   SS(0) = S_in,  SS(g + 1) = SS(g) PI(g) + SE(g),
+// in fp32 for state rows 16 vs .. +15 of one (sequence, head).  PI(g) passes
+// through LDS; thread t owns row t / 16 and d_k / 16 columns.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_prefill_link_kernel(PrefillArgs a) {
+  using G = SegL<DK, DV>;
+  constexpr int NCOL = DK / 16;  // columns per thread
+  const int vs = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
+  const int in = a.in_idx[s], out = a.out_idx[s];
+  if (tok0 < 0 || len < 0 || len > a.max_len) return;                       // the scan reports it
+  if (in < -1 || in >= a.n_slots || out < 0 || out >= a.n_slots) return;
+  __shared__ __align__(16) float pis[DK][DK];
+  __shared__ float srow[16][DK + 1];
+  const int t = threadIdx.x, r = t / 16, col0 = (t % 16) * NCOL;
+  const size_t seg_stride = static_cast<size_t>(a.H) * G::TOTAL;  // between segments of one (s, h)
+  float* base = a.seg + (static_cast<size_t>(s) * a.n_segs * a.H + h) * G::TOTAL;
+  const size_t row = static_cast<size_t>(16 * vs + r) * DK;
+  float acc[NCOL];
+  {
+    const float* src = a.pool + (static_cast<size_t>(max(in, 0)) * a.H + h) * DV * DK + row + col0;
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) acc[j] = in >= 0 ? src[j] : 0.f;
+  }
+  for (int g = 0;; ++g) {
+    float* sg = base + g * seg_stride;
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) {
+      sg[G::SS + row + col0 + j] = acc[j];
+      srow[r][col0 + j] = acc[j];
+    }
+    if (g + 1 >= a.n_segs) break;
+    for (int i = t; i < DK * DK / 4; i += 256)
+      reinterpret_cast<f32x4_t*>(&pis[0][0])[i] = reinterpret_cast<const f32x4_t*>(sg + G::PI)[i];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) acc[j] = sg[G::SE + row + col0 + j];
+    for (int k = 0; k < DK; ++k) {
+      const float x = srow[r][k];
+#pragma unroll
+      for (int j = 0; j < NCOL; ++j) acc[j] = fmaf(x, pis[k][col0 + j], acc[j]);
+    }
+    __syncthreads();
   }
 }
 
@@ -642,20 +754,63 @@ int check(const had_gdn_prefill_desc* d) {
   if ((d->d_k != 64 && d->d_k != 128) || (d->d_v != 64 && d->d_v != 128))
     return fail(HAD_ERR_UNSUPPORTED_SHAPE, "gdn_prefill: d_k=%d d_v=%d (supported: 64, 128)", d->d_k, d->d_v);
   if (d->flags & ~HAD_GDN_RAW_GATES) return fail(HAD_ERR_INVALID_ARG, "gdn_prefill: unknown flags 0x%x", d->flags);
+  if (d->n_segments < 0) return fail(HAD_ERR_INVALID_ARG, "gdn_prefill: n_segments %d < 0", d->n_segments);
   return HAD_OK;
 }
 
+// Segments of the scan.  One pass keeps n_seqs x H x d_v/16 workgroups busy
+// along a chain of every chunk; segments run side by side at the price of a
+// second scan pass (twice the rows: the transition) and the link.  Worth it
+// for long prompts that leave most CUs idle: chains of >= 32 chunks, and
+// at most 512 one-pass workgroups (two per CU).
+int plan_segments(const had_gdn_prefill_desc* d) {
+  const int chunks = (d->max_len + kC - 1) / kC;
+  int g;
+  if (d->n_segments > 0) {
+    g = d->n_segments;
+  } else {
+    const int per_seg = d->n_seqs * d->H * (d->d_v / 16);
+    g = std::min(chunks / 32, 512 / std::max(per_seg, 1));
+  }
+  return std::max(1, std::min(g, std::max(chunks, 1)));
+}
+
+size_t chunk_bytes(const had_gdn_prefill_desc* d) {
+  const size_t chunks = static_cast<size_t>((d->max_len + kC - 1) / kC);
+  return (static_cast<size_t>(d->n_seqs) * chunks * d->H * block_bytes(d->d_k, d->d_v) + 255) & ~size_t(255);
+}
+
+size_t seg_bytes(const had_gdn_prefill_desc* d) {
+  const int g = plan_segments(d);
+  if (g < 2) return 0;
+  const size_t per = static_cast<size_t>(d->d_k) * d->d_k + 2 * static_cast<size_t>(d->d_v) * d->d_k;
+  return static_cast<size_t>(d->n_seqs) * g * d->H * per * sizeof(float);
+}
+
 template <int DK, int DV>
-int launch(const had_gdn_prefill_desc* d, const PrefillArgs& a, hipStream_t st) {
+int launch(const had_gdn_prefill_desc* d, PrefillArgs a, hipStream_t st) {
   if (a.max_chunks > 0) {
     hipLaunchKernelGGL((gdn_prefill_prep_kernel<DK, DV>), dim3(a.max_chunks, d->H, d->n_seqs), dim3(256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: prep launch: %s", hipGetErrorString(e));
   }
-  const int units = d->n_seqs * d->H;
-  const int blocks = (units + 7) / 8 * 8 * (DV / 16);
-  hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3(blocks), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
+  const int items = d->n_seqs * d->H * a.n_segs;
+  hipError_t e;
+  if (a.n_segs > 1) {
+    a.phase = 1;
+    hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3((items + 7) / 8 * 8 * (DV / 16 + DK / 16)), dim3(256),
+                       0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: segment scan launch: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL((gdn_prefill_link_kernel<DK, DV>), dim3(DV / 16, d->H, d->n_seqs), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: link launch: %s", hipGetErrorString(e));
+    a.phase = 3;
+  } else {
+    a.phase = 0;
+  }
+  hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3((items + 7) / 8 * 8 * (DV / 16)), dim3(256), 0, st, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: scan launch: %s", hipGetErrorString(e));
   if (a.max_chunks > 0) {
     hipLaunchKernelGGL((gdn_prefill_out_kernel<DK, DV>), dim3(a.max_chunks, d->H, d->n_seqs), dim3(256), 0, st, a);
@@ -672,8 +827,7 @@ extern "C" {
 
 size_t had_gdn_prefill_workspace_bytes(const had_gdn_prefill_desc* d) {
   if (had::check(d) != HAD_OK) return 0;
-  const size_t chunks = static_cast<size_t>((d->max_len + had::kC - 1) / had::kC);
-  return static_cast<size_t>(d->n_seqs) * chunks * d->H * had::block_bytes(d->d_k, d->d_v);
+  return had::chunk_bytes(d) + had::seg_bytes(d);
 }
 
 int had_gdn_prefill(const had_gdn_prefill_desc* d, const had_gdn_prefill_ptrs* p, void* stream) {
@@ -709,6 +863,9 @@ int had_gdn_prefill(const had_gdn_prefill_desc* d, const had_gdn_prefill_ptrs* p
   a.max_chunks = (d->max_len + had::kC - 1) / had::kC;
   a.raw_gates = (d->flags & HAD_GDN_RAW_GATES) ? 1 : 0;
   a.q_scale = d->q_scale;
+  a.n_segs = had::plan_segments(d);
+  a.seg_chunks = (a.max_chunks + a.n_segs - 1) / a.n_segs;
+  a.seg = a.n_segs > 1 ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) + had::chunk_bytes(d)) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d->d_k == 128 && d->d_v == 128) st = had::launch<128, 128>(d, a, s);
   else if (d->d_k == 128) st = had::launch<128, 64>(d, a, s);

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define HAD_ABI_VERSION 2
+#define HAD_ABI_VERSION 3
 
 enum {
   HAD_OK = 0,
@@ -541,8 +541,13 @@ int had_gdn_check_slots(int32_t n_seqs, int32_t T, int32_t n_slots, const int32_
  * a chunk-parallel kernel forms each chunk's triangular solve and
  * state-independent products, then a scan kernel carries the state across
  * the chunks of a sequence (MFMA; state kept in fp32, its matrix products
- * in split bf16 pairs).  The result equals the token-by-token recurrence up
- * to rounding (fp32 accumulation; relative error ~1e-5 per chunk).
+ * in split bf16 pairs).  For long prompts the scan runs in segments side by
+ * side: each segment's map S -> S PI + SE (PI the d_k x d_k product of the
+ * chunks' transitions, SE the state reached from zero) is scanned first,
+ * the segments' start states are chained (fp32), and the segments are
+ * scanned again from their start states.  The result equals the
+ * token-by-token recurrence up to rounding (fp32 accumulation; relative
+ * error ~1e-5 per chunk).
  *
  * Shapes: d_k, d_v in {64, 128}; any H; 0 <= length <= max_len.
  * state_pool, q, k, v and the workspace must be 16-byte aligned
@@ -559,6 +564,10 @@ typedef struct {
   int32_t max_len;           /* host bound on every sequence's length      */
   float q_scale;
   int32_t flags;             /* HAD_GDN_RAW_GATES                          */
+  int32_t n_segments;        /* scan segments (>= 0; 0 = automatic: one     *
+                              * unless the prompt spans >= 64 chunks and   *
+                              * n_seqs x H x d_v/16 <= 256; capped at the  *
+                              * chunk count)                               */
 } had_gdn_prefill_desc;
 
 typedef struct {
@@ -576,7 +585,9 @@ typedef struct {
 } had_gdn_prefill_ptrs;
 
 /* Workspace: per (sequence, chunk of 64 tokens up to max_len, head) the
- * chunk's solve results; 0 for an invalid descriptor. */
+ * chunk's solve results, and with segments per (sequence, segment, head)
+ * three fp32 d_k-wide blocks (PI, SE, the start state); 0 for an invalid
+ * descriptor. */
 size_t had_gdn_prefill_workspace_bytes(const had_gdn_prefill_desc *d);
 int had_gdn_prefill(const had_gdn_prefill_desc *d, const had_gdn_prefill_ptrs *p, void *stream);
 

@@ -31,21 +31,22 @@ def _pool(seed, n_slots, H, dk, dv):
     return synth.normal_f32((n_slots, H, dv, dk), synth.seed_of(seed, 6)) * 0.1
 
 
-def _run(seed, lens, H, dk, dv, in_idx, out_idx, n_slots, raw=False, q_scale=1.0, max_len=None):
+def _run(seed, lens, H, dk, dv, in_idx, out_idx, n_slots, raw=False, q_scale=1.0, max_len=None, n_segments=0,
+         alpha_lo=0.9):
     N = int(sum(lens))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    q, k, v, al, be = _inputs(seed, N, H, dk, dv)
+    q, k, v, al, be = _inputs(seed, N, H, dk, dv, alpha_lo)
     if raw:  # raw gate values: the kernel forms exp(g) and sigmoid(b)
         al = -synth.uniform_f32((N, H), 0.0, 0.1, synth.seed_of(seed, 7))
         be = synth.uniform_f32((N, H), -3.0, 3.0, synth.seed_of(seed, 8))
     pool = _pool(seed, n_slots, H, dk, dv)
-    print("case seed=%d lens=%s H=%d dk=%d dv=%d in=%s out=%s raw=%d" % (seed, list(lens), H, dk, dv, in_idx, out_idx,
-                                                                         raw), flush=True)
+    print("case seed=%d lens=%s H=%d dk=%d dv=%d in=%s out=%s raw=%d segments=%d" % (
+        seed, list(lens), H, dk, dv, in_idx, out_idx, raw, n_segments), flush=True)
     pd = to_dev(pool)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     o = had.gdn_prefill(pd, to_dev(np.asarray(in_idx, np.int32)), to_dev(np.asarray(out_idx, np.int32)), to_dev(cu),
                         to_dev(q), to_dev(k), to_dev(v), to_dev(al), to_dev(be), max_len=max_len, q_scale=q_scale,
-                        d_err=err, raw_gates=raw)
+                        d_err=err, raw_gates=raw, n_segments=n_segments)
     torch.cuda.synchronize()
     alpha, beta = al.numpy().astype(np.float64), be.numpy().astype(np.float64)
     if raw:
@@ -107,6 +108,46 @@ def test_raw_gates():
 def test_loose_max_len_bound():
     # max_len well above the real lengths: chunks past a sequence do nothing
     c = _run(4400, [70, 10], 2, 128, 128, [1, 1], [0, 2], 3, max_len=1000)
+    _check(c)
+
+
+@pytest.mark.parametrize("lens,H,dk,dv,segs,max_len", [
+    ([640], 2, 128, 128, 2, None),          # two segments of 5 chunks
+    ([700, 77], 2, 128, 128, 3, None),      # ragged; the short sequence leaves segments empty
+    ([1000], 1, 64, 128, 5, 1280),          # loose bound: the last segments are empty
+    ([333, 0, 901], 2, 128, 64, 8, None),   # an empty sequence, d_v 64; one chunk per segment and less
+    ([520], 3, 64, 64, 9, None),            # more segments than a sequence has chunks to spare
+])
+def test_segmented_scan_matches_oracle(lens, H, dk, dv, segs, max_len):
+    n = len(lens)
+    in_idx = [-1] + [2 * i + 1 for i in range(1, n)]
+    out_idx = [2 * i for i in range(n)]
+    c = _run(4700 + sum(lens) + segs, lens, H, dk, dv, in_idx, out_idx, 2 * n + 1, max_len=max_len,
+             n_segments=segs)
+    _check(c)
+
+
+def test_segmented_scan_in_place_raw_gates():
+    # segments with an in-place slot update (the link reads the input slot
+    # before any segment writes the output slot) and raw gates
+    c = _run(4800, [900, 450], 4, 128, 128, [2, 0], [2, 1], 3, raw=True, n_segments=4)
+    _check(c)
+
+
+def test_segmented_scan_weak_decay():
+    # alpha in [0.999, 1]: the state keeps its history across segments, so
+    # each segment's transition (near the identity) carries it and the link
+    # is exercised, not just a state that has forgotten its start
+    c = _run(4850, [1500], 2, 128, 128, [1], [0], 2, n_segments=6, alpha_lo=0.999)
+    _check(c)
+
+
+def test_segments_chosen_automatically_for_a_long_prompt():
+    # one 4,096-token prompt with 2 heads: the plan segments the scan
+    desc = had.gdn_prefill_desc((2, 2, 128, 128), 1, 4096)
+    one = had.gdn_prefill_desc((2, 2, 128, 128), 1, 4096, n_segments=1)
+    assert had.gdn_prefill_workspace_bytes(desc) > had.gdn_prefill_workspace_bytes(one)
+    c = _run(4900, [4096], 2, 128, 128, [0], [1], 2)
     _check(c)
 
 

@@ -98,9 +98,12 @@ def test_decode_layer_pair_replays_equal_eager_runs():
             assert np.array_equal(bits_of(x), bits_of(y), equal_nan=True)
 
 
-def test_gdn_prefill_replays_equal_eager_runs():
+@pytest.mark.parametrize("n_segments", [0, 3])
+def test_gdn_prefill_replays_equal_eager_runs(n_segments):
     # the prefill captured once for a max_len bound, replayed on different
-    # packings of the same token buffer (cu_seqlens and slots change)
+    # packings of the same token buffer (cu_seqlens and slots change); also
+    # with the scan in segments (its link reads the input slot, the last
+    # segment writes the output slot)
     H, DK, DV, N = 4, 128, 128, 700
     q = to_dev(synth.l2_normalised_bf16((N, H, DK), synth.seed_of(7100, 1)))
     k = to_dev(synth.l2_normalised_bf16((N, H, DK), synth.seed_of(7100, 2)))
@@ -115,11 +118,12 @@ def test_gdn_prefill_replays_equal_eager_runs():
     pool = pool0.clone()
     o = torch.zeros((N, H, DV), dtype=torch.float32, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    desc = had.gdn_prefill_desc(pool.shape, 2, max_len)
+    desc = had.gdn_prefill_desc(pool.shape, 2, max_len, n_segments=n_segments)
     ws = torch.empty(had.gdn_prefill_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
 
     def run(pool_, cu_, in_, out_, o_, ws_):
-        had.gdn_prefill(pool_, in_, out_, cu_, q, k, v, al, be, max_len=max_len, o=o_, workspace=ws_, d_err=err)
+        had.gdn_prefill(pool_, in_, out_, cu_, q, k, v, al, be, max_len=max_len, o=o_, workspace=ws_, d_err=err,
+                        n_segments=n_segments)
 
     cu.copy_(torch.tensor([0, 300, 700], dtype=torch.int32))
     i_in.copy_(torch.tensor([0, -1], dtype=torch.int32))
@@ -127,7 +131,7 @@ def test_gdn_prefill_replays_equal_eager_runs():
     g = _capture(lambda: run(pool, cu, i_in, i_out, o, ws))
     for rep, (c, a, b) in enumerate([([0, 300, 700], [0, -1], [1, 2]), ([0, 64, 464], [3, 3], [4, 5]),
                                      ([0, 0, 1], [-1, 2], [0, 1]), ([0, 399, 700], [5, 4], [5, 3])]):
-        print("case prefill replay %d: cu=%s in=%s out=%s" % (rep, c, a, b), flush=True)
+        print("case prefill replay %d (segments %d): cu=%s in=%s out=%s" % (rep, n_segments, c, a, b), flush=True)
         pool.copy_(pool0)
         o.zero_()
         err.zero_()
