@@ -386,11 +386,13 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
 // units x d_v/16 workgroups busy along a chain of every chunk).  With
 // S_{c+1} = S_c A_c + B_c per chunk, a run of chunks maps its start state
 // S to S PI + SE, PI = prod A_c (d_k x d_k) and SE the state reached from
-// zero.  Phase 1 scans every segment at once, twice over: the d_v state
-// rows from zero (giving SE) and the d_k rows of the identity with U' = 0
-// (giving PI), storing nothing per chunk; the link kernel chains the
-// segments' start states; phase 3 is the one-pass scan again, every segment
-// at once from its start state, storing U and the chunk states.
+// zero.  Phase 1 scans every segment but the last at once, twice over: the
+// d_v state rows from zero (giving SE; the first segment starts from the
+// input state instead, so its SE is the second segment's start state) and,
+// past the first segment, the d_k rows of the identity with U' = 0 (giving
+// PI), storing nothing per chunk; the link kernel chains the segments'
+// start states; phase 3 is the one-pass scan again, every segment at once
+// from its start state, storing U and the chunk states.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   using L = PL<DK, DV>;
@@ -401,12 +403,14 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
   // (blocks are dealt to the 8 XCDs round robin).  Phase 1 has VT slices of
   // state rows and DT of transition rows.
   const int NSL = a.phase == 1 ? VT + DT : VT;
+  const int n_items_seg = a.phase == 1 ? a.n_segs - 1 : a.n_segs;  // phase 1 skips the last segment
   const int b = blockIdx.x;
   const int item = (b / 8 / NSL) * 8 + b % 8, vs = (b / 8) % NSL;
-  if (item >= a.n_seqs * a.H * a.n_segs) return;
-  const int seg = item % a.n_segs, unit = item / a.n_segs;
+  if (item >= a.n_seqs * a.H * n_items_seg) return;
+  const int seg = item % n_items_seg, unit = item / n_items_seg;
   const int s = unit / a.H, h = unit % a.H;
   const bool pi_rows = vs >= VT;            // phase 1: rows of the transition
+  if (a.phase == 1 && pi_rows && seg == 0) return;  // the first segment's transition is not needed
   const int vsc = pi_rows ? VT - 1 : vs;    // (their U' loads read a real slice and are discarded)
   const bool chunk_out = a.phase != 1;      // per-chunk U and states are stored
   // (wave is made uniform so that tests on it are scalar branches)
@@ -448,11 +452,12 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
     // every segment's, the first included)
     const float* src = a.phase == 3 ? segb + G::SS + static_cast<size_t>(16 * vs + r16) * DK
                                     : a.pool + static_cast<size_t>(max(in, 0)) * slot_elems + row_off;
-    const bool zero = a.phase == 0 && in < 0;
+    const bool from_slot = a.phase == 0 || (a.phase == 1 && seg == 0 && !pi_rows);
+    const bool zero = from_slot && in < 0;
     const int id_row = 16 * (vs - VT) + r16;  // phase 1, transition rows: row of the identity
     // columns col0 .. +3 and col0 + 16 .. +3 of this lane's row
     auto start = [&](int col0, f32x4_t& p0, f32x4_t& p1) {
-      if (a.phase == 1) {
+      if (a.phase == 1 && !from_slot) {
         const float on = pi_rows ? 1.f : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -611,31 +616,50 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
 }
 
 // Segmented scan, phase 2: the start state of every segment,
-//   SS(0) = S_in,  SS(g + 1) = SS(g) PI(g) + SE(g),
-// in fp32 for state rows 16 vs .. +15 of one (sequence, head).  PI(g) passes
-// through LDS; thread t owns row t / 16 and d_k / 16 columns.
+//   SS(0) = S_in,  SS(1) = SE(0),  SS(g + 1) = SS(g) PI(g) + SE(g),
+// in fp32 for state rows 16 vs .. +15 of one (sequence, head).  PI(g)
+// passes through LDS; the next segment's PI and SE are loaded into
+// registers while this segment's products run.  Thread t owns row t / 16
+// and d_k / 16 columns.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prefill_link_kernel(PrefillArgs a) {
   using G = SegL<DK, DV>;
-  constexpr int NCOL = DK / 16;  // columns per thread
+  constexpr int NCOL = DK / 16;            // columns per thread
+  constexpr int NV4 = DK * DK / 4 / 256;   // float4 of PI per thread
   const int vs = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
   const int in = a.in_idx[s], out = a.out_idx[s];
   if (tok0 < 0 || len < 0 || len > a.max_len) return;                       // the scan reports it
   if (in < -1 || in >= a.n_slots || out < 0 || out >= a.n_slots) return;
-  __shared__ __align__(16) float pis[DK][DK];
+  __shared__ __align__(16) float pis[DK * DK];
   __shared__ float srow[16][DK + 1];
   const int t = threadIdx.x, r = t / 16, col0 = (t % 16) * NCOL;
   const size_t seg_stride = static_cast<size_t>(a.H) * G::TOTAL;  // between segments of one (s, h)
   float* base = a.seg + (static_cast<size_t>(s) * a.n_segs * a.H + h) * G::TOTAL;
   const size_t row = static_cast<size_t>(16 * vs + r) * DK;
+  f32x4_t pre[NV4];
+  float se[NCOL];
+  auto fetch = [&](int g) {
+    const float* sg = base + g * seg_stride;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) pre[i] = reinterpret_cast<const f32x4_t*>(sg + G::PI)[t + 256 * i];
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) se[j] = sg[G::SE + row + col0 + j];
+  };
   float acc[NCOL];
   {
     const float* src = a.pool + (static_cast<size_t>(max(in, 0)) * a.H + h) * DV * DK + row + col0;
 #pragma unroll
     for (int j = 0; j < NCOL; ++j) acc[j] = in >= 0 ? src[j] : 0.f;
   }
-  for (int g = 0;; ++g) {
+  // SS(0): the input state; SS(1): the first segment's end state, which
+  // phase 1 computed from the input state
+#pragma unroll
+  for (int j = 0; j < NCOL; ++j) base[G::SS + row + col0 + j] = acc[j];
+#pragma unroll
+  for (int j = 0; j < NCOL; ++j) acc[j] = base[G::SE + row + col0 + j];
+  fetch(min(1, a.n_segs - 1));
+  for (int g = 1;; ++g) {
     float* sg = base + g * seg_stride;
 #pragma unroll
     for (int j = 0; j < NCOL; ++j) {
@@ -643,15 +667,16 @@ __global__ __launch_bounds__(256) void gdn_prefill_link_kernel(PrefillArgs a) {
       srow[r][col0 + j] = acc[j];
     }
     if (g + 1 >= a.n_segs) break;
-    for (int i = t; i < DK * DK / 4; i += 256)
-      reinterpret_cast<f32x4_t*>(&pis[0][0])[i] = reinterpret_cast<const f32x4_t*>(sg + G::PI)[i];
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NCOL; ++j) acc[j] = sg[G::SE + row + col0 + j];
+    for (int i = 0; i < NV4; ++i) reinterpret_cast<f32x4_t*>(pis)[t + 256 * i] = pre[i];
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) acc[j] = se[j];
+    __syncthreads();
+    fetch(min(g + 1, a.n_segs - 1));  // (the last round reloads a segment that exists)
     for (int k = 0; k < DK; ++k) {
       const float x = srow[r][k];
 #pragma unroll
-      for (int j = 0; j < NCOL; ++j) acc[j] = fmaf(x, pis[k][col0 + j], acc[j]);
+      for (int j = 0; j < NCOL; ++j) acc[j] = fmaf(x, pis[k * DK + col0 + j], acc[j]);
     }
     __syncthreads();
   }
@@ -798,8 +823,9 @@ int launch(const had_gdn_prefill_desc* d, PrefillArgs a, hipStream_t st) {
   hipError_t e;
   if (a.n_segs > 1) {
     a.phase = 1;
-    hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3((items + 7) / 8 * 8 * (DV / 16 + DK / 16)), dim3(256),
-                       0, st, a);
+    const int items1 = d->n_seqs * d->H * (a.n_segs - 1);  // every segment but the last
+    hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3((items1 + 7) / 8 * 8 * (DV / 16 + DK / 16)),
+                       dim3(256), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: segment scan launch: %s", hipGetErrorString(e));
     hipLaunchKernelGGL((gdn_prefill_link_kernel<DK, DV>), dim3(DV / 16, d->H, d->n_seqs), dim3(256), 0, st, a);
