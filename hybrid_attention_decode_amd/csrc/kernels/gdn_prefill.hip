@@ -785,9 +785,10 @@ int check(const had_gdn_prefill_desc* d) {
 
 // Segments of the scan.  One pass keeps n_seqs x H x d_v/16 workgroups busy
 // along a chain of every chunk; segments run side by side at the price of a
-// second scan pass (twice the rows: the transition) and the link.  Worth it
-// for long prompts that leave most CUs idle: chains of >= 32 chunks, and
-// at most 512 one-pass workgroups (two per CU).
+// second scan pass (twice the rows: the transition) and the link, and the
+// chain becomes two segment lengths (so two segments gain nothing).  Worth
+// it for long prompts that leave most CUs idle: segments of >= 32 chunks,
+// at most 512 phase-3 workgroups (two per CU), at least three segments.
 int plan_segments(const had_gdn_prefill_desc* d) {
   const int chunks = (d->max_len + kC - 1) / kC;
   int g;
@@ -796,6 +797,7 @@ int plan_segments(const had_gdn_prefill_desc* d) {
   } else {
     const int per_seg = d->n_seqs * d->H * (d->d_v / 16);
     g = std::min(chunks / 32, 512 / std::max(per_seg, 1));
+    if (g < 3) g = 1;
   }
   return std::max(1, std::min(g, std::max(chunks, 1)));
 }

@@ -564,10 +564,10 @@ typedef struct {
   int32_t max_len;           /* host bound on every sequence's length      */
   float q_scale;
   int32_t flags;             /* HAD_GDN_RAW_GATES                          */
-  int32_t n_segments;        /* scan segments (>= 0; 0 = automatic: one     *
-                              * unless the prompt spans >= 64 chunks and   *
-                              * n_seqs x H x d_v/16 <= 256; capped at the  *
-                              * chunk count)                               */
+  int32_t n_segments;        /* scan segments (>= 0; capped at the chunk    *
+                              * count).  0 = automatic: g = min(chunks/32, *
+                              * 512 / (n_seqs x H x d_v/16)), one segment  *
+                              * when g < 3                                 */
 } had_gdn_prefill_desc;
 
 typedef struct {

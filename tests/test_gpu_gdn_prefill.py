@@ -143,11 +143,11 @@ def test_segmented_scan_weak_decay():
 
 
 def test_segments_chosen_automatically_for_a_long_prompt():
-    # one 4,096-token prompt with 2 heads: the plan segments the scan
-    desc = had.gdn_prefill_desc((2, 2, 128, 128), 1, 4096)
-    one = had.gdn_prefill_desc((2, 2, 128, 128), 1, 4096, n_segments=1)
+    # one 6,144-token prompt with 2 heads: the plan segments the scan (3)
+    desc = had.gdn_prefill_desc((2, 2, 128, 128), 1, 6144)
+    one = had.gdn_prefill_desc((2, 2, 128, 128), 1, 6144, n_segments=1)
     assert had.gdn_prefill_workspace_bytes(desc) > had.gdn_prefill_workspace_bytes(one)
-    c = _run(4900, [4096], 2, 128, 128, [0], [1], 2)
+    c = _run(4900, [6144], 2, 128, 128, [0], [1], 2)
     _check(c)
 
 

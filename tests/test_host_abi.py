@@ -161,3 +161,28 @@ def test_gdn_slot_precondition_checker():
         with pytest.raises(HadError) as e:
             had.gdn_check_slots(6, np.array(in_idx), np.array(out_idx), inplace)
         assert e.value.kind == "bad_slot", (in_idx, out_idx)
+
+
+def _prefill_segments(n_seqs, H, dk, dv, max_len, n_segments=0):
+    """Segments the prefill plans, read back from its workspace size (host
+    call, no GPU): the segmented layout adds n_seqs x G x H blocks of
+    (d_k x d_k + 2 x d_v x d_k) floats after the 256-byte-aligned chunk part."""
+    one = had.gdn_prefill_workspace_bytes(had.gdn_prefill_desc((1, H, dv, dk), n_seqs, max_len, n_segments=1))
+    got = had.gdn_prefill_workspace_bytes(had.gdn_prefill_desc((1, H, dv, dk), n_seqs, max_len,
+                                                               n_segments=n_segments))
+    extra = got - one
+    per = n_seqs * H * (dk * dk + 2 * dv * dk) * 4
+    assert extra % per == 0
+    return 1 if extra == 0 else extra // per
+
+
+def test_prefill_segment_plan():
+    assert _prefill_segments(1, 8, 128, 128, 50000) == 8       # 782 chunks, 64 one-pass workgroups
+    assert _prefill_segments(1, 8, 128, 128, 800) == 1         # 13 chunks: one pass
+    assert _prefill_segments(1, 2, 128, 128, 6144) == 3        # 96 chunks
+    assert _prefill_segments(1, 2, 128, 128, 4096) == 1        # two segments would gain nothing
+    assert _prefill_segments(16, 8, 128, 128, 50000) == 1      # the batch already fills the GPU
+    assert _prefill_segments(1, 8, 128, 128, 800, n_segments=5) == 5
+    assert _prefill_segments(1, 8, 128, 128, 800, n_segments=100) == 13   # capped at the chunk count
+    with pytest.raises(HadError):
+        had.gdn_prefill_workspace_bytes(had.gdn_prefill_desc((1, 8, 128, 128), 1, 800, n_segments=-1))
