@@ -1,7 +1,8 @@
 """GPU parity over seeded random shapes: decode attention (both paths,
 gated or not, forced or planned splits), the fused layer, and the GDN
-prefill, each against the fp64 oracle.  The shapes are drawn once from a
-fixed seed, so every run checks the same cases."""
+prefill (one pass and in 3-8 segments), each against the fp64 oracle.
+The shapes are drawn once from a fixed seed, so every run checks the same
+cases."""
 
 import numpy as np
 import pytest
@@ -105,18 +106,20 @@ def test_random_fused_layer_shapes(case):
         assert_attn_close(out[s], ref)
 
 
-def _prefill_cases(n):
+def _prefill_cases(n, max_tokens=260, segmented=False):
     out = []
     for i in range(n):
-        lens = [int(x) for x in _rng.integers(0, 260, int(_rng.integers(1, 4)))]
+        lens = [int(x) for x in _rng.integers(0, max_tokens, int(_rng.integers(1, 4)))]
+        segs = int(_rng.integers(3, 9)) if segmented else 0
         out.append((i, lens, int(_rng.integers(1, 5)), int(_rng.choice([64, 128])), int(_rng.choice([64, 128])),
-                    bool(_rng.integers(0, 2))))
+                    bool(_rng.integers(0, 2)), segs))
     return out
 
 
-@pytest.mark.parametrize("case", _prefill_cases(10), ids=lambda c: "prefill%d" % c[0])
+@pytest.mark.parametrize("case", _prefill_cases(10) + [(10 + c[0],) + c[1:] for c in _prefill_cases(5, 1600, True)],
+                         ids=lambda c: "prefill%d" % c[0])
 def test_random_gdn_prefill_shapes(case):
-    i, lens, H, dk, dv, raw = case
+    i, lens, H, dk, dv, raw, segs = case
     seed = 8200 + i
     n = len(lens)
     N = max(1, sum(lens))
@@ -136,11 +139,12 @@ def test_random_gdn_prefill_shapes(case):
     pool = synth.normal_f32((n_slots, H, dv, dk), synth.seed_of(seed, 6)) * 0.1
     in_idx = np.array([(2 * s + 1) if s % 2 else -1 for s in range(n)], np.int32)
     out_idx = np.array([2 * s for s in range(n)], np.int32)
-    print("case %d: lens=%s H=%d dk=%d dv=%d raw=%d" % (i, lens, H, dk, dv, raw), flush=True)
+    print("case %d: lens=%s H=%d dk=%d dv=%d raw=%d segments=%d" % (i, lens, H, dk, dv, raw, segs), flush=True)
     pd = to_dev(pool)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     o = had.gdn_prefill(pd, to_dev(in_idx), to_dev(out_idx), to_dev(cu), to_dev(q), to_dev(k), to_dev(v),
-                        to_dev(a_in), to_dev(b_in), max_len=max(max(lens), 1), d_err=err, raw_gates=raw)
+                        to_dev(a_in), to_dev(b_in), max_len=max(max(lens), 1), d_err=err, raw_gates=raw,
+                        n_segments=segs)
     torch.cuda.synchronize()
     assert err.item() == 0
     new_ref, o_ref = gdn.prefill(pool.numpy(), in_idx, out_idx, cu, bf16.to_f64(bits_of(q)), bf16.to_f64(bits_of(k)),
