@@ -917,7 +917,7 @@ def main():
                     help="also run a 1 GiB device copy (scales PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: one GPU only; --gpus %d is not supported "
               "(the multi-GPU split of this path is a design note, not a code path)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
