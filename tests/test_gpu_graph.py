@@ -150,3 +150,90 @@ def test_gdn_prefill_replays_equal_eager_runs(n_segments):
         assert np.array_equal(got_pool.cpu().numpy(), pool2.cpu().numpy())
         n = c[-1]
         assert np.array_equal(got_o[:n].cpu().numpy(), o2[:n].cpu().numpy())
+
+
+def test_speculative_layer_replays_equal_eager_runs():
+    # 16 query heads x 4 drafts per KV head: prologue kernel + MFMA partials
+    # + combine, gated output; 3 replays at different lengths
+    P, H_q, H_kv, D, R, T = 64, 16, 1, 256, 64, 4
+    L0 = 2500
+    _, k_pool, v_pool, pt, _ = paged_case(7100, [L0 + 3 * T], 1, H_q, H_kv, D, P)
+    qg = to_dev(synth.normal_bf16((1, T, H_q, 2, D), synth.seed_of(7100, 1)))
+    k = to_dev(synth.normal_bf16((1, T, H_kv, D), synth.seed_of(7100, 2)))
+    v = to_dev(synth.normal_bf16((1, T, H_kv, D), synth.seed_of(7100, 3)))
+    w = to_dev(synth.uniform_f32((D,), 0.5, 1.5, synth.seed_of(7100, 4)))
+    kd0, vd0, ptd = to_dev(k_pool), to_dev(v_pool), to_dev(pt)
+    max_len = L0 + 3 * T
+    kd, vd = kd0.clone(), vd0.clone()
+    lens = torch.tensor([L0], dtype=torch.int32, device=DEV)
+    out = torch.empty((1, T, H_q, D), dtype=torch.bfloat16, device=DEV)
+    gate = torch.empty_like(out)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    desc = had.attn_desc((1, T, H_q, D), kd.shape, pt.shape[1], max_seq_len=max_len, deterministic=True, gated=True)
+    ws = torch.empty(had.decode_attn_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+
+    def layer(kd_, vd_, lens_, out_, gate_, ws_):
+        had.decode_attn_layer(qg, k, v, w, w, ptd, lens_, kd_, vd_, R, max_seq_len=max_len, workspace=ws_, out=out_,
+                              gate_out=gate_, d_err=err, deterministic=True, gated=True)
+
+    g = _capture(lambda: layer(kd, vd, lens, out, gate, ws))
+    for rep, L in enumerate([L0 + T, L0 + 2 * T + 1, L0 + 3 * T]):
+        print("case speculative graph replay %d: L=%d" % (rep, L), flush=True)
+        kd.copy_(kd0)
+        vd.copy_(vd0)
+        lens.fill_(L)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in (out, gate, kd, vd)]
+        kd2, vd2 = kd0.clone(), vd0.clone()
+        out2, gate2, ws2 = torch.empty_like(out), torch.empty_like(gate), torch.empty_like(ws)
+        layer(kd2, vd2, torch.tensor([L], dtype=torch.int32, device=DEV), out2, gate2, ws2)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        for x, y in zip(got, (out2, gate2, kd2, vd2)):
+            assert np.array_equal(bits_of(x), bits_of(y), equal_nan=True)
+
+
+def test_cascade_replays_equal_eager_runs():
+    # 16 sequences on one 40-page prefix (128 rows in the prefix pass), each
+    # with 3 private pages; the suffix lengths change between replays
+    n, P, H_q, H_kv, D, pp, priv = 16, 64, 8, 1, 256, 40, 3
+    N = pp + n * priv + 2
+    order = synth.permutation(N, synth.seed_of(7200, 0))
+    table = np.zeros((n, pp + priv + 1), np.int32)
+    for s in range(n):
+        table[s, :pp] = order[:pp]
+        table[s, pp:pp + priv] = order[pp + s * priv:pp + (s + 1) * priv]
+        table[s, pp + priv] = order[-1]
+    kd = to_dev(synth.normal_bf16((N, H_kv, P, D), synth.seed_of(7200, 1)))
+    vd = to_dev(synth.normal_bf16((N, H_kv, P, D), synth.seed_of(7200, 2)))
+    q = to_dev(synth.normal_bf16((n, 1, H_q, D), synth.seed_of(7200, 3)))
+    gt = to_dev(synth.normal_bf16((n, 1, H_q, D), synth.seed_of(7200, 4)))
+    ptd, prefix = to_dev(table), to_dev(table[0, :pp].copy())
+    max_len = (pp + priv) * P
+    lens = torch.zeros(n, dtype=torch.int32, device=DEV)
+    out = torch.empty((n, 1, H_q, D), dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    desc = had.attn_desc(q.shape, kd.shape, table.shape[1], max_seq_len=max_len, deterministic=True, gated=True)
+    ws = torch.empty(had.decode_attn_cascade_workspace_bytes(desc, pp), dtype=torch.uint8, device=DEV)
+
+    def run(lens_, out_, ws_):
+        had.decode_attn_cascade(q, kd, vd, ptd, lens_, prefix, max_seq_len=max_len, workspace=ws_, out=out_,
+                                d_err=err, deterministic=True, gate=gt)
+
+    lens.copy_(torch.from_numpy(np.full(n, pp * P + 1, np.int32)))
+    g = _capture(lambda: run(lens, out, ws))
+    for rep in range(3):
+        L = pp * P + synth.integers(1, priv * P + 1, n, synth.seed_of(7200, 10 + rep))
+        print("case cascade graph replay %d: lens=%s" % (rep, [int(x) for x in L]), flush=True)
+        lens.copy_(torch.from_numpy(L.astype(np.int32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        out2, ws2 = torch.empty_like(out), torch.empty_like(ws)
+        run(to_dev(L.astype(np.int32)), out2, ws2)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        assert np.array_equal(bits_of(got), bits_of(out2), equal_nan=True)
