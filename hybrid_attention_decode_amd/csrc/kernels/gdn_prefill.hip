@@ -137,10 +137,13 @@ struct SegL {
 };
 
 // One 16-byte piece of a bf16 row (zeros for rows past the chunk).
-__device__ __forceinline__ u32x4_t row16(const uint16_t* p, bool ok) {
-  u32x4_t r = {0u, 0u, 0u, 0u};
-  if (ok) r = *reinterpret_cast<const u32x4_t*>(p);
-  return r;
+// 16 bytes at src of token row t of the chunk (zero past its n tokens); the
+// address is clamped to the chunk's last token, so the load is unconditional
+// (loads of a thread batch up instead of each waiting behind a branch) and
+// stays inside the input
+__device__ __forceinline__ u32x4_t row16(const uint16_t* src, size_t stride, int base, int t, int n) {
+  const u32x4_t r = *reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(base + min(t, n - 1)) * stride);
+  return t < n ? r : u32x4_t{0u, 0u, 0u, 0u};
 }
 
 template <int DK, int DV>
@@ -163,7 +166,39 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
   __shared__ __align__(16) float amat[kC][kC + 4];    // A, then T diag(beta)
   __shared__ __align__(16) float tbg[kC][kC + 4];     // T diag(beta gamma)
 
-  // gates: lg = inclusive prefix sum of log alpha (0 past the chunk), beta
+  // K^T and V^T into LDS: an item is (token pair p, 8 dims dc); two 16-byte
+  // rows transpose into 8 words of (token 2p, token 2p+1) at one dim.  A
+  // thread holds DD / 64 items of each; all their loads, and those of the
+  // K operand rows below, are in flight before the first LDS write.
+  constexpr int NKI = DK / 64, NVI = DV / 64;
+  const size_t vstride = static_cast<size_t>(a.H) * DV;
+  u32x4_t sk[NKI][2], sv[NVI][2];
+#pragma unroll
+  for (int j = 0; j < NKI; ++j) {
+    const int it = threadIdx.x + 256 * j, p = it & 31, dc = it >> 5;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) sk[j][e] = row16(a.k + h * DK + 8 * dc, rstride, base, 2 * p + e, n);
+  }
+#pragma unroll
+  for (int j = 0; j < NVI; ++j) {
+    const int it = threadIdx.x + 256 * j, p = it & 31, dc = it >> 5;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) sv[j][e] = row16(a.v + h * DV + 8 * dc, vstride, base, 2 * p + e, n);
+  }
+  // K rows of the four token tiles as MFMA operands (zero past the chunk),
+  // and this wave's own tile once more for A (a register copy indexed by the
+  // wave would compile to selects)
+  u32x4_t kr[4][KS], kown[KS];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[tt][ks] = row16(a.k + h * DK + 32 * ks + 8 * g, rstride, base, 16 * tt + r16, n);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kown[ks] = row16(a.k + h * DK + 32 * ks + 8 * g, rstride, base, 16 * wave + r16, n);
+  // gates (after the loads above are issued, so wave 0's round trip for
+  // them overlaps the rest): lg = inclusive prefix sum of log alpha (0 past
+  // the chunk), beta
   if (wave == 0) {
     float la = 0.f, be = 0.f;
     if (lane < n) {
@@ -190,43 +225,23 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
     gw[kC + lane] = expf(lgC - la);
   }
 
-  // K^T and V^T into LDS: an item is (token pair p, 8 dims dc); two 16-byte
-  // rows transpose into 8 words of (token 2p, token 2p+1) at one dim
-  auto stage_t = [&](const uint16_t* src, size_t stride, int DD, uint16_t* dst) {
-    for (int it = threadIdx.x; it < 32 * (DD / 8); it += 256) {
-      const int p = it & 31, dc = it >> 5;
-      const int t0 = 2 * p, t1 = 2 * p + 1;
-      const u32x4_t x0 = row16(src + static_cast<size_t>(base + t0) * stride + 8 * dc, t0 < n);
-      const u32x4_t x1 = row16(src + static_cast<size_t>(base + t1) * stride + 8 * dc, t1 < n);
+  auto put_t = [&](const u32x4_t& x0, const u32x4_t& x1, int it, uint16_t* dst) {
+    const int p = it & 31, dc = it >> 5, t0 = 2 * p;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // dims 8dc + 2j (low halves) and 8dc + 2j + 1 (high halves)
-        *reinterpret_cast<uint32_t*>(dst + (8 * dc + 2 * j) * (kC + 8) + t0) = perm_b32(x1[j], x0[j], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(dst + (8 * dc + 2 * j + 1) * (kC + 8) + t0) = perm_b32(x1[j], x0[j], 0x07060302u);
-      }
+    for (int j = 0; j < 4; ++j) {
+      // dims 8dc + 2j (low halves) and 8dc + 2j + 1 (high halves)
+      *reinterpret_cast<uint32_t*>(dst + (8 * dc + 2 * j) * (kC + 8) + t0) = perm_b32(x1[j], x0[j], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(dst + (8 * dc + 2 * j + 1) * (kC + 8) + t0) = perm_b32(x1[j], x0[j], 0x07060302u);
     }
   };
-  stage_t(a.k + static_cast<size_t>(h) * DK, rstride, DK, &ktL[0][0]);
-  stage_t(a.v + static_cast<size_t>(h) * DV, static_cast<size_t>(a.H) * DV, DV, &vtL[0][0]);
-
-  // K rows of the four token tiles as MFMA operands (zero past the chunk)
-  u32x4_t kr[4][KS];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int t = 16 * tt + r16;
+  for (int j = 0; j < NKI; ++j) put_t(sk[j][0], sk[j][1], threadIdx.x + 256 * j, &ktL[0][0]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kr[tt][ks] = row16(a.k + static_cast<size_t>(base + t) * rstride + h * DK + 32 * ks + 8 * g, t < n);
-  }
+  for (int j = 0; j < NVI; ++j) put_t(sv[j][0], sv[j][1], threadIdx.x + 256 * j, &vtL[0][0]);
   __syncthreads();
 
   // A (strictly lower): wave w forms the tiles of token rows 16w .. 16w+15
   {
-    u32x4_t kown[KS];
-    const int t = 16 * wave + r16;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kown[ks] = row16(a.k + static_cast<size_t>(base + t) * rstride + h * DK + 32 * ks + 8 * g, t < n);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       if (nt > wave) break;
@@ -287,7 +302,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
       u32x4_t qr[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qr[ks] = row16(a.q + static_cast<size_t>(base + t) * rstride + h * DK + 32 * ks + 8 * g, t < n);
+        qr[ks] = row16(a.q + h * DK + 32 * ks + 8 * g, rstride, base, t, n);
       float e[4][4];
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -686,7 +701,9 @@ __global__ __launch_bounds__(256) void gdn_prefill_link_kernel(PrefillArgs a) {
 //   o = q_scale (diag(gamma) Q S0^T + Aqk U)
 // with S0 the chunk's initial state and U as the scan kernel left them.
 // Wave w owns token rows 16w .. 16w+15; the state's B operands pass through
-// LDS once for the four waves.
+// LDS once for the four waves.  Every load of the block (state, Q, Aqk, U,
+// gamma) is issued before the first is used: one memory round trip per
+// block, not one per staging round and d_v slice.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
   using L = PL<DK, DV>;
@@ -703,10 +720,12 @@ __global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
 
   __shared__ u32x4_t sc[VT][KS][2][64];  // S0 B operands [v-slice][d_k step][hi, lo][lane]
-  for (int i = threadIdx.x; i < VT * KS * 64; i += 256) {
-    const int l = i & 63, k = i >> 6;  // k = vs * KS + ks
-    (&sc[0][0][0][0])[(k * 2) * 64 + l] = blk[L::SC_HI + k * 64 + l];
-    (&sc[0][0][0][0])[(k * 2 + 1) * 64 + l] = blk[L::SC_LO + k * 64 + l];
+  constexpr int NST = VT * KS * 64 / 256;  // staging rounds (VT * KS * 64 is a multiple of 256)
+  u32x4_t st_hi[NST], st_lo[NST];
+#pragma unroll
+  for (int j = 0; j < NST; ++j) {
+    st_hi[j] = blk[L::SC_HI + threadIdx.x + 256 * j];
+    st_lo[j] = blk[L::SC_LO + threadIdx.x + 256 * j];
   }
   // Q rows 16w + r (rows past the chunk: any real row; their o is not stored), d_k in sigma order
   u32x4_t qa[KS];
@@ -727,6 +746,24 @@ __global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
     alo[kp] = blk[L::A_LO + (wave * 2 + kp) * 64 + lane];
   }
   const f32x4_t gam = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(blk + L::GAM) + 16 * wave + 4 * g);
+  const int nkp = wave < 2 ? 1 : 2;  // token step 1 holds only zeros for rows 0 .. 31
+  // U in result layout, token tiles 2kp and 2kp + 1 of every d_v slice
+  u32x4_t up[2][2][VT];
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    if (kp >= nkp) break;
+#pragma unroll
+    for (int vs = 0; vs < VT; ++vs) {
+      up[kp][0][vs] = blk[L::UP + ((2 * kp) * VT + vs) * 64 + lane];
+      up[kp][1][vs] = blk[L::UP + ((2 * kp + 1) * VT + vs) * 64 + lane];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NST; ++j) {
+    const int i = threadIdx.x + 256 * j, l = i & 63, k = i >> 6;  // k = vs * KS + ks
+    (&sc[0][0][0][0])[(k * 2) * 64 + l] = st_hi[j];
+    (&sc[0][0][0][0])[(k * 2 + 1) * 64 + l] = st_lo[j];
+  }
   __syncthreads();
 
   const size_t o0 = (static_cast<size_t>(base) * a.H + h) * DV;
@@ -734,8 +771,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
   // first such row is H * d_v floats past the last real one)
   const __amdgpu_buffer_rsrc_t orsrc =
       __builtin_amdgcn_make_buffer_rsrc(a.o + o0, 0, static_cast<int>(((n - 1) * a.H + 1) * DV * 4), 0x00020000);
-  const int nkp = wave < 2 ? 1 : 2;  // token step 1 holds only zeros for rows 0 .. 31
-#pragma unroll 2
+#pragma unroll
   for (int vs = 0; vs < VT; ++vs) {
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
     f32x4_t Y0 = z, Y1 = z, O0 = z, O1 = z;
@@ -749,8 +785,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
       if (kp >= nkp) break;
       // U over tokens in tau order: result tiles 2kp and 2kp + 1 of this lane
       float x8[8];
-      cat8(__builtin_bit_cast(f32x4_t, blk[L::UP + ((2 * kp) * VT + vs) * 64 + lane]),
-           __builtin_bit_cast(f32x4_t, blk[L::UP + ((2 * kp + 1) * VT + vs) * 64 + lane]), x8);
+      cat8(__builtin_bit_cast(f32x4_t, up[kp][0][vs]), __builtin_bit_cast(f32x4_t, up[kp][1][vs]), x8);
       u32x4_t uh, ul;
       split8(x8, uh, ul);
       O0 = mfma(ahi[kp], uh, O0);
