@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
 // start states; phase 3 is the one-pass scan again, every segment at once
 // from its start state, storing U and the chunk states.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void gdn_prefill_scan_kernel(PrefillArgs a) {
   using L = PL<DK, DV>;
   using G = SegL<DK, DV>;
   constexpr int KS = L::KS, VT = L::VT, DT = L::DT;
@@ -604,18 +604,23 @@ __global__ __launch_bounds__(256) void gdn_prefill_scan_kernel(PrefillArgs a) {
     }
   };
 
-  // chunk c + 1's operands load while chunk c computes (two register sets;
-  // the last chunk reloads itself so that no load sits under a branch)
-  Ops pa, pb;
+  // chunk c + 2's operands load while chunk c computes (three register
+  // sets; past the end the last chunk reloads itself, so that no load sits
+  // under a branch)
+  Ops pa, pb, pc;
   if (c1 > c0) {
     load_w(c0, pa);
     load_rest(c0, pa);
+    load_w(min(c0 + 1, c1 - 1), pb);
+    load_rest(min(c0 + 1, c1 - 1), pb);
     if (chunk_out && wave < KS) store_sc(c0);
   }
-  for (int c = c0; c < c1; c += 2) {
-    step(c, pa, min(c + 1, c1 - 1), pb);
+  for (int c = c0; c < c1; c += 3) {
+    step(c, pa, min(c + 2, c1 - 1), pc);
     if (c + 1 >= c1) break;
-    step(c + 1, pb, min(c + 2, c1 - 1), pa);
+    step(c + 1, pb, min(c + 3, c1 - 1), pa);
+    if (c + 2 >= c1) break;
+    step(c + 2, pc, min(c + 4, c1 - 1), pb);
   }
 
   // end state: the output slot (one pass, and the last segment of phase 3),
