@@ -46,43 +46,49 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   __shared__ float row[kWaves][D];
   const int s = blockIdx.x / a.T, j = blockIdx.x % a.T;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t tok = static_cast<size_t>(s) * a.T + j;
+  const int hh = blockIdx.y * kWaves + wave;  // one head per wave
+  if (hh >= a.H_q + a.H_kv) return;           // (wave 0 of block row 0 always has a head)
+  const bool is_q = hh < a.H_q;
+  const int h = is_q ? hh : hh - a.H_q;
+
+  // Every load is issued before the first is used, none under a branch (a
+  // load under a branch waits for itself before the branch ends): the row,
+  // the row that is only copied (a q head's gate half, a KV head's v row),
+  // then the length and the page id that depends on it.
+  const uint16_t* src = is_q ? a.qg + (tok * a.H_q + h) * 2 * D : a.k + (tok * a.H_kv + h) * D;
+  const uint16_t* side = is_q ? src + D : a.v + (tok * a.H_kv + h) * D;
+  RowIn<D> in;
+  row_load<D>(in, src, is_q ? a.w_q : a.w_k, lane);
+  uint16_t cp[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) cp[m] = side[lane + 64 * m];
   const int L = a.seq_lens[s];
   const int pos = L - a.T + j;
   const bool pos_ok = L >= a.T && pos < a.max_pages * a.P;
-  int pid = -1;
-  if (pos_ok) pid = a.page_table[static_cast<size_t>(s) * a.max_pages + pos / a.P];
+  const int pid = a.page_table[static_cast<size_t>(s) * a.max_pages + (pos_ok ? pos / a.P : 0)];
   const bool page_ok = pos_ok && pid >= 0 && pid < a.num_pages;
   if (threadIdx.x == 0 && blockIdx.y == 0) {
     if (!pos_ok) set_err(a.d_err, HAD_DERR_SEQLEN);
     else if (!page_ok) set_err(a.d_err, HAD_DERR_PAGE);
   }
-  const size_t tok = static_cast<size_t>(s) * a.T + j;
 
-  const int hh = blockIdx.y * kWaves + wave;  // one head per wave
-  if (hh >= a.H_q + a.H_kv) return;
-  const bool is_q = hh < a.H_q;
-  const int h = is_q ? hh : hh - a.H_q;
-  const uint16_t* src = is_q ? a.qg + (tok * a.H_q + h) * 2 * D : a.k + (tok * a.H_kv + h) * D;
-  RowIn<D> in;
-  row_load<D>(in, src, is_q ? a.w_q : a.w_k, lane);
   uint16_t y[E];
   row_norm_rope<D>(in, pos, a.R, a.base, a.eps, row[wave], lane, y);
   if (is_q) {
     uint16_t* qo = a.q_out + (tok * a.H_q + h) * D;
     uint16_t* go = a.gate_out + (tok * a.H_q + h) * D;
-    const uint16_t* gi = src + D;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       qo[lane + 64 * m] = y[m];
-      go[lane + 64 * m] = gi[lane + 64 * m];
+      go[lane + 64 * m] = cp[m];
     }
   } else if (page_ok) {
     const size_t dst = ((static_cast<size_t>(pid) * a.H_kv + h) * a.P + pos % a.P) * D;
-    const uint16_t* vi = a.v + (tok * a.H_kv + h) * D;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       a.k_pool[dst + lane + 64 * m] = y[m];
-      a.v_pool[dst + lane + 64 * m] = vi[lane + 64 * m];
+      a.v_pool[dst + lane + 64 * m] = cp[m];
     }
   }
 }
