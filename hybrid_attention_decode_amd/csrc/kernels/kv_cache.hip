@@ -42,8 +42,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(uint4* k_pool, uint4* v_
   for (int c = threadIdx.x; c < H_kv * cpr; c += blockDim.x) {
     const int h = c / cpr, q = c % cpr;
     const size_t dst = ((static_cast<size_t>(pid) * H_kv + h) * P + pos % P) * cpr + q;
-    k_pool[dst] = k_new[(src_row + h) * cpr + q];
-    v_pool[dst] = v_new[(src_row + h) * cpr + q];
+    // both loads before either store (in program order the store to k_pool
+    // could alias v_new, so each load would wait for the store before it)
+    const uint4 kx = k_new[(src_row + h) * cpr + q], vx = v_new[(src_row + h) * cpr + q];
+    k_pool[dst] = kx;
+    v_pool[dst] = vx;
   }
 }
 
@@ -57,8 +60,11 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(uint4* k_pool, uint4* v_po
   const size_t src = static_cast<size_t>(list.src[blockIdx.y]) * chunks;
   const size_t dst = static_cast<size_t>(list.dst[blockIdx.y]) * chunks;
   for (size_t c = blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    k_pool[dst + c] = k_pool[src + c];
-    v_pool[dst + c] = v_pool[src + c];
+    // both loads first (source and destination pages differ, so the loads
+    // never see either store)
+    const uint4 kx = k_pool[src + c], vx = v_pool[src + c];
+    k_pool[dst + c] = kx;
+    v_pool[dst + c] = vx;
   }
 }
 
