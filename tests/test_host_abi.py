@@ -186,3 +186,28 @@ def test_prefill_segment_plan():
     assert _prefill_segments(1, 8, 128, 128, 800, n_segments=100) == 13   # capped at the chunk count
     with pytest.raises(HadError):
         had.gdn_prefill_workspace_bytes(had.gdn_prefill_desc((1, 8, 128, 128), 1, 800, n_segments=-1))
+
+
+def test_attention_split_plan():
+    # the benchmark's shapes (head_dim 256, 64-token pages, 1 KV head): one
+    # split per CU from 128K on, for 8 rows (VALU) and 64 rows (MFMA);
+    # short contexts keep >= 4 tiles of 8 tokens per wave (VALU) or >= 4
+    # iterations of 64 tokens (MFMA) per split
+    def plan(q_shape, max_len):
+        pages = -(-max_len // 64) + 1
+        return had.decode_attn_plan(had.attn_desc(q_shape, (pages, 1, 64, 256), pages, max_seq_len=max_len))
+    assert plan((1, 1, 8, 256), 131072 + 266) == (256, 9)
+    assert plan((1, 1, 8, 256), 262144 + 266) == (256, 17)
+    assert plan((1, 1, 8, 256), 1048576 + 266) == (256, 65)
+    assert plan((1, 4, 16, 256), 262144 + 1034) == (256, 17)
+    assert plan((1, 1, 8, 256), 513) == (2, 5)
+    assert plan((1, 4, 16, 256), 2000) == (8, 4)       # 32 pages, 4 per split
+    # cascade: 16 sequences on a 781-page prefix (prefix pass: 195 splits of
+    # >= 4 pages), suffixes up to 12,288 tokens (16 splits per sequence);
+    # the split count is read back from the partials' workspace size
+    n, rows, D = 16, 8, 256
+    max_len = 50000 + 12288 + 300
+    pages = -(-max_len // 64) + 1
+    desc = had.attn_desc((n, 1, 8, D), (4096, 1, 64, D), pages, max_seq_len=max_len)
+    ws = had.decode_attn_cascade_workspace_bytes(desc, 781)
+    assert ws == n * 1 * (195 + 16) * rows * (D + 2) * 4
