@@ -55,8 +55,10 @@ int no_gate(const had_attn_desc* d, const char* who) {
 }
 
 // Split plan over the pages a sequence can reach (max_seq_len, a host bound,
-// so the plan does not depend on device data).  Split i owns pages
-// [i*n/ns, (i+1)*n/ns): balanced to within one page.
+// so the plan does not depend on device data).  Below 16 rows split i owns
+// the tiles [i*N/ns, (i+1)*N/ns) of the N = n * page_size / 8 tiles of 8
+// tokens (balanced to within one tile); at 16 or more rows the pages
+// [i*n/ns, (i+1)*n/ns) (within one page).
 int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   const int64_t max_len = d->max_seq_len > 0 ? d->max_seq_len : static_cast<int64_t>(d->max_pages) * d->page_size;
   const int64_t n_pages = std::max<int64_t>(1, ceil_div(max_len, d->page_size));
@@ -72,12 +74,14 @@ int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
     const int64_t want = std::max<int64_t>(1, ceil_div(kTargetUnits, units));
     const int64_t min_pps = mfma ? ceil_div(256, d->page_size) : ceil_div(kMinTilesPerUnit, d->page_size / 8);
     ns = std::max<int64_t>(1, std::min<int64_t>(want, n_pages / min_pps));
-    ns = std::max<int64_t>(ns, ceil_div(n_pages, had::kMaxPagesPerSplit));
+    // (with several splits a tile-aligned range can touch one page more)
+    if (n_pages > had::kMaxPagesPerSplit) ns = std::max<int64_t>(ns, ceil_div(n_pages, had::kMaxPagesPerSplit - 1));
   }
   const int64_t pps = ceil_div(n_pages, ns);
-  if (pps > had::kMaxPagesPerSplit)
-    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %lld splits leave %lld pages per split (max %d)",
-                static_cast<long long>(ns), static_cast<long long>(pps), had::kMaxPagesPerSplit);
+  const int64_t pps_max = ns > 1 ? had::kMaxPagesPerSplit - 1 : had::kMaxPagesPerSplit;
+  if (pps > pps_max)
+    return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %lld splits leave %lld pages per split (max %lld)",
+                static_cast<long long>(ns), static_cast<long long>(pps), static_cast<long long>(pps_max));
   if (ns > had::kMaxSplits)
     return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %lld splits (max %d)", static_cast<long long>(ns),
                 had::kMaxSplits);

@@ -9,8 +9,8 @@
 // (24-ai.news long-context table).
 //
 // gfx950 mapping (one workgroup = 8 waves, two per SIMD, each wave streams
-// its own tiles of 8 tokens; the workgroup owns a contiguous, balanced range
-// of pages, one workgroup per CU):
+// its own tiles of 8 tokens; the workgroup owns a contiguous range of
+// tiles, balanced to within one tile, one workgroup per CU):
 //  * QK: a tile step covers TPS tokens with LPT lanes per token; lane j of a
 //    token loads 16-byte chunks j, j+LPT of the K row (coalesced 128-bit
 //    loads straight into registers) and accumulates all 8 rows with
@@ -128,11 +128,17 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // branches make the compiler's wait-count bookkeeping fall back to
   // "wait for everything", which would serialise the K/V prefetch.
   //
-  // This split owns pages [pg0, pg1_plan) of the plan (balanced to within one
-  // page); tiles are numbered from the split's first token.
-  const int pg0 = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
-  const int pg1_plan = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
+  // This split owns the tiles [t0, t1) of the plan's tiles (counted from page
+  // pg_begin; balanced to within one tile, so no workgroup holds a page more
+  // than another), which lie on the pages [pg0, pg1_plan); tiles are numbered
+  // from pg0's first token, this split's being [tile_lo, tile_hi).
+  const int64_t n_tiles_plan = static_cast<int64_t>(a.n_pages_plan) * tpp;
+  const int t0 = static_cast<int>(static_cast<int64_t>(sp) * n_tiles_plan / a.num_splits);
+  const int t1 = static_cast<int>(static_cast<int64_t>(sp + 1) * n_tiles_plan / a.num_splits);
+  const int pg0 = a.pg_begin + t0 / tpp;
+  const int pg1_plan = a.pg_begin + (t1 + tpp - 1) / tpp;
   const int npg_plan = pg1_plan - pg0;
+  const int tile_lo = t0 % tpp, tile_hi = t1 - (t0 / tpp) * tpp;
   const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
 
   // Start-up order.  Vector loads retire in issue order, so the small loads
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // (Issue order: all of buffer 0, then all of buffer 1, the order the loop
   // refills them in, so the wait counts inside the loop stay exact.)
   Tile<D> buf[2];
-  int tcur[2] = {wave, wave + kWaves};
+  int tcur[2] = {tile_lo + wave, tile_lo + wave + kWaves};
   // both page ids in one scalar round trip (the fences keep the two loads
   // adjacent: left to itself the scheduler waits for the first before it
   // computes the second address)
@@ -195,8 +201,9 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
 
   // (a suffix pass also needs every query to see the whole prefix before pg_begin)
   const bool bad_len = L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P;
-  // fused: the workgroup whose split holds the last position owns the new tokens
-  const bool own = FUSED && !bad_len && (L - 1) / P >= pg0 && (L - 1) / P < pg1_plan;
+  // fused: the workgroup whose split holds the last position's tile owns the new tokens
+  const int last_tile = (L - 1) / kTT - a.pg_begin * tpp;
+  const bool own = FUSED && !bad_len && last_tile >= t0 && last_tile < t1;
   int errs = (bad_len && threadIdx.x == 0) ? HAD_DERR_SEQLEN : 0;
 
   // query block -> LDS (rows past `rows` are zero)
@@ -246,9 +253,9 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
 
   const int n_pages = bad_len ? 0 : (L + P - 1) / P;
   const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
-  const int ntiles = npg * tpp;
+  const int ntiles = min(npg * tpp, tile_hi);  // end of this split's tiles (tiles past L are masked)
   if (threadIdx.x == 0) {
-    sh.next = 2 * kWaves;
+    sh.next = tile_lo + 2 * kWaves;
     sh.err = 0;
   }
   // checked page ids of the split -> LDS (-1 marks an invalid id)
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // later ones come from an LDS counter, so the two waves sharing a SIMD
   // (which the issue arbiter does not serve equally) finish together.  In
   // deterministic mode wave w takes tiles w + 2*kWaves*i and w + kWaves +
-  // 2*kWaves*i instead.  Claims grow monotonically, so tcur[0] < tcur[1]
+  // 2*kWaves*i (counted from tile_lo) instead.  Claims grow monotonically, so tcur[0] < tcur[1]
   // always: the loop runs while both buffers hold a tile (its only exit test
   // is at the top -- with exits between the two halves the compiler's wait
   // counts at the loop head fall back to waiting for every load), and at

@@ -334,9 +334,12 @@ int had_qk_norm_rope_gate(const had_qknrg_desc *d, const had_qknrg_ptrs *p, void
  * (long-context table).
  *
  * Work is split over the context ("split-K"): of the n pages that
- * max_seq_len can reach, work unit (s, h, split i of ns) covers pages
- * [i*n/ns, (i+1)*n/ns) (balanced to within one page; pages_per_split of the
- * plan = ceil(n/ns)) and writes an unnormalised partial
+ * max_seq_len can reach (N = n * page_size / 8 tiles of 8 tokens), work
+ * unit (s, h, split i of ns) covers, below 16 rows, the tiles
+ * [i*N/ns, (i+1)*N/ns) (balanced to within one tile) and, at 16 rows or
+ * more, the pages [i*n/ns, (i+1)*n/ns) (within one page); pages_per_split of
+ * the plan = ceil(n/ns), at most 511 when ns > 1 (a tile range can touch one
+ * page more, and one split reads at most 512), and writes an unnormalised partial
  * (o, m, l) to the workspace; a second kernel merges the partials by
  * log-sum-exp and writes bf16 (round to nearest even).  Query rows per KV
  * head = q_len * (H_q / H_kv); below 16 rows a VALU kernel runs, at 16 or
@@ -390,8 +393,8 @@ typedef struct {
                               * that had_qk_norm_rope_gate splits off)      */
 } had_attn_ptrs;
 
-/* Split plan for desc: number of splits and the largest page count of a
- * split (both depend on the descriptor only, never on device data). */
+/* Split plan for desc: number of splits and ceil(pages / splits) (both
+ * depend on the descriptor only, never on device data). */
 int had_decode_attn_plan(const had_attn_desc *d, int32_t *num_splits, int32_t *pages_per_split);
 size_t had_decode_attn_workspace_bytes(const had_attn_desc *d);
 int had_decode_attn(const had_attn_desc *d, const had_attn_ptrs *p, void *stream);
