@@ -42,7 +42,10 @@ def gates_from_raw(g, b):
     layer's projections."""
     g = np.asarray(g, np.float64)
     b = np.asarray(b, np.float64)
-    return np.exp(g), 1.0 / (1.0 + np.exp(-b))
+    # the logistic function in its two-branch form (exp of -|b| only, so no
+    # overflow for large |b|): 1 / (1 + e^-b) for b >= 0, e^b / (1 + e^b) below
+    e = np.exp(-np.abs(b))
+    return np.exp(g), np.where(b >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
 
 
 def step(S, q, k, v, alpha, beta):
