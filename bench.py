@@ -198,8 +198,9 @@ class LongContextStack:
         self.graphs[t % 2].replay()
 
 
-def time_graph(torch, fn, reps):
-    """Average duration of one call of fn, from a captured batch of `reps` calls."""
+def time_graph(torch, fn, reps, n_timed=5):
+    """Average duration of one call of fn, from a captured batch of `reps`
+    calls: the median over `n_timed` timed replays of the batch's average."""
     gr = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -213,11 +214,14 @@ def time_graph(torch, fn, reps):
     gr.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    gr.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps  # microseconds
+    batch_ms = []
+    for _ in range(n_timed):
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        batch_ms.append(e0.elapsed_time(e1))
+    return float(np.median(batch_ms)) * 1e3 / reps  # microseconds
 
 
 def run_context(L0, steps, warmup, kernel_reps, seed=0):
