@@ -101,6 +101,17 @@ def test_new_tokens_straddle_splits(H_q):
     _check_against_oracle(c)
 
 
+@pytest.mark.parametrize("L,num_splits", [(658, 7), (643, 13), (700, 5)])
+def test_valu_fused_tile_boundaries(L, num_splits):
+    # 8 rows (2 q heads x 4 new tokens) on the fused VALU path, whose splits
+    # are balanced to within one 8-token tile: boundaries fall inside pages
+    # (96 tiles of 64-token pages over 7, 13 or 5 splits), and with L = 658
+    # and 7 splits the new tokens lie on both sides of one (tiles 81 | 82);
+    # the split holding the last position's tile owns them
+    c = _run(2150 + num_splits, [L], 4, 2, 1, 128, 32, 64, num_splits=num_splits)
+    _check_against_oracle(c)
+
+
 @pytest.mark.parametrize("lens,T,H_q,H_kv,D,R,P", [
     ([50001], 1, 8, 1, 256, 64, 64),          # VALU path
     ([7000, 300], 4, 16, 1, 256, 64, 64),     # MFMA path
