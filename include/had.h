@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define HAD_ABI_VERSION 3
+#define HAD_ABI_VERSION 4
 
 enum {
   HAD_OK = 0,

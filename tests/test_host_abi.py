@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(L, name), name
     assert declared == had.exported_symbols()
-    assert had.abi_version() == 3
+    assert had.abi_version() == 4
 
 
 def test_scenario_on_the_cpp_manager():
