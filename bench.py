@@ -317,12 +317,16 @@ class Stack:
         self.n, self.T, self.H_q = n_seqs, T, H_q
         self.num_pages, self.max_pages, self.max_seq_len = num_pages, max_pages, max_seq_len
         n = n_seqs
-        self.ctrl_len = 2 * n + n * T
+        # control block: lengths, GDN input slots, GDN output slots, then the
+        # copy-on-write pairs (source, destination) per sequence (-1: none)
+        self.ctrl_len = 2 * n + n * T + 2 * n
         self.ctrl = torch.zeros(self.ctrl_len, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)  # device sentinel, read after the run
         self.lens_dev = self.ctrl[:n]
         self.in_dev = self.ctrl[n:2 * n]
-        self.out_dev = self.ctrl[2 * n:].view(n, T)
+        self.out_dev = self.ctrl[2 * n:2 * n + n * T].view(n, T)
+        self.cow_src = self.ctrl[2 * n + n * T:3 * n + n * T]
+        self.cow_dst = self.ctrl[3 * n + n * T:]
         self.ctrl_pin = torch.empty((n_steps + 4, self.ctrl_len), dtype=torch.int32, pin_memory=True)
         self.pt_dev = torch.full((n, max_pages), -1, dtype=torch.int32, device=dev)
         self.pt_pin = torch.empty(n_steps * n * (T // P + 2) + 16, dtype=torch.int32, pin_memory=True)
@@ -398,7 +402,16 @@ class Stack:
                 self.gdn_layer(ig)
                 ig += 1
 
+    def cow_copies(self):
+        """The device half of copy-on-write in every attention layer's pools:
+        pairs from the control block (unused entries -1 copy nothing)."""
+        for a in self.attn:
+            self.had.kv_copy_pages(a["k_pool"], a["v_pool"], self.cow_src, self.cow_dst, d_err=self.err)
+
     def capture(self):
+        """Two step graphs: the 48 layers, and the same step preceded by the
+        copy-on-write page copies (replayed on steps whose reservation copied a
+        shared partial page)."""
         torch = self.torch
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -409,7 +422,14 @@ class Stack:
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
             self.layers()
+        self.graph_cow = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph_cow):
+            self.cow_copies()
+            self.layers()
         torch.cuda.synchronize()
+
+    def replay(self, cow):
+        (self.graph_cow if cow else self.graph).replay()
 
     def set_page(self, s, idx, pid):
         """Patch one device page-table entry (pinned staging, never reused)."""
@@ -417,12 +437,20 @@ class Stack:
         self.pt_dev[s, idx].copy_(self.pt_pin[self.pt_pin_at], non_blocking=True)
         self.pt_pin_at += 1
 
-    def push_ctrl(self, t, lens, in_idx, out_idx):
+    def push_ctrl(self, t, lens, in_idx, out_idx, cow=None):
+        """cow: per sequence a (source, destination) page pair or None."""
         row = self.ctrl_pin[t]
-        n = self.n
+        n, T = self.n, self.T
         row[:n] = torch_int(lens)
         row[n:2 * n] = torch_int(in_idx)
-        row[2 * n:] = torch_int(out_idx).reshape(-1)
+        row[2 * n:2 * n + n * T] = torch_int(out_idx).reshape(-1)
+        src = [-1] * n
+        dst = [-1] * n
+        for i, c in enumerate(cow or []):
+            if c is not None:
+                src[i], dst[i] = int(c[0]), int(c[1])
+        row[2 * n + n * T:3 * n + n * T] = torch_int(src)
+        row[3 * n + n * T:] = torch_int(dst)
         self.ctrl.copy_(row, non_blocking=True)
 
 
@@ -509,7 +537,7 @@ def run_speculative(L0=262144, steps=256, warmup=10, kernel_reps=4, T=4, G=16, s
             for idx in range(held, -(-(L + T) // P)):
                 st.set_page(0, idx, row[idx])
         st.push_ctrl(t, [L + T], [cur], [outs])
-        st.graph.replay()
+        st.replay(False)
         a = int(accepted[t])
         cur = had.spec_rollback(pt, slots, seq, T, a, cur, outs)
         L += a
@@ -605,14 +633,12 @@ def run_agentic(first_turn=50000, turns=12, turn_len=800, kernel_reps=4, seed=6)
         out = slots.acquire()
         trip = pt.reserve(seq, 1)
         L += 1
-        if trip is not None:                       # the cache shares the partial last page: copy it first
-            for a in st.attn:
-                had.kv_copy_pages(a["k_pool"], a["v_pool"], [trip[0]], [trip[1]])
+        if trip is not None:                       # the cache shares the partial last page: the step copies it
             n_cow[0] += 1
         if trip is not None or (L - 1) % P == 0:
             st.set_page(0, (L - 1) // P, pt.export([seq], max_pages)[0][0, (L - 1) // P])
-        st.push_ctrl(t, [L], [cur], [[out]])
-        st.graph.replay()
+        st.push_ctrl(t, [L], [cur], [[out]], cow=[trip])
+        st.replay(trip is not None)
         slots.release(cur)
         cur = out
 
@@ -690,12 +716,12 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
     seqs = [pt.seq_fork(root, prefix) for _ in range(n_seqs)]
     n_cow = 0
 
-    def cow(trip):
+    def cow(trip):                                            # set-up time copies (eager)
         nonlocal n_cow
         if trip is None:
             return False
         for a in st.attn:
-            had.kv_copy_pages(a["k_pool"], a["v_pool"], [trip[0]], [trip[1]])
+            had.kv_copy_pages(a["k_pool"], a["v_pool"], [trip[0]], [trip[1]], d_err=st.err)
         n_cow += 1
         return True
 
@@ -719,15 +745,20 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
     Ls = [int(x) for x in lens]
 
     def step(t):
+        nonlocal n_cow
         outs = [slots.acquire() for _ in range(n_seqs)]
+        trips = []
         for i, sq in enumerate(seqs):
             pos = Ls[i]
-            copied = cow(pt.reserve(sq, 1))
+            trip = pt.reserve(sq, 1)                    # a shared partial page is copied inside the step
+            trips.append(trip)
             Ls[i] += 1
-            if copied or pos % P == 0:                  # the token's page entry changed
+            if trip is not None or pos % P == 0:        # the token's page entry changed
                 st.set_page(i, pos // P, pt.export([sq], max_pages)[0][0, pos // P])
-        st.push_ctrl(t, Ls, cur, [[o] for o in outs])
-        st.graph.replay()
+        n_step_cow = sum(x is not None for x in trips)
+        n_cow += n_step_cow
+        st.push_ctrl(t, Ls, cur, [[o] for o in outs], cow=trips)
+        st.replay(n_step_cow > 0)
         for i in range(n_seqs):
             slots.release(cur[i])
             cur[i] = outs[i]

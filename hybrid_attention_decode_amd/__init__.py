@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     RadixCache,
     SlotPool,
     abi_version,
+    attn_check_prefix,
     attn_desc,
     decode_attn,
     decode_attn_cascade,
@@ -31,6 +32,7 @@ from ._lib import (  # noqa: F401
     gdn_prefill_workspace_bytes,
     gdn_state_update,
     kv_append,
+    kv_check_copy_pages,
     kv_copy_pages,
     lib,
     qk_norm_rope_gate,
@@ -38,4 +40,5 @@ from ._lib import (  # noqa: F401
     DERR_PAGE,
     DERR_SLOT,
     DERR_SEQLEN,
+    DERR_COPY,
 )

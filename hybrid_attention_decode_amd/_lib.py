@@ -28,7 +28,7 @@ _STATUS = {
     -9: "capacity",
     -10: "range",
 }
-DERR_PAGE, DERR_SLOT, DERR_SEQLEN = 1, 2, 4
+DERR_PAGE, DERR_SLOT, DERR_SEQLEN, DERR_COPY = 1, 2, 4, 8
 ATTN_DETERMINISTIC = 1
 ATTN_GATED_OUTPUT = 4
 GDN_RAW_GATES = 1
@@ -131,7 +131,9 @@ _SIGS = {
     "had_slots_release": ([_p, _i32], ctypes.c_int),
     "had_slots_stats": ([_p, _pi32, _pi32], ctypes.c_int),
     "had_spec_rollback": ([_p, _p, _i32, _i32, _i32, _i32, _pi32, _pi32], ctypes.c_int),
-    "had_kv_copy_pages": ([ctypes.POINTER(KvLayout), _p, _p, _pi32, _pi32, _i32, _p], ctypes.c_int),
+    "had_kv_copy_pages": ([ctypes.POINTER(KvLayout), _p, _p, _p, _p, _i32, _p, _p], ctypes.c_int),
+    "had_kv_check_copy_pages": ([_i32, _pi32, _pi32, _i32], ctypes.c_int),
+    "had_attn_check_prefix": ([_i32, _i32, _pi32, _i32, _pi32], ctypes.c_int),
     "had_kv_append": ([ctypes.POINTER(KvLayout), _p, _p, _p, _i32, _p, _p, _p, _i32, _i32, _p, _p], ctypes.c_int),
     "had_qk_norm_rope_gate": ([ctypes.POINTER(QknrgDesc), ctypes.POINTER(QknrgPtrs), _p], ctypes.c_int),
     "had_decode_attn_plan": ([ctypes.POINTER(AttnDesc), _pi32, _pi32], ctypes.c_int),
@@ -406,17 +408,50 @@ def _opt(t, name):
     return None if t is None else _dev(t, _torch().int32, name)
 
 
-def kv_copy_pages(k_pool, v_pool, src, dst):
-    """Copy whole pages src[i] -> dst[i] in both pools (src, dst: host ints)."""
+def kv_check_copy_pages(num_pages, src, dst):
+    """Host check of a page-copy list (see had_kv_check_copy_pages); src, dst
+    as host sequences or tensors.  Raises HadError."""
+    if hasattr(src, "cpu"):
+        src, dst = src.cpu().numpy(), dst.cpu().numpy()
+    s_a, sp = _i32_array(np.asarray(src).reshape(-1))
+    d_a, dp = _i32_array(np.asarray(dst).reshape(-1))
+    if len(s_a) != len(d_a):
+        raise ValueError("src and dst differ in length")
+    _check(lib().had_kv_check_copy_pages(int(num_pages), sp, dp, len(s_a)))
+
+
+def kv_copy_pages(k_pool, v_pool, src, dst, d_err=None):
+    """Copy whole pages src[i] -> dst[i] in both pools.  src, dst: int32 device
+    tensors (read when the copy runs; a -1 source marks an unused entry) or
+    host sequences (copied to the device first)."""
     torch = _torch()
     N, H_kv, P, D = k_pool.shape
     L = KvLayout(N, H_kv, P, D)
-    s_a, sp = _i32_array(src)
-    d_a, dp = _i32_array(dst)
-    if len(s_a) != len(d_a):
+    if not isinstance(src, torch.Tensor):
+        src = torch.tensor(np.asarray(src, dtype=np.int32).reshape(-1), device=k_pool.device)
+    if not isinstance(dst, torch.Tensor):
+        dst = torch.tensor(np.asarray(dst, dtype=np.int32).reshape(-1), device=k_pool.device)
+    if src.numel() != dst.numel():
         raise ValueError("src and dst differ in length")
+    if _debug():
+        kv_check_copy_pages(N, src, dst)
     _check(lib().had_kv_copy_pages(ctypes.byref(L), _dev(k_pool, torch.bfloat16, "k_pool"),
-                                   _dev(v_pool, torch.bfloat16, "v_pool"), sp, dp, len(s_a), _stream()))
+                                   _dev(v_pool, torch.bfloat16, "v_pool"), _dev(src, torch.int32, "src"),
+                                   _dev(dst, torch.int32, "dst"), src.numel(), _opt(d_err, "d_err"), _stream()))
+
+
+def attn_check_prefix(page_table, prefix_page_table):
+    """Host check of the cascade precondition (see had_attn_check_prefix):
+    every row of page_table [S, max_pages] begins with prefix_page_table.
+    Host arrays or tensors.  Raises HadError."""
+    if hasattr(page_table, "cpu"):
+        page_table = page_table.cpu().numpy()
+    if hasattr(prefix_page_table, "cpu"):
+        prefix_page_table = prefix_page_table.cpu().numpy()
+    pt = np.asarray(page_table, dtype=np.int32)
+    pa, pp = _i32_array(pt)
+    xa, xp = _i32_array(np.asarray(prefix_page_table).reshape(-1))
+    _check(lib().had_attn_check_prefix(pa.shape[0], pa.shape[1], pp, len(xa), xp))
 
 
 def kv_append(k_pool, v_pool, page_table, seq_lens, k_new, v_new, d_err=None):
@@ -510,6 +545,8 @@ def decode_attn_cascade(q, k_pool, v_pool, page_table, seq_lens, prefix_page_tab
     desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, 0, deterministic,
                      gate is not None)
     px = AttnPrefix(prefix_page_table.numel(), _dev(prefix_page_table, torch.int32, "prefix_page_table"))
+    if _debug():
+        attn_check_prefix(page_table, prefix_page_table)
     need = lib().had_decode_attn_cascade_workspace_bytes(ctypes.byref(desc), ctypes.byref(px))
     if need == 0:  # invalid descriptor or prefix: the call itself reports why
         _check(lib().had_decode_attn_cascade(ctypes.byref(desc), ctypes.byref(px), None, _stream()))

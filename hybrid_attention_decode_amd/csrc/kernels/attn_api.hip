@@ -57,8 +57,10 @@ int no_gate(const had_attn_desc* d, const char* who) {
 // Split plan over the pages a sequence can reach (max_seq_len, a host bound,
 // so the plan does not depend on device data).  Below 16 rows split i owns
 // the tiles [i*N/ns, (i+1)*N/ns) of the N = n * page_size / 8 tiles of 8
-// tokens (balanced to within one tile); at 16 or more rows the pages
-// [i*n/ns, (i+1)*n/ns) (within one page).
+// tokens (balanced to within one tile; such a range can start and end inside
+// a page, so it touches at most ceil(n/ns) + 1 pages, and the plan keeps
+// ceil(n/ns) <= 511 when ns > 1); at 16 or more rows the pages
+// [i*n/ns, (i+1)*n/ns) (within one page, at most 512).
 int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   const int64_t max_len = d->max_seq_len > 0 ? d->max_seq_len : static_cast<int64_t>(d->max_pages) * d->page_size;
   const int64_t n_pages = std::max<int64_t>(1, ceil_div(max_len, d->page_size));
@@ -74,11 +76,14 @@ int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
     const int64_t want = std::max<int64_t>(1, ceil_div(kTargetUnits, units));
     const int64_t min_pps = mfma ? ceil_div(256, d->page_size) : ceil_div(kMinTilesPerUnit, d->page_size / 8);
     ns = std::max<int64_t>(1, std::min<int64_t>(want, n_pages / min_pps));
-    // (with several splits a tile-aligned range can touch one page more)
-    if (n_pages > had::kMaxPagesPerSplit) ns = std::max<int64_t>(ns, ceil_div(n_pages, had::kMaxPagesPerSplit - 1));
+    // (below 16 rows, with several splits, a tile range can touch one page more)
+    const int64_t cap = mfma ? had::kMaxPagesPerSplit : had::kMaxPagesPerSplit - 1;
+    if (n_pages > had::kMaxPagesPerSplit) ns = std::max<int64_t>(ns, ceil_div(n_pages, cap));
   }
   const int64_t pps = ceil_div(n_pages, ns);
-  const int64_t pps_max = ns > 1 ? had::kMaxPagesPerSplit - 1 : had::kMaxPagesPerSplit;
+  // the VALU path's tile ranges can straddle one page more than their share
+  const bool tile_ranges = d->q_len * (d->H_q / d->H_kv) < 16;
+  const int64_t pps_max = (ns > 1 && tile_ranges) ? had::kMaxPagesPerSplit - 1 : had::kMaxPagesPerSplit;
   if (pps > pps_max)
     return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %lld splits leave %lld pages per split (max %lld)",
                 static_cast<long long>(ns), static_cast<long long>(pps), static_cast<long long>(pps_max));
@@ -375,6 +380,21 @@ static int cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int* 
     return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn_cascade: %d + %d splits (max %d)", *ns_p, *ns_s,
                 had::kMaxSplits);
   return HAD_OK;
+}
+
+int had_attn_check_prefix(int32_t n_seqs, int32_t max_pages, const int32_t* page_table, int32_t prefix_pages,
+                          const int32_t* prefix) {
+  if (n_seqs < 0 || max_pages < 1 || prefix_pages < 1 || prefix_pages > max_pages || !prefix ||
+      (n_seqs > 0 && !page_table))
+    return fail(HAD_ERR_INVALID_ARG, "attn_check_prefix: bad argument (n_seqs=%d max_pages=%d prefix_pages=%d)",
+                n_seqs, max_pages, prefix_pages);
+  for (int32_t s = 0; s < n_seqs; ++s)
+    for (int32_t i = 0; i < prefix_pages; ++i)
+      if (page_table[static_cast<size_t>(s) * max_pages + i] != prefix[i])
+        return fail(HAD_ERR_INVALID_ARG,
+                    "decode_attn_cascade: sequence %d holds page %d at prefix position %d, the prefix list page %d", s,
+                    page_table[static_cast<size_t>(s) * max_pages + i], i, prefix[i]);
+  return had::ok();
 }
 
 size_t had_decode_attn_cascade_workspace_bytes(const had_attn_desc* d, const had_attn_prefix* px) {

@@ -110,8 +110,10 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   const int npg_plan = pg1_plan - pg0;
   const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
   const int L = a.fixed_len >= 0 ? a.fixed_len : a.seq_lens[s];
-  // (a suffix pass also needs every query to see the whole prefix before pg_begin)
-  const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P);
+  // (a suffix pass also needs every query to see the whole prefix before
+  // pg_begin; a length past the plan's pages would leave tokens no split reads)
+  const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P ||
+                                           L > (a.pg_begin + a.n_pages_plan) * P);
   const int n_pages = bad_len ? 0 : (L + P - 1) / P;
   const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
   const int tok0 = pg0 * P;

@@ -199,8 +199,10 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
 
   const int L = a.seq_lens[s];  // (a scalar load: it does not queue behind the tiles)
 
-  // (a suffix pass also needs every query to see the whole prefix before pg_begin)
-  const bool bad_len = L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P;
+  // (a suffix pass also needs every query to see the whole prefix before
+  // pg_begin; a length past the plan's pages would leave tokens no split reads)
+  const bool bad_len = L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P ||
+                       L > (a.pg_begin + a.n_pages_plan) * P;
   // fused: the workgroup whose split holds the last position's tile owns the new tokens
   const int last_tile = (L - 1) / kTT - a.pg_begin * tpp;
   const bool own = FUSED && !bad_len && last_tile >= t0 && last_tile < t1;

@@ -50,21 +50,39 @@ __global__ __launch_bounds__(256) void kv_append_kernel(uint4* k_pool, uint4* v_
   }
 }
 
-struct CopyList {
-  int32_t src[32];
-  int32_t dst[32];
-};
-
 // blockIdx.y = pair index; blocks along x stride over the page's chunks.
-__global__ __launch_bounds__(256) void kv_copy_kernel(uint4* k_pool, uint4* v_pool, CopyList list, size_t chunks) {
-  const size_t src = static_cast<size_t>(list.src[blockIdx.y]) * chunks;
-  const size_t dst = static_cast<size_t>(list.dst[blockIdx.y]) * chunks;
+// The pairs live in device memory, so a captured graph can be replayed with
+// new pairs; a pair whose source is -1 is an unused entry.  Every block checks
+// its own pair before it touches a byte: ids in range (HAD_DERR_PAGE), and
+// its destination neither the source of an active pair nor the destination
+// of an earlier one (HAD_DERR_COPY) -- two such blocks would race on a page.
+// A pair that fails is skipped.
+__global__ __launch_bounds__(256) void kv_copy_kernel(uint4* k_pool, uint4* v_pool, const int32_t* d_src,
+                                                      const int32_t* d_dst, int n, int num_pages, size_t chunks,
+                                                      int32_t* d_err) {
+  const int i = blockIdx.y;
+  const int src = d_src[i], dst = d_dst[i];
+  if (src == -1) return;  // unused entry (uniform over the block)
+  if (src < 0 || src >= num_pages || dst < 0 || dst >= num_pages) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) set_err(d_err, HAD_DERR_PAGE);
+    return;
+  }
+  int clash = 0;
+  for (int k = threadIdx.x; k < n; k += blockDim.x) {
+    const int sk = d_src[k];
+    if (sk != -1 && (dst == sk || (k < i && dst == d_dst[k]))) clash = 1;
+  }
+  if (__syncthreads_or(clash)) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) set_err(d_err, HAD_DERR_COPY);
+    return;
+  }
+  const size_t so = static_cast<size_t>(src) * chunks, dof = static_cast<size_t>(dst) * chunks;
   for (size_t c = blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += static_cast<size_t>(gridDim.x) * blockDim.x) {
     // both loads first (source and destination pages differ, so the loads
     // never see either store)
-    const uint4 kx = k_pool[src + c], vx = v_pool[src + c];
-    k_pool[dst + c] = kx;
-    v_pool[dst + c] = vx;
+    const uint4 kx = k_pool[so + c], vx = v_pool[so + c];
+    k_pool[dof + c] = kx;
+    v_pool[dof + c] = vx;
   }
 }
 
@@ -85,37 +103,40 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int had_kv_copy_pages(const had_kv_layout* L, void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
-                      int32_t n, void* stream) {
+int had_kv_copy_pages(const had_kv_layout* L, void* k_pool, void* v_pool, const int32_t* d_src,
+                      const int32_t* d_dst, int32_t n, int32_t* d_err, void* stream) {
   int st = had::check_layout(L, "kv_copy_pages");
   if (st != HAD_OK) return st;
-  if (n < 0 || (n > 0 && (!src || !dst || !k_pool || !v_pool)))
-    return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: bad argument (n=%d)", n);
+  if (n < 0 || n > 65535 || (n > 0 && (!d_src || !d_dst || !k_pool || !v_pool)))
+    return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: bad argument (n=%d, at most 65535 pairs)", n);
   if (!had::aligned16(k_pool) || !had::aligned16(v_pool))
     return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: pools must be 16-byte aligned");
-  for (int32_t i = 0; i < n; ++i) {
-    if (src[i] < 0 || src[i] >= L->num_pages || dst[i] < 0 || dst[i] >= L->num_pages)
-      return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: pair %d (%d -> %d) outside [0, %d)", i, src[i], dst[i],
-                  L->num_pages);
-    for (int32_t k = 0; k < n; ++k)
-      if (dst[i] == src[k]) return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: page %d is both a source and a destination", dst[i]);
-    for (int32_t k = 0; k < i; ++k)
-      if (dst[i] == dst[k]) return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: destination %d repeated", dst[i]);
-  }
+  if (n == 0) return had::ok();
   const size_t chunks = static_cast<size_t>(L->H_kv) * L->page_size * L->head_dim / 8;
   const size_t blocks_x = std::min<size_t>(64, (chunks + 255) / 256);
-  for (int32_t i0 = 0; i0 < n; i0 += 32) {
-    had::CopyList list{};
-    const int m = std::min<int32_t>(32, n - i0);
-    for (int k = 0; k < m; ++k) {
-      list.src[k] = src[i0 + k];
-      list.dst[k] = dst[i0 + k];
+  hipLaunchKernelGGL(had::kv_copy_kernel, dim3(static_cast<unsigned>(blocks_x), n), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), d_src,
+                     d_dst, n, L->num_pages, chunks, d_err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(HAD_ERR_HIP, "kv_copy_pages: launch: %s", hipGetErrorString(e));
+  return had::ok();
+}
+
+int had_kv_check_copy_pages(int32_t num_pages, const int32_t* src, const int32_t* dst, int32_t n) {
+  if (num_pages < 1 || n < 0 || (n > 0 && (!src || !dst)))
+    return fail(HAD_ERR_INVALID_ARG, "kv_check_copy_pages: bad argument (num_pages=%d n=%d)", num_pages, n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (src[i] == -1) continue;
+    if (src[i] < 0 || src[i] >= num_pages || dst[i] < 0 || dst[i] >= num_pages)
+      return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: pair %d (%d -> %d) outside [0, %d)", i, src[i], dst[i],
+                  num_pages);
+    for (int32_t k = 0; k < n; ++k) {
+      if (src[k] == -1) continue;
+      if (dst[i] == src[k])
+        return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: page %d is both a source and a destination", dst[i]);
+      if (k < i && dst[i] == dst[k])
+        return fail(HAD_ERR_INVALID_ARG, "kv_copy_pages: destination %d repeated", dst[i]);
     }
-    hipLaunchKernelGGL(had::kv_copy_kernel, dim3(static_cast<unsigned>(blocks_x), m), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool),
-                       list, chunks);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(HAD_ERR_HIP, "kv_copy_pages: launch: %s", hipGetErrorString(e));
   }
   return had::ok();
 }

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define HAD_ABI_VERSION 4
+#define HAD_ABI_VERSION 5
 
 enum {
   HAD_OK = 0,
@@ -83,7 +83,10 @@ enum {
 enum {
   HAD_DERR_PAGE = 1,    /* page id < 0 or >= num_pages for a position < seq_len */
   HAD_DERR_SLOT = 2,    /* slot id >= n_slots, or out slot < 0                 */
-  HAD_DERR_SEQLEN = 4   /* seq_len < q_len (or T) or beyond max_pages*page_size */
+  HAD_DERR_SEQLEN = 4,  /* seq_len < q_len (or T), beyond max_pages*page_size,
+                           or (attention) beyond the pages the split plan covers */
+  HAD_DERR_COPY = 8     /* page-copy list: a destination that is also a source or
+                           repeats an earlier destination                      */
 };
 
 int had_abi_version(void);
@@ -269,12 +272,27 @@ typedef struct {
  * pair per attention layer.  One (page, head) is a contiguous block of
  * page_size * head_dim * 2 bytes. */
 
-/* Copy whole pages src[i] -> dst[i] (all heads) in both pools, i < n.
- * src, dst: HOST int32 arrays (ids are checked on the host: HAD_ERR_INVALID_ARG
- * when out of range or when a dst also appears as a src).  This is the device
- * half of copy-on-write (the triple from had_kvpt_reserve). */
+/* Copy whole pages d_src[i] -> d_dst[i] (all heads) in both pools, i < n
+ * (n <= 65535).  This is the device half of copy-on-write: the (src, dst) of
+ * the triple from had_kvpt_reserve (zubnet.ai TokenSpeed article, second
+ * paragraph: cached pages reused without being written).
+ * d_src, d_dst: DEVICE int32 [n], read when the copy runs, so a captured
+ * graph can be replayed with new pairs.  A pair with d_src[i] == -1 is an
+ * unused entry and copies nothing (a graph can carry a fixed number of
+ * entries).  Checked on the device, pair by pair, before any byte moves: a
+ * pair with an id outside [0, num_pages) sets HAD_DERR_PAGE, a pair whose
+ * destination is the source of an active pair (itself included) or the
+ * destination of an earlier active pair sets HAD_DERR_COPY; such a pair is
+ * skipped, the others are copied.  d_err: optional device word.
+ * had_kv_check_copy_pages runs the same checks on host copies of the arrays
+ * (the binding calls it when the environment sets HAD_DEBUG=1). */
 int had_kv_copy_pages(const had_kv_layout *L, void *k_pool, void *v_pool,
-                      const int32_t *src, const int32_t *dst, int32_t n, void *stream);
+                      const int32_t *d_src, const int32_t *d_dst, int32_t n, int32_t *d_err,
+                      void *stream);
+
+/* The checks of had_kv_copy_pages on host arrays src, dst (int32 [n]):
+ * HAD_ERR_INVALID_ARG names the first pair that the device would skip. */
+int had_kv_check_copy_pages(int32_t num_pages, const int32_t *src, const int32_t *dst, int32_t n);
 
 /* Raw append: write t_new tokens per sequence at positions
  * seq_lens[s] - t_new + j (seq_lens already include them).
@@ -338,8 +356,11 @@ int had_qk_norm_rope_gate(const had_qknrg_desc *d, const had_qknrg_ptrs *p, void
  * unit (s, h, split i of ns) covers, below 16 rows, the tiles
  * [i*N/ns, (i+1)*N/ns) (balanced to within one tile) and, at 16 rows or
  * more, the pages [i*n/ns, (i+1)*n/ns) (within one page); pages_per_split of
- * the plan = ceil(n/ns), at most 511 when ns > 1 (a tile range can touch one
- * page more, and one split reads at most 512), and writes an unnormalised partial
+ * the plan = ceil(n/ns), at most 512, and below 16 rows at most 511 when
+ * ns > 1 (a tile range can touch one page more, and one split reads at most
+ * 512); every seq_lens[s] must lie within the n pages (n * page_size tokens),
+ * else HAD_DERR_SEQLEN is set and the sequence is skipped (nothing written for
+ * it, the fused prologue's K/V rows included).  A unit writes an unnormalised partial
  * (o, m, l) to the workspace; a second kernel merges the partials by
  * log-sum-exp and writes bf16 (round to nearest even).  Query rows per KV
  * head = q_len * (H_q / H_kv); below 16 rows a VALU kernel runs, at 16 or
@@ -423,7 +444,8 @@ int had_decode_attn_combine(const had_attn_desc *d, int32_t num_splits,
  *
  * px->prefix_pages whole pages (>= 1) form the shared prefix; px's page list
  * must equal the first prefix_pages entries of every sequence's page-table
- * row (not checked), and every sequence must see the whole prefix:
+ * row (not checked on the device: had_attn_check_prefix checks host copies,
+ * and the binding runs it when HAD_DEBUG=1), and every sequence must see the whole prefix:
  * seq_lens[s] - q_len >= prefix_pages * page_size (HAD_DERR_SEQLEN in d_err
  * otherwise).  A prefix page still being written (a shared partial page) is
  * not part of it: such a page belongs to each sequence after copy-on-write.
@@ -437,6 +459,13 @@ typedef struct {
 } had_attn_prefix;
 
 size_t had_decode_attn_cascade_workspace_bytes(const had_attn_desc *d, const had_attn_prefix *px);
+
+/* Host check of the cascade's page-list precondition on host copies:
+ * page_table int32 [n_seqs][max_pages], prefix int32 [prefix_pages].
+ * HAD_ERR_INVALID_ARG names the first sequence whose row does not begin with
+ * the prefix's pages (e.g. a prefix page replaced by copy-on-write). */
+int had_attn_check_prefix(int32_t n_seqs, int32_t max_pages, const int32_t *page_table, int32_t prefix_pages,
+                          const int32_t *prefix);
 int had_decode_attn_cascade(const had_attn_desc *d, const had_attn_prefix *px, const had_attn_ptrs *p,
                             void *stream);
 

@@ -125,6 +125,57 @@ def test_long_context_attention_layer(L0):
     assert_attn_close(out[0], ref)
 
 
+# The benchmark's launch: bench.py's long-context step calls
+# had_decode_attn_layer (prologue fused into the VALU partial kernel, gated
+# output) with max_seq_len = L0 + warmup + steps + 2, which fixes the split
+# plan (256 splits, tile ranges inside 9 / 17 / 65-page spans).  Its default
+# run (10 + 256 steps) and a short run (5 + 20 steps) give different plans.
+@pytest.mark.parametrize("L0,extra,at", [
+    (131072, 268, 1), (131072, 268, 268), (131072, 27, 27), (262144, 268, 1), (1048576, 268, 1)])
+def test_long_context_fused_gated_layer_bench_plan(L0, extra, at):
+    seed, H_q, T = 350 + L0 % 89 + at, 8, 1
+    L = L0 + at                                  # the decode token at position L - 1
+    max_len = L0 + extra
+    n_pages = -(-L // P)
+    max_pages = -(-max_len // P) + 1             # as the benchmark's stack
+    N = max_pages + 4
+    pages = synth.permutation(N, synth.seed_of(seed, 0))[:n_pages]
+    pt = np.full((1, max_pages), -1, np.int32)
+    pt[0, :n_pages] = pages
+    desc = had.attn_desc((1, 1, H_q, D), (N, H_KV, P, D), max_pages, max_seq_len=max_len, gated=True)
+    ns, pps = had.decode_attn_plan(desc)
+    _say("fused gated layer L0=%d L=%d plan: %d splits, %d pages per split" % (L0, L, ns, pps))
+    assert ns == 256
+    kd, vd, kb, vb = _pools(seed, N)
+    qg, k, v, w_q, w_k = _prologue_inputs(seed, 1, T, H_q)
+    pt_d, lens_d = to_dev(pt), to_dev(np.array([L], np.int32))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(had.decode_attn_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    out = torch.empty((1, 1, H_q, D), dtype=torch.bfloat16, device=DEV)
+    gate = torch.empty_like(out)
+    q_out = torch.empty_like(out)
+    had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), pt_d, lens_d, kd, vd, R,
+                          max_seq_len=max_len, workspace=ws, out=out, gate_out=gate, q_out=q_out, d_err=err,
+                          gated=True)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    q_ref, k_new, v_new = _oracle_prologue(qg, k, v, w_q, w_k, 0, [L - 1])
+    # q and the new K/V row (within 1 bf16 ulp of the fp64 value; v and the gate bit-exact)
+    assert np.all(np.abs(bf16.to_f64(bits_of(q_out)[0]) - q_ref) <= bf16.ulp(q_ref))
+    assert np.array_equal(bits_of(gate)[0], bits_of(qg)[0, :, :, 1])
+    page, row = pages[(L - 1) // P], (L - 1) % P
+    kb_after, vb_after = bits_of(kd), bits_of(vd)
+    assert np.all(np.abs(bf16.to_f64(kb_after[page, :, row]) - k_new[0]) <= bf16.ulp(k_new[0]))
+    assert np.array_equal(vb_after[page, :, row], bits_of(v)[0, 0])
+    kb_after[page, :, row] = kb[page, :, row]
+    vb_after[page, :, row] = vb[page, :, row]
+    assert np.array_equal(kb_after, kb) and np.array_equal(vb_after, vb)      # nothing else written
+    K, V = _context(kb, vb, pages, L - 1)
+    ref = A.attention(q_ref, np.concatenate([K, k_new]), np.concatenate([V, v_new]), 1.0 / np.sqrt(D))
+    ref = Pr.output_gate(ref, bf16.to_f64(bits_of(qg)[0, :, :, 1]))
+    assert_attn_close(out[0], ref)
+
+
 # ---------------------------------------------------------------- speculative
 
 def test_speculative_verify_rollback_256k():
@@ -432,3 +483,119 @@ def test_gdn_prefill_first_turn_50k():
         for h in range(GH):
             rel = np.linalg.norm(oc[t, h] - o_ref[t, h]) / max(np.linalg.norm(o_ref[t, h]), 1e-30)
             assert rel <= 1e-4, (t, h, rel)
+
+
+def test_agentic_turn_resumes_from_the_prefix_cache():
+    """A turn of the agentic loop ends: the conversation goes into the radix
+    prefix cache (its pages and the GDN checkpoint slot) and the request is
+    freed.  The next turn starts from had_radix_match -> had_kvpt_seq_create_from
+    on the matched pages and reads the cached checkpoint slot (never writing
+    it); its first append copies the shared partial page on the device.
+    Attention and the GDN state after the resumed steps must equal the oracle
+    run over the whole history."""
+    seed, H_q, first, per = 650, 8, 50000, 800
+    max_pages = -(-(first + 2 * per + 2) // P) + 1
+    N = max_pages + 8
+    n_slots = 8
+    pt = had.PageTable(N, P, 2, max_pages, free_order=synth.permutation(N, synth.seed_of(seed, 0)))
+    slots = had.SlotPool(n_slots, free_order=synth.permutation(n_slots, synth.seed_of(seed, 1)))
+    cache = had.RadixCache(pt, slots)
+    tokens = synth.integers(0, 49, first + 2 * per + 2, synth.seed_of(seed, 2)).astype(np.int32)
+    sq = pt.seq_create()
+    pt.reserve(sq, first)
+    _say("agentic resume: %d-token first turn + %d steps, cache, %d resumed steps" % (first, per, per))
+    kd, vd, kb, vb = _pools(seed, N)
+    cur = cur0 = slots.acquire()
+    pool0 = np.zeros((n_slots, GH, DV, DK), np.float32)
+    pool0[cur] = _warm_state(seed)
+    pool_d = to_dev(pool0)
+    steps = 2 * per
+    qg, k, v, w_q, w_k = _prologue_inputs(seed, steps, 1, H_q)
+    gq, gk, gv, gal, gbe = _gdn_inputs(seed, steps, 1)
+    qg_d, k_d, v_d, wq_d, wk_d = to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k)
+    gdn_d = [to_dev(x) for x in (gq, gk, gv, gal, gbe)]
+    table0, _ = pt.export([sq], max_pages)
+    first_pages = table0[0, :-(-first // P)].copy()
+    lens_d = torch.zeros(1, dtype=torch.int32, device=DEV)
+    in_d = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out_d = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    src_d = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    dst_d = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    max_len = first + steps + 1
+    desc = had.attn_desc((1, 1, H_q, D), kd.shape, max_pages, max_seq_len=max_len, gated=True)
+    ws = torch.empty(had.decode_attn_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    sampled = {}
+    first_resumed = []
+    n_cow = 0
+
+    def decode(t, seq, L):
+        nonlocal cur, n_cow
+        out_slot = slots.acquire()
+        trip = pt.reserve(seq, 1)
+        if trip is not None:                                # the cache shares the partial last page
+            src_d.fill_(int(trip[0]))
+            dst_d.fill_(int(trip[1]))
+            had.kv_copy_pages(kd, vd, src_d, dst_d, d_err=err)
+            n_cow += 1
+        table, _ = pt.export([seq], max_pages)
+        lens_d.fill_(L + 1)
+        in_d.fill_(cur)
+        out_d.fill_(out_slot)
+        out, _ = had.decode_attn_layer(qg_d[t:t + 1], k_d[t:t + 1], v_d[t:t + 1], wq_d, wk_d, to_dev(table), lens_d,
+                                       kd, vd, R, max_seq_len=max_len, workspace=ws, d_err=err, gated=True)
+        had.gdn_state_update(pool_d, in_d, out_d, *[x[t:t + 1] for x in gdn_d], d_err=err)
+        if t in (0, per, per + 1, steps - 1):
+            sampled[t] = out.clone()
+        if t == per:                                        # the first step read from the cached checkpoint
+            first_resumed.append(pool_d[out_slot].clone())
+        slots.release(cur)
+        cur = out_slot
+
+    for t in range(per):                                    # turn 1
+        decode(t, sq, first + t)
+    L = first + per
+    torch.cuda.synchronize()
+    row = pt.export([sq], max_pages)[0][0]
+    cache.insert(tokens[:L], row[:-(-L // P)], cur)
+    ckpt_slot = cur
+    ckpt_bits = pool_d[ckpt_slot].cpu().numpy().copy()
+    pt.seq_free(sq)                                         # the request ends; the cache keeps pages + slot
+    slots.release(cur)
+
+    m, slot, pages, lock = cache.match(tokens[:L + 1])      # the next turn: the whole history + one token
+    assert m == L and slot == ckpt_slot
+    sq2 = pt.seq_create_from(pages, m)
+    slots.retain(slot)
+    cur = slot
+    for t in range(per, steps):                             # turn 2, resumed from the cache
+        decode(t, sq2, first + t)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert n_cow == 1
+    assert np.array_equal(pool_d[ckpt_slot].cpu().numpy(), ckpt_bits)     # the checkpoint was never written
+
+    # oracle: the whole history (prior context, then every decoded row) in fp64
+    _, k_rows, v_rows = _oracle_prologue(
+        qg.reshape(1, steps, H_q, 2, D), k.reshape(1, steps, H_KV, D), v.reshape(1, steps, H_KV, D), w_q, w_k, 0,
+        np.arange(first, first + steps))
+    K0, V0 = _context(kb, vb, first_pages, first)
+    scale = 1.0 / np.sqrt(D)
+    for t, o in sampled.items():
+        q_ref, _, _ = _oracle_prologue(qg, k, v, w_q, w_k, t, [first + t])
+        ref = A.attention(q_ref, np.concatenate([K0, k_rows[:t + 1]]), np.concatenate([V0, v_rows[:t + 1]]), scale)
+        ref = Pr.output_gate(ref, bf16.to_f64(bits_of(qg)[t, :, :, 1]))
+        assert_attn_close(o[0], ref)
+    f = [_gdn_f64(x)[:, 0] for x in (gq, gk, gv, gal, gbe)]
+    # the first resumed step, from the fp32 checkpoint it read: per-step tolerance
+    S1, _ = gdn.sequential_heads(ckpt_bits.astype(np.float64), *[x[per:per + 1] for x in f])
+    got1 = first_resumed[0].cpu().numpy().astype(np.float64)
+    for h in range(GH):
+        assert _rel_fro(got1[h], S1[h]) <= 1e-4, h
+    # the whole chain in fp64 from the initial state: chain tolerance
+    S, _ = gdn.sequential_heads(pool0[cur0].astype(np.float64), *[x[:steps] for x in f])
+    got = pool_d[cur].cpu().numpy().astype(np.float64)
+    for h in range(GH):
+        assert _rel_fro(got[h], S[h]) <= 1e-3, h
+    cache.unlock(lock)
+    cache.close()

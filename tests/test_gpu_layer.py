@@ -29,7 +29,7 @@ def _inputs(seed, S, T, H_q, H_kv, D):
     return qg, k, v, w_q, w_k
 
 
-def _run(seed, lens, T, H_q, H_kv, D, R, P, num_splits=0, deterministic=False, gated=False):
+def _run(seed, lens, T, H_q, H_kv, D, R, P, num_splits=0, deterministic=False, gated=False, max_seq_len=0):
     _, k_pool, v_pool, pt, L = paged_case(seed, lens, T, H_q, H_kv, D, P)
     qg, k, v, w_q, w_k = _inputs(seed, len(lens), T, H_q, H_kv, D)
     print("case seed=%d lens=%s T=%d H_q=%d H_kv=%d D=%d R=%d P=%d splits=%d gated=%d" % (
@@ -39,7 +39,7 @@ def _run(seed, lens, T, H_q, H_kv, D, R, P, num_splits=0, deterministic=False, g
     q_out = torch.empty((len(lens), T, H_q, D), dtype=torch.bfloat16, device=DEV)
     out, gate = had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt),
                                       to_dev(L), kd, vd, R, num_splits=num_splits, q_out=q_out, d_err=err,
-                                      deterministic=deterministic, gated=gated)
+                                      deterministic=deterministic, gated=gated, max_seq_len=max_seq_len)
     torch.cuda.synchronize()
     assert err.item() == 0
     return dict(k_pool=k_pool, v_pool=v_pool, pt=pt, L=L, qg=qg, k=k, v=v, w_q=w_q, w_k=w_k, kd=kd, vd=vd,
@@ -204,3 +204,37 @@ def test_disagreeing_descriptors_are_rejected():
                               torch.zeros((1, 4), dtype=torch.int32, device=DEV),
                               torch.tensor([20], dtype=torch.int32, device=DEV), pool, pool.clone(), 16)
     assert e.value.kind == "unsupported_shape"          # T = 9 > 8
+
+
+def test_split_touching_512_pages():
+    # 4 rows, 64-token pages, 1532 planned pages over 3 splits: split 1's
+    # tiles [4085, 8170) start and end inside pages 510 and 1021, so it reads
+    # 512 page ids, the most a split holds; the context ends inside page 1531
+    L = 1532 * 64 - 20
+    c = _run(2800, [L], 1, 4, 1, 64, 16, 64, num_splits=3, max_seq_len=1532 * 64, gated=True)
+    _check_against_oracle(c)
+
+
+def test_length_beyond_the_split_plan_is_reported_and_writes_nothing():
+    # max_seq_len bounds the plan (15 pages of 64 = 960 tokens); a length of
+    # 1000 lies past it: the fused layer reports HAD_DERR_SEQLEN and neither
+    # attends nor writes the new token's K/V
+    _, k_pool, v_pool, pt, L = paged_case(2900, [1000], 1, 8, 1, 128, 64)
+    qg, k, v, w_q, w_k = _inputs(2900, 1, 1, 8, 1, 128)
+    kd, vd = to_dev(k_pool), to_dev(v_pool)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("case length past the plan (fused VALU)", flush=True)
+    had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L), kd, vd,
+                          32, max_seq_len=900, d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_SEQLEN
+    assert np.array_equal(bits_of(kd), bits_of(k_pool), equal_nan=True)
+    assert np.array_equal(bits_of(vd), bits_of(v_pool), equal_nan=True)
+    # the plain call, VALU (8 rows) and MFMA (64 rows), reports it too
+    for H_q, q_len in ((8, 1), (16, 4)):
+        q, kp, vp, pt2, L2 = paged_case(2901 + H_q, [1000], q_len, H_q, 1, 128, 64)
+        err.zero_()
+        print("case length past the plan (decode_attn, %d rows)" % (H_q * q_len), flush=True)
+        had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt2), to_dev(L2), max_seq_len=900, d_err=err)
+        torch.cuda.synchronize()
+        assert err.item() & had.DERR_SEQLEN

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(L, name), name
     assert declared == had.exported_symbols()
-    assert had.abi_version() == 4
+    assert had.abi_version() == 5
 
 
 def test_scenario_on_the_cpp_manager():
@@ -211,3 +211,45 @@ def test_attention_split_plan():
     desc = had.attn_desc((n, 1, 8, D), (4096, 1, 64, D), pages, max_seq_len=max_len)
     ws = had.decode_attn_cascade_workspace_bytes(desc, 781)
     assert ws == n * 1 * (195 + 16) * rows * (D + 2) * 4
+
+
+def test_split_page_cap_applies_to_tile_ranges_only():
+    # below 16 rows a split's tile range can straddle one page more than its
+    # share, so ceil(n / ns) <= 511 when ns > 1; the MFMA path's ranges are
+    # whole pages and may hold 512
+    def plan(q_shape, pages, ns):
+        return had.decode_attn_plan(had.attn_desc(q_shape, (pages + 2, 1, 64, 64), pages, num_splits=ns))
+    assert plan((1, 1, 4, 64), 1532, 3) == (3, 511)          # split 1 touches pages 510..1021: 512 ids
+    with pytest.raises(HadError):
+        plan((1, 1, 4, 64), 1024, 2)                          # 512 pages per split, a range could need 513
+    assert plan((1, 4, 16, 64), 1024, 2) == (2, 512)         # MFMA: page ranges, 512 allowed
+    with pytest.raises(HadError):
+        plan((1, 4, 16, 64), 1026, 2)                         # 513 pages per split
+    assert plan((1, 1, 4, 64), 512, 1) == (1, 512)           # one split reads the whole range
+
+
+def test_page_copy_list_check():
+    ok = [([3, -1, 5], [7, 0, 8]), ([], []), ([-1, -1], [3, 3])]
+    for src, dst in ok:
+        had.kv_check_copy_pages(10, src, dst)
+    bad = [([3], [10]),            # destination out of range
+           ([-2], [1]),            # only -1 marks an unused entry
+           ([3, 4], [4, 5]),       # 4 is a destination and a source
+           ([3, 4], [6, 6]),       # destination repeated
+           ([3], [3])]             # copy onto itself
+    for src, dst in bad:
+        with pytest.raises(HadError):
+            had.kv_check_copy_pages(10, src, dst)
+    with pytest.raises(ValueError):
+        had.kv_check_copy_pages(10, [1, 2], [3])
+
+
+def test_cascade_prefix_check():
+    pt = np.array([[4, 9, 2, 7], [4, 9, 5, -1], [4, 9, 2, 1]], np.int32)
+    had.attn_check_prefix(pt, [4, 9])
+    with pytest.raises(HadError, match="sequence 1"):
+        had.attn_check_prefix(pt, [4, 9, 2])                 # sequence 1's third page was copied on write
+    with pytest.raises(HadError):
+        had.attn_check_prefix(pt, [4, 8])
+    with pytest.raises(HadError):
+        had.attn_check_prefix(pt, [4, 9, 2, 7, 0])           # longer than a row
