@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     decode_attn_cascade_workspace_bytes,
     decode_attn_combine,
     decode_attn_layer,
+    decode_attn_layer_static,
     decode_attn_partial,
     decode_attn_plan,
     decode_attn_workspace_bytes,

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "../host/status.h"
 #include "attn_internal.h"
@@ -108,6 +109,36 @@ size_t ws_q_offset(const had_attn_desc* d, int ns) { return (ws_partials_bytes(d
 size_t ws_bytes(const had_attn_desc* d, int ns) {
   return ws_q_offset(d, ns) +
          static_cast<size_t>(d->n_seqs) * d->q_len * d->H_q * d->head_dim * sizeof(uint16_t);
+}
+
+// Workspace of had_decode_attn_layer_static: one array per GPU, in the code
+// object's device memory (allocated when the library's kernels are loaded on
+// a device, held until the process ends).  Host code never uses its name as
+// an address: the device address comes from hipGetSymbolAddress, once per
+// device, and is kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[HAD_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn_layer_static: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HAD_ERR_HIP, "decode_attn_layer_static: device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HAD_ERR_HIP, "decode_attn_layer_static: hipGetSymbolAddress on device %d: %s", dev,
+                  hipGetErrorString(e));
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return HAD_OK;
 }
 
 }  // namespace
@@ -308,6 +339,25 @@ int had_decode_attn_layer(const had_attn_desc* d, const had_qknrg_desc* pd, cons
   // the gate half of each head's (q, gate) pair in qg
   st = launch_combine_after(d, a, out, stream, static_cast<const uint16_t*>(pp->qg) + d->head_dim, 2 * d->head_dim);
   return st == HAD_OK ? had::ok() : st;
+}
+
+int had_decode_attn_layer_static(const had_attn_desc* d, const had_qknrg_desc* pd, const had_qknrg_ptrs* pp,
+                                 void* out, void* stream) {
+  if (!out) return fail(HAD_ERR_INVALID_ARG, "decode_attn_layer_static: out is NULL");
+  int st = check_desc(d);
+  if (st != HAD_OK) return st;
+  int ns, pps;
+  st = plan(d, &ns, &pps, nullptr);
+  if (st != HAD_OK) return st;
+  const size_t need = ws_bytes(d, ns);
+  if (need > HAD_STATIC_WORKSPACE_BYTES)
+    return fail(HAD_ERR_WORKSPACE_TOO_SMALL,
+                "decode_attn_layer_static: the layer needs %zu workspace bytes, the static array holds %zu", need,
+                static_cast<size_t>(HAD_STATIC_WORKSPACE_BYTES));
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != HAD_OK) return st;
+  return had_decode_attn_layer(d, pd, pp, ws, HAD_STATIC_WORKSPACE_BYTES, out, stream);
 }
 
 int had_decode_attn_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd, const had_qknrg_ptrs* pp,

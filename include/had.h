@@ -496,6 +496,24 @@ int had_decode_attn_cascade(const had_attn_desc *d, const had_attn_prefix *px, c
 int had_decode_attn_layer(const had_attn_desc *d, const had_qknrg_desc *pd, const had_qknrg_ptrs *pp,
                           void *workspace, size_t workspace_bytes, void *out, void *stream);
 
+/* Allocation-free form of had_decode_attn_layer, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split-K workspace is an array of
+ * HAD_STATIC_WORKSPACE_BYTES inside the library, one per GPU, held from the
+ * time the library's kernels are loaded on that GPU until the process ends;
+ * the caller passes only inputs and outputs.  Same operation, arguments and
+ * results as had_decode_attn_layer.  The call allocates nothing; the first
+ * call on each device looks up that device's array address
+ * (hipGetSymbolAddress), so make it outside graph capture.
+ * HAD_ERR_WORKSPACE_TOO_SMALL when had_decode_attn_workspace_bytes(d) exceeds
+ * the array (e.g. 64 query rows x 256 splits x head_dim 256 need 17 MB).
+ * Every call on one GPU uses that GPU's single array and leaves its partials
+ * there: calls that overlap in time on one GPU (two streams, two host
+ * threads) race on it and must be ordered by the caller. */
+#define HAD_STATIC_WORKSPACE_BYTES (32u << 20)
+int had_decode_attn_layer_static(const had_attn_desc *d, const had_qknrg_desc *pd, const had_qknrg_ptrs *pp,
+                                 void *out, void *stream);
+
 /* Its first half: the prologue and the partials only (workspace layout of
  * had_decode_attn); had_decode_attn_combine finishes. */
 int had_decode_attn_layer_partial(const had_attn_desc *d, const had_qknrg_desc *pd, const had_qknrg_ptrs *pp,
