@@ -12,6 +12,7 @@
 #include "../host/status.h"
 #include "attn_internal.h"
 #include "had.h"
+#include "prologue_math.h"
 
 using had::fail;
 
@@ -299,7 +300,7 @@ static int launch_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd
   f.v_pool = static_cast<uint16_t*>(pp->v_pool);
   f.gate_out = static_cast<uint16_t*>(pp->gate_out);
   f.q_out = static_cast<uint16_t*>(pp->q_out);
-  f.rope_base = pd->rope_base;
+  f.rope_coef = had::rope_coef(pd->rope_base, pd->rotary_dim);
   f.eps = pd->eps;
   f.R = pd->rotary_dim;
   had_attn_ptrs p{};

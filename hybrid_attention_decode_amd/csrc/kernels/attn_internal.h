@@ -57,7 +57,7 @@ struct FusedArgs {
   uint16_t* v_pool;
   uint16_t* gate_out;     // [n_seqs][q_len][H_q][D]
   uint16_t* q_out;        // optional, same layout
-  double rope_base;
+  double rope_coef;       // -2 log2(rope base) / R (rope_coef())
   float eps;
   int R;                  // rotary dims
 };

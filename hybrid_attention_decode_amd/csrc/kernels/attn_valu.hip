@@ -74,40 +74,47 @@ struct Lds {
   uint16_t knew[kRows][256];         // fused: the new tokens' K rows (bf16, normalised and rotated)
   uint16_t vnew[kRows][256];         // fused: the new tokens' V rows
   uint32_t p[kWaves][4][kRows];     // bf16 p pairs: [pair][row]
-  float alpha[kWaves + 1][kRows];   // per-row rescale factor of the current tile; merge weights
+  float alpha[kWaves][kRows];       // per-row rescale factor of the current tile
   int32_t pages[kMaxPagesPerSplit];  // page ids of the workgroup's range (-1 = invalid)
   int next;                          // next tile to claim
   int err;                           // HAD_DERR bits seen by the workgroup
 };
 
 // K and V of one 8-token tile: page `pid`, tile `tip` inside the page.
-// The loads carry the non-temporal hint: every K/V byte is read once per
-// launch, and streaming the context through the caches would evict what the
-// rest of the decode step reuses (recurrent states, page tables, the
-// partials the merge reads); measured on the 48-layer step it is also the
-// faster stream (1M context: 6.4 instead of 5.8 TB/s).
+// Buffer loads over one (page, KV head) block: a refill past the split's
+// last tile passes live = false, its descriptor covers 0 bytes and the loads
+// return zeros without a memory request (the wave would otherwise wait for
+// a useless 8 KB re-read before it leaves the loop), and no offset can leave
+// the block.  The loads carry the non-temporal hint: every K/V byte is read
+// once per launch, and streaming the context through the caches would evict
+// what the rest of the decode step reuses (recurrent states, page tables,
+// the partials the merge reads); measured on the 48-layer step it is also
+// the faster stream (1M context: 6.4 instead of 5.8 TB/s).
 template <int D>
-__device__ __forceinline__ void load_tile_at(Tile<D>& T, const ValuArgs& a, int pid, int tip, int h, int tg, int j,
-                                             int tgv, int dl) {
+__device__ __forceinline__ void load_tile_at(Tile<D>& T, const ValuArgs& a, int pid, int tip, bool live, int h, int tg,
+                                             int j, int tgv, int dl) {
   using C = Cfg<D>;
-  typedef uint32_t nt4_t __attribute__((ext_vector_type(4)));
-  typedef uint32_t nt2_t __attribute__((ext_vector_type(2)));
   const int pu = __builtin_amdgcn_readfirstlane(pid);
-  const size_t base = ((static_cast<size_t>(pu) * a.H_kv + h) * a.page_size + tip * kTT) * D;
-  const uint16_t* kb = a.k_pool + base;
-  const uint16_t* vb = a.v_pool + base;
+  const int nbytes = __builtin_amdgcn_readfirstlane(live ? a.page_size * D * 2 : 0);
+  const size_t blk = (static_cast<size_t>(pu) * a.H_kv + h) * a.page_size * D;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k_pool + blk), 0, nbytes,
+                                                                      kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_pool + blk), 0, nbytes,
+                                                                      kBufferRsrcWord3);
+  const int t0 = tip * kTT;
 #pragma unroll
   for (int i = 0; i < C::TS; ++i)
 #pragma unroll
     for (int c = 0; c < C::CH; ++c) {
-      const nt4_t x = __builtin_nontemporal_load(
-          reinterpret_cast<const nt4_t*>(kb + (i * C::TPS + tg) * D + (j + c * C::LPT) * 8));
-      T.k[i][c] = make_uint4(x.x, x.y, x.z, x.w);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, ((t0 + i * C::TPS + tg) * D + (j + c * C::LPT) * 8) * 2,
+                                                           0, kBufferNT);
+      T.k[i][c] = make_uint4(x[0], x[1], x[2], x[3]);
     }
 #pragma unroll
   for (int i = 0; i < C::VPL; ++i) {
-    const nt2_t x = __builtin_nontemporal_load(reinterpret_cast<const nt2_t*>(vb + (tgv + C::TG * i) * D + dl * C::DPL));
-    T.v[i] = make_uint2(x.x, x.y);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(vr, ((t0 + tgv + C::TG * i) * D + dl * C::DPL) * 2, 0,
+                                                        kBufferNT);
+    T.v[i] = make_uint2(x[0], x[1]);
   }
 }
 
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
 #pragma unroll
   for (int b = 0; b < 2; ++b) pid0[b] = (pid0[b] < 0 || pid0[b] >= a.num_pages) ? 0 : pid0[b];
   __builtin_amdgcn_sched_barrier(0);
-  load_tile_at<D>(buf[0], a, pid0[0], tcur[0] % tpp, h, tg, j, tgv, dl);
+  load_tile_at<D>(buf[0], a, pid0[0], tcur[0] % tpp, tcur[0] < tile_hi, h, tg, j, tgv, dl);
   __builtin_amdgcn_sched_barrier(0);
 
   const int L = a.seq_lens[s];  // (a scalar load: it does not queue behind the tiles)
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
     float* xrow = &sh.o[wave][0][0];
     if (a.row_base + wave < a.rows) {
       uint16_t y[E];
-      row_norm_rope<D>(f_qin, L - a.q_len + f_j, f.R, f.rope_base, f.eps, xrow, lane, y);
+      row_norm_rope<D>(f_qin, L - a.q_len + f_j, f.R, f.rope_coef, f.eps, xrow, lane, y);
       const size_t orow = ((static_cast<size_t>(s) * a.q_len + f_j) * a.H_q + f_hq) * D;
       const uint16_t* gate = f.qg + ((static_cast<size_t>(s) * a.q_len + f_j) * a.H_q + f_hq) * 2 * D + D;
 #pragma unroll
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
       // the new token `wave`: normalised, rotated key into the pool and LDS
       const int pos = L - a.q_len + wave;
       uint16_t y[E];
-      row_norm_rope<D>(f_kin, pos, f.R, f.rope_base, f.eps, xrow, lane, y);
+      row_norm_rope<D>(f_kin, pos, f.R, f.rope_coef, f.eps, xrow, lane, y);
       const int pid = pt_row[pos / P];
       const bool ok = pid >= 0 && pid < a.num_pages;
       const size_t dst = ((static_cast<size_t>(ok ? pid : 0) * a.H_kv + h) * P + pos % P) * D;
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   const int lim_min = FUSED ? L - a.q_len : L - a.q_len + 1;  // every row sees positions below this
   const int kv_end = FUSED ? L - a.q_len : L;                   // V rows at or past this are zeroed
 
-  load_tile_at<D>(buf[1], a, pid0[1], tcur[1] % tpp, h, tg, j, tgv, dl);
+  load_tile_at<D>(buf[1], a, pid0[1], tcur[1] % tpp, tcur[1] < tile_hi, h, tg, j, tgv, dl);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   };
   auto refill = [&](Tile<D>& T, int& tc) __attribute__((always_inline)) {
     // claim the next tile for this buffer and start its loads; past the end
-    // the loads re-read the last tile (never used)
+    // the loads cover no bytes (zeros, never used)
     int nxt = tc + 2 * kWaves;
     if (!a.deterministic) {
       if (lane == 0) nxt = atomicAdd(&sh.next, 1);
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
     tc = nxt;
     const int nc = min(nxt, ntiles - 1);
     const int pid = sh.pages[nc / tpp];
-    load_tile_at<D>(T, a, pid < 0 ? 0 : pid, nc % tpp, h, tg, j, tgv, dl);
+    load_tile_at<D>(T, a, pid < 0 ? 0 : pid, nc % tpp, nxt < ntiles, h, tg, j, tgv, dl);
     // keep the refill here: the scheduler would otherwise sink it below the
     // wait for the other buffer, halving the prefetch distance
     __builtin_amdgcn_sched_barrier(0);
@@ -510,40 +517,44 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   if (errs) atomicOr(&sh.err, errs);
   __syncthreads();
   if (threadIdx.x == 0 && sh.err) set_err(a.d_err, sh.err);
-  const int n_parts = (FUSED && own) ? kWaves + 1 : kWaves;  // partials to merge
+  const int n_parts = (FUSED && own) ? kWaves + 1 : kWaves;  // partials to merge (uniform)
 
-  // ---- merge the waves and store the split's partial: the per-row wave
-  // weights once (kRows threads), then one float4 of one row per thread
+  // ---- merge the waves and store the split's partial: one float4 of one
+  // row per thread, each thread forming its row's wave weights itself (the
+  // (m, l) reads are LDS broadcasts), so the merge needs no second barrier
   const size_t unit = (static_cast<size_t>(s) * a.H_kv + h) * a.ns_total + a.split_offset + sp;
-  if (threadIdx.x < kRows) {
-    const int r = threadIdx.x;
-    float M = -INFINITY;
-    for (int w = 0; w < n_parts; ++w) M = fmaxf(M, sh.ml[w][r][0]);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float lsum = 0.f;
-    for (int w = 0; w < n_parts; ++w) {
-      const float wt = exp2f(sh.ml[w][r][0] - Ms);
-      sh.alpha[w][r] = wt;  // (the per-tile rescale slots are free now)
-      lsum += wt * sh.ml[w][r][1];
-    }
-    const int row = a.row_base + r;
-    if (row < a.rows) {
-      a.ws_ml[(unit * a.ws_rows + row) * 2 + 0] = M;
-      a.ws_ml[(unit * a.ws_rows + row) * 2 + 1] = lsum;
-    }
-  }
-  __syncthreads();
   for (int idx = threadIdx.x; idx < kRows * D / 4; idx += blockDim.x) {
     const int r = idx / (D / 4), c4 = idx % (D / 4);
     const int row = a.row_base + r;
     if (row >= a.rows) continue;
+    // every LDS read first (part kWaves is read even when absent and then
+    // not used), then the arithmetic
+    float2 ml[kWaves + 1];
+    float4 o4[kWaves + 1];
+#pragma unroll
+    for (int w = 0; w <= kWaves; ++w) {
+      ml[w] = *reinterpret_cast<const float2*>(&sh.ml[w][r][0]);
+      o4[w] = *reinterpret_cast<const float4*>(&sh.o[w][r][4 * c4]);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w <= kWaves; ++w) M = fmaxf(M, w < n_parts ? ml[w].x : -INFINITY);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float lsum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int w = 0; w < n_parts; ++w) {
-      const float wt = sh.alpha[w][r];
-      const float4 o4 = *reinterpret_cast<const float4*>(&sh.o[w][r][4 * c4]);
-      acc.x += wt * o4.x; acc.y += wt * o4.y; acc.z += wt * o4.z; acc.w += wt * o4.w;
+#pragma unroll
+    for (int w = 0; w <= kWaves; ++w) {
+      // (v_exp_f32: a weight below 2^-126 flushes to 0)
+      const float wt = __builtin_amdgcn_exp2f(ml[w].x - Ms);
+      const bool use = w < n_parts;
+      lsum += use ? wt * ml[w].y : 0.f;
+      acc.x += use ? wt * o4[w].x : 0.f;
+      acc.y += use ? wt * o4[w].y : 0.f;
+      acc.z += use ? wt * o4[w].z : 0.f;
+      acc.w += use ? wt * o4[w].w : 0.f;
     }
     *reinterpret_cast<float4*>(&a.ws_o[(unit * a.ws_rows + row) * D + 4 * c4]) = acc;
+    if (c4 == 0) *reinterpret_cast<float2*>(&a.ws_ml[(unit * a.ws_rows + row) * 2]) = make_float2(M, lsum);
   }
 }
 

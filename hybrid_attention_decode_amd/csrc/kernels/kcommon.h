@@ -60,4 +60,10 @@ __device__ __forceinline__ void set_err(int32_t* d_err, int bits) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle;
+// range checking against num_records on), and the non-temporal cache-policy
+// bit of a buffer instruction on gfx950.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kBufferNT = 2;
+
 }  // namespace had

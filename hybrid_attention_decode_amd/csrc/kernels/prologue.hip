@@ -36,7 +36,7 @@ struct PrologueArgs {
   uint16_t* gate_out;
   int32_t* d_err;
   int T, H_q, H_kv, R, num_pages, P, max_pages;
-  double base;
+  double coef;  // rope_coef(base, R)
   float eps;
 };
 
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   }
 
   uint16_t y[E];
-  row_norm_rope<D>(in, pos, a.R, a.base, a.eps, row[wave], lane, y);
+  row_norm_rope<D>(in, pos, a.R, a.coef, a.eps, row[wave], lane, y);
   if (is_q) {
     uint16_t* qo = a.q_out + (tok * a.H_q + h) * D;
     uint16_t* go = a.gate_out + (tok * a.H_q + h) * D;
@@ -133,7 +133,7 @@ extern "C" int had_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_pt
   a.num_pages = d->num_pages;
   a.P = d->page_size;
   a.max_pages = d->max_pages;
-  a.base = d->rope_base;
+  a.coef = had::rope_coef(d->rope_base, d->rotary_dim);
   a.eps = d->eps;
   const dim3 grid(d->n_seqs * d->T, (d->H_q + d->H_kv + 3) / 4), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);

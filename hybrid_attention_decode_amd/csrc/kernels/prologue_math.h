@@ -11,10 +11,14 @@
 //   (rotary embedding, Su et al. RoFormer 2021, on a prefix of the head).
 // The angle is formed in fp64 (at pos ~ 1e6 an fp32 product is off by
 // ~0.06 rad), reduced to [-pi, pi] in fp64, and its sine and cosine taken in
-// fp32; the result is rounded to bf16 (nearest even).
+// fp32; the result is rounded to bf16 (nearest even).  The host passes the
+// exponent coefficient c = -2 log2(base) / R, so the frequency of pair i is
+// exp2(i * c) with no fp64 logarithm or division on the device.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cmath>
 
 #include "kcommon.h"
 
@@ -45,13 +49,19 @@ __device__ __forceinline__ void row_load_x(RowIn<D>& in, const uint16_t* __restr
   for (int m = 0; m < D / 64; ++m) in.x[m] = src[lane + 64 * m];
 }
 
-// cos and sin of the rotation angle pos * base^(-2i/R): the angle in fp64,
-// reduced to [-pi, pi] in fp64, then an fp32 sine and cosine.
-__device__ __forceinline__ void rope_cs(int pos, int i, int R, double log2_base, float& c, float& s) {
-  const double inv_freq = exp2(-2.0 * i / R * log2_base);
+// Exponent coefficient of the rotation frequencies, -2 log2(base) / R
+// (host side; 0 when nothing rotates).
+inline double rope_coef(double base, int R) { return R > 0 ? -2.0 * std::log2(base) / R : 0.0; }
+
+// cos and sin of the rotation angle pos * 2^(i c), c = rope_coef(base, R):
+// the angle in fp64, reduced to [-pi, pi] in fp64 (multiplication by 1/(2 pi)
+// and one fused multiply-add), then an fp32 sine and cosine.
+__device__ __forceinline__ void rope_cs(int pos, int i, double coef, float& c, float& s) {
+  const double inv_freq = exp2(static_cast<double>(i) * coef);
   const double theta = static_cast<double>(pos) * inv_freq;
   const double two_pi = 6.283185307179586476925286766559;
-  const double red = theta - two_pi * rint(theta / two_pi);
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  const double red = fma(-two_pi, rint(theta * inv_two_pi), theta);
   sincosf(static_cast<float>(red), &s, &c);
 }
 
@@ -71,8 +81,14 @@ __device__ __forceinline__ void row_norm_rope_cs(const RowIn<D>& in, const float
     x[m] = bf16_to_f32(in.x[m]);
     ss += x[m] * x[m];
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor_f(ss, off);
+  // sum over the wave: inside each 16-lane row by DPP (quad pairs, quad
+  // halves, the other quad of 8, the other 8 of 16), then across the rows
+  ss += dpp<DPP_QUAD_XOR1>(ss);
+  ss += dpp<DPP_QUAD_XOR2>(ss);
+  ss += dpp<DPP_ROW_HALF_MIRROR>(ss);
+  ss += dpp<DPP_ROW_ROR8>(ss);
+  ss += shfl_xor_f(ss, 16);
+  ss += shfl_xor_f(ss, 32);
   const float inv = 1.f / sqrtf(ss / static_cast<float>(D) + eps);
 #pragma unroll
   for (int m = 0; m < E; ++m) {
@@ -95,20 +111,19 @@ __device__ __forceinline__ void row_norm_rope_cs(const RowIn<D>& in, const float
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
-// The same, forming this row's angles at `pos` itself.
+// The same, forming this row's angles at `pos` itself (coef = rope_coef).
 template <int D>
-__device__ __forceinline__ void row_norm_rope(const RowIn<D>& in, int pos, int R, double base, float eps, float* xrow,
+__device__ __forceinline__ void row_norm_rope(const RowIn<D>& in, int pos, int R, double coef, float eps, float* xrow,
                                               int lane, uint16_t (&y)[D / 64]) {
   constexpr int E = D / 64;
   const int half = R / 2;
-  const double log2_base = log2(base);
   float cs[E], sn[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     const int d = lane + 64 * m;
     cs[m] = 1.f;
     sn[m] = 0.f;
-    if (d < R) rope_cs(pos, d % half, R, log2_base, cs[m], sn[m]);
+    if (64 * m < R && d < R) rope_cs(pos, d % half, coef, cs[m], sn[m]);
   }
   row_norm_rope_cs<D>(in, cs, sn, R, eps, xrow, lane, y);
 }
