@@ -454,14 +454,16 @@ size_t had_decode_attn_cascade_workspace_bytes(const had_attn_desc* d, const had
   return ws_partials_bytes(d, ns_p + ns_s);
 }
 
-int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, void* stream) {
-  if (d && p && (d->flags & HAD_ATTN_GATED_OUTPUT) && !p->gate)
+// passes: 1 = the prefix pass, 2 = the suffix pass, 3 = both; merge = run the combine after them
+static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, int passes,
+                          bool merge, void* stream) {
+  if (merge && d && p && (d->flags & HAD_ATTN_GATED_OUTPUT) && !p->gate)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: HAD_ATTN_GATED_OUTPUT with a NULL gate");
   int ns_p, ns_s, n_sfx;
   int st = cascade_plan(d, px, &ns_p, &ns_s, &n_sfx);
   if (st != HAD_OK) return st;
-  if (!p || !p->q || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace || !p->out ||
-      !px->prefix_page_table)
+  if (!p || !p->q || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace ||
+      (merge && !p->out) || !px->prefix_page_table)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: NULL pointer in ptrs or prefix");
   if (!aligned16(p->q) || !aligned16(p->k_pool) || !aligned16(p->v_pool) || !aligned16(p->workspace))
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: q, pools and workspace must be 16-byte aligned");
@@ -490,22 +492,26 @@ int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, c
   a.scale_log2 = d->sm_scale * 1.4426950408889634f;
   a.ns_total = ns_total;
   a.ws_rows = rows;
-  // prefix pass: all sequences' rows, the prefix page list as page-table row 0
-  had::ValuArgs ap = a;
-  ap.page_table = px->prefix_page_table;
-  ap.seq_lens = p->seq_lens;  // unused (fixed_len)
-  ap.n_seqs = 1;
-  ap.rows = d->n_seqs * rows;
-  ap.max_pages = px->prefix_pages;
-  ap.num_splits = ns_p;
-  ap.pps = 0;
-  ap.n_pages_plan = px->prefix_pages;
-  ap.pg_begin = 0;
-  ap.split_offset = 0;
-  ap.batch_rows = rows;
-  ap.fixed_len = px->prefix_pages * d->page_size;
-  hipError_t e = had::launch_attn_mfma(ap, d->head_dim, dim3(ns_p, d->H_kv, 1), s);
-  if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn_cascade: prefix kernel launch: %s", hipGetErrorString(e));
+  hipError_t e = hipSuccess;
+  if (passes & 1) {
+    // prefix pass: all sequences' rows, the prefix page list as page-table row 0
+    had::ValuArgs ap = a;
+    ap.page_table = px->prefix_page_table;
+    ap.seq_lens = p->seq_lens;  // unused (fixed_len)
+    ap.n_seqs = 1;
+    ap.rows = d->n_seqs * rows;
+    ap.max_pages = px->prefix_pages;
+    ap.num_splits = ns_p;
+    ap.pps = 0;
+    ap.n_pages_plan = px->prefix_pages;
+    ap.pg_begin = 0;
+    ap.split_offset = 0;
+    ap.batch_rows = rows;
+    ap.fixed_len = px->prefix_pages * d->page_size;
+    e = had::launch_attn_mfma(ap, d->head_dim, dim3(ns_p, d->H_kv, 1), s);
+    if (e != hipSuccess)
+      return fail(HAD_ERR_HIP, "decode_attn_cascade: prefix kernel launch: %s", hipGetErrorString(e));
+  }
   // suffix pass: each sequence from page prefix_pages on
   had::ValuArgs as = a;
   as.page_table = p->page_table;
@@ -520,20 +526,47 @@ int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, c
   as.split_offset = ns_p;
   as.batch_rows = 0;
   as.fixed_len = -1;
-  const dim3 grid(ns_s, d->H_kv, d->n_seqs);
-  if (rows >= 16) {
-    as.row_base = 0;
-    e = had::launch_attn_mfma(as, d->head_dim, grid, s);
-  } else {
-    for (int rb = 0; rb < rows && e == hipSuccess; rb += 8) {
-      as.row_base = rb;
-      e = had::launch_attn_valu(as, d->head_dim, grid, s);
+  if (passes & 2) {
+    const dim3 grid(ns_s, d->H_kv, d->n_seqs);
+    if (rows >= 16) {
+      as.row_base = 0;
+      e = had::launch_attn_mfma(as, d->head_dim, grid, s);
+    } else {
+      for (int rb = 0; rb < rows && e == hipSuccess; rb += 8) {
+        as.row_base = rb;
+        e = had::launch_attn_valu(as, d->head_dim, grid, s);
+      }
     }
+    if (e != hipSuccess)
+      return fail(HAD_ERR_HIP, "decode_attn_cascade: suffix kernel launch: %s", hipGetErrorString(e));
   }
-  if (e != hipSuccess) return fail(HAD_ERR_HIP, "decode_attn_cascade: suffix kernel launch: %s", hipGetErrorString(e));
+  if (!merge) return had::ok();
   had::ValuArgs am = as;
   am.num_splits = ns_total;
   return launch_combine_after(d, am, p->out, stream, p->gate, d->head_dim);
+}
+
+int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, void* stream) {
+  return cascade_launch(d, px, p, 3, true, stream);
+}
+
+int had_decode_attn_cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int32_t* prefix_splits,
+                                 int32_t* suffix_splits) {
+  if (!prefix_splits || !suffix_splits) return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade_plan: NULL output");
+  int ns_p, ns_s, n_sfx;
+  const int st = cascade_plan(d, px, &ns_p, &ns_s, &n_sfx);
+  if (st != HAD_OK) return st;
+  *prefix_splits = ns_p;
+  *suffix_splits = ns_s;
+  return had::ok();
+}
+
+int had_decode_attn_cascade_partial(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p,
+                                    int32_t passes, void* stream) {
+  if (no_gate(d, "decode_attn_cascade_partial") != HAD_OK) return HAD_ERR_INVALID_ARG;
+  if (passes < 1 || passes > 3)
+    return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade_partial: passes %d not in {1, 2, 3}", passes);
+  return cascade_launch(d, px, p, passes, false, stream);
 }
 
 }  // extern "C"

@@ -469,6 +469,20 @@ int had_attn_check_prefix(int32_t n_seqs, int32_t max_pages, const int32_t *page
 int had_decode_attn_cascade(const had_attn_desc *d, const had_attn_prefix *px, const had_attn_ptrs *p,
                             void *stream);
 
+/* The cascade's split plan: *prefix_splits partials of the prefix pass come
+ * first in each (sequence, KV head) slot of the workspace, then
+ * *suffix_splits of the suffix pass. */
+int had_decode_attn_cascade_plan(const had_attn_desc *d, const had_attn_prefix *px, int32_t *prefix_splits,
+                                 int32_t *suffix_splits);
+
+/* The cascade's passes without the merge: passes = 1 (prefix pass), 2
+ * (suffix pass) or 3 (both) write their partials into the workspace (layout
+ * above; p->out and p->gate are ignored, HAD_ATTN_GATED_OUTPUT is rejected);
+ * had_decode_attn_combine with num_splits = prefix_splits + suffix_splits
+ * finishes.  For callers that schedule or time the passes separately. */
+int had_decode_attn_cascade_partial(const had_attn_desc *d, const had_attn_prefix *px, const had_attn_ptrs *p,
+                                    int32_t passes, void *stream);
+
 /* ======================================================================
  * decode_attn_layer -- qk_norm_rope_gate and decode_attn in one pass
  *

@@ -123,3 +123,29 @@ def test_cascade_rejects_bad_prefix():
         had.decode_attn_cascade(q, pool, pool, torch.zeros((2, 4), dtype=torch.int32, device=DEV),
                                 torch.tensor([40, 40], dtype=torch.int32, device=DEV),
                                 torch.zeros(0, dtype=torch.int32, device=DEV))
+
+
+def test_split_passes_and_merge_equal_the_one_call_cascade():
+    # prefix pass, suffix pass and merge called one by one give the bits of
+    # had_decode_attn_cascade (deterministic mode), and the plan reports the
+    # workspace's split counts
+    P, D, H_q = 64, 256, 8
+    q, kb, vb, table, L, prefix = _batch(4100, 5, 3200, [0, 700, 65, 1500, 9], 1, H_q, 1, D, P)
+    print("case cascade split passes", flush=True)
+    qd, kd, vd, ptd, ld, pxd = to_dev(q), to_dev(kb), to_dev(vb), to_dev(table), to_dev(L), to_dev(prefix)
+    desc = had.attn_desc(q.shape, kb.shape, table.shape[1], deterministic=True)
+    ns_p, ns_s = had.decode_attn_cascade_plan(desc, len(prefix))
+    nbytes = had.decode_attn_cascade_workspace_bytes(desc, len(prefix))
+    assert nbytes == len(L) * (ns_p + ns_s) * H_q * (D + 2) * 4
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 1, d_err=err, deterministic=True)
+    had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 2, d_err=err, deterministic=True)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+    had.decode_attn_combine(desc, ns_p + ns_s, ws, out)
+    ref = had.decode_attn_cascade(qd, kd, vd, ptd, ld, pxd, d_err=err, deterministic=True)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(bits_of(out), bits_of(ref))
+    with pytest.raises(had.HadError):
+        had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 4)
