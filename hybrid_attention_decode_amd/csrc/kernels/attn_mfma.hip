@@ -92,7 +92,7 @@ __device__ __forceinline__ int kswz(int r, int mask) { return (r ^ (r >> 2)) & m
 // R128: 128 query rows per launch, wave w owning rows 16w .. 16w+15 and
 // working through both 32-token halves of every staged tile itself (no team
 // merge); otherwise 64 rows, the two teams splitting the tile's tokens.
-template <int D, bool R128>
+template <int D, bool R128, bool PAGE32>
 __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   using C = MCfg<D>;
   constexpr int TPT = C::TPT;
@@ -162,26 +162,60 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   const int last_tok = max(tok_end - 1, tok0);
   const int last_pg = max(npg - 1, 0);
 
-  __syncthreads();
-
   // every staging load is unconditional: tokens past the split clamp to its
   // last token, so the addresses stay in bounds and the compiler can count
-  // the loads in flight exactly
-  auto load = [&](u32x4_t (&kr)[TPT], u32x4_t (&vr)[TPT], int it) __attribute__((always_inline)) {
+  // the loads in flight exactly.  A wave stages 32 consecutive tokens; when
+  // pages hold a multiple of 32 tokens they lie in one page, and the loads
+  // are buffer loads over that (page, KV head) block: a stage past the
+  // split's last one (the loop's trailing prefetches) covers 0 bytes and
+  // returns zeros without a memory request.  Otherwise every lane addresses
+  // its own page.
+  auto load_pid = [&](u32x4_t (&kr)[TPT], u32x4_t (&vr)[TPT], int it, int pid) __attribute__((always_inline)) {
     const int t0 = min(tok0 + it * kMTile + ltok, last_tok);
-    int pid = sh.pages[min(t0 / P - pg0, last_pg)];
-    pid = pid < 0 ? 0 : pid;
-    const uint16_t* kb = a.k_pool + (static_cast<size_t>(pid) * a.H_kv + h) * P * D + lc * 8;
-    const uint16_t* vb = a.v_pool + (static_cast<size_t>(pid) * a.H_kv + h) * P * D + lc * 8;
+    if constexpr (PAGE32) {
+      const int pu = __builtin_amdgcn_readfirstlane(pid < 0 ? 0 : pid);
+      const int nbytes = __builtin_amdgcn_readfirstlane(it < n_it ? P * D * 2 : 0);
+      const size_t blk = (static_cast<size_t>(pu) * a.H_kv + h) * P * D;
+      const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k_pool + blk), 0,
+                                                                           nbytes, kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_pool + blk), 0,
+                                                                           nbytes, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int t = min(t0 + i, last_tok) % P;  // the group never leaves its page (P % TPT == 0)
-      // non-temporal: the context streams through once per launch (as in the VALU kernel)
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + t * D));
-      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + t * D));
+      for (int i = 0; i < TPT; ++i) {
+        const int t = min(t0 + i, last_tok) % P;
+        // non-temporal: the context streams through once per launch (as in the VALU kernel)
+        const int off = (t * D + lc * 8) * 2;
+        kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kr_, off, 0, kBufferNT);
+        vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vr_, off, 0, kBufferNT);
+      }
+    } else {
+      const int pl = pid < 0 ? 0 : pid;
+      const uint16_t* kb = a.k_pool + (static_cast<size_t>(pl) * a.H_kv + h) * P * D + lc * 8;
+      const uint16_t* vb = a.v_pool + (static_cast<size_t>(pl) * a.H_kv + h) * P * D + lc * 8;
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int t = min(t0 + i, last_tok) % P;  // the group never leaves its page (P % TPT == 0)
+        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + t * D));
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + t * D));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto load = [&](u32x4_t (&kr)[TPT], u32x4_t (&vr)[TPT], int it) __attribute__((always_inline)) {
+    const int t0 = min(tok0 + it * kMTile + ltok, last_tok);
+    load_pid(kr, vr, it, sh.pages[min(t0 / P - pg0, last_pg)]);
+  };
+
+  // The first stage's loads go out before the setup barrier, their page id
+  // read from the page table itself (an id out of range reads page 0; the
+  // staging below zeroes what the checked list marks invalid).
+  u32x4_t kA[TPT], vA[TPT], kB[TPT], vB[TPT];
+  {
+    const int t0 = min(tok0 + ltok, last_tok);
+    const int pid = pt_row[min(pg0 + min(t0 / P - pg0, last_pg), a.max_pages - 1)];
+    load_pid(kA, vA, 0, (pid >= 0 && pid < a.num_pages) ? pid : 0);
+  }
+  __syncthreads();
 
   auto stage = [&](const u32x4_t (&kr)[TPT], const u32x4_t (&vr)[TPT], int it, int b) __attribute__((always_inline)) {
 #pragma unroll
@@ -302,8 +336,6 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
 
   // ---- main loop: register stages A (even tiles) and B (odd tiles), LDS
   // buffer 0 for A and 1 for B; the loop exits only at its header
-  u32x4_t kA[TPT], vA[TPT], kB[TPT], vB[TPT];
-  load(kA, vA, 0);
   load(kB, vB, 1);
   int it = 0;
   while (it + 1 < n_it) {
@@ -388,13 +420,20 @@ hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipSt
   for (int rb = 0; rb < a.rows && e == hipSuccess; rb += r128 ? 2 * kMRows : kMRows) {
     a.row_base = rb;
     const dim3 blk(64 * kMWaves);
-    switch (head_dim * 2 + (r128 ? 1 : 0)) {
-      case 128: hipLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, blk, 0, stream, a); break;
-      case 129: hipLaunchKernelGGL((attn_mfma_kernel<64, true>), grid, blk, 0, stream, a); break;
-      case 256: hipLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, blk, 0, stream, a); break;
-      case 257: hipLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, blk, 0, stream, a); break;
-      case 512: hipLaunchKernelGGL((attn_mfma_kernel<256, false>), grid, blk, 0, stream, a); break;
-      case 513: hipLaunchKernelGGL((attn_mfma_kernel<256, true>), grid, blk, 0, stream, a); break;
+    const bool p32 = a.page_size % 32 == 0;
+    switch (head_dim * 4 + (r128 ? 2 : 0) + (p32 ? 1 : 0)) {
+      case 256: hipLaunchKernelGGL((attn_mfma_kernel<64, false, false>), grid, blk, 0, stream, a); break;
+      case 257: hipLaunchKernelGGL((attn_mfma_kernel<64, false, true>), grid, blk, 0, stream, a); break;
+      case 258: hipLaunchKernelGGL((attn_mfma_kernel<64, true, false>), grid, blk, 0, stream, a); break;
+      case 259: hipLaunchKernelGGL((attn_mfma_kernel<64, true, true>), grid, blk, 0, stream, a); break;
+      case 512: hipLaunchKernelGGL((attn_mfma_kernel<128, false, false>), grid, blk, 0, stream, a); break;
+      case 513: hipLaunchKernelGGL((attn_mfma_kernel<128, false, true>), grid, blk, 0, stream, a); break;
+      case 514: hipLaunchKernelGGL((attn_mfma_kernel<128, true, false>), grid, blk, 0, stream, a); break;
+      case 515: hipLaunchKernelGGL((attn_mfma_kernel<128, true, true>), grid, blk, 0, stream, a); break;
+      case 1024: hipLaunchKernelGGL((attn_mfma_kernel<256, false, false>), grid, blk, 0, stream, a); break;
+      case 1025: hipLaunchKernelGGL((attn_mfma_kernel<256, false, true>), grid, blk, 0, stream, a); break;
+      case 1026: hipLaunchKernelGGL((attn_mfma_kernel<256, true, false>), grid, blk, 0, stream, a); break;
+      case 1027: hipLaunchKernelGGL((attn_mfma_kernel<256, true, true>), grid, blk, 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();
