@@ -503,7 +503,10 @@ def stack_kernel_us(st, kernel_reps):
                                             st.prefix_dev, st.cws, 2, max_seq_len=st.max_seq_len)
 
         def merge(r):
-            had.decode_attn_combine(st.desc, ns_p + ns_s, st.cws, st.attn[r % N_ATTN]["out"])
+            a = st.attn[r % N_ATTN]
+            had.decode_attn_cascade_combine(a["q_out"], a["k_pool"], a["v_pool"], st.pt_dev, st.lens_dev,
+                                            st.prefix_dev, st.cws, out=a["out"], max_seq_len=st.max_seq_len,
+                                            gate=a["gate"])
 
         return {
             "prologue": round(time_graph(torch, prologue, n * N_ATTN), 3),

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     attn_desc,
     decode_attn,
     decode_attn_cascade,
+    decode_attn_cascade_combine,
     decode_attn_cascade_partial,
     decode_attn_cascade_plan,
     decode_attn_cascade_workspace_bytes,

@@ -149,6 +149,8 @@ _SIGS = {
                                      ctypes.c_int),
     "had_decode_attn_cascade_partial": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPrefix),
                                         ctypes.POINTER(AttnPtrs), _i32, _p], ctypes.c_int),
+    "had_decode_attn_cascade_combine": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnPrefix),
+                                        ctypes.POINTER(AttnPtrs), _p], ctypes.c_int),
     "had_decode_attn_layer": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc), ctypes.POINTER(QknrgPtrs), _p,
                                ctypes.c_size_t, _p, _p], ctypes.c_int),
     "had_decode_attn_layer_static": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(QknrgDesc), ctypes.POINTER(QknrgPtrs),
@@ -580,8 +582,7 @@ def decode_attn_cascade_plan(desc, prefix_pages):
 def decode_attn_cascade_partial(q, k_pool, v_pool, page_table, seq_lens, prefix_page_table, workspace, passes,
                                 sm_scale=None, max_seq_len=0, d_err=None, deterministic=False):
     """The cascade's prefix pass (passes = 1), suffix pass (2) or both (3),
-    partials only; decode_attn_combine(desc, prefix_splits + suffix_splits,
-    workspace, out) finishes."""
+    partials only; decode_attn_cascade_combine finishes."""
     torch = _torch()
     desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, 0, deterministic, False)
     px = AttnPrefix(prefix_page_table.numel(), _dev(prefix_page_table, torch.int32, "prefix_page_table"))
@@ -591,6 +592,24 @@ def decode_attn_cascade_partial(q, k_pool, v_pool, page_table, seq_lens, prefix_
                     workspace.numel(), None, _opt(d_err, "d_err"), None)
     _check(lib().had_decode_attn_cascade_partial(ctypes.byref(desc), ctypes.byref(px), ctypes.byref(ptrs),
                                                  int(passes), _stream()))
+
+
+def decode_attn_cascade_combine(q, k_pool, v_pool, page_table, seq_lens, prefix_page_table, workspace, out=None,
+                                sm_scale=None, max_seq_len=0, d_err=None, deterministic=False, gate=None):
+    """The cascade's merge of the partials decode_attn_cascade_partial wrote."""
+    torch = _torch()
+    desc = attn_desc(q.shape, k_pool.shape, page_table.shape[1], sm_scale, max_seq_len, 0, deterministic,
+                     gate is not None)
+    px = AttnPrefix(prefix_page_table.numel(), _dev(prefix_page_table, torch.int32, "prefix_page_table"))
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    ptrs = AttnPtrs(_dev(q, torch.bfloat16, "q"), _dev(k_pool, torch.bfloat16, "k_pool"),
+                    _dev(v_pool, torch.bfloat16, "v_pool"), _dev(page_table, torch.int32, "page_table"),
+                    _dev(seq_lens, torch.int32, "seq_lens"), _dev(workspace, torch.uint8, "workspace"),
+                    workspace.numel(), _dev(out, torch.bfloat16, "out"), _opt(d_err, "d_err"),
+                    None if gate is None else _dev(gate, torch.bfloat16, "gate"))
+    _check(lib().had_decode_attn_cascade_combine(ctypes.byref(desc), ctypes.byref(px), ctypes.byref(ptrs), _stream()))
+    return out
 
 
 def decode_attn_cascade_workspace_bytes(desc, prefix_pages):

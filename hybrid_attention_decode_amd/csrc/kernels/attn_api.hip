@@ -241,8 +241,16 @@ int had_decode_attn_partial(const had_attn_desc* d, const had_attn_ptrs* p, void
 // gate / gate_hstride: bf16 gate of head (s, j, hq) at gate + ((s*q_len + j)*H_q + hq)*gate_hstride,
 // applied when the descriptor asks for the gated output.
 static int launch_combine_after(const had_attn_desc* d, const had::ValuArgs& a, void* out, void* stream,
-                                const void* gate = nullptr, int gate_hstride = 0) {
+                                const void* gate = nullptr, int gate_hstride = 0, int bal_units = 0,
+                                int prefix_splits = 0) {
   had::CombineArgs c{};
+  if (bal_units > 0) {  // a cascade whose suffix units were shared out by length
+    c.seq_lens = a.seq_lens;
+    c.bal_units = bal_units;
+    c.prefix_splits = prefix_splits;
+    c.tok_begin = a.pg_begin * a.page_size;
+    c.max_tiles = a.n_pages_plan * (a.page_size / 8);
+  }
   if (d->flags & HAD_ATTN_GATED_OUTPUT) {
     c.gate = static_cast<const uint16_t*>(gate);
     c.gate_hstride = gate_hstride;
@@ -402,7 +410,17 @@ int had_decode_attn_combine(const had_attn_desc* d, int32_t num_splits, const vo
 // each sequence's suffix is read by the usual kernel from page prefix_pages
 // on; both write partials into one workspace (prefix splits first) and the
 // ordinary combine merges them.  Same result as had_decode_attn.
-static int cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int* ns_p, int* ns_s, int* n_sfx) {
+// Suffix pass shared out by length (below 16 rows): G work units per KV
+// head over all sequences' suffixes, when every unit's tiles fit one split's
+// page list and the merge's per-sequence share fits one wave (n_seqs <= 64).
+static int cascade_bal_units(const had_attn_desc* d, int n_sfx) {
+  const int rows = d->q_len * (d->H_q / d->H_kv);
+  if (rows >= 16 || d->n_seqs > 64 || n_sfx > had::kMaxPagesPerSplit - 2 || d->num_splits != 0) return 0;
+  return std::max<int>(d->n_seqs, static_cast<int>(ceil_div(kTargetUnits, d->H_kv)));
+}
+
+static int cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int* ns_p, int* ns_s, int* n_sfx,
+                        int* bal = nullptr) {
   int st = check_desc(d);
   if (st != HAD_OK) return st;
   if (!px || px->prefix_pages < 1)
@@ -421,12 +439,16 @@ static int cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int* 
   int pps;
   st = plan(&dp, ns_p, &pps, nullptr);
   if (st != HAD_OK) return st;
-  // suffix pass: the usual plan over the pages after the prefix
+  // suffix pass: the usual plan over the pages after the prefix, or units
+  // shared out by length (slots for all of them in every sequence's row)
   had_attn_desc ds = *d;
   ds.max_seq_len = static_cast<int32_t>(max_len - prefix_len);
   ds.num_splits = 0;
   st = plan(&ds, ns_s, &pps, n_sfx);
   if (st != HAD_OK) return st;
+  const int b = cascade_bal_units(d, *n_sfx);
+  if (b > 0) *ns_s = b;
+  if (bal) *bal = b;
   if (*ns_p + *ns_s > had::kMaxSplits)
     return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn_cascade: %d + %d splits (max %d)", *ns_p, *ns_s,
                 had::kMaxSplits);
@@ -459,8 +481,8 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
                           bool merge, void* stream) {
   if (merge && d && p && (d->flags & HAD_ATTN_GATED_OUTPUT) && !p->gate)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: HAD_ATTN_GATED_OUTPUT with a NULL gate");
-  int ns_p, ns_s, n_sfx;
-  int st = cascade_plan(d, px, &ns_p, &ns_s, &n_sfx);
+  int ns_p, ns_s, n_sfx, bal;
+  int st = cascade_plan(d, px, &ns_p, &ns_s, &n_sfx, &bal);
   if (st != HAD_OK) return st;
   if (!p || !p->q || !p->k_pool || !p->v_pool || !p->page_table || !p->seq_lens || !p->workspace ||
       (merge && !p->out) || !px->prefix_page_table)
@@ -526,8 +548,9 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
   as.split_offset = ns_p;
   as.batch_rows = 0;
   as.fixed_len = -1;
+  as.bal_units = bal;
   if (passes & 2) {
-    const dim3 grid(ns_s, d->H_kv, d->n_seqs);
+    const dim3 grid(ns_s, d->H_kv, bal > 0 ? 1 : d->n_seqs);
     if (rows >= 16) {
       as.row_base = 0;
       e = had::launch_attn_mfma(as, d->head_dim, grid, s);
@@ -543,7 +566,7 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
   if (!merge) return had::ok();
   had::ValuArgs am = as;
   am.num_splits = ns_total;
-  return launch_combine_after(d, am, p->out, stream, p->gate, d->head_dim);
+  return launch_combine_after(d, am, p->out, stream, p->gate, d->head_dim, bal, ns_p);
 }
 
 int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, void* stream) {
@@ -567,6 +590,11 @@ int had_decode_attn_cascade_partial(const had_attn_desc* d, const had_attn_prefi
   if (passes < 1 || passes > 3)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade_partial: passes %d not in {1, 2, 3}", passes);
   return cascade_launch(d, px, p, passes, false, stream);
+}
+
+int had_decode_attn_cascade_combine(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p,
+                                    void* stream) {
+  return cascade_launch(d, px, p, 0, true, stream);
 }
 
 }  // extern "C"

@@ -42,8 +42,15 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
   const int row = blockIdx.x;
   const int d0 = blockIdx.y * kDC;
   const int unit = blockIdx.z;  // s * H_kv + h
-  const int ns = a.num_splits;
-  const size_t base = static_cast<size_t>(unit) * ns;
+  // partials of this sequence: all num_splits slots, or after a suffix pass
+  // shared out by length the prefix splits and the sequence's own share
+  int ns = a.num_splits;
+  if (a.bal_units > 0) {
+    int n_t, W_t, O_t;
+    bal_share(a.seq_lens, a.n_seqs, a.tok_begin, a.max_tiles, a.bal_units, lane, n_t, W_t, O_t);
+    ns = a.prefix_splits + __builtin_amdgcn_readfirstlane(__shfl(W_t, unit / a.H_kv));
+  }
+  const size_t base = static_cast<size_t>(unit) * a.num_splits;
   const float* ml = a.ws_ml;
   const size_t ostride4 = static_cast<size_t>(a.rows) * D / 4;  // float4s between consecutive splits
   const float4* o4 = reinterpret_cast<const float4*>(a.ws_o + (base * a.rows + row) * D + d0);
@@ -59,19 +66,19 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
   float M = -INFINITY;
   float lsum = 0.f;
   for (int p0 = 0; p0 < ns; p0 += kPass) {
-    // issue every load of this pass first
+    // issue every load of this pass first (unconditional, the index clamped
+    // to the last partial: a load under a branch would make the compiler
+    // wait for each one in turn)
     float4 ov[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = p0 + (u * kWaves + wave) * kSPW + sub;
-      ov[u] = (i < ns) ? o4[i * ostride4 + dl] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int i = min(p0 + (u * kWaves + wave) * kSPW + sub, ns - 1);
+      ov[u] = o4[i * ostride4 + dl];
     }
-    float mi = -INFINITY, li = 0.f;
     const int my = p0 + tid;  // this thread's split for the maxima
-    if (tid < kPass && my < ns) {
-      mi = ml[((base + my) * a.rows + row) * 2];
-      li = ml[((base + my) * a.rows + row) * 2 + 1];
-    }
+    const float2 mlv = *reinterpret_cast<const float2*>(&ml[((base + min(my, ns - 1)) * a.rows + row) * 2]);
+    float mi = mlv.x, li = mlv.y;
+    if (my >= ns) mi = -INFINITY, li = 0.f;  // past the partials
     // block maximum of this pass, merged into the running maximum
     float mw = mi;
 #pragma unroll
@@ -87,7 +94,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
     acc.x *= rescale; acc.y *= rescale; acc.z *= rescale; acc.w *= rescale;
     lsum *= rescale;
     M = M_new;
-    if (tid < kPass && my < ns) {
+    {
       const float w = (mi == -INFINITY) ? 0.f : exp2f(mi - Ms);
       wsh[tid] = w;
       lsum += w * li;

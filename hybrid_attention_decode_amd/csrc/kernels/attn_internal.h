@@ -39,7 +39,36 @@ struct ValuArgs {
   int batch_rows;    // MFMA prefix pass: > 0 = the launch's rows are those of all sequences
                      // (row r belongs to sequence r / batch_rows); page table row 0 is the prefix
   int fixed_len;     // >= 0: every row sees exactly this many tokens (the prefix), seq_lens unused
+  int bal_units;     // > 0 (suffix pass of the cascade, VALU): the launch's blockIdx.x is one of bal_units
+                     // work units shared out over the sequences in proportion to their suffix length
+                     // (bal_share below); 0 = the split plan above
 };
+
+// Work units of a batch's suffix pass shared out by length: sequence t has
+// n_t tiles of 8 tokens from token tok_begin on; every sequence with a tile
+// gets one unit and the units left over are given in proportion to n_t
+// (floor), so sum W_t <= G.  Lane t of the calling wave returns sequence t's
+// n_t, W_t and first unit O_t (n_seqs <= 64); every wave that calls it with
+// the same lengths gets the same integers, so the partial kernel and the
+// merge agree without exchanging anything.
+__device__ __forceinline__ void bal_share(const int32_t* seq_lens, int n_seqs, int tok_begin, int max_tiles, int G,
+                                          int lane, int& n_t, int& W_t, int& O_t) {
+  const int L = lane < n_seqs ? seq_lens[lane] : 0;
+  n_t = lane < n_seqs ? min(max(0, (L - tok_begin + 7) / 8), max_tiles) : 0;
+  const int K = __popcll(__ballot(n_t > 0));
+  long long N = n_t;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) N += __shfl_xor(N, off);
+  const long long spare = G > K ? G - K : 0;
+  W_t = n_t > 0 ? 1 + static_cast<int>(spare * n_t / (N > 0 ? N : 1)) : 0;
+  int x = W_t;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  O_t = x - W_t;
+}
 
 // Inputs of the prologue when the VALU attention kernel runs it inline (the
 // fused layer entry point, below 16 query rows per KV head): every
@@ -71,6 +100,11 @@ struct CombineArgs {
   // gate + ((s * q_len + j) * H_q + hq) * gate_hstride (the gate half of qg)
   const uint16_t* gate;
   int gate_hstride;
+  // merge of a cascade whose suffix pass shared out bal_units work units
+  // (ValuArgs::bal_units): sequence s merges prefix_splits + W_s partials of
+  // its num_splits slots (W_s from bal_share over seq_lens)
+  const int32_t* seq_lens;
+  int bal_units, prefix_splits, tok_begin, max_tiles;
 };
 
 hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);

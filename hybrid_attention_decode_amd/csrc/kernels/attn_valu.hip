@@ -122,13 +122,40 @@ template <int D, bool FUSED>
 __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs f) {
   using C = Cfg<D>;
   __shared__ Lds sh;
-  const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int h = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int tg = lane / C::LPT, j = lane % C::LPT, j8 = j & 7;
   const int tgv = lane / (D / C::DPL), dl = lane % (D / C::DPL);
   const int P = a.page_size;
   const int tpp = P / kTT;
+
+  // Which sequence and split this workgroup is, and how many splits share
+  // the sequence's tiles: the launch grid (split, KV head, sequence) over
+  // the plan's tiles, or -- the suffix pass of a batch -- work unit blockIdx.x
+  // of the units shared out by suffix length (bal_share), over the
+  // sequence's own tiles.
+  int s = blockIdx.z, sp = blockIdx.x, nsplit = a.num_splits;
+  int64_t n_tiles_plan = static_cast<int64_t>(a.n_pages_plan) * tpp;
+  if constexpr (!FUSED) {
+    if (a.bal_units > 0) {
+      int n_t, W_t, O_t;
+      bal_share(a.seq_lens, a.n_seqs, a.pg_begin * P, a.n_pages_plan * tpp, a.bal_units, lane, n_t, W_t, O_t);
+      const int g = blockIdx.x;
+      const unsigned long long hit = __ballot(lane < a.n_seqs && g >= O_t && g < O_t + W_t);
+      // a sequence too short to reach past the prefix owns no unit: unit 0
+      // reports it (the per-unit length check below covers the others)
+      if (g == 0 && h == 0 && threadIdx.x < a.n_seqs) {
+        const int Lt = a.seq_lens[threadIdx.x];
+        if (Lt - a.q_len < a.pg_begin * P || Lt < a.q_len) set_err(a.d_err, HAD_DERR_SEQLEN);
+      }
+      if (hit == 0) return;  // a unit left over (uniform over the workgroup)
+      s = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(hit)) - 1);
+      sp = g - __builtin_amdgcn_readfirstlane(__shfl(O_t, s));
+      nsplit = __builtin_amdgcn_readfirstlane(__shfl(W_t, s));
+      n_tiles_plan = __builtin_amdgcn_readfirstlane(__shfl(n_t, s));
+    }
+  }
 
   // Every global load below is unconditional (addresses clamped to valid
   // memory, results masked afterwards): loads under divergent or uniform
@@ -139,9 +166,8 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // pg_begin; balanced to within one tile, so no workgroup holds a page more
   // than another), which lie on the pages [pg0, pg1_plan); tiles are numbered
   // from pg0's first token, this split's being [tile_lo, tile_hi).
-  const int64_t n_tiles_plan = static_cast<int64_t>(a.n_pages_plan) * tpp;
-  const int t0 = static_cast<int>(static_cast<int64_t>(sp) * n_tiles_plan / a.num_splits);
-  const int t1 = static_cast<int>(static_cast<int64_t>(sp + 1) * n_tiles_plan / a.num_splits);
+  const int t0 = static_cast<int>(static_cast<int64_t>(sp) * n_tiles_plan / nsplit);
+  const int t1 = static_cast<int>(static_cast<int64_t>(sp + 1) * n_tiles_plan / nsplit);
   const int pg0 = a.pg_begin + t0 / tpp;
   const int pg1_plan = a.pg_begin + (t1 + tpp - 1) / tpp;
   const int npg_plan = pg1_plan - pg0;

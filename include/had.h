@@ -452,6 +452,19 @@ int had_decode_attn_combine(const had_attn_desc *d, int32_t num_splits,
  * Workspace: >= had_decode_attn_cascade_workspace_bytes(d, px) bytes, layout
  * of had_decode_attn's ws_o / ws_ml with the prefix splits first (returns 0
  * for an invalid descriptor).
+ *
+ * Suffix pass below 16 rows (n_seqs <= 64, suffix plan <= 510 pages,
+ * num_splits = 0): the suffixes differ in length, so instead of the same
+ * number of splits per sequence the pass runs G work units per KV head
+ * (G = max(n_seqs, 256 / H_kv)); every sequence with a suffix tile gets one
+ * unit and the rest go to the sequences in proportion to their suffix length
+ * (8-token tiles from token prefix_pages * page_size on, the floor of the
+ * proportional share), each unit taking an equal range of its sequence's
+ * tiles.  The units are read from seq_lens on the device, so the shares
+ * follow the lengths of every step (and a captured graph).  Each
+ * sequence's row of the workspace has slots for G suffix partials, of which
+ * its own share is written; had_decode_attn_cascade_combine merges exactly
+ * those.
  * ====================================================================== */
 typedef struct {
   int32_t prefix_pages;              /* whole pages shared by every sequence (>= 1)  */
@@ -471,17 +484,24 @@ int had_decode_attn_cascade(const had_attn_desc *d, const had_attn_prefix *px, c
 
 /* The cascade's split plan: *prefix_splits partials of the prefix pass come
  * first in each (sequence, KV head) slot of the workspace, then
- * *suffix_splits of the suffix pass. */
+ * *suffix_splits slots of the suffix pass (G when the suffix units are
+ * shared out by length, see above). */
 int had_decode_attn_cascade_plan(const had_attn_desc *d, const had_attn_prefix *px, int32_t *prefix_splits,
                                  int32_t *suffix_splits);
 
 /* The cascade's passes without the merge: passes = 1 (prefix pass), 2
  * (suffix pass) or 3 (both) write their partials into the workspace (layout
  * above; p->out and p->gate are ignored, HAD_ATTN_GATED_OUTPUT is rejected);
- * had_decode_attn_combine with num_splits = prefix_splits + suffix_splits
- * finishes.  For callers that schedule or time the passes separately. */
+ * had_decode_attn_cascade_combine with the same arguments finishes (not
+ * had_decode_attn_combine: with the suffix shared out by length not every
+ * slot is written).  For callers that schedule or time the passes
+ * separately. */
 int had_decode_attn_cascade_partial(const had_attn_desc *d, const had_attn_prefix *px, const had_attn_ptrs *p,
                                     int32_t passes, void *stream);
+/* The cascade's merge alone: out (and the gate, with HAD_ATTN_GATED_OUTPUT)
+ * from the partials both passes wrote; ptrs as had_decode_attn_cascade. */
+int had_decode_attn_cascade_combine(const had_attn_desc *d, const had_attn_prefix *px, const had_attn_ptrs *p,
+                                    void *stream);
 
 /* ======================================================================
  * decode_attn_layer -- qk_norm_rope_gate and decode_attn in one pass

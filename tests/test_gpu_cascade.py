@@ -141,11 +141,34 @@ def test_split_passes_and_merge_equal_the_one_call_cascade():
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 1, d_err=err, deterministic=True)
     had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 2, d_err=err, deterministic=True)
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
-    had.decode_attn_combine(desc, ns_p + ns_s, ws, out)
+    out = had.decode_attn_cascade_combine(qd, kd, vd, ptd, ld, pxd, ws, d_err=err, deterministic=True)
     ref = had.decode_attn_cascade(qd, kd, vd, ptd, ld, pxd, d_err=err, deterministic=True)
     torch.cuda.synchronize()
     assert err.item() == 0
     assert np.array_equal(bits_of(out), bits_of(ref))
     with pytest.raises(had.HadError):
         had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 4)
+
+
+@pytest.mark.parametrize("n,spread,prefix_len,D,P", [
+    (12, 6000, 3000, 256, 64),     # one long suffix among short ones: most units go to it
+    (64, 900, 1000, 128, 16),      # as many sequences as the shares allow (one wave)
+    (7, 0, 2048, 256, 64),         # only the decode tokens after the prefix
+])
+def test_cascade_suffix_units_by_length(n, spread, prefix_len, D, P):
+    # the suffix pass shares its units out by suffix length (read from
+    # seq_lens on the device) and the merge takes each sequence's own share
+    seed = 3300 + n + spread % 97
+    suffixes = [int(x) for x in synth.integers(0, max(spread // 8, 0), n, synth.seed_of(seed, 9))]
+    if spread:
+        suffixes[n // 2] = spread
+    q, kb, vb, table, L, prefix = _batch(seed, n, prefix_len, suffixes, 1, 8, 1, D, P)
+    print("case cascade units by length n=%d prefix=%d suffixes=%s" % (n, prefix_len, suffixes), flush=True)
+    desc = had.attn_desc(q.shape, kb.shape, table.shape[1])
+    assert had.decode_attn_cascade_plan(desc, len(prefix))[1] == max(n, 256)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn_cascade(to_dev(q), to_dev(kb), to_dev(vb), to_dev(table), to_dev(L), to_dev(prefix),
+                                  d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert_attn_close(out, _oracle(q, kb, vb, table, L, P, D))
