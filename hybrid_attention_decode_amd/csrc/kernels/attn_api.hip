@@ -58,11 +58,12 @@ int no_gate(const had_attn_desc* d, const char* who) {
 
 // Split plan over the pages a sequence can reach (max_seq_len, a host bound,
 // so the plan does not depend on device data).  Below 16 rows split i owns
-// the tiles [i*N/ns, (i+1)*N/ns) of the N = n * page_size / 8 tiles of 8
-// tokens (balanced to within one tile; such a range can start and end inside
-// a page, so it touches at most ceil(n/ns) + 1 pages, and the plan keeps
-// ceil(n/ns) <= 511 when ns > 1); at 16 or more rows the pages
-// [i*n/ns, (i+1)*n/ns) (within one page, at most 512).
+// the tiles [i*b + min(i, r), (i+1)*b + min(i+1, r)) of the N = n * page_size
+// / 8 tiles of 8 tokens, b = N / ns, r = N % ns (balanced to within one tile;
+// such a range can start and end inside a page, so it touches at most
+// ceil(n/ns) + 1 pages, and the plan keeps ceil(n/ns) <= 511 when ns > 1);
+// at 16 or more rows the pages [i*n/ns, (i+1)*n/ns) (within one page, at
+// most 512).
 int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   const int64_t max_len = d->max_seq_len > 0 ? d->max_seq_len : static_cast<int64_t>(d->max_pages) * d->page_size;
   const int64_t n_pages = std::max<int64_t>(1, ceil_div(max_len, d->page_size));
@@ -204,6 +205,11 @@ static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* 
   a.num_splits = ns;
   a.pps = pps;
   a.n_pages_plan = n_plan;
+  {
+    const int64_t n_tiles = static_cast<int64_t>(n_plan) * (d->page_size / 8);
+    a.split_base = static_cast<int>(n_tiles / ns);
+    a.split_rem = static_cast<int>(n_tiles % ns);
+  }
   a.deterministic = (d->flags & HAD_ATTN_DETERMINISTIC) ? 1 : 0;
   a.scale_log2 = d->sm_scale * 1.4426950408889634f;
   a.pg_begin = 0;
@@ -544,6 +550,11 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
   as.num_splits = ns_s;
   as.pps = 0;
   as.n_pages_plan = n_sfx;
+  {
+    const int64_t n_tiles = static_cast<int64_t>(n_sfx) * (d->page_size / 8);
+    as.split_base = static_cast<int>(n_tiles / ns_s);
+    as.split_rem = static_cast<int>(n_tiles % ns_s);
+  }
   as.pg_begin = px->prefix_pages;
   as.split_offset = ns_p;
   as.batch_rows = 0;

@@ -25,9 +25,12 @@ struct ValuArgs {
   int32_t* d_err;
   int n_seqs, q_len, H_q, H_kv, G, rows, row_base;
   int num_pages, page_size, max_pages, num_splits, pps;
-  int n_pages_plan;  // pages the split plan covers (n).  VALU kernel: split i owns the 8-token tiles
-                     // [i*N/ns, (i+1)*N/ns) of the N = n*page_size/8 tiles (its first and last page
-                     // possibly shared with a neighbour); MFMA kernel: the pages [i*n/ns, (i+1)*n/ns)
+  int n_pages_plan;  // pages the split plan covers (n).  VALU kernel: of the N = n*page_size/8 tiles of 8
+                     // tokens split i owns [i*base + min(i, rem), (i+1)*base + min(i+1, rem)) with
+                     // base = N / ns, rem = N % ns (the first rem splits one tile more; a split's first
+                     // and last page possibly shared with a neighbour); MFMA kernel: the pages
+                     // [i*n/ns, (i+1)*n/ns)
+  int split_base, split_rem;  // N / ns and N % ns of the VALU plan (host side)
   int deterministic;  // fixed tile stride per wave instead of dynamic claims
   float scale_log2;
   // Shared-prefix (cascade) passes.  Defaults (0, 0, num_splits, rows, 0, -1)

@@ -135,8 +135,7 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // the plan's tiles, or -- the suffix pass of a batch -- work unit blockIdx.x
   // of the units shared out by suffix length (bal_share), over the
   // sequence's own tiles.
-  int s = blockIdx.z, sp = blockIdx.x, nsplit = a.num_splits;
-  int64_t n_tiles_plan = static_cast<int64_t>(a.n_pages_plan) * tpp;
+  int s = blockIdx.z, sp = blockIdx.x, base = a.split_base, rem = a.split_rem;
   if constexpr (!FUSED) {
     if (a.bal_units > 0) {
       int n_t, W_t, O_t;
@@ -152,8 +151,10 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
       if (hit == 0) return;  // a unit left over (uniform over the workgroup)
       s = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(hit)) - 1);
       sp = g - __builtin_amdgcn_readfirstlane(__shfl(O_t, s));
-      nsplit = __builtin_amdgcn_readfirstlane(__shfl(W_t, s));
-      n_tiles_plan = __builtin_amdgcn_readfirstlane(__shfl(n_t, s));
+      const int nsplit = __builtin_amdgcn_readfirstlane(__shfl(W_t, s));
+      const int n_tiles = __builtin_amdgcn_readfirstlane(__shfl(n_t, s));
+      base = n_tiles / nsplit;
+      rem = n_tiles % nsplit;
     }
   }
 
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // pg_begin; balanced to within one tile, so no workgroup holds a page more
   // than another), which lie on the pages [pg0, pg1_plan); tiles are numbered
   // from pg0's first token, this split's being [tile_lo, tile_hi).
-  const int t0 = static_cast<int>(static_cast<int64_t>(sp) * n_tiles_plan / nsplit);
-  const int t1 = static_cast<int>(static_cast<int64_t>(sp + 1) * n_tiles_plan / nsplit);
+  const int t0 = sp * base + min(sp, rem);
+  const int t1 = t0 + base + (sp < rem ? 1 : 0);
   const int pg0 = a.pg_begin + t0 / tpp;
   const int pg1_plan = a.pg_begin + (t1 + tpp - 1) / tpp;
   const int npg_plan = pg1_plan - pg0;
@@ -217,20 +218,21 @@ __global__ __launch_bounds__(512, 2) void attn_valu_kernel(ValuArgs a, FusedArgs
   // refills them in, so the wait counts inside the loop stay exact.)
   Tile<D> buf[2];
   int tcur[2] = {tile_lo + wave, tile_lo + wave + kWaves};
-  // both page ids in one scalar round trip (the fences keep the two loads
-  // adjacent: left to itself the scheduler waits for the first before it
-  // computes the second address)
+  // both page ids and the length in one scalar round trip (the fences keep
+  // the loads adjacent: left to itself the scheduler waits for the first
+  // before it computes the next address; the length, needed for the
+  // prologue's angles, would otherwise be a second round trip after the
+  // first tile's loads)
   const int pix0 = min(pg0 + tcur[0] / tpp, a.max_pages - 1), pix1 = min(pg0 + tcur[1] / tpp, a.max_pages - 1);
   __builtin_amdgcn_sched_barrier(0);
   int pid0[2] = {pt_row[pix0], pt_row[pix1]};
+  const int L = a.seq_lens[s];  // (scalar loads: they do not queue behind the tiles)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 0; b < 2; ++b) pid0[b] = (pid0[b] < 0 || pid0[b] >= a.num_pages) ? 0 : pid0[b];
   __builtin_amdgcn_sched_barrier(0);
   load_tile_at<D>(buf[0], a, pid0[0], tcur[0] % tpp, tcur[0] < tile_hi, h, tg, j, tgv, dl);
   __builtin_amdgcn_sched_barrier(0);
-
-  const int L = a.seq_lens[s];  // (a scalar load: it does not queue behind the tiles)
 
   // (a suffix pass also needs every query to see the whole prefix before
   // pg_begin; a length past the plan's pages would leave tokens no split reads)

@@ -354,8 +354,9 @@ int had_qk_norm_rope_gate(const had_qknrg_desc *d, const had_qknrg_ptrs *p, void
  * Work is split over the context ("split-K"): of the n pages that
  * max_seq_len can reach (N = n * page_size / 8 tiles of 8 tokens), work
  * unit (s, h, split i of ns) covers, below 16 rows, the tiles
- * [i*N/ns, (i+1)*N/ns) (balanced to within one tile) and, at 16 rows or
- * more, the pages [i*n/ns, (i+1)*n/ns) (within one page); pages_per_split of
+ * [i*b + min(i, r), (i+1)*b + min(i+1, r)) with b = N / ns, r = N % ns
+ * (balanced to within one tile) and, at 16 rows or more, the pages
+ * [i*n/ns, (i+1)*n/ns) (within one page); pages_per_split of
  * the plan = ceil(n/ns), at most 512, and below 16 rows at most 511 when
  * ns > 1 (a tile range can touch one page more, and one split reads at most
  * 512); every seq_lens[s] must lie within the n pages (n * page_size tokens),

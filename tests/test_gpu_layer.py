@@ -101,13 +101,14 @@ def test_new_tokens_straddle_splits(H_q):
     _check_against_oracle(c)
 
 
-@pytest.mark.parametrize("L,num_splits", [(658, 7), (643, 13), (700, 5)])
+@pytest.mark.parametrize("L,num_splits", [(666, 7), (643, 13), (700, 5)])
 def test_valu_fused_tile_boundaries(L, num_splits):
     # 8 rows (2 q heads x 4 new tokens) on the fused VALU path, whose splits
     # are balanced to within one 8-token tile: boundaries fall inside pages
-    # (96 tiles of 64-token pages over 7, 13 or 5 splits), and with L = 658
-    # and 7 splits the new tokens lie on both sides of one (tiles 81 | 82);
-    # the split holding the last position's tile owns them
+    # (96 tiles of 64-token pages over 7, 13 or 5 splits; over 7 splits the
+    # first 5 take 14 tiles, the last 2 take 13), and with L = 666 and 7
+    # splits the new tokens lie on both sides of one (tiles 82 | 83); the
+    # split holding the last position's tile owns them
     c = _run(2150 + num_splits, [L], 4, 2, 1, 128, 32, 64, num_splits=num_splits)
     _check_against_oracle(c)
 
@@ -208,7 +209,7 @@ def test_disagreeing_descriptors_are_rejected():
 
 def test_split_touching_512_pages():
     # 4 rows, 64-token pages, 1532 planned pages over 3 splits: split 1's
-    # tiles [4085, 8170) start and end inside pages 510 and 1021, so it reads
+    # tiles [4086, 8171) start and end inside pages 510 and 1021, so it reads
     # 512 page ids, the most a split holds; the context ends inside page 1531
     L = 1532 * 64 - 20
     c = _run(2800, [L], 1, 4, 1, 64, 16, 64, num_splits=3, max_seq_len=1532 * 64, gated=True)
