@@ -79,6 +79,13 @@ int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
     const int64_t want = std::max<int64_t>(1, ceil_div(kTargetUnits, units));
     const int64_t min_pps = mfma ? ceil_div(256, d->page_size) : ceil_div(kMinTilesPerUnit, d->page_size / 8);
     ns = std::max<int64_t>(1, std::min<int64_t>(want, n_pages / min_pps));
+    if (mfma) {
+      // whole-page ranges: as many splits as the shortest longest split
+      // needs (q pages), if that is more -- 781 pages: 196 splits of <= 4
+      // pages rather than 195 with one of 5
+      const int64_t q = std::max<int64_t>(min_pps, ceil_div(n_pages, want));
+      ns = std::max<int64_t>(ns, std::min<int64_t>(want, ceil_div(n_pages, q)));
+    }
     // (below 16 rows, with several splits, a tile range can touch one page more)
     const int64_t cap = mfma ? had::kMaxPagesPerSplit : had::kMaxPagesPerSplit - 1;
     if (n_pages > had::kMaxPagesPerSplit) ns = std::max<int64_t>(ns, ceil_div(n_pages, cap));

@@ -29,8 +29,9 @@ struct ValuArgs {
                      // tokens split i owns [i*base + min(i, rem), (i+1)*base + min(i+1, rem)) with
                      // base = N / ns, rem = N % ns (the first rem splits one tile more; a split's first
                      // and last page possibly shared with a neighbour); MFMA kernel: the pages
-                     // [i*n/ns, (i+1)*n/ns)
-  int split_base, split_rem;  // N / ns and N % ns of the VALU plan (host side)
+                     // [i*b + min(i, r), (i+1)*b + min(i+1, r)) with b = n / ns, r = n % ns
+  int split_base, split_rem;  // N / ns and N % ns of the VALU plan, n / ns and n % ns of the MFMA
+                              // plan (host side)
   int deterministic;  // fixed tile stride per wave instead of dynamic claims
   float scale_log2;
   // Shared-prefix (cascade) passes.  Defaults (0, 0, num_splits, rows, 0, -1)

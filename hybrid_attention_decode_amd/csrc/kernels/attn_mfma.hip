@@ -105,31 +105,32 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   const int team = R128 ? 0 : wave >> 2, rb = R128 ? wave : wave & 3;
   const int P = a.page_size;
 
-  const int pg0 = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp) * a.n_pages_plan / a.num_splits);
-  const int pg1_plan = a.pg_begin + static_cast<int>(static_cast<int64_t>(sp + 1) * a.n_pages_plan / a.num_splits);
-  const int npg_plan = pg1_plan - pg0;
+  // split sp owns pages [sp*base + min(sp, rem), ...) of the plan, base and
+  // rem computed on the host (balanced to within one page)
+  const int pg0 = a.pg_begin + sp * a.split_base + min(sp, a.split_rem);
+  const int npg_plan = a.split_base + (sp < a.split_rem ? 1 : 0);
+  const int pg1_plan = pg0 + npg_plan;
   const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
-  const int L = a.fixed_len >= 0 ? a.fixed_len : a.seq_lens[s];
-  // (a suffix pass also needs every query to see the whole prefix before
-  // pg_begin; a length past the plan's pages would leave tokens no split reads)
-  const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P ||
-                                           L > (a.pg_begin + a.n_pages_plan) * P);
-  const int n_pages = bad_len ? 0 : (L + P - 1) / P;
-  const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
-  const int tok0 = pg0 * P;
-  const int tok_end = npg > 0 ? min((pg0 + npg) * P, L) : tok0;  // this split's tokens: [tok0, tok_end)
-  const int n_it = (tok_end - tok0 + kMTile - 1) / kMTile;
-
-  int errs = (bad_len && tid == 0) ? HAD_DERR_SEQLEN : 0;
-  if (tid == 0) sh.err = 0;
-  // page ids of the split (entry 0 always written, so the clamped loads of an
-  // empty split still read a valid page); bad ids become -1 and read page 0
-  for (int i = tid; i < max(npg_plan, 1); i += blockDim.x) {
-    const int pid = i < npg_plan ? pt_row[pg0 + i] : -1;
-    const bool ok = pid >= 0 && pid < a.num_pages;
-    if (!ok && i < npg) errs |= HAD_DERR_PAGE;
-    sh.pages[i] = ok ? pid : -1;
+  // Setup loads, none under a branch: first the scalar ones (the length and,
+  // when pages hold a multiple of 32 tokens so that the 32 tokens a wave
+  // stages lie in one page, the page ids of this wave's part of the first two
+  // stages), then the small vector loads (this thread's page id of the split,
+  // the q rows); the scalar values are waited for after both have gone out,
+  // and the first stages' K/V loads follow, so no wait on a small load ever
+  // has to wait for K/V too.
+  int pidA = 0, pidB = 0;
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PAGE32) {
+    const int half = wave >> 2;
+    pidA = pt_row[min(pg0 + (half * kMTeamTok) / P, a.max_pages - 1)];
+    pidB = pt_row[min(pg0 + (kMTile + half * kMTeamTok) / P, a.max_pages - 1)];
   }
+  const int L_mem = a.seq_lens[s];  // (the prefix pass passes the batch's lengths too, unused)
+  __builtin_amdgcn_sched_barrier(0);
+  // page ids of the split, one per thread (npg_plan <= kMaxPagesPerSplit =
+  // blockDim.x; the index clamped so that the load needs no branch), written
+  // to LDS after the first stages' loads have gone out
+  const int pt_raw = pt_row[min(pg0 + min(tid, max(npg_plan - 1, 0)), a.max_pages - 1)];
 
   // q rows of this wave as the B operand of S^T = K Q^T: lane (r16, g) holds
   // row 16*rb + r16, dims 32*ks + 8g .. +8 (zero for padding rows)
@@ -139,16 +140,29 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
   const int s_row = a.batch_rows > 0 ? (row_ok ? row : 0) / a.batch_rows : s;
   const int rr = a.batch_rows > 0 ? (row_ok ? row : 0) % a.batch_rows : row;  // row within its sequence
   const bool wave_active = a.row_base + 16 * rb < a.rows;  // uniform: any row of this wave real
-  u32x4_t qb[C::KS];
+  u32x4_t qraw[C::KS];
   {
     const int rc = row_ok ? rr : 0;
     const uint16_t* qp = a.q + ((static_cast<size_t>(s_row) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g);
-      qb[ks] = row_ok ? v : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int ks = 0; ks < C::KS; ++ks) qraw[ks] = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // the scalar results are needed from here on (an empty asm that reads them
+  // keeps their loads up at the top instead of next to their first use)
+  asm volatile("" ::"s"(pidA), "s"(pidB), "s"(L_mem));
+  const int L = a.fixed_len >= 0 ? a.fixed_len : L_mem;
+  // (a suffix pass also needs every query to see the whole prefix before
+  // pg_begin; a length past the plan's pages would leave tokens no split reads)
+  const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P ||
+                                           L > (a.pg_begin + a.n_pages_plan) * P);
+  const int n_pages = bad_len ? 0 : (L + P - 1) / P;
+  const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
+  const int tok0 = pg0 * P;
+  const int tok_end = npg > 0 ? min((pg0 + npg) * P, L) : tok0;  // this split's tokens: [tok0, tok_end)
+  const int n_it = (tok_end - tok0 + kMTile - 1) / kMTile;
+  int errs = (bad_len && tid == 0) ? HAD_DERR_SEQLEN : 0;
+
   // visible keys of this lane's row (causal inside the draft; a prefix pass
   // sees the whole prefix)
   const int lim = (row_ok && a.fixed_len < 0) ? (L - a.q_len + rr / a.G + 1) : L;
@@ -206,15 +220,32 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
     load_pid(kr, vr, it, sh.pages[min(t0 / P - pg0, last_pg)]);
   };
 
-  // The first stage's loads go out before the setup barrier, their page id
+  // The first stages' loads go out before the setup barrier, their page ids
   // read from the page table itself (an id out of range reads page 0; the
-  // staging below zeroes what the checked list marks invalid).
+  // staging below zeroes what the checked list marks invalid): with PAGE32
+  // both stages from the scalar ids read at the start, otherwise the first
+  // from a per-lane id and the second after the barrier.
   u32x4_t kA[TPT], vA[TPT], kB[TPT], vB[TPT];
-  {
+  if constexpr (PAGE32) {
+    load_pid(kA, vA, 0, (pidA >= 0 && pidA < a.num_pages) ? pidA : 0);
+    load_pid(kB, vB, 1, (pidB >= 0 && pidB < a.num_pages) ? pidB : 0);
+  } else {
     const int t0 = min(tok0 + ltok, last_tok);
     const int pid = pt_row[min(pg0 + min(t0 / P - pg0, last_pg), a.max_pages - 1)];
     load_pid(kA, vA, 0, (pid >= 0 && pid < a.num_pages) ? pid : 0);
   }
+  // (entry 0 always written, so the clamped loads of an empty split still
+  // read a valid page; bad ids become -1 and read page 0)
+  if (tid == 0) sh.err = 0;
+  if (tid < max(npg_plan, 1)) {
+    const int pt_val = tid < npg_plan ? pt_raw : -1;
+    const bool ok = pt_val >= 0 && pt_val < a.num_pages;
+    if (!ok && tid < npg) errs |= HAD_DERR_PAGE;
+    sh.pages[tid] = ok ? pt_val : -1;
+  }
+  u32x4_t qb[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) qb[ks] = row_ok ? qraw[ks] : u32x4_t{0u, 0u, 0u, 0u};
   __syncthreads();
 
   auto stage = [&](const u32x4_t (&kr)[TPT], const u32x4_t (&vr)[TPT], int it, int b) __attribute__((always_inline)) {
@@ -336,7 +367,7 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
 
   // ---- main loop: register stages A (even tiles) and B (odd tiles), LDS
   // buffer 0 for A and 1 for B; the loop exits only at its header
-  load(kB, vB, 1);
+  if constexpr (!PAGE32) load(kB, vB, 1);
   int it = 0;
   while (it + 1 < n_it) {
     stage(kA, vA, it, 0);
@@ -414,6 +445,13 @@ __global__ __launch_bounds__(512, 2) void attn_mfma_kernel(ValuArgs a) {
 
 hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipStream_t stream) {
   ValuArgs a = a_in;
+  // page-granular split ranges (the VALU plan's base and remainder count
+  // tiles); one thread per page id of a split
+  static_assert(kMWaves * 64 >= kMaxPagesPerSplit, "a split's page ids are read one per thread");
+  if (a.num_splits < 1 || (a.n_pages_plan + a.num_splits - 1) / a.num_splits > kMaxPagesPerSplit)
+    return hipErrorInvalidValue;
+  a.split_base = a.n_pages_plan / a.num_splits;
+  a.split_rem = a.n_pages_plan % a.num_splits;
   hipError_t e = hipSuccess;
   // up to 64 rows: the token-split teams; more: 128 rows per launch
   const bool r128 = a.rows > kMRows;

@@ -202,16 +202,18 @@ def test_attention_split_plan():
     assert plan((1, 4, 16, 256), 262144 + 1034) == (256, 17)
     assert plan((1, 1, 8, 256), 513) == (2, 5)
     assert plan((1, 4, 16, 256), 2000) == (8, 4)       # 32 pages, 4 per split
-    # cascade: 16 sequences on a 781-page prefix (prefix pass: 195 splits of
-    # >= 4 pages), suffixes up to 12,288 tokens: 256 suffix units shared out
-    # by length, so every sequence's workspace row has 195 + 256 slots
+    assert plan((1, 4, 16, 256), 640) == (3, 4)        # 10 pages: 3 splits of <= 4, not 2 of 5
+    # cascade: 16 sequences on a 781-page prefix (prefix pass: 196 splits of
+    # <= 4 pages -- 195 would leave one of 5), suffixes up to 12,288 tokens:
+    # 256 suffix units shared out by length, so every sequence's workspace
+    # row has 196 + 256 slots
     n, rows, D = 16, 8, 256
     max_len = 50000 + 12288 + 300
     pages = -(-max_len // 64) + 1
     desc = had.attn_desc((n, 1, 8, D), (4096, 1, 64, D), pages, max_seq_len=max_len)
-    assert had.decode_attn_cascade_plan(desc, 781) == (195, 256)
+    assert had.decode_attn_cascade_plan(desc, 781) == (196, 256)
     ws = had.decode_attn_cascade_workspace_bytes(desc, 781)
-    assert ws == n * 1 * (195 + 256) * rows * (D + 2) * 4
+    assert ws == n * 1 * (196 + 256) * rows * (D + 2) * 4
     # the per-sequence plan where the shares do not apply: 16 rows or more
     # (MFMA suffix pass), more than 64 sequences, or a forced split count
     d16 = had.attn_desc((n, 2, 8, D), (4096, 1, 64, D), pages, max_seq_len=max_len)
