@@ -48,7 +48,8 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_valu_d256_longctx_pmc.json")
 KERNEL_DIR = os.path.join(ROOT, "hybrid_attention_decode_amd", "csrc", "kernels")
 # the partial kernel's source and the headers it includes: the PMC summary is
 # used only while they are unchanged
-KERNEL_SRCS = [os.path.join(KERNEL_DIR, f) for f in ("attn_valu.hip", "attn_internal.h", "prologue_math.h", "kcommon.h")]
+KERNEL_SRCS = [os.path.join(KERNEL_DIR, f)
+               for f in ("attn_valu.hip", "attn_valu_body.h", "attn_internal.h", "prologue_math.h", "kcommon.h")]
 
 
 def kernel_source_hash():
@@ -508,13 +509,15 @@ def stack_kernel_us(st, kernel_reps):
                                             st.prefix_dev, st.cws, out=a["out"], max_seq_len=st.max_seq_len,
                                             gate=a["gate"])
 
+        # the whole call (both passes in one launch, then the merge), and the
+        # two-pass form through the split entry points, pass by pass
         return {
             "prologue": round(time_graph(torch, prologue, n * N_ATTN), 3),
-            "attn_cascade_prefix_suffix_combine": round(time_graph(torch, cascade, n * N_ATTN), 3),
-            "cascade_prefix_pass": round(time_graph(torch, prefix_pass, n * N_ATTN), 3),
-            "cascade_suffix_pass": round(time_graph(torch, suffix_pass, n * N_ATTN), 3),
-            "cascade_merge": round(time_graph(torch, merge, n * N_ATTN), 3),
-            "cascade_splits": [ns_p, ns_s],
+            "attn_cascade_one_launch_and_merge": round(time_graph(torch, cascade, n * N_ATTN), 3),
+            "two_pass_prefix_pass": round(time_graph(torch, prefix_pass, n * N_ATTN), 3),
+            "two_pass_suffix_pass": round(time_graph(torch, suffix_pass, n * N_ATTN), 3),
+            "two_pass_merge": round(time_graph(torch, merge, n * N_ATTN), 3),
+            "two_pass_splits": [ns_p, ns_s],
             "gdn_update": round(time_graph(torch, gdn, max(2, n) * N_GDN), 3),
         }
     return {
@@ -811,7 +814,8 @@ def run_prefix_shared(n_seqs=16, prefix=50000, max_suffix=12288, steps=256, warm
     res = dict(workload="prefix-shared: %d sequences fork a %d-token prefix (copy-on-write on the first divergent "
                         "page), private suffixes ~ U{0..%d}, %d GDN slots, one token per sequence per step; attention %s"
                         % (n_seqs, prefix, max_suffix, n_slots,
-                           "reads the prefix's whole pages once for all sequences (cascade)" if cascade
+                           "reads the prefix's whole pages once for all sequences (cascade: prefix and suffix passes in one "
+                           "launch, units split by length on the device)" if cascade
                            else "per sequence (fused prologue + split-K)"),
                steps=steps, warmup=warmup, ms_per_step=round(ms, 5), steps_per_s=round(1e3 / ms, 3),
                tokens_per_s=round(n_seqs * 1e3 / ms, 2), cow_copies=n_cow,

@@ -255,12 +255,16 @@ int had_decode_attn_partial(const had_attn_desc* d, const had_attn_ptrs* p, void
 // applied when the descriptor asks for the gated output.
 static int launch_combine_after(const had_attn_desc* d, const had::ValuArgs& a, void* out, void* stream,
                                 const void* gate = nullptr, int gate_hstride = 0, int bal_units = 0,
-                                int prefix_splits = 0) {
+                                int prefix_splits = 0, int prefix_tiles = 0, int prefix_weight16 = 0,
+                                int min_prefix_units = 0) {
   had::CombineArgs c{};
   if (bal_units > 0) {  // a cascade whose suffix units were shared out by length
     c.seq_lens = a.seq_lens;
     c.bal_units = bal_units;
     c.prefix_splits = prefix_splits;
+    c.prefix_tiles = prefix_tiles;  // > 0: one-launch cascade, prefix units computed on the device
+    c.prefix_weight16 = prefix_weight16;
+    c.min_prefix_units = min_prefix_units;
     c.tok_begin = a.pg_begin * a.page_size;
     c.max_tiles = a.n_pages_plan * (a.page_size / 8);
   }
@@ -432,6 +436,19 @@ static int cascade_bal_units(const had_attn_desc* d, int n_sfx) {
   return std::max<int>(d->n_seqs, static_cast<int>(ceil_div(kTargetUnits, d->H_kv)));
 }
 
+// Units per KV head of the one-launch cascade (both passes in one grid), or 0
+// where it does not apply: suffix units shared out by length, at most 8 rows
+// per sequence and 128 in the prefix pass (one row block each), pages of a
+// multiple of 32 tokens.  At least one unit per sequence plus the prefix's
+// minimum (page cap), and no more slots than the two-pass plan's workspace.
+static int cascade_one_launch_units(const had_attn_desc* d, const had_attn_prefix* px, int bal, int ns_p, int ns_s) {
+  const int rows = d->q_len * (d->H_q / d->H_kv);
+  if (bal <= 0 || rows > 8 || d->n_seqs * rows > 128 || d->page_size % 32 != 0) return 0;
+  const int min_pu = static_cast<int>(ceil_div(px->prefix_pages, had::kMaxPagesPerSplit));
+  const int G = std::max<int>(static_cast<int>(ceil_div(kTargetUnits, d->H_kv)), min_pu + d->n_seqs);
+  return G <= ns_p + ns_s ? G : 0;
+}
+
 static int cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int* ns_p, int* ns_s, int* n_sfx,
                         int* bal = nullptr) {
   int st = check_desc(d);
@@ -491,7 +508,7 @@ size_t had_decode_attn_cascade_workspace_bytes(const had_attn_desc* d, const had
 
 // passes: 1 = the prefix pass, 2 = the suffix pass, 3 = both; merge = run the combine after them
 static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, int passes,
-                          bool merge, void* stream) {
+                          bool merge, void* stream, bool one_launch = false) {
   if (merge && d && p && (d->flags & HAD_ATTN_GATED_OUTPUT) && !p->gate)
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: HAD_ATTN_GATED_OUTPUT with a NULL gate");
   int ns_p, ns_s, n_sfx, bal;
@@ -502,8 +519,12 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: NULL pointer in ptrs or prefix");
   if (!aligned16(p->q) || !aligned16(p->k_pool) || !aligned16(p->v_pool) || !aligned16(p->workspace))
     return fail(HAD_ERR_INVALID_ARG, "decode_attn_cascade: q, pools and workspace must be 16-byte aligned");
-  const int ns_total = ns_p + ns_s;
-  const size_t need = ws_partials_bytes(d, ns_total);
+  // both passes in one grid of G1 units per KV head where that applies (the
+  // whole call only: the split entry points keep the two-pass layout, which
+  // their merge expects), its G1 slots inside the two-pass workspace
+  const int G1 = one_launch ? cascade_one_launch_units(d, px, bal, ns_p, ns_s) : 0;
+  const int ns_total = G1 > 0 ? G1 : ns_p + ns_s;
+  const size_t need = ws_partials_bytes(d, ns_p + ns_s);
   if (p->workspace_bytes < need)
     return fail(HAD_ERR_WORKSPACE_TOO_SMALL, "decode_attn_cascade: workspace %zu bytes < %zu", p->workspace_bytes,
                 need);
@@ -527,26 +548,20 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
   a.scale_log2 = d->sm_scale * 1.4426950408889634f;
   a.ns_total = ns_total;
   a.ws_rows = rows;
-  hipError_t e = hipSuccess;
-  if (passes & 1) {
-    // prefix pass: all sequences' rows, the prefix page list as page-table row 0
-    had::ValuArgs ap = a;
-    ap.page_table = px->prefix_page_table;
-    ap.seq_lens = p->seq_lens;  // unused (fixed_len)
-    ap.n_seqs = 1;
-    ap.rows = d->n_seqs * rows;
-    ap.max_pages = px->prefix_pages;
-    ap.num_splits = ns_p;
-    ap.pps = 0;
-    ap.n_pages_plan = px->prefix_pages;
-    ap.pg_begin = 0;
-    ap.split_offset = 0;
-    ap.batch_rows = rows;
-    ap.fixed_len = px->prefix_pages * d->page_size;
-    e = had::launch_attn_mfma(ap, d->head_dim, dim3(ns_p, d->H_kv, 1), s);
-    if (e != hipSuccess)
-      return fail(HAD_ERR_HIP, "decode_attn_cascade: prefix kernel launch: %s", hipGetErrorString(e));
-  }
+  // prefix pass: all sequences' rows, the prefix page list as page-table row 0
+  had::ValuArgs ap = a;
+  ap.page_table = px->prefix_page_table;
+  ap.seq_lens = p->seq_lens;  // unused (fixed_len)
+  ap.n_seqs = 1;
+  ap.rows = d->n_seqs * rows;
+  ap.max_pages = px->prefix_pages;
+  ap.num_splits = ns_p;
+  ap.pps = 0;
+  ap.n_pages_plan = px->prefix_pages;
+  ap.pg_begin = 0;
+  ap.split_offset = 0;
+  ap.batch_rows = rows;
+  ap.fixed_len = px->prefix_pages * d->page_size;
   // suffix pass: each sequence from page prefix_pages on
   had::ValuArgs as = a;
   as.page_table = p->page_table;
@@ -567,28 +582,51 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
   as.batch_rows = 0;
   as.fixed_len = -1;
   as.bal_units = bal;
-  if (passes & 2) {
-    const dim3 grid(ns_s, d->H_kv, bal > 0 ? 1 : d->n_seqs);
-    if (rows >= 16) {
-      as.row_base = 0;
-      e = had::launch_attn_mfma(as, d->head_dim, grid, s);
-    } else {
-      for (int rb = 0; rb < rows && e == hipSuccess; rb += 8) {
-        as.row_base = rb;
-        e = had::launch_attn_valu(as, d->head_dim, grid, s);
-      }
+  const int prefix_tiles = px->prefix_pages * (d->page_size / 8);
+  const int weight16 = had::cascade_prefix_weight16(d->n_seqs * rows);
+  const int min_pu = static_cast<int>(ceil_div(px->prefix_pages, had::kMaxPagesPerSplit));
+  hipError_t e = hipSuccess;
+  if (G1 > 0) {
+    if (passes == 3) {
+      had::ValuArgs as1 = as;
+      as1.bal_units = 0;  // set per workgroup
+      as1.row_base = 0;
+      ap.row_base = 0;
+      e = had::launch_attn_cascade(ap, as1, prefix_tiles, weight16, min_pu, d->head_dim, dim3(G1, d->H_kv, 1), s);
+      if (e != hipSuccess)
+        return fail(HAD_ERR_HIP, "decode_attn_cascade: one-launch kernel: %s", hipGetErrorString(e));
     }
-    if (e != hipSuccess)
-      return fail(HAD_ERR_HIP, "decode_attn_cascade: suffix kernel launch: %s", hipGetErrorString(e));
+  } else {
+    if (passes & 1) {
+      e = had::launch_attn_mfma(ap, d->head_dim, dim3(ns_p, d->H_kv, 1), s);
+      if (e != hipSuccess)
+        return fail(HAD_ERR_HIP, "decode_attn_cascade: prefix kernel launch: %s", hipGetErrorString(e));
+    }
+    if (passes & 2) {
+      const dim3 grid(ns_s, d->H_kv, bal > 0 ? 1 : d->n_seqs);
+      if (rows >= 16) {
+        as.row_base = 0;
+        e = had::launch_attn_mfma(as, d->head_dim, grid, s);
+      } else {
+        for (int rb = 0; rb < rows && e == hipSuccess; rb += 8) {
+          as.row_base = rb;
+          e = had::launch_attn_valu(as, d->head_dim, grid, s);
+        }
+      }
+      if (e != hipSuccess)
+        return fail(HAD_ERR_HIP, "decode_attn_cascade: suffix kernel launch: %s", hipGetErrorString(e));
+    }
   }
   if (!merge) return had::ok();
   had::ValuArgs am = as;
   am.num_splits = ns_total;
+  if (G1 > 0)
+    return launch_combine_after(d, am, p->out, stream, p->gate, d->head_dim, G1, 0, prefix_tiles, weight16, min_pu);
   return launch_combine_after(d, am, p->out, stream, p->gate, d->head_dim, bal, ns_p);
 }
 
 int had_decode_attn_cascade(const had_attn_desc* d, const had_attn_prefix* px, const had_attn_ptrs* p, void* stream) {
-  return cascade_launch(d, px, p, 3, true, stream);
+  return cascade_launch(d, px, p, 3, true, stream, true);
 }
 
 int had_decode_attn_cascade_plan(const had_attn_desc* d, const had_attn_prefix* px, int32_t* prefix_splits,

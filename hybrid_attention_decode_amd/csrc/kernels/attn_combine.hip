@@ -46,9 +46,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
   // shared out by length the prefix splits and the sequence's own share
   int ns = a.num_splits;
   if (a.bal_units > 0) {
+    // (one-launch cascade: the prefix's units first, the same integer the
+    // partial kernel computed)
+    const int n_pre = a.prefix_tiles > 0 ? cascade_prefix_units(a.seq_lens, a.n_seqs, a.tok_begin, a.max_tiles,
+                                                                a.bal_units, a.prefix_tiles, a.prefix_weight16,
+                                                                a.min_prefix_units, lane)
+                                         : a.prefix_splits;
     int n_t, W_t, O_t;
-    bal_share(a.seq_lens, a.n_seqs, a.tok_begin, a.max_tiles, a.bal_units, lane, n_t, W_t, O_t);
-    ns = a.prefix_splits + __builtin_amdgcn_readfirstlane(__shfl(W_t, unit / a.H_kv));
+    bal_share(a.seq_lens, a.n_seqs, a.tok_begin, a.max_tiles, a.prefix_tiles > 0 ? a.bal_units - n_pre : a.bal_units,
+              lane, n_t, W_t, O_t);
+    ns = n_pre + __builtin_amdgcn_readfirstlane(__shfl(W_t, unit / a.H_kv));
   }
   const size_t base = static_cast<size_t>(unit) * a.num_splits;
   const float* ml = a.ws_ml;

@@ -48,6 +48,31 @@ struct ValuArgs {
                      // (bal_share below); 0 = the split plan above
 };
 
+// LDS of a kernel, one variable per storage type T: a partial body names its
+// part of g_lds<Store> directly (Store = its own layout, or the union of both
+// layouts in the one-launch cascade), so every LDS address stays a constant
+// offset of one variable -- reached through a reference parameter instead,
+// the compiler no longer pairs neighbouring reads into one instruction and
+// the 128-row MFMA partial runs out of registers.
+namespace {
+template <class T>
+__shared__ T g_lds;
+}  // namespace
+
+// Suffix tiles of a batch: lane t of the calling wave gets sequence t's
+// n_t, the tiles of 8 tokens from token tok_begin on (at most max_tiles);
+// every lane gets K, the number of sequences with a tile, and N, the total
+// (n_seqs <= 64).
+__device__ __forceinline__ void suffix_tiles(const int32_t* seq_lens, int n_seqs, int tok_begin, int max_tiles,
+                                             int lane, int& n_t, int& K, long long& N) {
+  const int L = lane < n_seqs ? seq_lens[lane] : 0;
+  n_t = lane < n_seqs ? min(max(0, (L - tok_begin + 7) / 8), max_tiles) : 0;
+  K = __popcll(__ballot(n_t > 0));
+  N = n_t;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) N += __shfl_xor(N, off);
+}
+
 // Work units of a batch's suffix pass shared out by length: sequence t has
 // n_t tiles of 8 tokens from token tok_begin on; every sequence with a tile
 // gets one unit and the units left over are given in proportion to n_t
@@ -57,12 +82,9 @@ struct ValuArgs {
 // merge agree without exchanging anything.
 __device__ __forceinline__ void bal_share(const int32_t* seq_lens, int n_seqs, int tok_begin, int max_tiles, int G,
                                           int lane, int& n_t, int& W_t, int& O_t) {
-  const int L = lane < n_seqs ? seq_lens[lane] : 0;
-  n_t = lane < n_seqs ? min(max(0, (L - tok_begin + 7) / 8), max_tiles) : 0;
-  const int K = __popcll(__ballot(n_t > 0));
-  long long N = n_t;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) N += __shfl_xor(N, off);
+  int K;
+  long long N;
+  suffix_tiles(seq_lens, n_seqs, tok_begin, max_tiles, lane, n_t, K, N);
   const long long spare = G > K ? G - K : 0;
   W_t = n_t > 0 ? 1 + static_cast<int>(spare * n_t / (N > 0 ? N : 1)) : 0;
   int x = W_t;
@@ -72,6 +94,26 @@ __device__ __forceinline__ void bal_share(const int32_t* seq_lens, int n_seqs, i
     if (lane >= off) x += y;
   }
   O_t = x - W_t;
+}
+
+// One-launch cascade: G workgroups do both passes, the first G_p the prefix
+// pass (prefix_tiles tiles of 8 tokens, read once for the rows of every
+// sequence) and the rest the suffixes, shared out by bal_share.  G_p is G in
+// proportion to the prefix's cost against the suffixes' (rounded), a prefix
+// tile costing weight16 / 16 suffix tiles, at least min_pu (so that no prefix
+// split exceeds the page cap) and at most G - K (one unit for each sequence
+// with a suffix; the host guarantees min_pu + n_seqs <= G).  The same integer
+// in every wave that calls it with the same lengths.
+__device__ __forceinline__ int cascade_prefix_units(const int32_t* seq_lens, int n_seqs, int tok_begin, int max_tiles,
+                                                    int G, int prefix_tiles, int weight16, int min_pu, int lane) {
+  int n_t, K;
+  long long N;
+  suffix_tiles(seq_lens, n_seqs, tok_begin, max_tiles, lane, n_t, K, N);
+  const long long T = static_cast<long long>(prefix_tiles) * weight16, tot = T + 16 * N;
+  long long gp = (2 * static_cast<long long>(G) * T + tot) / (2 * tot);
+  gp = gp < min_pu ? min_pu : gp;
+  gp = gp > G - max(K, 1) ? G - max(K, 1) : gp;  // (one suffix unit at least: it reports short sequences)
+  return static_cast<int>(gp);
 }
 
 // Inputs of the prologue when the VALU attention kernel runs it inline (the
@@ -106,14 +148,30 @@ struct CombineArgs {
   int gate_hstride;
   // merge of a cascade whose suffix pass shared out bal_units work units
   // (ValuArgs::bal_units): sequence s merges prefix_splits + W_s partials of
-  // its num_splits slots (W_s from bal_share over seq_lens)
+  // its num_splits slots (W_s from bal_share over seq_lens).  One-launch
+  // cascade (prefix_tiles > 0): bal_units is the launch's G units of both
+  // passes, prefix_splits = cascade_prefix_units(...) and the suffixes share
+  // the other G - prefix_splits.
   const int32_t* seq_lens;
   int bal_units, prefix_splits, tok_begin, max_tiles;
+  int prefix_tiles, prefix_weight16, min_prefix_units;
 };
 
 hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_valu_fused(const ValuArgs& a, const FusedArgs& f, int head_dim, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_mfma(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
+// both cascade passes in one grid (grid.x = G units per KV head): prefix args
+// ap as for the MFMA prefix pass, suffix args as as for the shared-out suffix
+// pass with bal_units 0 (set per workgroup), ns_total = G in both
+hipError_t launch_attn_cascade(const ValuArgs& ap, const ValuArgs& as, int prefix_tiles, int weight16, int min_pu,
+                               int head_dim, dim3 grid, hipStream_t stream);
+// cost of a prefix tile in suffix tiles (x16) in the one-launch cascade's
+// unit split, measured with both sides running: a 64-token page costs the
+// 128-row MFMA side about 2.2x what it costs the 8-row VALU side (16 x 50K
+// prefix: the weights 16 / 24 / 28 / 32 / 36 gave 54.9 / 47.9 / 44.0 / 45.0
+// / 42.6 us per launch); up to 64 rows the MFMA side streams at about the
+// VALU side's rate
+inline int cascade_prefix_weight16(int prefix_rows) { return prefix_rows > 64 ? 36 : 18; }
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace had

@@ -125,10 +125,11 @@ def test_cascade_rejects_bad_prefix():
                                 torch.zeros(0, dtype=torch.int32, device=DEV))
 
 
-def test_split_passes_and_merge_equal_the_one_call_cascade():
-    # prefix pass, suffix pass and merge called one by one give the bits of
-    # had_decode_attn_cascade (deterministic mode), and the plan reports the
-    # workspace's split counts
+def test_split_passes_and_one_call_cascade_match_the_oracle():
+    # prefix pass, suffix pass and merge called one by one (the two-pass
+    # layout) and had_decode_attn_cascade (here both passes in one launch,
+    # units split on the device) each match the oracle, and the plan reports
+    # the workspace's split counts
     P, D, H_q = 64, 256, 8
     q, kb, vb, table, L, prefix = _batch(4100, 5, 3200, [0, 700, 65, 1500, 9], 1, H_q, 1, D, P)
     print("case cascade split passes", flush=True)
@@ -142,12 +143,52 @@ def test_split_passes_and_merge_equal_the_one_call_cascade():
     had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 1, d_err=err, deterministic=True)
     had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 2, d_err=err, deterministic=True)
     out = had.decode_attn_cascade_combine(qd, kd, vd, ptd, ld, pxd, ws, d_err=err, deterministic=True)
-    ref = had.decode_attn_cascade(qd, kd, vd, ptd, ld, pxd, d_err=err, deterministic=True)
+    one = had.decode_attn_cascade(qd, kd, vd, ptd, ld, pxd, d_err=err, deterministic=True)
+    again = had.decode_attn_cascade(qd, kd, vd, ptd, ld, pxd, d_err=err, deterministic=True)
     torch.cuda.synchronize()
     assert err.item() == 0
-    assert np.array_equal(bits_of(out), bits_of(ref))
+    ref = _oracle(q, kb, vb, table, L, P, D)
+    assert_attn_close(out, ref)
+    assert_attn_close(one, ref)
+    assert np.array_equal(bits_of(one), bits_of(again))      # deterministic mode: same bits every call
     with pytest.raises(had.HadError):
         had.decode_attn_cascade_partial(qd, kd, vd, ptd, ld, pxd, ws, 4)
+
+
+@pytest.mark.parametrize("n,prefix_len,suffixes", [
+    (16, 4096, [0] * 16),                       # only the decode tokens: few suffix tiles, most units to the prefix
+    (9, 640, [9000] + [3] * 8),                 # one suffix much longer than the prefix: most units to it
+    (2, 64 * 600, [1, 2]),                      # a prefix of 600 pages: at least 2 prefix units (page cap)
+    (16, 2048, [int(x) for x in range(0, 16 * 700, 700)]),  # 128 prefix rows (two row groups of the MFMA side)
+])
+def test_one_launch_cascade_unit_split(n, prefix_len, suffixes):
+    # both passes in one grid: the prefix's share of the units follows its
+    # share of the tiles, computed on the device from the lengths
+    P, D, H_q = 64, 256, 8
+    seed = 4200 + n + prefix_len % 89
+    q, kb, vb, table, L, prefix = _batch(seed, n, prefix_len, suffixes, 1, H_q, 1, D, P)
+    print("case one-launch cascade n=%d prefix=%d suffixes=%s" % (n, prefix_len, suffixes), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn_cascade(to_dev(q), to_dev(kb), to_dev(vb), to_dev(table), to_dev(L), to_dev(prefix),
+                                  d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert_attn_close(out, _oracle(q, kb, vb, table, L, P, D))
+
+
+def test_one_launch_cascade_reports_a_sequence_inside_the_prefix():
+    n, prefix_len, P = 3, 1024, 64
+    q, kb, vb, table, L, prefix = _batch(3150, n, prefix_len, [5, 0, 70], 1, 8, 1, 256, P)
+    L = L.copy()
+    L[1] = prefix_len - 3                                # this sequence does not see the whole prefix
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("case one-launch cascade with a too-short sequence", flush=True)
+    out = had.decode_attn_cascade(to_dev(q), to_dev(kb), to_dev(vb), to_dev(table), to_dev(L), to_dev(prefix),
+                                  d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_SEQLEN
+    ref = _oracle(q[[0, 2]], kb, vb, table[[0, 2]], L[[0, 2]], P, 256)   # the others are unaffected
+    assert_attn_close(out[[0, 2]], ref)
 
 
 @pytest.mark.parametrize("n,spread,prefix_len,D,P", [
