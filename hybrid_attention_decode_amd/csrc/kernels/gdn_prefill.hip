@@ -15,7 +15,7 @@
 // recurrence of the Gated DeltaNet paper, Yang, Kautz & Hatamizadeh, ICLR
 // 2025.  GDN layers of the hybrid model: 24-ai.news TokenSpeed article.)
 //
-// Three kernels:
+// Two kernels (and a link kernel between two scan passes for long prompts):
 //  * prep, one workgroup per (sequence, chunk, head), all chunks at once:
 //    K K^T and K Q^T on MFMA, the triangular solve by forward substitution
 //    (one wave, lane j = column j of T, fp32), then U' and W on MFMA.  The
@@ -23,13 +23,12 @@
 //    kernel's MFMA operands.
 //  * scan, one workgroup of 4 waves per (sequence, head, 16 rows of S): the
 //    state slice stays in registers across the chunks of the sequence; wave
-//    w owns the chunk's tokens 16w .. 16w+15 for U and the state columns
-//    32w .. 32w+31 for the update.  Two barriers per chunk exchange U and the
-//    new state through LDS.  Only W, K^T and U' are read on this sequential
-//    path (the per-chunk operand stream through each CU bounds it); it
-//    leaves U and each chunk's initial state in the workspace.
-//  * output, again one workgroup per (sequence, chunk, head), all chunks at
-//    once: o = q_scale (diag(gamma) Q S0^T + Aqk U).
+//    w owns the chunk's tokens 16w .. 16w+15 for U and the output and the
+//    state columns 32w .. 32w+31 for the update.  Two barriers per chunk
+//    exchange U and the new state through LDS.  The chunk's output columns
+//    of the slice, o = q_scale (diag(gamma) Q S0^T + Aqk U), are formed
+//    while S0 and U are at hand (Q read from the input, Aqk from the
+//    workspace), so neither U nor the chunk states go back to memory.
 // Products with a fp32 operand (the state, T, W, Aqk, U) use the split
 // x = hi + lo of both bf16 halves (hi*hi + hi*lo + lo*hi, or two terms when
 // the other operand is exact bf16), so each product keeps ~16 mantissa bits.
@@ -96,9 +95,7 @@ struct PL {
   static constexpr int A_LO = A_HI + 4 * 2 * 64;
   static constexpr int KT = A_LO + 4 * 2 * 64;   // K^T, A operand: [d_k tile][ks'][lane], tokens in tau order
   static constexpr int GAM = KT + DT * 2 * 64;   // 64 floats gamma_t, then 64 floats gamma_C / gamma_t
-  static constexpr int SC_HI = GAM + 2 * kC / 4; // chunk's initial state, B operand: [v-slice][ks][lane] (scan)
-  static constexpr int SC_LO = SC_HI + VT * KS * 64;
-  static constexpr int TOTAL = SC_LO + VT * KS * 64;
+  static constexpr int TOTAL = GAM + 2 * kC / 4;
 };
 
 struct PrefillArgs {
@@ -393,9 +390,9 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
 }
 
 // Scan over the chunks of one (sequence, head) for state rows 16 vs .. +15:
-// only what the state needs (W, K^T, U') is on this sequential path.  Per
-// chunk it leaves U (over U' in the workspace) and the chunk's initial
-// state (as B operands) for the output kernel.
+// what the state needs (W, K^T, U') is on this sequential path; the pass
+// that emits the output (EMIT) also reads Q and Aqk, one chunk ahead like
+// the rest, and writes the chunk's output columns of the slice.
 //
 // Segmented form (a long prompt with few heads: one pass would keep only
 // units x d_v/16 workgroups busy along a chain of every chunk).  With
@@ -407,8 +404,8 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(PrefillArgs a) {
 // past the first segment, the d_k rows of the identity with U' = 0 (giving
 // PI), storing nothing per chunk; the link kernel chains the segments'
 // start states; phase 3 is the one-pass scan again, every segment at once
-// from its start state, storing U and the chunk states.
-template <int DK, int DV>
+// from its start state, emitting the output.
+template <int DK, int DV, bool EMIT>
 __global__ __launch_bounds__(256, 2) void gdn_prefill_scan_kernel(PrefillArgs a) {
   using L = PL<DK, DV>;
   using G = SegL<DK, DV>;
@@ -427,7 +424,6 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_scan_kernel(PrefillArgs a)
   const bool pi_rows = vs >= VT;            // phase 1: rows of the transition
   if (a.phase == 1 && pi_rows && seg == 0) return;  // the first segment's transition is not needed
   const int vsc = pi_rows ? VT - 1 : vs;    // (their U' loads read a real slice and are discarded)
-  const bool chunk_out = a.phase != 1;      // per-chunk U and states are stored
   // (wave is made uniform so that tests on it are scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
@@ -533,34 +529,66 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_scan_kernel(PrefillArgs a)
     p.rat = gw[kC + lane];
     p.gC = gw[kC - 1];
   };
-
-  // the chunk's initial state for the output kernel: this wave's d_k step
-  // (chunk c + 1's is stored at the end of step c)
-  auto store_sc = [&](int c) {
-    u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
-    blk[L::SC_HI + (vs * KS + wave) * 64 + lane] = ohi;
-    blk[L::SC_LO + (vs * KS + wave) * 64 + lane] = olo;
+  // The output's operands of one chunk (EMIT): Q rows 16w + r (d_k in sigma
+  // order; rows past the sequence read its last row, their output is not
+  // stored), the Aqk rows and gamma_t of this lane's output rows.  One
+  // register set, refilled for the next chunk as soon as this chunk's
+  // products have read it (a step ahead, the latency stays hidden).
+  struct OutOps {
+    u32x4_t qa[KS], ahi[2], alo[2];
+    f32x4_t gam;
+  };
+  auto load_out = [&](int c, OutOps& p) {
+    const u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
+    const int tq = min(c * kC + 16 * wave + r16, len - 1);
+    const uint16_t* qp = a.q + (static_cast<size_t>(tok0 + tq) * a.H + h) * DK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint2 x0 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 4 * g);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 16 + 4 * g);
+      p.qa[ks] = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+    }
+    // Aqk rows of the wave: the second token step only for rows 32 .. 63 (it
+    // holds zeros above); a zero-size descriptor returns zeros for waves 0
+    // and 1 without a memory request, and no load sits under a branch
+    constexpr int kAqk = L::A_LO + 4 * 2 * 64 - L::A_HI;  // 16-byte units of Aqk (hi, lo)
+    const __amdgpu_buffer_rsrc_t ar0 =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4_t*>(blk + L::A_HI), 0, kAqk * 16, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ar1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4_t*>(blk + L::A_HI), 0,
+                                                                         wave < 2 ? 0 : kAqk * 16, kBufferRsrcWord3);
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const int off = ((wave * 2 + kp) * 64 + lane) * 16;
+      p.ahi[kp] = __builtin_amdgcn_raw_buffer_load_b128(kp ? ar1 : ar0, off, 0, 0);
+      p.alo[kp] = __builtin_amdgcn_raw_buffer_load_b128(kp ? ar1 : ar0, off + (L::A_LO - L::A_HI) * 16, 0, 0);
+    }
+    p.gam = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(blk + L::GAM) + 16 * wave + 4 * g);
   };
 
   // one chunk: c with operands p; the operands of chunk cn load into pn
+  OutOps po;
   auto step = [&](int c, const Ops& p, int cn, Ops& pn) {
-    u32x4_t* blk = blk0 + static_cast<size_t>(c) * a.H * L::TOTAL;
     if (wave == 0) rbuf[lane] = p.rat;
     // U = U' - W S0^T for token rows 16w .. (the split terms accumulate in
     // separate chains); chunk cn's operands load between the products
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t X0 = z, X1 = z, X2 = z;
+    f32x4_t X0 = z, X1 = z, X2 = z, Y0 = z, Y1 = z;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       X0 = mfma(p.whi[ks], shi[ks], X0);
       X1 = mfma(p.whi[ks], slo[ks], X1);
       X2 = mfma(p.wlo[ks], shi[ks], X2);
+      if constexpr (EMIT) {
+        // the output's Q S0^T on the same B operands (S0 = the state the
+        // chunk starts from, in shi / slo until the end of the step)
+        Y0 = mfma(po.qa[ks], shi[ks], Y0);
+        Y1 = mfma(po.qa[ks], slo[ks], Y1);
+      }
     }
     load_w(cn, pn);
     load_rest(cn, pn);
     const f32x4_t U = p.up - (X0 + (X1 + X2));
     ubuf[wave][lane] = U;
-    if (chunk_out) blk[L::UP + (wave * VT + vs) * 64 + lane] = __builtin_bit_cast(u32x4_t, U);  // U replaces U'
     __syncthreads();
 
     // S_C columns of d_k step `wave`: gamma_C S0 + K^T diag(gamma_C / gamma) U,
@@ -594,7 +622,40 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_scan_kernel(PrefillArgs a)
       split8(x8, ohi, olo);
       sbuf[wave][0][lane] = ohi;
       sbuf[wave][1][lane] = olo;
-      if (chunk_out && c + 1 < c1) store_sc(c + 1);
+    }
+    if constexpr (EMIT) {
+      // output rows 16w .. of the chunk, this slice's columns (off the
+      // state's path, so after the update): diag(gamma) Q S0^T + Aqk U; then
+      // the next chunk's output operands load into the same registers
+      f32x4_t O0 = z, O1 = z;
+      const int nkp = wave < 2 ? 1 : 2;  // token step 1 holds only zeros for rows 0 .. 31
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        if (kp >= nkp) break;
+        // U over tokens in tau order: result tiles 2kp and 2kp + 1
+        float x8[8];
+        cat8(ubuf[2 * kp][lane], ubuf[2 * kp + 1][lane], x8);
+        u32x4_t uh, ul;
+        split8(x8, uh, ul);
+        O0 = mfma(po.ahi[kp], uh, O0);
+        O1 = mfma(po.ahi[kp], ul, O1);
+        O0 = mfma(po.alo[kp], uh, O0);
+      }
+      float ov[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ov[r] = a.q_scale * fmaf(po.gam[r], Y0[r] + Y1[r], O0[r] + O1[r]);
+      load_out(min(c + 1, c1 - 1), po);
+      // rows past the chunk fall outside the buffer range and are dropped
+      // (the first such row is H * d_v floats past the last real one)
+      const int n = min(kC, len - c * kC);
+      const size_t o0 = (static_cast<size_t>(tok0 + c * kC) * a.H + h) * DV;
+      const __amdgpu_buffer_rsrc_t orsrc =
+          __builtin_amdgcn_make_buffer_rsrc(a.o + o0, 0, static_cast<int>(((n - 1) * a.H + 1) * DV * 4), 0x00020000);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * g + r;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[r]), orsrc, (t * a.H * DV + 16 * vs + r16) * 4, 0, 0);
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -606,21 +667,36 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_scan_kernel(PrefillArgs a)
 
   // chunk c + 2's operands load while chunk c computes (three register
   // sets; past the end the last chunk reloads itself, so that no load sits
-  // under a branch)
-  Ops pa, pb, pc;
-  if (c1 > c0) {
-    load_w(c0, pa);
-    load_rest(c0, pa);
-    load_w(min(c0 + 1, c1 - 1), pb);
-    load_rest(min(c0 + 1, c1 - 1), pb);
-    if (chunk_out && wave < KS) store_sc(c0);
-  }
-  for (int c = c0; c < c1; c += 3) {
-    step(c, pa, min(c + 2, c1 - 1), pc);
-    if (c + 1 >= c1) break;
-    step(c + 1, pb, min(c + 3, c1 - 1), pa);
-    if (c + 2 >= c1) break;
-    step(c + 2, pc, min(c + 4, c1 - 1), pb);
+  // under a branch).  The pass that emits the output holds the output's
+  // operands too and loads one chunk ahead (two sets): three would not fit
+  // the registers of two waves per SIMD.
+  if constexpr (EMIT) {
+    Ops pa, pb;
+    if (c1 > c0) {
+      load_w(c0, pa);
+      load_rest(c0, pa);
+      load_out(c0, po);
+    }
+    for (int c = c0; c < c1; c += 2) {
+      step(c, pa, min(c + 1, c1 - 1), pb);
+      if (c + 1 >= c1) break;
+      step(c + 1, pb, min(c + 2, c1 - 1), pa);
+    }
+  } else {
+    Ops pa, pb, pc;
+    if (c1 > c0) {
+      load_w(c0, pa);
+      load_rest(c0, pa);
+      load_w(min(c0 + 1, c1 - 1), pb);
+      load_rest(min(c0 + 1, c1 - 1), pb);
+    }
+    for (int c = c0; c < c1; c += 3) {
+      step(c, pa, min(c + 2, c1 - 1), pc);
+      if (c + 1 >= c1) break;
+      step(c + 1, pb, min(c + 3, c1 - 1), pa);
+      if (c + 2 >= c1) break;
+      step(c + 2, pc, min(c + 4, c1 - 1), pb);
+    }
   }
 
   // end state: the output slot (one pass, and the last segment of phase 3),
@@ -702,110 +778,6 @@ __global__ __launch_bounds__(256) void gdn_prefill_link_kernel(PrefillArgs a) {
   }
 }
 
-// Outputs of one (sequence, chunk, head), all chunks at once:
-//   o = q_scale (diag(gamma) Q S0^T + Aqk U)
-// with S0 the chunk's initial state and U as the scan kernel left them.
-// Wave w owns token rows 16w .. 16w+15; the state's B operands pass through
-// LDS once for the four waves.  Every load of the block (state, Q, Aqk, U,
-// gamma) is issued before the first is used: one memory round trip per
-// block, not one per staging round and d_v slice.
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_prefill_out_kernel(PrefillArgs a) {
-  using L = PL<DK, DV>;
-  constexpr int KS = L::KS, VT = L::VT;
-  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int tok0 = a.cu[s], len = a.cu[s + 1] - tok0;
-  if (tok0 < 0 || len < 0 || len > a.max_len) return;
-  const int in = a.in_idx[s], out = a.out_idx[s];
-  if (in < -1 || in >= a.n_slots || out < 0 || out >= a.n_slots) return;  // the scan skipped it
-  const int n = min(kC, len - c * kC);
-  if (n <= 0) return;
-  const int base = tok0 + c * kC;
-  const u32x4_t* blk = a.ws + ((static_cast<size_t>(s) * a.max_chunks + c) * a.H + h) * L::TOTAL;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
-
-  __shared__ u32x4_t sc[VT][KS][2][64];  // S0 B operands [v-slice][d_k step][hi, lo][lane]
-  constexpr int NST = VT * KS * 64 / 256;  // staging rounds (VT * KS * 64 is a multiple of 256)
-  u32x4_t st_hi[NST], st_lo[NST];
-#pragma unroll
-  for (int j = 0; j < NST; ++j) {
-    st_hi[j] = blk[L::SC_HI + threadIdx.x + 256 * j];
-    st_lo[j] = blk[L::SC_LO + threadIdx.x + 256 * j];
-  }
-  // Q rows 16w + r (rows past the chunk: any real row; their o is not stored), d_k in sigma order
-  u32x4_t qa[KS];
-  {
-    const int tq = min(16 * wave + r16, n - 1);
-    const uint16_t* qp = a.q + (static_cast<size_t>(base + tq) * a.H + h) * DK;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint2 x0 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 4 * g);
-      const uint2 x1 = *reinterpret_cast<const uint2*>(qp + 32 * ks + 16 + 4 * g);
-      qa[ks] = u32x4_t{x0.x, x0.y, x1.x, x1.y};
-    }
-  }
-  u32x4_t ahi[2], alo[2];
-#pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    ahi[kp] = blk[L::A_HI + (wave * 2 + kp) * 64 + lane];
-    alo[kp] = blk[L::A_LO + (wave * 2 + kp) * 64 + lane];
-  }
-  const f32x4_t gam = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(blk + L::GAM) + 16 * wave + 4 * g);
-  const int nkp = wave < 2 ? 1 : 2;  // token step 1 holds only zeros for rows 0 .. 31
-  // U in result layout, token tiles 2kp and 2kp + 1 of every d_v slice
-  u32x4_t up[2][2][VT];
-#pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    if (kp >= nkp) break;
-#pragma unroll
-    for (int vs = 0; vs < VT; ++vs) {
-      up[kp][0][vs] = blk[L::UP + ((2 * kp) * VT + vs) * 64 + lane];
-      up[kp][1][vs] = blk[L::UP + ((2 * kp + 1) * VT + vs) * 64 + lane];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NST; ++j) {
-    const int i = threadIdx.x + 256 * j, l = i & 63, k = i >> 6;  // k = vs * KS + ks
-    (&sc[0][0][0][0])[(k * 2) * 64 + l] = st_hi[j];
-    (&sc[0][0][0][0])[(k * 2 + 1) * 64 + l] = st_lo[j];
-  }
-  __syncthreads();
-
-  const size_t o0 = (static_cast<size_t>(base) * a.H + h) * DV;
-  // rows past the chunk fall outside the buffer range and are dropped (the
-  // first such row is H * d_v floats past the last real one)
-  const __amdgpu_buffer_rsrc_t orsrc =
-      __builtin_amdgcn_make_buffer_rsrc(a.o + o0, 0, static_cast<int>(((n - 1) * a.H + 1) * DV * 4), 0x00020000);
-#pragma unroll
-  for (int vs = 0; vs < VT; ++vs) {
-    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t Y0 = z, Y1 = z, O0 = z, O1 = z;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      Y0 = mfma(qa[ks], sc[vs][ks][0][lane], Y0);
-      Y1 = mfma(qa[ks], sc[vs][ks][1][lane], Y1);
-    }
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      if (kp >= nkp) break;
-      // U over tokens in tau order: result tiles 2kp and 2kp + 1 of this lane
-      float x8[8];
-      cat8(__builtin_bit_cast(f32x4_t, up[kp][0][vs]), __builtin_bit_cast(f32x4_t, up[kp][1][vs]), x8);
-      u32x4_t uh, ul;
-      split8(x8, uh, ul);
-      O0 = mfma(ahi[kp], uh, O0);
-      O1 = mfma(ahi[kp], ul, O1);
-      O0 = mfma(alo[kp], uh, O0);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * g + r;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.q_scale * fmaf(gam[r], Y0[r] + Y1[r], O0[r] + O1[r])),
-                                            orsrc, (t * a.H * DV + 16 * vs + r16) * 4, 0, 0);
-    }
-  }
-}
-
 size_t block_bytes(int dk, int dv) {
   if (dk == 128) return 16 * static_cast<size_t>(dv == 128 ? PL<128, 128>::TOTAL : PL<128, 64>::TOTAL);
   return 16 * static_cast<size_t>(dv == 128 ? PL<64, 128>::TOTAL : PL<64, 64>::TOTAL);
@@ -866,7 +838,7 @@ int launch(const had_gdn_prefill_desc* d, PrefillArgs a, hipStream_t st) {
   if (a.n_segs > 1) {
     a.phase = 1;
     const int items1 = d->n_seqs * d->H * (a.n_segs - 1);  // every segment but the last
-    hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3((items1 + 7) / 8 * 8 * (DV / 16 + DK / 16)),
+    hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV, false>), dim3((items1 + 7) / 8 * 8 * (DV / 16 + DK / 16)),
                        dim3(256), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: segment scan launch: %s", hipGetErrorString(e));
@@ -877,14 +849,10 @@ int launch(const had_gdn_prefill_desc* d, PrefillArgs a, hipStream_t st) {
   } else {
     a.phase = 0;
   }
-  hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV>), dim3((items + 7) / 8 * 8 * (DV / 16)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((gdn_prefill_scan_kernel<DK, DV, true>), dim3((items + 7) / 8 * 8 * (DV / 16)), dim3(256), 0, st,
+                     a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: scan launch: %s", hipGetErrorString(e));
-  if (a.max_chunks > 0) {
-    hipLaunchKernelGGL((gdn_prefill_out_kernel<DK, DV>), dim3(a.max_chunks, d->H, d->n_seqs), dim3(256), 0, st, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(HAD_ERR_HIP, "gdn_prefill: output launch: %s", hipGetErrorString(e));
-  }
   return HAD_OK;
 }
 
