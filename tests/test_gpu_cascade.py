@@ -176,6 +176,29 @@ def test_one_launch_cascade_unit_split(n, prefix_len, suffixes):
     assert_attn_close(out, _oracle(q, kb, vb, table, L, P, D))
 
 
+@pytest.mark.parametrize("n,prefix_len,H_q,H_kv,D,P,gated", [
+    (6, 3000, 8, 1, 256, 64, True),     # gated output applied in the merge of the one-launch layout
+    (4, 2048, 16, 2, 128, 64, False),   # two KV heads, 8 rows each, head_dim 128
+    (3, 1280, 4, 1, 64, 32, True),      # 4 rows per sequence, 32-token pages
+])
+def test_one_launch_cascade_shapes(n, prefix_len, H_q, H_kv, D, P, gated):
+    seed = 4300 + n * 11 + D
+    suffixes = [int(x) for x in synth.integers(0, 6 * P, n, synth.seed_of(seed, 9))]
+    q, kb, vb, table, L, prefix = _batch(seed, n, prefix_len, suffixes, 1, H_q, H_kv, D, P)
+    gate = synth.normal_bf16(tuple(q.shape), synth.seed_of(seed, 8)) if gated else None
+    print("case one-launch cascade n=%d prefix=%d H_q=%d H_kv=%d D=%d P=%d gated=%s suffixes=%s" % (
+        n, prefix_len, H_q, H_kv, D, P, gated, suffixes), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn_cascade(to_dev(q), to_dev(kb), to_dev(vb), to_dev(table), to_dev(L), to_dev(prefix),
+                                  d_err=err, gate=to_dev(gate) if gated else None)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref = _oracle(q, kb, vb, table, L, P, D)
+    if gated:
+        ref = Pr.output_gate(ref, bf16.to_f64(bits_of(gate)))
+    assert_attn_close(out, ref)
+
+
 def test_one_launch_cascade_reports_a_sequence_inside_the_prefix():
     n, prefix_len, P = 3, 1024, 64
     q, kb, vb, table, L, prefix = _batch(3150, n, prefix_len, [5, 0, 70], 1, 8, 1, 256, P)
