@@ -14,9 +14,10 @@
 // G_p first, then each sequence's own suffix units, and the usual merge reads
 // prefix + own (the merge recomputes the same integers).
 //
-// The prefix side is the MFMA partial (R128 above 64 rows), the suffix side
-// the VALU partial in its shared-out mode; LDS is the union of the two.
-#include "attn_mfma_body.h"
+// The prefix side is the MFMA partial (above 64 rows the one that stages K
+// and V straight into LDS, attn_mfma128_body.h), the suffix side the VALU
+// partial in its shared-out mode; LDS is the union of the two.
+#include "attn_mfma128_body.h"
 #include "attn_valu_body.h"
 
 namespace had {
@@ -31,9 +32,9 @@ struct PrefixSide {
 };
 
 // LDS: the two sides' layouts overlaid
-template <int D>
+template <int D, bool R128>
 union CascadeStore {
-  MLds<D> m;
+  typename std::conditional<R128, M128Lds<D>, MLds<D>>::type m;
   Lds v;
 };
 
@@ -60,13 +61,16 @@ __global__ __launch_bounds__(512, 2) void attn_cascade_kernel(ValuArgs as, Prefi
     a.bal_units = 0;
     a.split_base = px.pages / gp;
     a.split_rem = px.pages % gp;
-    mfma_partial<D, R128, true, CascadeStore<D>>(a, blockIdx.x, blockIdx.y, 0);
+    if constexpr (R128)
+      mfma128_partial<D, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
+    else
+      mfma_partial<D, false, true, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
   } else {
     ValuArgs a = as;  // suffix unit blockIdx.x - gp of G - gp, after the prefix's slots
     a.split_offset = gp;
     a.bal_units = G - gp;
     const FusedArgs f{};
-    valu_partial<D, false, CascadeStore<D>>(a, f, static_cast<int>(blockIdx.x) - gp, blockIdx.y, 0);
+    valu_partial<D, false, CascadeStore<D, R128>>(a, f, static_cast<int>(blockIdx.x) - gp, blockIdx.y, 0);
   }
 }
 

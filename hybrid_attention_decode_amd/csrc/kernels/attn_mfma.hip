@@ -28,6 +28,10 @@
 //    online-softmax rescale of a lane's O^T accumulators uses the lane's own
 //    row state (skipped when no row maximum of the wave moved).
 //  * Row maxima and sums combine the 4 lanes of a row with two bpermutes.
+// Above 64 rows the 128-row launches go to attn_mfma128.hip when pages hold
+// a multiple of 32 tokens (K and V staged straight into LDS); the R128 form
+// here (each wave its 16 rows over both halves of every tile, no team
+// merge) serves the other page sizes.
 #include "attn_mfma_body.h"
 
 namespace had {
@@ -56,19 +60,20 @@ hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipSt
     a.row_base = rb;
     const dim3 blk(64 * kMWaves);
     const bool p32 = a.page_size % 32 == 0;
+    if (r128 && p32) {  // K and V staged straight into LDS
+      e = launch_attn_mfma128(a, head_dim, grid, stream);
+      continue;
+    }
     switch (head_dim * 4 + (r128 ? 2 : 0) + (p32 ? 1 : 0)) {
       case 256: hipLaunchKernelGGL((attn_mfma_kernel<64, false, false>), grid, blk, 0, stream, a); break;
       case 257: hipLaunchKernelGGL((attn_mfma_kernel<64, false, true>), grid, blk, 0, stream, a); break;
       case 258: hipLaunchKernelGGL((attn_mfma_kernel<64, true, false>), grid, blk, 0, stream, a); break;
-      case 259: hipLaunchKernelGGL((attn_mfma_kernel<64, true, true>), grid, blk, 0, stream, a); break;
       case 512: hipLaunchKernelGGL((attn_mfma_kernel<128, false, false>), grid, blk, 0, stream, a); break;
       case 513: hipLaunchKernelGGL((attn_mfma_kernel<128, false, true>), grid, blk, 0, stream, a); break;
       case 514: hipLaunchKernelGGL((attn_mfma_kernel<128, true, false>), grid, blk, 0, stream, a); break;
-      case 515: hipLaunchKernelGGL((attn_mfma_kernel<128, true, true>), grid, blk, 0, stream, a); break;
       case 1024: hipLaunchKernelGGL((attn_mfma_kernel<256, false, false>), grid, blk, 0, stream, a); break;
       case 1025: hipLaunchKernelGGL((attn_mfma_kernel<256, false, true>), grid, blk, 0, stream, a); break;
       case 1026: hipLaunchKernelGGL((attn_mfma_kernel<256, true, false>), grid, blk, 0, stream, a); break;
-      case 1027: hipLaunchKernelGGL((attn_mfma_kernel<256, true, true>), grid, blk, 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();

@@ -1,0 +1,424 @@
+// Body of the MFMA split-K decode partial for 65..128 query rows per launch
+// with pages of a multiple of 32 tokens (e.g. the 128 rows of every sequence
+// of a batch that share one prefix, in the prefix pass of cascade decoding:
+// 24-ai.news TokenSpeed article, optimisation list, hybrid prefix caching),
+// shared by its own kernel (attn_mfma128.hip) and the prefix side of the
+// one-launch cascade (attn_cascade.hip).
+//
+// Same operation, split plan and partial format as attn_mfma.hip; the
+// staging differs:
+//  * Eight waves, wave w owning query rows 16w .. 16w+15, two per SIMD, each
+//    working through every token of every stage (no team merge).
+//  * K and V go from HBM straight into LDS (buffer loads with the LDS flag:
+//    lane l's 16 bytes land at the instruction's LDS base + 16 l), in stages
+//    of 32 tokens and kM128Bufs LDS buffers, kM128Bufs - 1 stages in flight;
+//    no staging registers and no transposing work in the waves.  A stage
+//    lies in one page; its loads are buffer loads over that (page, KV head)
+//    block whose size counts only the page's tokens before the split's end,
+//    so tokens past the end, a stage past the split's last one and a page
+//    whose id is out of range all read as zeros without a memory request.
+//  * K row-major with its 16-byte chunks XOR-swizzled by token row (as in
+//    attn_mfma.hip); V row-major with two 16-byte pad slots per row: the rows
+//    of consecutive tokens start 8 banks apart, so the 8 tokens one
+//    transposing read touches per 32 lanes meet on no bank, and the read
+//    addresses are a lane base plus constants.
+//  * V^T as the A operand of O^T += V^T P^T comes from the transposing LDS
+//    read ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+//    element i mod 4 of the 8-byte rows addressed by lanes i/4 + 4k (k =
+//    0..3).  Lane j = r16 of group g addresses token 4g + j/4 (+16), dims
+//    16 mb + 4 (j mod 4) .. +3, so lane i receives dim 16 mb + i of tokens
+//    4g + k (+16): the A operand for K indices in the order tau(g, i) of
+//    attn_mfma.hip, matching P^T in the layout S^T's accumulators leave.
+//  * The stage barrier waits only for this wave's loads of the stage about
+//    to be computed (vmcnt) and for LDS operations (lgkmcnt), so the later
+//    stages stay in flight across it.
+//  * Softmax in base 2 with the scale folded into the exponent's FMA and
+//    v_exp_f32 directly (a probability below 2^-126 of the running maximum
+//    flushes to zero); row sums of the bf16 probabilities by v_dot2.
+#pragma once
+#include "attn_mfma_body.h"
+
+namespace had {
+namespace {
+
+constexpr int kM128Waves = 8;  // wave w owns query rows 16w .. 16w+15 of the launch
+constexpr int kM128Tok = 32;   // tokens per stage
+constexpr int kM128Bufs = 4;   // LDS stage buffers
+
+template <int D>
+struct M128Cfg {
+  static constexpr int KS = D / 32;                    // QK k-steps (32 d each)
+  static constexpr int MB = D / 16;                    // PV output blocks (16 d each)
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
+  static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+  static constexpr int VP = CPR + 2;                   // V row pitch in 16-byte slots (two pad slots)
+  static constexpr int NK = kM128Tok * CPR / 64;       // LDS-load instructions per stage: K
+  static constexpr int NV = (kM128Tok * VP + 63) / 64; // ... V (the pad slots included)
+  static constexpr int KJ = (NK + kM128Waves - 1) / kM128Waves;  // per wave, at most
+  static constexpr int VJ = (NV + kM128Waves - 1) / kM128Waves;
+  static_assert((KJ + VJ) * (kM128Bufs - 2) < 64, "vmcnt holds 6 bits");
+  static_assert(MB % 4 == 0, "output blocks in groups of four");
+};
+
+template <int D>
+struct M128Lds {
+  u32x4_t k[kM128Bufs][kM128Tok * M128Cfg<D>::CPR];  // [buffer][token][chunk ^ kswz]
+  u32x4_t v[kM128Bufs][64 * M128Cfg<D>::NV];         // [buffer][token * VP + chunk]
+  int32_t pages[kMaxPagesPerSplit];
+  int err;
+  int badw[kM128Waves];  // per wave: a page id of the split out of range
+};
+
+template <int D>
+struct M128Store {
+  M128Lds<D> m;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) const char lds_cchar_t;
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum does not wait)
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// Workgroup barrier over LDS accesses that leaves this wave's LDS loads in
+// flight except for the oldest ones (at most VM younger ones outstanding).
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+template <int VM>
+__device__ __forceinline__ void m128_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// the stage barrier of a wave that issues n LDS loads per stage (n <= MAX)
+template <int MAX, int NB>
+__device__ __forceinline__ void m128_stage_barrier(int n) {
+  if constexpr (MAX > 0) {
+    if (n == MAX) {
+      m128_barrier<MAX * (NB - 2)>();
+      return;
+    }
+    m128_stage_barrier<MAX - 1, NB>(n);
+  } else {
+    m128_barrier<0>();
+  }
+}
+
+// V^T operands of four consecutive output blocks: eight transposing reads,
+// at lo + 32 m and hi + 32 m (m = 0..3), completed before the block ends.
+// (In inline assembly, so that the compiler adds no wait for the LDS loads
+// still in flight into the other stage buffers: with the intrinsic form it
+// drains them all first.)
+__device__ __forceinline__ void lds_read_tr4(u32x4_t (&va)[4], const char* lo, const char* hi) {
+  const uint32_t alo = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cchar_t*)lo));
+  const uint32_t ahi = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cchar_t*)hi));
+  uint2 l0, l1, l2, l3, h0, h1, h2, h3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:32\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:64\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3)
+      : "v"(alo), "v"(ahi));
+  va[0] = u32x4_t{l0.x, l0.y, h0.x, h0.y};
+  va[1] = u32x4_t{l1.x, l1.y, h1.x, h1.y};
+  va[2] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
+  va[3] = u32x4_t{l3.x, l3.y, h3.x, h3.y};
+}
+
+// One workgroup's split: launched as attn_mfma128_kernel with (sp, h, s) =
+// the block indices, or as the prefix side of the one-launch cascade.
+template <int D, class Store = M128Store<D>>
+__device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp, const int h, const int s) {
+  M128Lds<D>& sh = g_lds<Store>.m;
+  using C = M128Cfg<D>;
+  constexpr int NB = kM128Bufs;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int P = a.page_size;
+
+  // whole pages balanced to within one (base and remainder from the host)
+  const int pg0 = a.pg_begin + sp * a.split_base + min(sp, a.split_rem);
+  const int npg_plan = a.split_base + (sp < a.split_rem ? 1 : 0);
+  const int pg1_plan = pg0 + npg_plan;
+  const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
+  // setup: scalar loads first (length, page ids of the first NB - 1
+  // stages), then the small vector loads (this thread's page id of the
+  // split, the q rows), then the LDS loads of the first stages
+  __builtin_amdgcn_sched_barrier(0);
+  int pid0[NB - 1];
+#pragma unroll
+  for (int r = 0; r < NB - 1; ++r) pid0[r] = pt_row[min(pg0 + (r * kM128Tok) / P, a.max_pages - 1)];
+  const int L_mem = a.seq_lens[s];
+  __builtin_amdgcn_sched_barrier(0);
+  static_assert(64 * kM128Waves >= kMaxPagesPerSplit, "a split's page ids are read one per thread");
+  const int pt_raw = pt_row[min(pg0 + min(tid, max(npg_plan - 1, 0)), a.max_pages - 1)];
+
+  // q rows of this wave as the B operand of S^T = K Q^T: lane (r16, g)
+  // holds row 16 wave + r16, dims 32 ks + 8 g .. +8 (zero for padding rows)
+  const int row = a.row_base + 16 * wave + r16;
+  const bool row_ok = row < a.rows;
+  // prefix pass: the launch's rows are those of every sequence of the batch
+  const int s_row = a.batch_rows > 0 ? (row_ok ? row : 0) / a.batch_rows : s;
+  const int rr = a.batch_rows > 0 ? (row_ok ? row : 0) % a.batch_rows : row;  // row within its sequence
+  const bool wave_active = a.row_base + 16 * wave < a.rows;                   // uniform
+  u32x4_t qb[C::KS];
+  {
+    const int rc = row_ok ? rr : 0;
+    const uint16_t* qp = a.q + ((static_cast<size_t>(s_row) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qb[ks] = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // the scalar results are needed from here on
+#pragma unroll
+  for (int r = 0; r < NB - 1; ++r) asm volatile("" ::"s"(pid0[r]));
+  asm volatile("" ::"s"(L_mem));
+  const int L = a.fixed_len >= 0 ? a.fixed_len : L_mem;
+  // (a suffix pass also needs every query to see the whole prefix before
+  // pg_begin; a length past the plan's pages would leave tokens no split reads)
+  const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P ||
+                                           L > (a.pg_begin + a.n_pages_plan) * P);
+  const int n_pages = bad_len ? 0 : (L + P - 1) / P;
+  const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
+  const int tok0 = pg0 * P;
+  const int tok_end = npg > 0 ? min((pg0 + npg) * P, L) : tok0;  // this split's tokens: [tok0, tok_end)
+  const int n_it = (tok_end - tok0 + kM128Tok - 1) / kM128Tok;
+  int errs = (bad_len && tid == 0) ? HAD_DERR_SEQLEN : 0;
+  // visible keys of this lane's row (causal inside the draft; a prefix pass
+  // sees the whole prefix), and the bound below which every row sees every
+  // split token
+  const int lim = (row_ok && a.fixed_len < 0) ? (L - a.q_len + rr / a.G + 1) : L;
+  const int vis_all = min(tok_end, a.fixed_len >= 0 ? L : L - a.q_len + 1);
+  const int last_pg = max(npg - 1, 0);
+
+  // LDS loads of stage it into buffer b, page id pid (-1: out of range).
+  // The stage's NK K and NV V instructions go round the waves; lane l of
+  // instruction j fills slot 64 j + l: for K token row (64 j + l) / CPR,
+  // slot column x = l mod CPR, holding the chunk the swizzle puts there;
+  // for V token row (64 j + l) / VP, chunk (64 j + l) mod VP, the pad slots
+  // loaded from past the buffer's end (zeros, no memory request).  Byte
+  // offsets within the stage's first token row are fixed per lane.
+  int kofs_dma[C::KJ], vofs_dma[C::VJ];
+#pragma unroll
+  for (int i = 0; i < C::KJ; ++i) {
+    const int sl = 64 * (wave + kM128Waves * i) + lane;
+    const int r = sl / C::CPR, xk = sl % C::CPR;
+    kofs_dma[i] = r * D * 2 + (xk ^ kswz(r, C::SWZ)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::VJ; ++i) {
+    const int sl = 64 * (wave + kM128Waves * i) + lane;
+    const int r = sl / C::VP, xv = sl % C::VP;
+    vofs_dma[i] = xv < C::CPR ? r * D * 2 + xv * 16 : 0x40000000;
+  }
+  int n_dma = 0;  // LDS-load instructions of this wave per stage
+#pragma unroll
+  for (int i = 0; i < C::KJ; ++i) n_dma += wave + kM128Waves * i < C::NK;
+#pragma unroll
+  for (int i = 0; i < C::VJ; ++i) n_dma += wave + kM128Waves * i < C::NV;
+  auto issue = [&](int it, int b, int pid) __attribute__((always_inline)) {
+    const int pg_rel = (it * kM128Tok) / P;  // page of the stage within the split
+    const int pg_tok0 = tok0 + pg_rel * P;
+    const int valid = (pid >= 0 && it < n_it) ? min(max(tok_end - pg_tok0, 0), P) : 0;  // tokens that count
+    const int nbytes = __builtin_amdgcn_readfirstlane(valid * D * 2);
+    const int pu = __builtin_amdgcn_readfirstlane(pid < 0 ? 0 : pid);
+    const size_t blk = (static_cast<size_t>(pu) * a.H_kv + h) * P * D;
+    const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k_pool + blk), 0,
+                                                                         nbytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_pool + blk), 0,
+                                                                         nbytes, kBufferRsrcWord3);
+    const int t_bytes = (it * kM128Tok - pg_rel * P) * D * 2;  // first token of the stage within its page
+    // non-temporal: the context streams through once per launch
+#pragma unroll
+    for (int i = 0; i < C::KJ; ++i) {
+      const int j = wave + kM128Waves * i;
+      if (C::NK % kM128Waves == 0 || j < C::NK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_, (lds_void_t*)&sh.k[b][64 * j], 16, t_bytes + kofs_dma[i], 0, 0,
+                                                 kBufferNT);
+    }
+#pragma unroll
+    for (int i = 0; i < C::VJ; ++i) {
+      const int j = wave + kM128Waves * i;
+      if (C::NV % kM128Waves == 0 || j < C::NV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr_, (lds_void_t*)&sh.v[b][64 * j], 16, t_bytes + vofs_dma[i], 0, 0,
+                                                 kBufferNT);
+    }
+  };
+
+  // first stages from the scalar page ids
+#pragma unroll
+  for (int r = 0; r < NB - 1; ++r) issue(r, r, (pid0[r] >= 0 && pid0[r] < a.num_pages) ? pid0[r] : -1);
+  if (tid == 0) sh.err = 0;
+  // the checked page list (bad ids become -1)
+  if (tid < max(npg_plan, 1)) {
+    const int pv = tid < npg_plan ? pt_raw : -1;
+    const bool pok = pv >= 0 && pv < a.num_pages;
+    if (!pok && tid < npg) errs |= HAD_DERR_PAGE;
+    sh.pages[tid] = pok ? pv : -1;
+  }
+  {
+    const bool wb = __any(errs & HAD_DERR_PAGE);
+    if (lane == 0) sh.badw[wave] = wb;
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) qb[ks] = row_ok ? qb[ks] : u32x4_t{0u, 0u, 0u, 0u};
+  m128_barrier<63>();  // the page list is in LDS; the first stages stay in flight
+  // the scores of a stage whose page id is out of range are dropped (its K
+  // and V read as zeros)
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < kM128Waves; ++w) any_bad |= sh.badw[w];
+
+  f32x4_t o[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  // transposing-read source of this lane: token 4g + r16/4 (+16), chunk
+  // 2 mb + (r16 mod 4)/2, 8-byte half r16 mod 2: a lane base plus constants
+  const int vlane = ((4 * g + (r16 >> 2)) * C::VP + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1);
+  // K operand of k-step ks = 4u + q for token block tb: row 16 tb + r16,
+  // chunk (4 ks + g) ^ kswz = 4 (4u + (q ^ kh)) + (g ^ kl), kh and kl the
+  // swizzle's high and low bits: byte offset koff[tb][q] + 256 u
+  constexpr int KQ = C::KS < 4 ? C::KS : 4;
+  int koff[2][KQ];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int sw = kswz(16 * tb + r16, C::SWZ);
+#pragma unroll
+    for (int qq = 0; qq < KQ; ++qq)
+      koff[tb][qq] = ((16 * tb + r16) * C::CPR + 4 * (qq ^ (sw >> 2)) + (g ^ (sw & 3))) * 16;
+  }
+
+  // Operand reads run ahead of their MFMAs: the K reads of the next KD
+  // k-steps; the V^T reads in groups of four output blocks, the first
+  // before the softmax, each later one while the previous group's MFMAs run.
+  constexpr int KD = 2;
+  auto compute = [&](int it, int bf) __attribute__((always_inline)) {
+    if (!wave_active) return;
+    const char* kb = reinterpret_cast<const char*>(sh.k[bf]);
+    const char* vb = reinterpret_cast<const char*>(sh.v[bf]) + vlane;
+    auto kread = [&](int ks, int tb) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4_t*>(kb + koff[tb][ks % KQ] + 256 * (ks / KQ));
+    };
+    // V^T operands of output blocks 4 grp .. 4 grp + 3
+    auto vread4 = [&](u32x4_t (&va)[4], int grp) __attribute__((always_inline)) {
+      lds_read_tr4(va, vb + 128 * grp, vb + 128 * grp + 16 * C::VP * 16);
+    };
+    // ---- S^T for both 16-token blocks: two independent accumulation chains
+    u32x4_t kr[KD][2];
+#pragma unroll
+    for (int d = 0; d < KD; ++d) {
+      kr[d][0] = kread(d, 0);
+      kr[d][1] = kread(d, 1);
+    }
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const u32x4_t k0 = kr[ks % KD][0], k1 = kr[ks % KD][1];
+      if (ks + KD < C::KS) {
+        kr[ks % KD][0] = kread(ks + KD, 0);
+        kr[ks % KD][1] = kread(ks + KD, 1);
+      }
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qb[ks]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qb[ks]), acc1, 0, 0, 0);
+    }
+    u32x4_t vr[4];
+    vread4(vr, 0);
+    // raw scores; tokens of slot i: tau(g, i) = 4g + i and 16 + 4g + i - 4
+    float raw[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      raw[i] = acc0[i];
+      raw[4 + i] = acc1[i];
+    }
+    const int pos0 = tok0 + it * kM128Tok;
+    const bool pg_bad = any_bad && sh.pages[min((pos0 - tok0) / P, last_pg)] < 0;  // a stage lies in one page
+    if (pos0 + kM128Tok > vis_all || pg_bad) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pos = pos0 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
+        if (pg_bad || pos >= tok_end || pos >= lim) raw[i] = -INFINITY;
+      }
+    }
+    // ---- online softmax for this lane's row (4 lanes per row), reference
+    // moved only when a score exceeds it by more than 2^8 (as attn_mfma.hip)
+    float mr = fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3]));
+    mr = fmaxf(mr, fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
+    mr = fmaxf(mr, shfl_xor_f(mr, 16));
+    mr = fmaxf(mr, shfl_xor_f(mr, 32));
+    const float mt = mr * sl2;
+    const bool move = mt > m_run + 8.f;
+    const float m_new = move ? mt : m_run;
+    const float m_sub = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
+    uint32_t pw[4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(raw[2 * i], sl2, -m_sub)),
+                          __builtin_amdgcn_exp2f(fmaf(raw[2 * i + 1], sl2, -m_sub)));
+      lsum = dot2_bf16(pw[i], 0x3F803F80u, lsum);  // + both bf16 probabilities
+    }
+    l_run = l_run * alpha + lsum;
+    if (__any(move)) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) o[mb] = o[mb] * alpha;
+    }
+    m_run = m_new;
+    const u32x4_t pb = {pw[0], pw[1], pw[2], pw[3]};
+    // ---- O^T += V^T P^T, four output blocks per group of V^T reads
+#pragma unroll
+    for (int grp = 0; grp < C::MB / 4; ++grp) {
+      if (grp > 0) vread4(vr, grp);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        o[4 * grp + m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[m]), as_bf16x8(pb), o[4 * grp + m], 0, 0, 0);
+    }
+  };
+
+  // main loop: wait for this wave's part of stage it (NB - 2 later stages
+  // may stay outstanding), barrier (every wave's part has landed, and every
+  // wave is done with stage it - 1, whose buffer is refilled next)
+  for (int it = 0; it < n_it; ++it) {
+    m128_stage_barrier<C::KJ + C::VJ, NB>(n_dma);
+    const int nx = it + NB - 1;
+    issue(nx, nx % NB, sh.pages[min((nx * kM128Tok) / P, last_pg)]);
+    compute(it, it % NB);
+  }
+  // no LDS load may still be landing when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+
+  // row totals; every wave owns its rows outright
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  if (errs) atomicOr(&sh.err, errs);
+  __syncthreads();
+  if (tid == 0 && sh.err) set_err(a.d_err, sh.err);
+  if (row_ok) {
+    const size_t unit = (static_cast<size_t>(s_row) * a.H_kv + h) * a.ns_total + a.split_offset + sp;
+    float* op = a.ws_o + (unit * a.ws_rows + rr) * D;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+      *reinterpret_cast<float4*>(op + 16 * mb + 4 * g) = make_float4(o[mb][0], o[mb][1], o[mb][2], o[mb][3]);
+    if (g == 0) {
+      a.ws_ml[(unit * a.ws_rows + rr) * 2 + 0] = m_run;
+      a.ws_ml[(unit * a.ws_rows + rr) * 2 + 1] = l_run;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace had

@@ -55,6 +55,7 @@ struct MLds {
   } u;
   int32_t pages[kMaxPagesPerSplit];
   int err;
+  int badw[kMWaves];  // per wave: a page id of the split out of range
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -224,10 +225,19 @@ __device__ __forceinline__ void mfma_partial(const ValuArgs& a, const int sp, co
     if (!ok && tid < npg) errs |= HAD_DERR_PAGE;
     sh.pages[tid] = ok ? pt_val : -1;
   }
+  {
+    const bool wb = __any(errs & HAD_DERR_PAGE);
+    if (lane == 0) sh.badw[wave] = wb;
+  }
   u32x4_t qb[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) qb[ks] = row_ok ? qraw[ks] : u32x4_t{0u, 0u, 0u, 0u};
   __syncthreads();
+  // the scores of tokens on a page whose id is out of range are dropped (its
+  // K was read from page 0, its V staged as zeros)
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < kMWaves; ++w) any_bad |= sh.badw[w];
 
   auto stage = [&](const u32x4_t (&kr)[TPT], const u32x4_t (&vr)[TPT], int it, int b) __attribute__((always_inline)) {
 #pragma unroll
@@ -290,11 +300,13 @@ __device__ __forceinline__ void mfma_partial(const ValuArgs& a, const int sp, co
     // tokens of slot i: tau(g, i) = 4g + i and 16 + 4g + i - 4 (the mask is
     // skipped for tiles every row sees in full)
     const int pos0 = tok0 + it * kMTile + tm * kMTeamTok;
-    if (pos0 + kMTeamTok > vis_all) {
+    if (pos0 + kMTeamTok > vis_all || any_bad) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int pos = pos0 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
-        if (pos >= tok_end || pos >= lim) sc[i] = -INFINITY;
+        bool drop = pos >= tok_end || pos >= lim;
+        if (any_bad && !drop) drop = sh.pages[min((pos - tok0) / P, last_pg)] < 0;
+        if (drop) sc[i] = -INFINITY;
       }
     }
 
@@ -423,4 +435,10 @@ __device__ __forceinline__ void mfma_partial(const ValuArgs& a, const int sp, co
 }
 
 }  // namespace
+
+// 65..128 rows of one launch, pages of a multiple of 32 tokens, K and V
+// staged straight into LDS (attn_mfma128.hip; called by launch_attn_mfma
+// with the row base and the page-split fields set)
+hipError_t launch_attn_mfma128(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
+
 }  // namespace had

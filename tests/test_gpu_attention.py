@@ -224,3 +224,50 @@ def test_rows_and_page_limits_are_rejected():
     with pytest.raises(had.HadError):                                       # 513 pages in one split
         had.decode_attn(q, pool, pool, torch.zeros((1, 600), dtype=torch.int32, device=DEV),
                         torch.tensor([513 * 16], dtype=torch.int32, device=DEV), num_splits=1)
+
+
+# 65 .. 128 rows per launch with pages of a multiple of 32 tokens: the
+# kernel that stages K and V straight into LDS (16 rows per wave)
+@pytest.mark.parametrize("G,q_len,H_kv,D,P", [
+    (16, 8, 1, 256, 64),   # 128 rows, one launch
+    (17, 7, 1, 256, 32),   # 119 rows: the last wave partly padding
+    (25, 5, 2, 64, 32),    # 125 rows per KV head, two KV heads
+    (32, 8, 1, 128, 32),   # 256 rows: two launches
+    (20, 4, 1, 128, 64),   # 80 rows: waves 5 .. 7 idle
+])
+def test_mfma128_path(G, q_len, H_kv, D, P):
+    out, ref = _run(1500 + G * 7 + q_len + D, [q_len, q_len + 31, 2080, 9000], q_len, G * H_kv, H_kv, D, P)
+    assert_attn_close(out, ref)
+
+
+@pytest.mark.parametrize("splits", [1, 5, 300])
+def test_mfma128_path_forced_splits(splits):
+    # 300 splits over 71 pages leave most splits empty
+    out, ref = _run(1600 + splits, [4500, 40], 8, 16, 1, 256, 64, num_splits=splits)
+    assert_attn_close(out, ref)
+
+
+def test_mfma128_path_structured_values():
+    out, ref = _run(1700, [20000], 8, 16, 1, 256, 64, structured=True)
+    assert np.abs(ref).max() > 0.2
+    assert_attn_close(out, ref)
+
+
+@pytest.mark.parametrize("q_len,H_q,P", [
+    (8, 16, 32),   # 128 rows, K and V staged straight into LDS
+    (4, 16, 64),   # 64 rows, pages of 64 tokens
+    (4, 16, 16),   # 64 rows, pages of 16 tokens
+    (8, 32, 16),   # 256 rows, pages of 16 tokens: two 128-row launches
+])
+def test_mfma_paths_out_of_range_page_id(q_len, H_q, P):
+    # the bad page's K is read from page 0 (NaN in these pools) or as zeros:
+    # its scores must be dropped, so the output stays finite and the sentinel
+    # is set
+    q, kp, vp, pt, L = paged_case(1800 + P, [700], q_len, H_q, 1, 256, P)
+    pt[0, 5] = -3
+    print("case bad page q_len=%d H_q=%d P=%d" % (q_len, H_q, P), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn(to_dev(q), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L), d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_PAGE
+    assert torch.isfinite(out.float()).all()

@@ -159,7 +159,7 @@ def test_split_passes_and_one_call_cascade_match_the_oracle():
     (16, 4096, [0] * 16),                       # only the decode tokens: few suffix tiles, most units to the prefix
     (9, 640, [9000] + [3] * 8),                 # one suffix much longer than the prefix: most units to it
     (2, 64 * 600, [1, 2]),                      # a prefix of 600 pages: at least 2 prefix units (page cap)
-    (16, 2048, [int(x) for x in range(0, 16 * 700, 700)]),  # 128 prefix rows (two row groups of the MFMA side)
+    (16, 2048, [int(x) for x in range(0, 16 * 700, 700)]),  # 128 prefix rows (the MFMA side that stages K and V straight into LDS)
 ])
 def test_one_launch_cascade_unit_split(n, prefix_len, suffixes):
     # both passes in one grid: the prefix's share of the units follows its
