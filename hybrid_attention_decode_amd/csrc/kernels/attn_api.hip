@@ -63,10 +63,14 @@ int no_gate(const had_attn_desc* d, const char* who) {
 // such a range can start and end inside a page, so it touches at most
 // ceil(n/ns) + 1 pages, and the plan keeps ceil(n/ns) <= 511 when ns > 1);
 // at 16 or more rows the pages [i*n/ns, (i+1)*n/ns) (within one page, at
-// most 512).
+// most 512), except above 64 rows with pages of a multiple of 32 tokens,
+// where the ranges are of 32-token stages (balanced to within one stage, one
+// page more than their share like the tile ranges, so again at most 511).
 int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   const int64_t max_len = d->max_seq_len > 0 ? d->max_seq_len : static_cast<int64_t>(d->max_pages) * d->page_size;
   const int64_t n_pages = std::max<int64_t>(1, ceil_div(max_len, d->page_size));
+  const int64_t rows_kv = static_cast<int64_t>(d->q_len) * (d->H_q / d->H_kv);
+  const bool straddle = rows_kv < 16 || (rows_kv > 64 && d->page_size % 32 == 0);
   int64_t ns;
   if (d->num_splits > 0) {
     ns = d->num_splits;
@@ -74,7 +78,7 @@ int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
     // one 8-wave workgroup per CU on either path; a VALU unit covers at
     // least 4 tiles of 8 tokens per wave, an MFMA unit (>= 16 rows) at least
     // 4 iterations of 64 tokens
-    const bool mfma = d->q_len * (d->H_q / d->H_kv) >= 16;
+    const bool mfma = rows_kv >= 16;
     const int64_t units = static_cast<int64_t>(d->n_seqs) * d->H_kv;
     const int64_t want = std::max<int64_t>(1, ceil_div(kTargetUnits, units));
     const int64_t min_pps = mfma ? ceil_div(256, d->page_size) : ceil_div(kMinTilesPerUnit, d->page_size / 8);
@@ -86,14 +90,15 @@ int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
       const int64_t q = std::max<int64_t>(min_pps, ceil_div(n_pages, want));
       ns = std::max<int64_t>(ns, std::min<int64_t>(want, ceil_div(n_pages, q)));
     }
-    // (below 16 rows, with several splits, a tile range can touch one page more)
-    const int64_t cap = mfma ? had::kMaxPagesPerSplit : had::kMaxPagesPerSplit - 1;
+    // (below 16 rows a tile range, above 64 rows with pages of a multiple of
+    // 32 tokens a range of 32-token stages, can touch one page more)
+    const int64_t cap = straddle ? had::kMaxPagesPerSplit - 1 : had::kMaxPagesPerSplit;
     if (n_pages > had::kMaxPagesPerSplit) ns = std::max<int64_t>(ns, ceil_div(n_pages, cap));
   }
   const int64_t pps = ceil_div(n_pages, ns);
-  // the VALU path's tile ranges can straddle one page more than their share
-  const bool tile_ranges = d->q_len * (d->H_q / d->H_kv) < 16;
-  const int64_t pps_max = (ns > 1 && tile_ranges) ? had::kMaxPagesPerSplit - 1 : had::kMaxPagesPerSplit;
+  // the VALU path's tile ranges and the 128-row MFMA path's stage ranges can
+  // straddle one page more than their share
+  const int64_t pps_max = (ns > 1 && straddle) ? had::kMaxPagesPerSplit - 1 : had::kMaxPagesPerSplit;
   if (pps > pps_max)
     return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: %lld splits leave %lld pages per split (max %lld)",
                 static_cast<long long>(ns), static_cast<long long>(pps), static_cast<long long>(pps_max));
@@ -444,7 +449,7 @@ static int cascade_bal_units(const had_attn_desc* d, int n_sfx) {
 static int cascade_one_launch_units(const had_attn_desc* d, const had_attn_prefix* px, int bal, int ns_p, int ns_s) {
   const int rows = d->q_len * (d->H_q / d->H_kv);
   if (bal <= 0 || rows > 8 || d->n_seqs * rows > 128 || d->page_size % 32 != 0) return 0;
-  const int min_pu = static_cast<int>(ceil_div(px->prefix_pages, had::kMaxPagesPerSplit));
+  const int min_pu = static_cast<int>(ceil_div(px->prefix_pages, had::kMaxPagesPerSplit - 1));
   const int G = std::max<int>(static_cast<int>(ceil_div(kTargetUnits, d->H_kv)), min_pu + d->n_seqs);
   return G <= ns_p + ns_s ? G : 0;
 }
@@ -584,7 +589,7 @@ static int cascade_launch(const had_attn_desc* d, const had_attn_prefix* px, con
   as.bal_units = bal;
   const int prefix_tiles = px->prefix_pages * (d->page_size / 8);
   const int weight16 = had::cascade_prefix_weight16(d->n_seqs * rows);
-  const int min_pu = static_cast<int>(ceil_div(px->prefix_pages, had::kMaxPagesPerSplit));
+  const int min_pu = static_cast<int>(ceil_div(px->prefix_pages, had::kMaxPagesPerSplit - 1));
   hipError_t e = hipSuccess;
   if (G1 > 0) {
     if (passes == 3) {

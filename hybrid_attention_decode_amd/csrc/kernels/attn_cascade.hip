@@ -59,12 +59,16 @@ __global__ __launch_bounds__(512, 2) void attn_cascade_kernel(ValuArgs as, Prefi
     a.batch_rows = as.rows;
     a.fixed_len = px.pages * P;
     a.bal_units = 0;
-    a.split_base = px.pages / gp;
-    a.split_rem = px.pages % gp;
-    if constexpr (R128)
+    if constexpr (R128) {  // 32-token stages balanced to within one
+      const int n_st = px.pages * (P / 32);
+      a.split_base = n_st / gp;
+      a.split_rem = n_st % gp;
       mfma128_partial<D, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
-    else
+    } else {  // whole pages balanced to within one
+      a.split_base = px.pages / gp;
+      a.split_rem = px.pages % gp;
       mfma_partial<D, false, true, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
+    }
   } else {
     ValuArgs a = as;  // suffix unit blockIdx.x - gp of G - gp, after the prefix's slots
     a.split_offset = gp;
@@ -82,7 +86,7 @@ hipError_t launch_attn_cascade(const ValuArgs& ap, const ValuArgs& as, int prefi
   // of a multiple of 32 tokens (the host checks; these keep a bad call out)
   if (ap.rows < 1 || ap.rows > 2 * kMRows || as.rows > kRows || ap.page_size % 32 != 0 || as.bal_units != 0 ||
       ap.n_pages_plan != ap.max_pages || ap.batch_rows != as.rows || static_cast<int>(grid.x) < min_pu + as.n_seqs ||
-      min_pu < 1 || (ap.n_pages_plan + min_pu - 1) / min_pu > kMaxPagesPerSplit || weight16 < 1 || weight16 > 256)
+      min_pu < 1 || (ap.n_pages_plan + min_pu - 1) / min_pu + 1 > kMaxPagesPerSplit || weight16 < 1 || weight16 > 256)
     return hipErrorInvalidValue;
   const PrefixSide px{ap.page_table, ap.rows, ap.n_pages_plan, prefix_tiles, weight16, min_pu};
   const dim3 blk(64 * kMWaves);

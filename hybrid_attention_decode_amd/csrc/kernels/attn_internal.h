@@ -167,11 +167,11 @@ hipError_t launch_attn_cascade(const ValuArgs& ap, const ValuArgs& as, int prefi
                                int head_dim, dim3 grid, hipStream_t stream);
 // cost of a prefix tile in suffix tiles (x16) in the one-launch cascade's
 // unit split, measured with both sides running: a 64-token page costs the
-// 128-row MFMA side (K and V staged straight into LDS) about 1.5x what it
-// costs the 8-row VALU side (16 x 50K prefix: the weights 16 / 20 / 24 / 28
-// / 32 / 36 gave 45.7 / 41.7 / 37.7 / 38.1 / 37.9 / 41.0 us per launch); up
-// to 64 rows the MFMA side streams at about the VALU side's rate
-inline int cascade_prefix_weight16(int prefix_rows) { return prefix_rows > 64 ? 24 : 18; }
+// 128-row MFMA side (K and V staged straight into LDS, ranges of 32-token
+// stages) about 1.75x what it costs the 8-row VALU side (16 x 50K prefix:
+// the weights 20 / 24 / 28 / 32 gave 39.9 / 37.1 / 35.9 / 37.7 us per
+// launch); up to 64 rows the MFMA side streams at about the VALU side's rate
+inline int cascade_prefix_weight16(int prefix_rows) { return prefix_rows > 64 ? 28 : 18; }
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace had

@@ -60,8 +60,17 @@ hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipSt
     a.row_base = rb;
     const dim3 blk(64 * kMWaves);
     const bool p32 = a.page_size % 32 == 0;
-    if (r128 && p32) {  // K and V staged straight into LDS
-      e = launch_attn_mfma128(a, head_dim, grid, stream);
+    if (r128 && p32) {  // K and V staged straight into LDS, 32-token-stage split ranges
+      ValuArgs b = a;
+      const int64_t n_st = static_cast<int64_t>(a.n_pages_plan) * (a.page_size / 32);
+      const int64_t st_max = (n_st + a.num_splits - 1) / a.num_splits;
+      // (with several splits a range of stages can start inside a page: one
+      // page more than its share)
+      if ((st_max * 32 + a.page_size - 1) / a.page_size + (a.num_splits > 1 ? 1 : 0) > kMaxPagesPerSplit)
+        return hipErrorInvalidValue;
+      b.split_base = static_cast<int>(n_st / a.num_splits);
+      b.split_rem = static_cast<int>(n_st % a.num_splits);
+      e = launch_attn_mfma128(b, head_dim, grid, stream);
       continue;
     }
     switch (head_dim * 4 + (r128 ? 2 : 0) + (p32 ? 1 : 0)) {

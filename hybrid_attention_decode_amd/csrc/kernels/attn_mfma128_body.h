@@ -135,7 +135,11 @@ __device__ __forceinline__ void lds_read_tr4(u32x4_t (&va)[4], const char* lo, c
 }
 
 // One workgroup's split: launched as attn_mfma128_kernel with (sp, h, s) =
-// the block indices, or as the prefix side of the one-launch cascade.
+// the block indices, or as the prefix side of the one-launch cascade.  For
+// this body a.split_base and a.split_rem count 32-token stages of the plan
+// (its n_pages_plan pages from pg_begin), not pages: split sp takes stages
+// sp * base + min(sp, rem) .. + base (+1 while sp < rem), so the splits are
+// balanced to within one stage and a split may start and end inside a page.
 template <int D, class Store = M128Store<D>>
 __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp, const int h, const int s) {
   M128Lds<D>& sh = g_lds<Store>.m;
@@ -147,10 +151,14 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   const int r16 = lane & 15, g = lane >> 4;
   const int P = a.page_size;
 
-  // whole pages balanced to within one (base and remainder from the host)
-  const int pg0 = a.pg_begin + sp * a.split_base + min(sp, a.split_rem);
-  const int npg_plan = a.split_base + (sp < a.split_rem ? 1 : 0);
-  const int pg1_plan = pg0 + npg_plan;
+  // this split's stages of the plan and the pages they touch
+  const int st0 = sp * a.split_base + min(sp, a.split_rem);
+  const int nst = a.split_base + (sp < a.split_rem ? 1 : 0);
+  const int tok0 = a.pg_begin * P + kM128Tok * st0;        // first token of the split
+  const int tok_plan_end = tok0 + kM128Tok * nst;          // ... past its last (plan)
+  const int pg0 = tok0 / P;                                // its first page
+  const int off0 = tok0 - pg0 * P;                         // token offset of the split in that page
+  const int npg_plan = nst > 0 ? (tok_plan_end - 1) / P - pg0 + 1 : 0;  // pages the plan's range touches
   const int32_t* pt_row = a.page_table + static_cast<size_t>(s) * a.max_pages;
   // setup: scalar loads first (length, page ids of the first NB - 1
   // stages), then the small vector loads (this thread's page id of the
@@ -158,7 +166,7 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   __builtin_amdgcn_sched_barrier(0);
   int pid0[NB - 1];
 #pragma unroll
-  for (int r = 0; r < NB - 1; ++r) pid0[r] = pt_row[min(pg0 + (r * kM128Tok) / P, a.max_pages - 1)];
+  for (int r = 0; r < NB - 1; ++r) pid0[r] = pt_row[min(pg0 + (off0 + r * kM128Tok) / P, a.max_pages - 1)];
   const int L_mem = a.seq_lens[s];
   __builtin_amdgcn_sched_barrier(0);
   static_assert(64 * kM128Waves >= kMaxPagesPerSplit, "a split's page ids are read one per thread");
@@ -189,10 +197,8 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   // pg_begin; a length past the plan's pages would leave tokens no split reads)
   const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P ||
                                            L > (a.pg_begin + a.n_pages_plan) * P);
-  const int n_pages = bad_len ? 0 : (L + P - 1) / P;
-  const int npg = max(min(pg1_plan, n_pages) - pg0, 0);
-  const int tok0 = pg0 * P;
-  const int tok_end = npg > 0 ? min((pg0 + npg) * P, L) : tok0;  // this split's tokens: [tok0, tok_end)
+  const int tok_end = bad_len ? tok0 : max(min(tok_plan_end, L), tok0);  // this split's tokens: [tok0, tok_end)
+  const int npg = tok_end > tok0 ? (tok_end - 1) / P - pg0 + 1 : 0;     // pages holding them
   const int n_it = (tok_end - tok0 + kM128Tok - 1) / kM128Tok;
   int errs = (bad_len && tid == 0) ? HAD_DERR_SEQLEN : 0;
   // visible keys of this lane's row (causal inside the draft; a prefix pass
@@ -228,8 +234,8 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
 #pragma unroll
   for (int i = 0; i < C::VJ; ++i) n_dma += wave + kM128Waves * i < C::NV;
   auto issue = [&](int it, int b, int pid) __attribute__((always_inline)) {
-    const int pg_rel = (it * kM128Tok) / P;  // page of the stage within the split
-    const int pg_tok0 = tok0 + pg_rel * P;
+    const int pg_rel = (off0 + it * kM128Tok) / P;  // page of the stage within the split
+    const int pg_tok0 = (pg0 + pg_rel) * P;
     const int valid = (pid >= 0 && it < n_it) ? min(max(tok_end - pg_tok0, 0), P) : 0;  // tokens that count
     const int nbytes = __builtin_amdgcn_readfirstlane(valid * D * 2);
     const int pu = __builtin_amdgcn_readfirstlane(pid < 0 ? 0 : pid);
@@ -238,7 +244,7 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
                                                                          nbytes, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_pool + blk), 0,
                                                                          nbytes, kBufferRsrcWord3);
-    const int t_bytes = (it * kM128Tok - pg_rel * P) * D * 2;  // first token of the stage within its page
+    const int t_bytes = (off0 + it * kM128Tok - pg_rel * P) * D * 2;  // first token of the stage within its page
     // non-temporal: the context streams through once per launch
 #pragma unroll
     for (int i = 0; i < C::KJ; ++i) {
@@ -345,7 +351,7 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
       raw[4 + i] = acc1[i];
     }
     const int pos0 = tok0 + it * kM128Tok;
-    const bool pg_bad = any_bad && sh.pages[min((pos0 - tok0) / P, last_pg)] < 0;  // a stage lies in one page
+    const bool pg_bad = any_bad && sh.pages[min((off0 + pos0 - tok0) / P, last_pg)] < 0;  // a stage lies in one page
     if (pos0 + kM128Tok > vis_all || pg_bad) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -395,7 +401,7 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   for (int it = 0; it < n_it; ++it) {
     m128_stage_barrier<C::KJ + C::VJ, NB>(n_dma);
     const int nx = it + NB - 1;
-    issue(nx, nx % NB, sh.pages[min((nx * kM128Tok) / P, last_pg)]);
+    issue(nx, nx % NB, sh.pages[min((off0 + nx * kM128Tok) / P, last_pg)]);
     compute(it, it % NB);
   }
   // no LDS load may still be landing when the workgroup ends

@@ -247,6 +247,15 @@ def test_mfma128_path_forced_splits(splits):
     assert_attn_close(out, ref)
 
 
+def test_mfma128_path_page_limits():
+    # one split over 512 pages (the per-split maximum); 511-page shares with
+    # several splits, whose 32-token-stage ranges start inside a page
+    out, ref = _run(1750, [512 * 32], 8, 16, 1, 64, 32, num_splits=1, max_seq_len=512 * 32)
+    assert_attn_close(out, ref)
+    out, ref = _run(1751, [1021 * 64 - 5], 8, 16, 1, 64, 64, num_splits=2, max_seq_len=1021 * 64)
+    assert_attn_close(out, ref)
+
+
 def test_mfma128_path_structured_values():
     out, ref = _run(1700, [20000], 8, 16, 1, 256, 64, structured=True)
     assert np.abs(ref).max() > 0.2
