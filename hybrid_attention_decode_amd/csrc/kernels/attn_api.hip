@@ -63,14 +63,20 @@ int no_gate(const had_attn_desc* d, const char* who) {
 // such a range can start and end inside a page, so it touches at most
 // ceil(n/ns) + 1 pages, and the plan keeps ceil(n/ns) <= 511 when ns > 1);
 // at 16 or more rows the pages [i*n/ns, (i+1)*n/ns) (within one page, at
-// most 512), except above 64 rows with pages of a multiple of 32 tokens,
-// where the ranges are of 32-token stages (balanced to within one stage, one
-// page more than their share like the tile ranges, so again at most 511).
+// most 512), except with pages of a multiple of 32 tokens above 64 rows or
+// at head_dim >= 128, where the ranges are of 32-token stages (balanced to
+// within one stage, one page more than their share like the tile ranges, so
+// again at most 511).
 int plan(const had_attn_desc* d, int* ns_out, int* pps_out, int* n_pages_out) {
   const int64_t max_len = d->max_seq_len > 0 ? d->max_seq_len : static_cast<int64_t>(d->max_pages) * d->page_size;
   const int64_t n_pages = std::max<int64_t>(1, ceil_div(max_len, d->page_size));
   const int64_t rows_kv = static_cast<int64_t>(d->q_len) * (d->H_q / d->H_kv);
-  const bool straddle = rows_kv < 16 || (rows_kv > 64 && d->page_size % 32 == 0);
+  // ranges that can straddle one page more than their share: the VALU
+  // path's tile ranges, and the 32-token-stage ranges of the MFMA kernel
+  // that loads K and V straight into LDS (pages of a multiple of 32 tokens,
+  // above 64 rows or at head_dim >= 128)
+  const bool straddle =
+      rows_kv < 16 || (rows_kv >= 16 && d->page_size % 32 == 0 && (rows_kv > 64 || d->head_dim >= 128));
   int64_t ns;
   if (d->num_splits > 0) {
     ns = d->num_splits;

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(512, 2) void attn_cascade_kernel(ValuArgs as, Prefi
       const int n_st = px.pages * (P / 32);
       a.split_base = n_st / gp;
       a.split_rem = n_st % gp;
-      mfma128_partial<D, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
+      mfma128_partial<D, 1, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
     } else {  // whole pages balanced to within one
       a.split_base = px.pages / gp;
       a.split_rem = px.pages % gp;

@@ -60,7 +60,7 @@ hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipSt
     a.row_base = rb;
     const dim3 blk(64 * kMWaves);
     const bool p32 = a.page_size % 32 == 0;
-    if (r128 && p32) {  // K and V staged straight into LDS, 32-token-stage split ranges
+    if (p32 && (r128 || head_dim >= 128)) {  // K and V staged straight into LDS, 32-token-stage split ranges
       ValuArgs b = a;
       const int64_t n_st = static_cast<int64_t>(a.n_pages_plan) * (a.page_size / 32);
       const int64_t st_max = (n_st + a.num_splits - 1) / a.num_splits;
@@ -70,7 +70,7 @@ hipError_t launch_attn_mfma(const ValuArgs& a_in, int head_dim, dim3 grid, hipSt
         return hipErrorInvalidValue;
       b.split_base = static_cast<int>(n_st / a.num_splits);
       b.split_rem = static_cast<int>(n_st % a.num_splits);
-      e = launch_attn_mfma128(b, head_dim, grid, stream);
+      e = launch_attn_mfma128(b, head_dim, r128 ? 1 : 2, grid, stream);
       continue;
     }
     switch (head_dim * 4 + (r128 ? 2 : 0) + (p32 ? 1 : 0)) {

@@ -5,10 +5,14 @@
 // shared by its own kernel (attn_mfma128.hip) and the prefix side of the
 // one-launch cascade (attn_cascade.hip).
 //
-// Same operation, split plan and partial format as attn_mfma.hip; the
-// staging differs:
-//  * Eight waves, wave w owning query rows 16w .. 16w+15, two per SIMD, each
-//    working through every token of every stage (no team merge).
+// Same operation and partial format as attn_mfma.hip; the staging and the
+// split ranges differ:
+//  * Eight waves, two per SIMD, each working through every token of every
+//    stage (no team merge).  DH = 1 (up to 128 rows per launch): wave w owns
+//    query rows 16w .. 16w+15 and every output dim.  DH = 2 (up to 64 rows):
+//    waves w and w + 4 own rows 16w .. 16w+15, each half of the output dims;
+//    both form the same scores and softmax state (the same instructions on
+//    the same data), so the PV work and its V^T reads are split between them.
 //  * K and V go from HBM straight into LDS (buffer loads with the LDS flag:
 //    lane l's 16 bytes land at the instruction's LDS base + 16 l), in stages
 //    of 32 tokens and kM128Bufs LDS buffers, kM128Bufs - 1 stages in flight;
@@ -45,10 +49,10 @@ constexpr int kM128Waves = 8;  // wave w owns query rows 16w .. 16w+15 of the la
 constexpr int kM128Tok = 32;   // tokens per stage
 constexpr int kM128Bufs = 4;   // LDS stage buffers
 
-template <int D>
+template <int D, int DH>
 struct M128Cfg {
   static constexpr int KS = D / 32;                    // QK k-steps (32 d each)
-  static constexpr int MB = D / 16;                    // PV output blocks (16 d each)
+  static constexpr int MB = D / 16 / DH;               // PV output blocks (16 d each) of one wave
   static constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
   static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
   static constexpr int VP = CPR + 2;                   // V row pitch in 16-byte slots (two pad slots)
@@ -57,13 +61,13 @@ struct M128Cfg {
   static constexpr int KJ = (NK + kM128Waves - 1) / kM128Waves;  // per wave, at most
   static constexpr int VJ = (NV + kM128Waves - 1) / kM128Waves;
   static_assert((KJ + VJ) * (kM128Bufs - 2) < 64, "vmcnt holds 6 bits");
-  static_assert(MB % 4 == 0, "output blocks in groups of four");
+  static_assert(MB % 4 == 0, "output blocks in groups of four (DH = 2 needs head_dim >= 128)");
 };
 
 template <int D>
 struct M128Lds {
-  u32x4_t k[kM128Bufs][kM128Tok * M128Cfg<D>::CPR];  // [buffer][token][chunk ^ kswz]
-  u32x4_t v[kM128Bufs][64 * M128Cfg<D>::NV];         // [buffer][token * VP + chunk]
+  u32x4_t k[kM128Bufs][kM128Tok * M128Cfg<D, 1>::CPR];  // [buffer][token][chunk ^ kswz]
+  u32x4_t v[kM128Bufs][64 * M128Cfg<D, 1>::NV];         // [buffer][token * VP + chunk]
   int32_t pages[kMaxPagesPerSplit];
   int err;
   int badw[kM128Waves];  // per wave: a page id of the split out of range
@@ -140,15 +144,18 @@ __device__ __forceinline__ void lds_read_tr4(u32x4_t (&va)[4], const char* lo, c
 // (its n_pages_plan pages from pg_begin), not pages: split sp takes stages
 // sp * base + min(sp, rem) .. + base (+1 while sp < rem), so the splits are
 // balanced to within one stage and a split may start and end inside a page.
-template <int D, class Store = M128Store<D>>
+template <int D, int DH, class Store = M128Store<D>>
 __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp, const int h, const int s) {
+  static_assert(DH == 1 || DH == 2, "rows per wave group");
   M128Lds<D>& sh = g_lds<Store>.m;
-  using C = M128Cfg<D>;
+  using C = M128Cfg<D, DH>;
+  constexpr int NRG = kM128Waves / DH;  // row groups of 16
   constexpr int NB = kM128Bufs;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
+  const int rg = wave % NRG, dh = wave / NRG;  // row group, part of the output dims
   const int P = a.page_size;
 
   // this split's stages of the plan and the pages they touch
@@ -174,12 +181,12 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
 
   // q rows of this wave as the B operand of S^T = K Q^T: lane (r16, g)
   // holds row 16 wave + r16, dims 32 ks + 8 g .. +8 (zero for padding rows)
-  const int row = a.row_base + 16 * wave + r16;
+  const int row = a.row_base + 16 * rg + r16;
   const bool row_ok = row < a.rows;
   // prefix pass: the launch's rows are those of every sequence of the batch
   const int s_row = a.batch_rows > 0 ? (row_ok ? row : 0) / a.batch_rows : s;
   const int rr = a.batch_rows > 0 ? (row_ok ? row : 0) % a.batch_rows : row;  // row within its sequence
-  const bool wave_active = a.row_base + 16 * wave < a.rows;                   // uniform
+  const bool wave_active = a.row_base + 16 * rg < a.rows;                     // uniform
   u32x4_t qb[C::KS];
   {
     const int rc = row_ok ? rr : 0;
@@ -294,7 +301,7 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
 
   // transposing-read source of this lane: token 4g + r16/4 (+16), chunk
   // 2 mb + (r16 mod 4)/2, 8-byte half r16 mod 2: a lane base plus constants
-  const int vlane = ((4 * g + (r16 >> 2)) * C::VP + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1);
+  const int vlane = ((4 * g + (r16 >> 2)) * C::VP + 2 * C::MB * dh + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1);
   // K operand of k-step ks = 4u + q for token block tb: row 16 tb + r16,
   // chunk (4 ks + g) ^ kswz = 4 (4u + (q ^ kh)) + (g ^ kl), kh and kl the
   // swizzle's high and low bits: byte offset koff[tb][q] + 256 u
@@ -415,11 +422,11 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   if (tid == 0 && sh.err) set_err(a.d_err, sh.err);
   if (row_ok) {
     const size_t unit = (static_cast<size_t>(s_row) * a.H_kv + h) * a.ns_total + a.split_offset + sp;
-    float* op = a.ws_o + (unit * a.ws_rows + rr) * D;
+    float* op = a.ws_o + (unit * a.ws_rows + rr) * D + 16 * C::MB * dh;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
       *reinterpret_cast<float4*>(op + 16 * mb + 4 * g) = make_float4(o[mb][0], o[mb][1], o[mb][2], o[mb][3]);
-    if (g == 0) {
+    if (g == 0 && dh == 0) {
       a.ws_ml[(unit * a.ws_rows + rr) * 2 + 0] = m_run;
       a.ws_ml[(unit * a.ws_rows + rr) * 2 + 1] = l_run;
     }

@@ -436,9 +436,10 @@ __device__ __forceinline__ void mfma_partial(const ValuArgs& a, const int sp, co
 
 }  // namespace
 
-// 65..128 rows of one launch, pages of a multiple of 32 tokens, K and V
-// staged straight into LDS (attn_mfma128.hip; called by launch_attn_mfma
-// with the row base and the page-split fields set)
-hipError_t launch_attn_mfma128(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
+// pages of a multiple of 32 tokens, K and V staged straight into LDS
+// (attn_mfma128.hip; called by launch_attn_mfma with the row base and the
+// split fields set): dh = 1, rows row_base .. +127; dh = 2 (head_dim >= 128),
+// rows row_base .. +63
+hipError_t launch_attn_mfma128(const ValuArgs& a, int head_dim, int dh, dim3 grid, hipStream_t stream);
 
 }  // namespace had
