@@ -71,6 +71,7 @@ struct M128Lds {
   int32_t pages[kMaxPagesPerSplit];
   int err;
   int badw[kM128Waves];  // per wave: a page id of the split out of range
+  u32x4_t dump[64];      // target of the filler loads that even out the waves' load counts
 };
 
 template <int D>
@@ -97,18 +98,57 @@ __device__ __forceinline__ void m128_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// the stage barrier of a wave that issues n LDS loads per stage (n <= MAX)
-template <int MAX, int NB>
-__device__ __forceinline__ void m128_stage_barrier(int n) {
-  if constexpr (MAX > 0) {
-    if (n == MAX) {
-      m128_barrier<MAX * (NB - 2)>();
-      return;
-    }
-    m128_stage_barrier<MAX - 1, NB>(n);
-  } else {
-    m128_barrier<0>();
-  }
+// max of three floats as one v_max3_f32 (fmaxf would first canonicalize
+// every operand that does not come from a float instruction, e.g. an MFMA
+// result or a lane swap)
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48: v_permlane16_swap exchanges the
+// upper 16 lanes of each 32-lane half of its first operand with the lower 16
+// of its second, v_permlane32_swap the upper 32 lanes of the first with the
+// lower 32 of the second; with both operands x, the two results hold x of
+// lane l and of its partner in either order
+__device__ __forceinline__ float max_lanes_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax3(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax3(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
+}
+
+// V^T operands of eight consecutive output blocks: sixteen transposing
+// reads at lo + 32 m and hi + 32 m (m = 0..7), completed before the block
+// ends (one LDS round trip for both groups of four)
+__device__ __forceinline__ void lds_read_tr8(u32x4_t (&va)[8], const char* lo, const char* hi) {
+  const uint32_t alo = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cchar_t*)lo));
+  const uint32_t ahi = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cchar_t*)hi));
+  uint2 l[8], h[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:32\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:32\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:64\n\t"
+      "ds_read_b64_tr_b16 %6, %16 offset:96\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:96\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:128\n\t"
+      "ds_read_b64_tr_b16 %10, %16 offset:160\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:160\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:192\n\t"
+      "ds_read_b64_tr_b16 %13, %17 offset:192\n\t"
+      "ds_read_b64_tr_b16 %14, %16 offset:224\n\t"
+      "ds_read_b64_tr_b16 %15, %17 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l[0]), "=&v"(h[0]), "=&v"(l[1]), "=&v"(h[1]), "=&v"(l[2]), "=&v"(h[2]), "=&v"(l[3]), "=&v"(h[3]),
+        "=&v"(l[4]), "=&v"(h[4]), "=&v"(l[5]), "=&v"(h[5]), "=&v"(l[6]), "=&v"(h[6]), "=&v"(l[7]), "=&v"(h[7])
+      : "v"(alo), "v"(ahi));
+#pragma unroll
+  for (int m = 0; m < 8; ++m) va[m] = u32x4_t{l[m].x, l[m].y, h[m].x, h[m].y};
 }
 
 // V^T operands of four consecutive output blocks: eight transposing reads,
@@ -215,33 +255,31 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   const int vis_all = min(tok_end, a.fixed_len >= 0 ? L : L - a.q_len + 1);
   const int last_pg = max(npg - 1, 0);
 
-  // LDS loads of stage it into buffer b, page id pid (-1: out of range).
-  // The stage's NK K and NV V instructions go round the waves; lane l of
-  // instruction j fills slot 64 j + l: for K token row (64 j + l) / CPR,
-  // slot column x = l mod CPR, holding the chunk the swizzle puts there;
-  // for V token row (64 j + l) / VP, chunk (64 j + l) mod VP, the pad slots
-  // loaded from past the buffer's end (zeros, no memory request).  Byte
-  // offsets within the stage's first token row are fixed per lane.
+  // LDS loads of stage it into buffer b, page id pid (-1: out of range),
+  // page pg_rel of the split, t_tok tokens into it.  The stage's NK K and
+  // NV V instructions go round the waves; lane l of instruction j fills
+  // slot 64 j + l: for K token row (64 j + l) / CPR, slot column x = l mod
+  // CPR, holding the chunk the swizzle puts there; for V token row
+  // (64 j + l) / VP, chunk (64 j + l) mod VP, the pad slots loaded from past
+  // the buffer's end (zeros, no memory request).  Every wave issues KJ + VJ
+  // instructions, those past NK or NV fillers of the same kind into the
+  // dump slots, so one fixed vmcnt bound serves every wave.  Byte offsets
+  // within the stage's first token row are fixed per lane.
+  constexpr int kPastEnd = 0x40000000;  // beyond any (page, head) block
   int kofs_dma[C::KJ], vofs_dma[C::VJ];
 #pragma unroll
   for (int i = 0; i < C::KJ; ++i) {
     const int sl = 64 * (wave + kM128Waves * i) + lane;
     const int r = sl / C::CPR, xk = sl % C::CPR;
-    kofs_dma[i] = r * D * 2 + (xk ^ kswz(r, C::SWZ)) * 16;
+    kofs_dma[i] = wave + kM128Waves * i < C::NK ? r * D * 2 + (xk ^ kswz(r, C::SWZ)) * 16 : kPastEnd;
   }
 #pragma unroll
   for (int i = 0; i < C::VJ; ++i) {
     const int sl = 64 * (wave + kM128Waves * i) + lane;
     const int r = sl / C::VP, xv = sl % C::VP;
-    vofs_dma[i] = xv < C::CPR ? r * D * 2 + xv * 16 : 0x40000000;
+    vofs_dma[i] = (wave + kM128Waves * i < C::NV && xv < C::CPR) ? r * D * 2 + xv * 16 : kPastEnd;
   }
-  int n_dma = 0;  // LDS-load instructions of this wave per stage
-#pragma unroll
-  for (int i = 0; i < C::KJ; ++i) n_dma += wave + kM128Waves * i < C::NK;
-#pragma unroll
-  for (int i = 0; i < C::VJ; ++i) n_dma += wave + kM128Waves * i < C::NV;
-  auto issue = [&](int it, int b, int pid) __attribute__((always_inline)) {
-    const int pg_rel = (off0 + it * kM128Tok) / P;  // page of the stage within the split
+  auto issue = [&](int it, int b, int pid, int pg_rel, int t_tok) __attribute__((always_inline)) {
     const int pg_tok0 = (pg0 + pg_rel) * P;
     const int valid = (pid >= 0 && it < n_it) ? min(max(tok_end - pg_tok0, 0), P) : 0;  // tokens that count
     const int nbytes = __builtin_amdgcn_readfirstlane(valid * D * 2);
@@ -251,27 +289,38 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
                                                                          nbytes, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_pool + blk), 0,
                                                                          nbytes, kBufferRsrcWord3);
-    const int t_bytes = (off0 + it * kM128Tok - pg_rel * P) * D * 2;  // first token of the stage within its page
+    const int t_bytes = t_tok * D * 2;  // first token of the stage within its page
     // non-temporal: the context streams through once per launch
 #pragma unroll
     for (int i = 0; i < C::KJ; ++i) {
       const int j = wave + kM128Waves * i;
-      if (C::NK % kM128Waves == 0 || j < C::NK)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_, (lds_void_t*)&sh.k[b][64 * j], 16, t_bytes + kofs_dma[i], 0, 0,
-                                                 kBufferNT);
+      u32x4_t* dst = (C::NK % kM128Waves == 0 || j < C::NK) ? &sh.k[b][64 * j] : sh.dump;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_, (lds_void_t*)dst, 16, t_bytes + kofs_dma[i], 0, 0, kBufferNT);
     }
 #pragma unroll
     for (int i = 0; i < C::VJ; ++i) {
       const int j = wave + kM128Waves * i;
-      if (C::NV % kM128Waves == 0 || j < C::NV)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr_, (lds_void_t*)&sh.v[b][64 * j], 16, t_bytes + vofs_dma[i], 0, 0,
-                                                 kBufferNT);
+      u32x4_t* dst = (C::NV % kM128Waves == 0 || j < C::NV) ? &sh.v[b][64 * j] : sh.dump;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr_, (lds_void_t*)dst, 16, t_bytes + vofs_dma[i], 0, 0, kBufferNT);
     }
   };
 
-  // first stages from the scalar page ids
+  // first stages from the scalar page ids; (nx_pg, nx_off) steps through
+  // the stages' pages and token offsets (a page holds a whole number of
+  // stages, and a split starts on a stage)
+  int nx_pg = 0, nx_off = off0;
+  auto step = [&]() __attribute__((always_inline)) {
+    nx_off += kM128Tok;
+    if (nx_off == P) {
+      nx_off = 0;
+      ++nx_pg;
+    }
+  };
 #pragma unroll
-  for (int r = 0; r < NB - 1; ++r) issue(r, r, (pid0[r] >= 0 && pid0[r] < a.num_pages) ? pid0[r] : -1);
+  for (int r = 0; r < NB - 1; ++r) {
+    issue(r, r, (pid0[r] >= 0 && pid0[r] < a.num_pages) ? pid0[r] : -1, nx_pg, nx_off);
+    step();
+  }
   if (tid == 0) sh.err = 0;
   // the checked page list (bad ids become -1)
   if (tid < max(npg_plan, 1)) {
@@ -316,9 +365,11 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   }
 
   // Operand reads run ahead of their MFMAs: the K reads of the next KD
-  // k-steps; the V^T reads in groups of four output blocks, the first
-  // before the softmax, each later one while the previous group's MFMAs run.
+  // k-steps; the V^T reads in groups of VG output blocks (eight where the
+  // wave's blocks come in eights), the first before the softmax, each later
+  // one while the previous group's MFMAs run.
   constexpr int KD = 2;
+  constexpr int VG = C::MB % 8 == 0 ? 8 : 4;
   auto compute = [&](int it, int bf) __attribute__((always_inline)) {
     if (!wave_active) return;
     const char* kb = reinterpret_cast<const char*>(sh.k[bf]);
@@ -326,9 +377,12 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
     auto kread = [&](int ks, int tb) __attribute__((always_inline)) {
       return *reinterpret_cast<const u32x4_t*>(kb + koff[tb][ks % KQ] + 256 * (ks / KQ));
     };
-    // V^T operands of output blocks 4 grp .. 4 grp + 3
-    auto vread4 = [&](u32x4_t (&va)[4], int grp) __attribute__((always_inline)) {
-      lds_read_tr4(va, vb + 128 * grp, vb + 128 * grp + 16 * C::VP * 16);
+    // V^T operands of output blocks VG grp .. VG grp + VG - 1
+    auto vread = [&](u32x4_t (&va)[VG], int grp) __attribute__((always_inline)) {
+      if constexpr (VG == 8)
+        lds_read_tr8(va, vb + 256 * grp, vb + 256 * grp + 16 * C::VP * 16);
+      else
+        lds_read_tr4(va, vb + 128 * grp, vb + 128 * grp + 16 * C::VP * 16);
     };
     // ---- S^T for both 16-token blocks: two independent accumulation chains
     u32x4_t kr[KD][2];
@@ -348,8 +402,8 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qb[ks]), acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qb[ks]), acc1, 0, 0, 0);
     }
-    u32x4_t vr[4];
-    vread4(vr, 0);
+    u32x4_t vr[VG];
+    vread(vr, 0);
     // raw scores; tokens of slot i: tau(g, i) = 4g + i and 16 + 4g + i - 4
     float raw[8];
 #pragma unroll
@@ -368,10 +422,8 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
     }
     // ---- online softmax for this lane's row (4 lanes per row), reference
     // moved only when a score exceeds it by more than 2^8 (as attn_mfma.hip)
-    float mr = fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3]));
-    mr = fmaxf(mr, fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
-    mr = fmaxf(mr, shfl_xor_f(mr, 16));
-    mr = fmaxf(mr, shfl_xor_f(mr, 32));
+    const float mr = max_lanes_xor16_32(
+        vmax3(vmax3(raw[0], raw[1], raw[2]), vmax3(raw[3], raw[4], raw[5]), vmax3(raw[6], raw[7], raw[7])));
     const float mt = mr * sl2;
     const bool move = mt > m_run + 8.f;
     const float m_new = move ? mt : m_run;
@@ -392,23 +444,29 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
     }
     m_run = m_new;
     const u32x4_t pb = {pw[0], pw[1], pw[2], pw[3]};
-    // ---- O^T += V^T P^T, four output blocks per group of V^T reads
+    // ---- O^T += V^T P^T, VG output blocks per group of V^T reads
 #pragma unroll
-    for (int grp = 0; grp < C::MB / 4; ++grp) {
-      if (grp > 0) vread4(vr, grp);
+    for (int grp = 0; grp < C::MB / VG; ++grp) {
+      if (grp > 0) vread(vr, grp);
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        o[4 * grp + m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[m]), as_bf16x8(pb), o[4 * grp + m], 0, 0, 0);
+      for (int m = 0; m < VG; ++m)
+        o[VG * grp + m] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[m]), as_bf16x8(pb), o[VG * grp + m], 0, 0, 0);
     }
   };
 
   // main loop: wait for this wave's part of stage it (NB - 2 later stages
   // may stay outstanding), barrier (every wave's part has landed, and every
   // wave is done with stage it - 1, whose buffer is refilled next)
+  // (the page id of the next stage to issue is read from LDS one iteration
+  // ahead)
+  int pid_nx = sh.pages[min(nx_pg, last_pg)];
   for (int it = 0; it < n_it; ++it) {
-    m128_stage_barrier<C::KJ + C::VJ, NB>(n_dma);
+    m128_barrier<(C::KJ + C::VJ) * (NB - 2)>();
     const int nx = it + NB - 1;
-    issue(nx, nx % NB, sh.pages[min((off0 + nx * kM128Tok) / P, last_pg)]);
+    issue(nx, nx % NB, pid_nx, nx_pg, nx_off);
+    step();
+    pid_nx = sh.pages[min(nx_pg, last_pg)];
     compute(it, it % NB);
   }
   // no LDS load may still be landing when the workgroup ends
