@@ -168,10 +168,12 @@ hipError_t launch_attn_cascade(const ValuArgs& ap, const ValuArgs& as, int prefi
 // cost of a prefix tile in suffix tiles (x16) in the one-launch cascade's
 // unit split, measured with both sides running: a 64-token page costs the
 // 128-row MFMA side (K and V staged straight into LDS, ranges of 32-token
-// stages) about 1.75x what it costs the 8-row VALU side (16 x 50K prefix:
-// the weights 20 / 24 / 28 / 32 gave 39.9 / 37.1 / 35.9 / 37.7 us per
-// launch); up to 64 rows the MFMA side streams at about the VALU side's rate
-inline int cascade_prefix_weight16(int prefix_rows) { return prefix_rows > 64 ? 28 : 18; }
+// stages) about 1.3x what it costs the 8-row VALU side (16 x 50K prefix, one
+// launch + merge: the weights 14 / 17 / 20 / 23 / 28 gave 48.0 / 46.6 /
+// 44.3-45.8 / 44.7 / 45.7-46.7 us, a smaller weight also leaving fewer
+// 128-row partials to merge); up to 64 rows the MFMA side streams at about
+// the VALU side's rate
+inline int cascade_prefix_weight16(int prefix_rows) { return prefix_rows > 64 ? 21 : 18; }
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace had
