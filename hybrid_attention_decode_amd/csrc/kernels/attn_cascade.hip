@@ -14,9 +14,11 @@
 // G_p first, then each sequence's own suffix units, and the usual merge reads
 // prefix + own (the merge recomputes the same integers).
 //
-// The prefix side is the MFMA partial (above 64 rows the one that stages K
-// and V straight into LDS, attn_mfma128_body.h), the suffix side the VALU
-// partial in its shared-out mode; LDS is the union of the two.
+// The prefix side is the MFMA partial that stages K and V straight into LDS
+// (attn_mfma128_body.h: 16 rows per wave above 64 rows, wave pairs on 16
+// rows up to 64 at head_dim >= 128; the register-staged attn_mfma_body.h up
+// to 64 rows at head_dim 64), the suffix side the VALU partial in its
+// shared-out mode; LDS is the union of the two.
 #include "attn_mfma128_body.h"
 #include "attn_valu_body.h"
 
@@ -31,14 +33,15 @@ struct PrefixSide {
   int prefix_tiles, weight16, min_pu;  // for cascade_prefix_units
 };
 
-// LDS: the two sides' layouts overlaid
-template <int D, bool R128>
+// LDS: the two sides' layouts overlaid.  DH: the prefix side's wave
+// arrangement in attn_mfma128_body.h (1 or 2), 0 for attn_mfma_body.h.
+template <int D, int DH>
 union CascadeStore {
-  typename std::conditional<R128, M128Lds<D>, MLds<D>>::type m;
+  typename std::conditional<DH != 0, M128Lds<D>, MLds<D>>::type m;
   Lds v;
 };
 
-template <int D, bool R128>
+template <int D, int DH>
 __global__ __launch_bounds__(512, 2) void attn_cascade_kernel(ValuArgs as, PrefixSide px) {
   const int lane = threadIdx.x & 63;
   const int P = as.page_size;
@@ -59,22 +62,22 @@ __global__ __launch_bounds__(512, 2) void attn_cascade_kernel(ValuArgs as, Prefi
     a.batch_rows = as.rows;
     a.fixed_len = px.pages * P;
     a.bal_units = 0;
-    if constexpr (R128) {  // 32-token stages balanced to within one
+    if constexpr (DH != 0) {  // 32-token stages balanced to within one
       const int n_st = px.pages * (P / 32);
       a.split_base = n_st / gp;
       a.split_rem = n_st % gp;
-      mfma128_partial<D, 1, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
+      mfma128_partial<D, DH, CascadeStore<D, DH>>(a, blockIdx.x, blockIdx.y, 0);
     } else {  // whole pages balanced to within one
       a.split_base = px.pages / gp;
       a.split_rem = px.pages % gp;
-      mfma_partial<D, false, true, CascadeStore<D, R128>>(a, blockIdx.x, blockIdx.y, 0);
+      mfma_partial<D, false, true, CascadeStore<D, DH>>(a, blockIdx.x, blockIdx.y, 0);
     }
   } else {
     ValuArgs a = as;  // suffix unit blockIdx.x - gp of G - gp, after the prefix's slots
     a.split_offset = gp;
     a.bal_units = G - gp;
     const FusedArgs f{};
-    valu_partial<D, false, CascadeStore<D, R128>>(a, f, static_cast<int>(blockIdx.x) - gp, blockIdx.y, 0);
+    valu_partial<D, false, CascadeStore<D, DH>>(a, f, static_cast<int>(blockIdx.x) - gp, blockIdx.y, 0);
   }
 }
 
@@ -90,14 +93,15 @@ hipError_t launch_attn_cascade(const ValuArgs& ap, const ValuArgs& as, int prefi
     return hipErrorInvalidValue;
   const PrefixSide px{ap.page_table, ap.rows, ap.n_pages_plan, prefix_tiles, weight16, min_pu};
   const dim3 blk(64 * kMWaves);
-  const bool r128 = ap.rows > kMRows;
-  switch (head_dim * 2 + (r128 ? 1 : 0)) {
-    case 128: hipLaunchKernelGGL((attn_cascade_kernel<64, false>), grid, blk, 0, stream, as, px); break;
-    case 129: hipLaunchKernelGGL((attn_cascade_kernel<64, true>), grid, blk, 0, stream, as, px); break;
-    case 256: hipLaunchKernelGGL((attn_cascade_kernel<128, false>), grid, blk, 0, stream, as, px); break;
-    case 257: hipLaunchKernelGGL((attn_cascade_kernel<128, true>), grid, blk, 0, stream, as, px); break;
-    case 512: hipLaunchKernelGGL((attn_cascade_kernel<256, false>), grid, blk, 0, stream, as, px); break;
-    case 513: hipLaunchKernelGGL((attn_cascade_kernel<256, true>), grid, blk, 0, stream, as, px); break;
+  // wave pairs on 16 rows need two groups of four 16-dim output blocks per wave
+  const int dh = ap.rows > kMRows ? 1 : (head_dim >= 128 ? 2 : 0);
+  switch (head_dim * 4 + dh) {
+    case 256: hipLaunchKernelGGL((attn_cascade_kernel<64, 0>), grid, blk, 0, stream, as, px); break;
+    case 257: hipLaunchKernelGGL((attn_cascade_kernel<64, 1>), grid, blk, 0, stream, as, px); break;
+    case 513: hipLaunchKernelGGL((attn_cascade_kernel<128, 1>), grid, blk, 0, stream, as, px); break;
+    case 514: hipLaunchKernelGGL((attn_cascade_kernel<128, 2>), grid, blk, 0, stream, as, px); break;
+    case 1025: hipLaunchKernelGGL((attn_cascade_kernel<256, 1>), grid, blk, 0, stream, as, px); break;
+    case 1026: hipLaunchKernelGGL((attn_cascade_kernel<256, 2>), grid, blk, 0, stream, as, px); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

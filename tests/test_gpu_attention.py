@@ -234,9 +234,24 @@ def test_rows_and_page_limits_are_rejected():
     (25, 5, 2, 64, 32),    # 125 rows per KV head, two KV heads
     (32, 8, 1, 128, 32),   # 256 rows: two launches
     (20, 4, 1, 128, 64),   # 80 rows: waves 5 .. 7 idle
+    (16, 6, 1, 128, 96),   # 96 rows, pages of 96 tokens (three stages per page)
 ])
 def test_mfma128_path(G, q_len, H_kv, D, P):
     out, ref = _run(1500 + G * 7 + q_len + D, [q_len, q_len + 31, 2080, 9000], q_len, G * H_kv, H_kv, D, P)
+    assert_attn_close(out, ref)
+
+
+# 16 .. 64 rows per launch at head_dim >= 128 with pages of a multiple of 32
+# tokens: the same kernel with wave pairs sharing 16 rows and splitting the
+# output dims
+@pytest.mark.parametrize("G,q_len,H_kv,D,P", [
+    (16, 2, 1, 128, 32),   # 32 rows at head_dim 128 (four output blocks per wave)
+    (12, 4, 2, 128, 64),   # 48 rows per KV head, two KV heads
+    (8, 2, 1, 256, 64),    # 16 rows: one wave pair busy, the other six idle
+    (9, 5, 1, 256, 96),    # 45 rows, pages of 96 tokens (three stages per page)
+])
+def test_mfma128_wave_pair_path(G, q_len, H_kv, D, P):
+    out, ref = _run(1550 + G * 7 + q_len + D, [q_len, q_len + 45, 3000, 7100], q_len, G * H_kv, H_kv, D, P)
     assert_attn_close(out, ref)
 
 
