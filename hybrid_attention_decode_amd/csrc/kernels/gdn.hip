@@ -14,10 +14,11 @@
 // token's state is written as a checkpoint; all tokens' inputs are loaded
 // before the first is processed.
 //
-// Mapping: one wave per (s, h, block of 8 rows of S).  Lane (r, c) holds
-// row r's columns {4c + 32i .. 4c + 32i + 3}, so each row's 8 lanes read a
-// contiguous 128-byte segment per float4; the dot products S k and S q are
-// all-reduced across those 8 lanes with three DPP adds.
+// Mapping: one wave per (s, h, block of RPW = 4 rows of S), so the 128 rows
+// of 8 heads of 128 x 128 take 256 waves, one per CU.  Lane (r, c) holds row
+// r's columns {4c + 64i .. 4c + 64i + 3} (16 lanes per row), so each row's
+// lanes read a contiguous 256-byte segment per float4; the dot products S k
+// and S q are all-reduced across those 16 lanes with four DPP adds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,10 +47,16 @@ struct GdnArgs {
   int raw_gates;  // alpha / beta hold g and b: alpha = exp(g), beta = sigmoid(b)
 };
 
-__device__ __forceinline__ float sum8(float x) {
+constexpr int kRPW = 4;          // state rows per wave
+constexpr int kLPR = 64 / kRPW;  // lanes per row
+
+// sum over the kLPR lanes of a row (groups of 8, then the two halves of a
+// 16-lane row)
+__device__ __forceinline__ float sum_row(float x) {
   x += dpp<DPP_QUAD_XOR1>(x);
   x += dpp<DPP_QUAD_XOR2>(x);
   x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (kLPR == 16) x += dpp<DPP_ROW_ROR8>(x);
   return x;
 }
 
@@ -60,11 +67,13 @@ __device__ __forceinline__ float sum8(float x) {
 // the previous token.
 template <int DK, int TM>
 __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
-  constexpr int NC = DK / 32;  // float4 column chunks per lane
+  static_assert(kLPR == 8 || kLPR == 16, "row sums over 8 or 16 lanes");
+  constexpr int NC = DK / (4 * kLPR);  // float4 column chunks per lane
+  constexpr int CS = 4 * kLPR;         // columns between a lane's chunks
   const int rb = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x;
-  const int r = lane >> 3, c = lane & 7;
-  const int row = rb * 8 + r;
+  const int r = lane / kLPR, c = lane % kLPR;
+  const int row = rb * kRPW + r;
   const size_t head_elems = static_cast<size_t>(a.d_v) * DK;
   const size_t row_off = static_cast<size_t>(h) * head_elems + static_cast<size_t>(row) * DK;
   const size_t slot_elems = static_cast<size_t>(a.H) * head_elems;
@@ -81,8 +90,8 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
     const uint16_t* qp = a.q + th * DK;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      kw[t][i] = *reinterpret_cast<const uint2*>(kp + 4 * c + 32 * i);
-      qw[t][i] = *reinterpret_cast<const uint2*>(qp + 4 * c + 32 * i);
+      kw[t][i] = *reinterpret_cast<const uint2*>(kp + 4 * c + CS * i);
+      qw[t][i] = *reinterpret_cast<const uint2*>(qp + 4 * c + CS * i);
     }
     vi[t] = bf16_to_f32(a.v[th * a.d_v + row]);
     al[t] = a.alpha[th];
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
     const float* src = a.pool + static_cast<size_t>(max(in, 0)) * slot_elems + row_off;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const float4 t4 = *reinterpret_cast<const float4*>(src + 4 * c + 32 * i);
+      const float4 t4 = *reinterpret_cast<const float4*>(src + 4 * c + CS * i);
       S[i][0] = in >= 0 ? t4.x : 0.f;
       S[i][1] = in >= 0 ? t4.y : 0.f;
       S[i][2] = in >= 0 ? t4.z : 0.f;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
     for (int i = 0; i < NC; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sk = fmaf(S[i][e], kk[i][e], sk);
-    sk = sum8(sk);
+    sk = sum_row(sk);
     const float u = bet * (vi[t] - alt * sk);
     float sq = 0.f;
 #pragma unroll
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
         S[i][e] = fmaf(u, kk[i][e], alt * S[i][e]);
         sq = fmaf(S[i][e], qq[i][e], sq);
       }
-    sq = sum8(sq);
+    sq = sum_row(sq);
     if (c == 0) a.o[th * a.d_v + row] = a.q_scale * sq;
     const int out = outs[t];
     if (out < 0 || out >= a.n_slots) {
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(64) void gdn_kernel(GdnArgs a) {
     float* dst = a.pool + static_cast<size_t>(out) * slot_elems + row_off;
 #pragma unroll
     for (int i = 0; i < NC; ++i)
-      *reinterpret_cast<float4*>(dst + 4 * c + 32 * i) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+      *reinterpret_cast<float4*>(dst + 4 * c + CS * i) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
   }
 }
 
@@ -187,7 +196,7 @@ extern "C" int had_gdn_state_update(const had_gdn_desc* d, const had_gdn_ptrs* p
   a.d_v = d->d_v;
   a.n_slots = d->n_slots;
   a.q_scale = d->q_scale;
-  const dim3 grid(d->d_v / 8, d->H, d->n_seqs);
+  const dim3 grid(d->d_v / had::kRPW, d->H, d->n_seqs);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the token bound the kernel is compiled for: 1, 4 or 8
   if (d->d_k == 64) {
