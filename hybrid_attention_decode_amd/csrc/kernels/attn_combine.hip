@@ -14,8 +14,11 @@
 // bound by memory latency and by how many CUs pull the partials, not by
 // HBM bandwidth: one 4-wave block per (row, 32-dim slice) -- 8 blocks per
 // row at head_dim 256 -- issues all of its partial loads (float4 per lane,
-// up to 256 splits per pass) before it touches any of them, reads the
-// maxima in the same round trip, and reduces across waves through LDS.
+// up to 256 splits per pass) and their maxima before it touches any of them.
+// Each wave merges its own 64 splits of a pass in registers against its own
+// running maximum (lane swaps across the split rows, no LDS), and the four
+// waves' results are merged once through LDS, rescaled to the block's
+// maximum: one barrier per block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,12 +34,21 @@ constexpr int kLS = kDC / 4;                 // lanes per split row (float4 each
 constexpr int kSPW = 64 / kLS;               // split rows per wave per load
 constexpr int kU = 8;                        // loads per lane per pass
 constexpr int kPass = kWaves * kSPW * kU;    // splits per pass (256)
-static_assert(kPass <= 64 * kWaves, "one maximum per thread per pass");
+static_assert(kLS == 8 && kSPW == 8, "split rows are lanes l, l ^ 8, l ^ 16, l ^ 32");
+
+// max (sum) over the kSPW split rows of a wave: lanes l, l ^ 8, l ^ 16, l ^ 32
+__device__ __forceinline__ float max_rows(float x) {
+  x = fmaxf(x, dpp<DPP_ROW_ROR8>(x));
+  return max_xor32(max_xor16(x));
+}
+__device__ __forceinline__ float sum_rows(float x) {
+  x += dpp<DPP_ROW_ROR8>(x);
+  return sum_xor32(sum_xor16(x));
+}
 
 __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a, int D) {
-  __shared__ float wsh[kPass];
   __shared__ float4 red[kWaves][kLS];
-  __shared__ float scal[kWaves];
+  __shared__ float2 wml[kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane / kLS, dl = lane % kLS;
   const int row = blockIdx.x;
@@ -58,9 +70,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
     ns = n_pre + __builtin_amdgcn_readfirstlane(__shfl(W_t, unit / a.H_kv));
   }
   const size_t base = static_cast<size_t>(unit) * a.num_splits;
-  const float* ml = a.ws_ml;
   const size_t ostride4 = static_cast<size_t>(a.rows) * D / 4;  // float4s between consecutive splits
   const float4* o4 = reinterpret_cast<const float4*>(a.ws_o + (base * a.rows + row) * D + d0);
+  const float2* ml2 = reinterpret_cast<const float2*>(a.ws_ml) + base * a.rows + row;
   const int s = unit / a.H_kv, h = unit % a.H_kv;
   const int jq = row / a.G, g = row % a.G;
   const size_t head = (static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + g;
@@ -69,72 +81,66 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
   const uint2 gw = *reinterpret_cast<const uint2*>(
       a.gate ? a.gate + head * a.gate_hstride + d0 + 4 * (tid % kLS) : a.out + head * D + d0 + 4 * (tid % kLS));
 
+  // this wave's running merge: maximum M, sum of weighted l (per split row,
+  // summed over the rows at the end) and of weighted o
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float M = -INFINITY;
   float lsum = 0.f;
   for (int p0 = 0; p0 < ns; p0 += kPass) {
     // issue every load of this pass first (unconditional, the index clamped
     // to the last partial: a load under a branch would make the compiler
-    // wait for each one in turn)
+    // wait for each one in turn); the kLS lanes of a split row read the same
+    // (m, l) pair
     float4 ov[kU];
+    float2 mlv[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = min(p0 + (u * kWaves + wave) * kSPW + sub, ns - 1);
       ov[u] = o4[i * ostride4 + dl];
+      mlv[u] = ml2[static_cast<size_t>(i) * a.rows];
     }
-    const int my = p0 + tid;  // this thread's split for the maxima
-    const float2 mlv = *reinterpret_cast<const float2*>(&ml[((base + min(my, ns - 1)) * a.rows + row) * 2]);
-    float mi = mlv.x, li = mlv.y;
-    if (my >= ns) mi = -INFINITY, li = 0.f;  // past the partials
-    // block maximum of this pass, merged into the running maximum
-    float mw = mi;
+    float mi[kU];
+    float mp = -INFINITY;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mw = fmaxf(mw, shfl_xor_f(mw, off));
-    if (lane == 0) scal[wave] = mw;
-    __syncthreads();
-    float mp = scal[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mp = fmaxf(mp, scal[w]);
+    for (int u = 0; u < kU; ++u) {
+      const bool in = p0 + (u * kWaves + wave) * kSPW + sub < ns;  // past the partials: weight 0
+      mi[u] = in ? mlv[u].x : -INFINITY;
+      mp = fmaxf(mp, mi[u]);
+    }
+    mp = max_rows(mp);
     const float M_new = fmaxf(M, mp);
     const float Ms = (M_new == -INFINITY) ? 0.f : M_new;
-    const float rescale = (M == -INFINITY) ? 0.f : exp2f(M - Ms);
+    const float rescale = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Ms);
     acc.x *= rescale; acc.y *= rescale; acc.z *= rescale; acc.w *= rescale;
     lsum *= rescale;
     M = M_new;
-    {
-      const float w = (mi == -INFINITY) ? 0.f : exp2f(mi - Ms);
-      wsh[tid] = w;
-      lsum += w * li;
-    }
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int il = (u * kWaves + wave) * kSPW + sub;
-      if (p0 + il < ns) {
-        const float w = wsh[il];
-        acc.x += w * ov[u].x; acc.y += w * ov[u].y; acc.z += w * ov[u].z; acc.w += w * ov[u].w;
-      }
+      // (v_exp_f32: a weight below 2^-126 of the maximum flushes to 0)
+      const float w = (mi[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi[u] - Ms);
+      lsum += w * mlv[u].y;
+      acc.x += w * ov[u].x; acc.y += w * ov[u].y; acc.z += w * ov[u].z; acc.w += w * ov[u].w;
     }
-    __syncthreads();
   }
-  // sum over the split sub-rows of a wave, then over the waves
-#pragma unroll
-  for (int off = kLS; off < 64; off <<= 1) {
-    acc.x += shfl_xor_f(acc.x, off); acc.y += shfl_xor_f(acc.y, off);
-    acc.z += shfl_xor_f(acc.z, off); acc.w += shfl_xor_f(acc.w, off);
-  }
+  // sum over the split rows of the wave, then merge the waves
+  acc.x = sum_rows(acc.x); acc.y = sum_rows(acc.y); acc.z = sum_rows(acc.z); acc.w = sum_rows(acc.w);
+  lsum = sum_rows(lsum);
   if (sub == 0) red[wave][dl] = acc;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) lsum += shfl_xor_f(lsum, off);
-  if (lane == 0) scal[wave] = lsum;
+  if (lane == 0) wml[wave] = make_float2(M, lsum);
   __syncthreads();
   if (tid < kLS) {
-    float4 t = red[0][tid];
-    float l = scal[0];
+    float Mt = -INFINITY;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      t.x += red[w][tid].x; t.y += red[w][tid].y; t.z += red[w][tid].z; t.w += red[w][tid].w;
-      l += scal[w];
+    for (int w = 0; w < kWaves; ++w) Mt = fmaxf(Mt, wml[w].x);
+    const float Ms = (Mt == -INFINITY) ? 0.f : Mt;
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float c = (wml[w].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wml[w].x - Ms);
+      const float4 r4 = red[w][tid];
+      t.x += c * r4.x; t.y += c * r4.y; t.z += c * r4.z; t.w += c * r4.w;
+      l += c * wml[w].y;
     }
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     float4 r = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
