@@ -13,8 +13,9 @@
 // The merge reads every partial once (rows x splits x head_dim fp32) and is
 // bound by memory latency and by how many CUs pull the partials, not by
 // HBM bandwidth: one 4-wave block per (row, 32-dim slice) -- 8 blocks per
-// row at head_dim 256 -- issues all of its partial loads (float4 per lane,
-// up to 256 splits per pass) and their maxima before it touches any of them.
+// row at head_dim 256, or 16-dim slices when that leaves under 256 blocks --
+// issues all of its partial loads (float4 per lane, up to 256 splits per
+// pass) and their maxima before it touches any of them.
 // Each wave merges its own 64 splits of a pass in registers against its own
 // running maximum (lane swaps across the split rows, no LDS), and the four
 // waves' results are merged once through LDS, rescaled to the block's
@@ -29,30 +30,36 @@ namespace had {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kDC = 32;                      // output dims per block
-constexpr int kLS = kDC / 4;                 // lanes per split row (float4 each)
-constexpr int kSPW = 64 / kLS;               // split rows per wave per load
-constexpr int kU = 8;                        // loads per lane per pass
-constexpr int kPass = kWaves * kSPW * kU;    // splits per pass (256)
-static_assert(kLS == 8 && kSPW == 8, "split rows are lanes l, l ^ 8, l ^ 16, l ^ 32");
+constexpr int kPass = 256;  // splits per pass
 
-// max (sum) over the kSPW split rows of a wave: lanes l, l ^ 8, l ^ 16, l ^ 32
+// max (sum) over the split rows of a wave, the lanes congruent to l mod LS:
+// rotations by 4 and 8 inside each 16-lane row, then lanes l ^ 16 and l ^ 32
+template <int LS>
 __device__ __forceinline__ float max_rows(float x) {
+  if constexpr (LS == 4) x = fmaxf(x, dpp<DPP_ROW_ROR4>(x));
   x = fmaxf(x, dpp<DPP_ROW_ROR8>(x));
   return max_xor32(max_xor16(x));
 }
+template <int LS>
 __device__ __forceinline__ float sum_rows(float x) {
+  if constexpr (LS == 4) x += dpp<DPP_ROW_ROR4>(x);
   x += dpp<DPP_ROW_ROR8>(x);
   return sum_xor32(sum_xor16(x));
 }
 
+// DC output dims per block: 32, or 16 when there are few blocks
+template <int DC>
 __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a, int D) {
+  constexpr int kLS = DC / 4;                // lanes per split row (float4 each)
+  constexpr int kSPW = 64 / kLS;             // split rows per wave per load
+  constexpr int kU = kPass / (kWaves * kSPW);  // loads per lane per pass
+  static_assert(kLS == 4 || kLS == 8, "split rows are the lanes congruent mod kLS");
   __shared__ float4 red[kWaves][kLS];
   __shared__ float2 wml[kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane / kLS, dl = lane % kLS;
   const int row = blockIdx.x;
-  const int d0 = blockIdx.y * kDC;
+  const int d0 = blockIdx.y * DC;
   const int unit = blockIdx.z;  // s * H_kv + h
   // partials of this sequence: all num_splits slots, or after a suffix pass
   // shared out by length the prefix splits and the sequence's own share
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
       mi[u] = in ? mlv[u].x : -INFINITY;
       mp = fmaxf(mp, mi[u]);
     }
-    mp = max_rows(mp);
+    mp = max_rows<kLS>(mp);
     const float M_new = fmaxf(M, mp);
     const float Ms = (M_new == -INFINITY) ? 0.f : M_new;
     const float rescale = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Ms);
@@ -123,8 +130,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
     }
   }
   // sum over the split rows of the wave, then merge the waves
-  acc.x = sum_rows(acc.x); acc.y = sum_rows(acc.y); acc.z = sum_rows(acc.z); acc.w = sum_rows(acc.w);
-  lsum = sum_rows(lsum);
+  acc.x = sum_rows<kLS>(acc.x); acc.y = sum_rows<kLS>(acc.y);
+  acc.z = sum_rows<kLS>(acc.z); acc.w = sum_rows<kLS>(acc.w);
+  lsum = sum_rows<kLS>(lsum);
   if (sub == 0) red[wave][dl] = acc;
   if (lane == 0) wml[wave] = make_float2(M, lsum);
   __syncthreads();
@@ -159,8 +167,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(CombineArgs a
 
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream) {
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return hipErrorInvalidValue;
-  const dim3 grid(a.rows, head_dim / kDC, a.n_seqs * a.H_kv);
-  hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(64 * kWaves), 0, stream, a, head_dim);
+  // 16-dim slices while 32-dim ones would leave most CUs idle (8 rows of
+  // one sequence: 64 blocks), 32-dim ones otherwise (64 rows at 16-dim
+  // slices, 1024 blocks, merged 25 % slower)
+  const int64_t blocks32 = static_cast<int64_t>(a.rows) * (head_dim / 32) * a.n_seqs * a.H_kv;
+  if (blocks32 < 256)
+    hipLaunchKernelGGL(attn_combine_kernel<16>, dim3(a.rows, head_dim / 16, a.n_seqs * a.H_kv), dim3(64 * kWaves), 0,
+                       stream, a, head_dim);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<32>, dim3(a.rows, head_dim / 32, a.n_seqs * a.H_kv), dim3(64 * kWaves), 0,
+                       stream, a, head_dim);
   return hipGetLastError();
 }
 

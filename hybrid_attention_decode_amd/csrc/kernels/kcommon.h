@@ -37,6 +37,7 @@ enum : int {
   DPP_QUAD_XOR1 = 0xB1,   // quad_perm [1,0,3,2]
   DPP_QUAD_XOR2 = 0x4E,   // quad_perm [2,3,0,1]
   DPP_ROW_HALF_MIRROR = 0x141,  // lane i <-> 7-i inside each group of 8
+  DPP_ROW_ROR4 = 0x124,   // rotate by 4 inside each 16-lane row
   DPP_ROW_ROR8 = 0x128    // rotate by 8 inside each 16-lane row (= xor 8)
 };
 
