@@ -353,15 +353,17 @@ static int launch_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd
   // 16 or more rows (MFMA path): every work unit would redo all of its
   // rows' prologue, so the prologue runs once as its own kernel and writes
   // q to the caller's q_out or to the workspace's q block
-  int ns, pps;
-  st = plan(d, &ns, &pps, nullptr);
+  int ns, pps, n_plan;
+  st = plan(d, &ns, &pps, &n_plan);
   if (st != HAD_OK) return st;
   if (workspace_bytes < ws_bytes(d, ns))
     return fail(HAD_ERR_WORKSPACE_TOO_SMALL, "decode_attn_layer: workspace %zu bytes < %zu", workspace_bytes,
                 ws_bytes(d, ns));
   had_qknrg_ptrs pq = *pp;
   if (!pq.q_out) pq.q_out = static_cast<char*>(workspace) + ws_q_offset(d, ns);
-  st = had_qk_norm_rope_gate(pd, &pq, stream);
+  // (a sequence past the plan's pages, which the attention skips, gets no
+  // K/V row either)
+  st = had::launch_qk_norm_rope_gate(pd, &pq, static_cast<int64_t>(n_plan) * d->page_size, stream);
   if (st != HAD_OK) return st;
   p.q = pq.q_out;
   return launch_partial(d, &p, stream, out_args);

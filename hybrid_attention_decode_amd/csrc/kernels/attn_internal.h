@@ -175,5 +175,8 @@ hipError_t launch_attn_cascade(const ValuArgs& ap, const ValuArgs& as, int prefi
 // the VALU side's rate
 inline int cascade_prefix_weight16(int prefix_rows) { return prefix_rows > 64 ? 21 : 18; }
 hipError_t launch_attn_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
+// had_qk_norm_rope_gate for sequences of at most max_len tokens (longer ones
+// are skipped with HAD_DERR_SEQLEN)
+int launch_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_ptrs* p, int64_t max_len, void* stream);
 
 }  // namespace had

@@ -98,14 +98,11 @@ __device__ __forceinline__ void m128_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// max of three floats as one v_max3_f32 (fmaxf would first canonicalize
-// every operand that does not come from a float instruction, e.g. an MFMA
-// result or a lane swap)
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// max of three floats.  (Not as inline assembly: the compiler inserts the
+// wait states a read of an MFMA result or of a lane swap's outputs needs
+// only before instructions it emits itself; a v_max3_f32 written in inline
+// assembly right after v_permlane16_swap read stale values in some waves.)
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // max over lanes l, l ^ 16, l ^ 32, l ^ 48: v_permlane16_swap exchanges the
 // upper 16 lanes of each 32-lane half of its first operand with the lower 16

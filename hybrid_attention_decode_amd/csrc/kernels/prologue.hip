@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../host/status.h"
 #include "had.h"
 #include "kcommon.h"
@@ -36,6 +38,7 @@ struct PrologueArgs {
   uint16_t* gate_out;
   int32_t* d_err;
   int T, H_q, H_kv, R, num_pages, P, max_pages;
+  int max_len;  // a longer sequence is skipped (HAD_DERR_SEQLEN): no K/V row written
   double coef;  // rope_coef(base, R)
   float eps;
 };
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   for (int m = 0; m < E; ++m) cp[m] = side[lane + 64 * m];
   const int L = a.seq_lens[s];
   const int pos = L - a.T + j;
-  const bool pos_ok = L >= a.T && pos < a.max_pages * a.P;
+  const bool pos_ok = L >= a.T && L <= a.max_len && pos < a.max_pages * a.P;
   const int pid = a.page_table[static_cast<size_t>(s) * a.max_pages + (pos_ok ? pos / a.P : 0)];
   const bool page_ok = pos_ok && pid >= 0 && pid < a.num_pages;
   if (threadIdx.x == 0 && blockIdx.y == 0) {
@@ -96,7 +99,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
 }  // namespace
 }  // namespace had
 
-extern "C" int had_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_ptrs* p, void* stream) {
+namespace had {
+
+// The prologue of sequences of at most max_len tokens (the attention layer
+// passes the length its split plan covers, so a longer sequence, which the
+// attention skips, gets no K/V row either).
+int launch_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_ptrs* p, int64_t max_len, void* stream) {
   if (!d || !p) return fail(HAD_ERR_INVALID_ARG, "qk_norm_rope_gate: NULL argument");
   if (d->n_seqs < 0 || d->T < 0 || d->H_q < 1 || d->H_kv < 1)
     return fail(HAD_ERR_INVALID_ARG, "qk_norm_rope_gate: bad sizes (n_seqs=%d T=%d H_q=%d H_kv=%d)", d->n_seqs, d->T,
@@ -133,6 +141,7 @@ extern "C" int had_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_pt
   a.num_pages = d->num_pages;
   a.P = d->page_size;
   a.max_pages = d->max_pages;
+  a.max_len = static_cast<int>(std::min<int64_t>(max_len, static_cast<int64_t>(d->max_pages) * d->page_size));
   a.coef = had::rope_coef(d->rope_base, d->rotary_dim);
   a.eps = d->eps;
   const dim3 grid(d->n_seqs * d->T, (d->H_q + d->H_kv + 3) / 4), block(256);
@@ -145,4 +154,11 @@ extern "C" int had_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_pt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HAD_ERR_HIP, "qk_norm_rope_gate: launch: %s", hipGetErrorString(e));
   return had::ok();
+}
+
+}  // namespace had
+
+extern "C" int had_qk_norm_rope_gate(const had_qknrg_desc* d, const had_qknrg_ptrs* p, void* stream) {
+  if (!d) return fail(HAD_ERR_INVALID_ARG, "qk_norm_rope_gate: NULL argument");
+  return had::launch_qk_norm_rope_gate(d, p, static_cast<int64_t>(d->max_pages) * d->page_size, stream);
 }

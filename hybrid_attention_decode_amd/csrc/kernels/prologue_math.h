@@ -66,8 +66,12 @@ __device__ __forceinline__ void rope_cs(int pos, int i, double coef, float& c, f
 }
 
 // RMSNorm * w, then the partial rotation with the given cos / sin of each
-// of this lane's elements (1 and 0 past R); xrow is a D-float LDS row
-// private to the calling wave (used to fetch rotation partners).
+// of this lane's elements (1 and 0 past R).  The rotation partner of
+// element d = l + 64 m is d +- R/2: in this lane's own registers when R/2 is
+// a multiple of 64, in lane l ^ 32 (l ^ 16) when R/2 = 32 (16), reached by a
+// lane swap; other R go through xrow, a D-float LDS row private to the
+// calling wave.  The sums and products are the same in every case, so the
+// result does not depend on how the partner is fetched.
 template <int D>
 __device__ __forceinline__ void row_norm_rope_cs(const RowIn<D>& in, const float (&cs)[D / 64],
                                                  const float (&sn)[D / 64], int R, float eps, float* xrow, int lane,
@@ -83,32 +87,57 @@ __device__ __forceinline__ void row_norm_rope_cs(const RowIn<D>& in, const float
   }
   // sum over the wave: inside each 16-lane row by DPP (quad pairs, quad
   // halves, the other quad of 8, the other 8 of 16), then across the rows
+  // (lanes l ^ 16, l ^ 32; a sum of two terms, in either order)
   ss += dpp<DPP_QUAD_XOR1>(ss);
   ss += dpp<DPP_QUAD_XOR2>(ss);
   ss += dpp<DPP_ROW_HALF_MIRROR>(ss);
   ss += dpp<DPP_ROW_ROR8>(ss);
-  ss += shfl_xor_f(ss, 16);
-  ss += shfl_xor_f(ss, 32);
+  ss = sum_xor16(ss);
+  ss = sum_xor32(ss);
   const float inv = 1.f / sqrtf(ss / static_cast<float>(D) + eps);
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    x[m] = x[m] * inv * in.w[m];
-    xrow[lane + 64 * m] = x[m];
+  for (int m = 0; m < E; ++m) x[m] = x[m] * inv * in.w[m];
+  float other[E];
+  const bool in_lane = half % 64 == 0, swap32 = half == 32, swap16 = half == 16;  // (uniform)
+  if (in_lane) {
+    const int hm = half / 64;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const int d = lane + 64 * m;
+      other[m] = 0.f;
+#pragma unroll
+      for (int n = 0; n < E; ++n)  // x[m + hm] below R/2, x[m - hm] above (a constant index each way)
+        if (n == m + hm || n == m - hm) other[m] = (d < half) == (n > m) ? x[n] : other[m];
+    }
+  } else if (swap32 || swap16) {
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const auto p = swap32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[m]), __float_as_uint(x[m]), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[m]), __float_as_uint(x[m]), false, false);
+      // the two results hold x[m] of this lane and of its partner, in either order
+      const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+      other[m] = __float_as_uint(a) == __float_as_uint(x[m]) ? b : a;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < E; ++m) xrow[lane + 64 * m] = x[m];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const int d = lane + 64 * m;
+      other[m] = d < R ? xrow[d < half ? d + half : d - half] : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     const int d = lane + 64 * m;
     float r = x[m];
-    if (d < R) {
-      const float other = xrow[d < half ? d + half : d - half];
-      r = d < half ? x[m] * cs[m] - other * sn[m] : x[m] * cs[m] + other * sn[m];
-    }
+    if (d < R) r = d < half ? x[m] * cs[m] - other[m] * sn[m] : x[m] * cs[m] + other[m] * sn[m];
     y[m] = f32_to_bf16(r);
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
 // The same, forming this row's angles at `pos` itself (coef = rope_coef).

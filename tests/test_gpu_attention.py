@@ -255,6 +255,34 @@ def test_mfma128_wave_pair_path(G, q_len, H_kv, D, P):
     assert_attn_close(out, ref)
 
 
+# Peaked attention (q scaled by 3: a few keys carry most of each row's
+# weight, and the running maximum moves during the context): every output
+# dim of every path.  (A row maximum taken over stale lane-swap outputs
+# left the upper half of the output dims of the wave-pair path at head_dim
+# 256 off by up to 100x here while the tests with unit-scale q passed.)
+@pytest.mark.parametrize("lens,q_len,G,D,P", [
+    ([182], 1, 16, 256, 64),          # 16 rows, wave pairs (head_dim 256)
+    ([3000, 182], 4, 16, 256, 64),    # 64 rows, wave pairs
+    ([700], 2, 16, 128, 32),          # 32 rows, wave pairs (head_dim 128)
+    ([1500], 4, 20, 256, 64),         # 80 rows, one wave per 16 rows
+    ([900], 4, 16, 256, 16),          # 64 rows, pages of 16 tokens (register-staged kernel)
+    ([5000], 1, 8, 256, 64),          # 8 rows (VALU kernel)
+])
+def test_peaked_attention_all_paths(lens, q_len, G, D, P):
+    seed = 1900 + sum(lens) % 97 + q_len + G
+    q, kp, vp, pt, L = paged_case(seed, lens, q_len, G, 1, D, P)
+    qs = bf16.from_f64(3.0 * bf16.to_f64(bits_of(q)))
+    qt = torch.from_numpy(qs.view(np.int16)).view(torch.bfloat16)
+    print("case peaked seed=%d lens=%s q_len=%d G=%d D=%d P=%d" % (seed, lens, q_len, G, D, P), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = had.decode_attn(to_dev(qt), to_dev(kp), to_dev(vp), to_dev(pt), to_dev(L), d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref = A.paged_attention(qs, bits_of(kp), bits_of(vp), pt, L, P, 1.0 / np.sqrt(D))
+    assert np.abs(ref).max() > 0.5
+    assert_attn_close(out, ref)
+
+
 @pytest.mark.parametrize("splits", [1, 5, 300])
 def test_mfma128_path_forced_splits(splits):
     # 300 splits over 71 pages leave most splits empty

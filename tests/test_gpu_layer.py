@@ -17,7 +17,12 @@ pytestmark = pytest.mark.gpu
 
 
 def _within_one_ulp(got_bits, ref):
-    return np.all(np.abs(bf16.to_f64(got_bits) - ref) <= bf16.ulp(ref))
+    # one bf16 ulp of the exact value, plus the fp32 rounding of the row's
+    # magnitude: the rotation y_i cos - y_j sin runs in fp32 on O(1) inputs,
+    # so a result that cancels to ~1e-5 carries an absolute error of a few
+    # fp32 ulps of its inputs, more than one bf16 ulp of itself
+    scale = np.abs(ref).max(axis=-1, keepdims=True)
+    return np.all(np.abs(bf16.to_f64(got_bits) - ref) <= bf16.ulp(ref) + 2.0 ** -21 * scale)
 
 
 def _inputs(seed, S, T, H_q, H_kv, D):
@@ -99,6 +104,59 @@ def test_new_tokens_straddle_splits(H_q):
     # splits hold new positions, the one with the last position owns them
     c = _run(2100 + H_q, [16 * 40 + 2], 4, H_q, 1, 128, 32, 16, num_splits=41)
     _check_against_oracle(c)
+
+
+# 16 to 64 rows at head_dim >= 128 with pages of a multiple of 32 tokens:
+# the prologue kernel, then the MFMA partial that loads K and V straight
+# into LDS with wave pairs
+@pytest.mark.parametrize("lens,T,H_q,H_kv,D,R,P", [
+    ([3000, 41], 2, 16, 1, 128, 128, 32),     # 32 rows, whole head rotated, a 41-token sequence
+    ([5000], 8, 8, 1, 256, 64, 96),           # 8 new tokens (one per wave), 96-token pages
+    ([1000, 700], 4, 4, 1, 256, 256, 64),     # 16 rows: one wave pair
+    ([900], 3, 16, 2, 128, 32, 32),           # 48 rows per KV head, two KV heads, 32 rotary dims
+    ([32 * 10 + 3], 4, 16, 1, 256, 64, 32),   # the new tokens across a page boundary
+])
+def test_mfma_layer_matches_oracle(lens, T, H_q, H_kv, D, R, P):
+    c = _run(3100 + sum(lens) % 997 + T, lens, T, H_q, H_kv, D, R, P)
+    _check_against_oracle(c)
+
+
+@pytest.mark.parametrize("num_splits", [1, 41, 300])
+def test_mfma_layer_split_counts(num_splits):
+    # one split; one 32-token stage per split with the 4 new tokens across
+    # two splits; 300 splits, most of them empty
+    c = _run(3200 + num_splits, [32 * 40 + 2], 4, 16, 1, 128, 64, 32, num_splits=num_splits)
+    _check_against_oracle(c)
+
+
+def test_mfma_layer_matches_two_call_path():
+    lens, T, H_q, H_kv, D, R, P = [3000, 70], 4, 16, 1, 256, 64, 64
+    c = _run(3300, lens, T, H_q, H_kv, D, R, P, deterministic=True)
+    kd2, vd2 = to_dev(c["k_pool"]), to_dev(c["v_pool"])
+    q2, g2 = had.qk_norm_rope_gate(to_dev(c["qg"]), to_dev(c["k"]), to_dev(c["v"]), to_dev(c["w_q"]),
+                                   to_dev(c["w_k"]), to_dev(c["pt"]), to_dev(c["L"]), kd2, vd2, R)
+    out2 = had.decode_attn(q2, kd2, vd2, to_dev(c["pt"]), to_dev(c["L"]), deterministic=True)
+    torch.cuda.synchronize()
+    # the prologue arithmetic is shared: q, gate and the written pools agree bit for bit
+    assert np.array_equal(bits_of(c["q_out"]), bits_of(q2))
+    assert np.array_equal(bits_of(c["gate"]), bits_of(g2))
+    assert np.array_equal(bits_of(c["kd"]), bits_of(kd2), equal_nan=True)
+    assert np.array_equal(bits_of(c["vd"]), bits_of(vd2), equal_nan=True)
+    a, b = bf16.to_f64(bits_of(c["out"])), bf16.to_f64(bits_of(out2))
+    assert np.abs(a - b).max() <= 4e-3
+
+
+def test_mfma_layer_bad_new_token_page_is_reported():
+    _, k_pool, v_pool, pt, L = paged_case(3400, [200], 4, 16, 1, 128, 32)
+    pt = pt.copy()
+    pt[0, 199 // 32] = 10 ** 6                     # the page of the new tokens: out of range
+    qg, k, v, w_q, w_k = _inputs(3400, 1, 4, 16, 1, 128)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("case bad new-token page (MFMA, 64 rows)", flush=True)
+    had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L),
+                          to_dev(k_pool), to_dev(v_pool), 32, d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_PAGE
 
 
 @pytest.mark.parametrize("L,num_splits", [(666, 7), (643, 13), (700, 5)])
@@ -225,6 +283,18 @@ def test_length_beyond_the_split_plan_is_reported_and_writes_nothing():
     kd, vd = to_dev(k_pool), to_dev(v_pool)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     print("case length past the plan (fused VALU)", flush=True)
+    had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L), kd, vd,
+                          32, max_seq_len=900, d_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & had.DERR_SEQLEN
+    assert np.array_equal(bits_of(kd), bits_of(k_pool), equal_nan=True)
+    assert np.array_equal(bits_of(vd), bits_of(v_pool), equal_nan=True)
+    # the same on the MFMA path (64 rows)
+    _, k_pool, v_pool, pt, L = paged_case(2902, [1000], 4, 16, 1, 128, 64)
+    qg, k, v, w_q, w_k = _inputs(2902, 1, 4, 16, 1, 128)
+    kd, vd = to_dev(k_pool), to_dev(v_pool)
+    err.zero_()
+    print("case length past the plan (MFMA layer, 64 rows)", flush=True)
     had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L), kd, vd,
                           32, max_seq_len=900, d_err=err)
     torch.cuda.synchronize()
