@@ -241,9 +241,9 @@ static int launch_partial(const had_attn_desc* d, const had_attn_ptrs* p, void* 
   const dim3 grid(ns, d->H_kv, d->n_seqs);
   hipError_t e = hipSuccess;
   if (rows >= 16) {
-    if (fused) return fail(HAD_ERR_UNSUPPORTED_SHAPE, "decode_attn: the fused prologue runs below 16 rows only");
     a.row_base = 0;
-    e = had::launch_attn_mfma(a, d->head_dim, grid, s);
+    e = fused ? had::launch_attn_mfma128_fused(a, *fused, d->head_dim, grid, s)
+              : had::launch_attn_mfma(a, d->head_dim, grid, s);
   } else {
     for (int rb = 0; rb < rows && e == hipSuccess; rb += 8) {
       a.row_base = rb;
@@ -349,10 +349,20 @@ static int launch_layer_partial(const had_attn_desc* d, const had_qknrg_desc* pd
   p.workspace_bytes = workspace_bytes;
   p.out = nullptr;
   p.d_err = pp->d_err;
-  if (d->q_len * (d->H_q / d->H_kv) < 16) return launch_partial(d, &p, stream, out_args, &f);
-  // 16 or more rows (MFMA path): every work unit would redo all of its
-  // rows' prologue, so the prologue runs once as its own kernel and writes
-  // q to the caller's q_out or to the workspace's q block
+  const int rows = d->q_len * (d->H_q / d->H_kv);
+  if (rows < 16) return launch_partial(d, &p, stream, out_args, &f);
+  // 16..128 rows on the MFMA partial that loads K and V straight into LDS
+  // (pages of a multiple of 32 tokens, 16..64 rows at head_dim >= 128):
+  // the prologue inline as well (rotation partners a whole number of
+  // 32-dim k-steps apart in one lane, or 32 dims apart for R = 64; 16-byte
+  // rows for the vector loads and stores)
+  const int R = pd->rotary_dim;
+  if (rows <= 128 && d->page_size % 32 == 0 && (rows > 64 || d->head_dim >= 128) &&
+      (R == 0 || R == 64 || R % 128 == 0) && aligned16(pp->qg) && aligned16(pp->w_q) && aligned16(pp->w_k) &&
+      aligned16(pp->gate_out) && (!pp->q_out || aligned16(pp->q_out)))
+    return launch_partial(d, &p, stream, out_args, &f);
+  // other MFMA shapes: the prologue once as its own kernel, q to the
+  // caller's q_out or to the workspace's q block
   int ns, pps, n_plan;
   st = plan(d, &ns, &pps, &n_plan);
   if (st != HAD_OK) return st;

@@ -116,8 +116,9 @@ __device__ __forceinline__ int cascade_prefix_units(const int32_t* seq_lens, int
   return static_cast<int>(gp);
 }
 
-// Inputs of the prologue when the VALU attention kernel runs it inline (the
-// fused layer entry point, below 16 query rows per KV head): every
+// Inputs of the prologue when an attention kernel runs it inline (the fused
+// layer entry point: the VALU partial below 16 query rows per KV head, the
+// MFMA partial that loads K and V straight into LDS at 16..128): every
 // workgroup normalises and rotates its own query rows; the workgroup whose
 // split holds the last position also normalises and rotates the new keys,
 // writes the new K/V rows to the pools and adds the new tokens to its
@@ -160,6 +161,12 @@ struct CombineArgs {
 hipError_t launch_attn_valu(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_valu_fused(const ValuArgs& a, const FusedArgs& f, int head_dim, dim3 grid, hipStream_t stream);
 hipError_t launch_attn_mfma(const ValuArgs& a, int head_dim, dim3 grid, hipStream_t stream);
+// the MFMA partial that loads K and V straight into LDS with the layer's
+// prologue inline: 16..128 rows in one launch (16..64 at head_dim >= 128),
+// pages of a multiple of 32 tokens, q_len <= 8, rotary dims 0, 64 or a
+// multiple of 128; a.split_base / split_rem are recomputed as stage ranges
+hipError_t launch_attn_mfma128_fused(const ValuArgs& a, const FusedArgs& f, int head_dim, dim3 grid,
+                                     hipStream_t stream);
 // both cascade passes in one grid (grid.x = G units per KV head): prefix args
 // ap as for the MFMA prefix pass, suffix args as as for the shared-out suffix
 // pass with bal_units 0 (set per workgroup), ns_total = G in both

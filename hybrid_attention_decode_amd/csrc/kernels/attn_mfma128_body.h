@@ -41,6 +41,7 @@
 //    flushes to zero); row sums of the bf16 probabilities by v_dot2.
 #pragma once
 #include "attn_mfma_body.h"
+#include "prologue_math.h"
 
 namespace had {
 namespace {
@@ -78,6 +79,75 @@ template <int D>
 struct M128Store {
   M128Lds<D> m;
 };
+
+// The prologue run inline (the layer entry point: QK-RMSNorm, partial
+// rotation and gate split of the new tokens; zubnet.ai TokenSpeed article,
+// second paragraph).  Every workgroup normalises and rotates its own query
+// rows straight into their B-operand registers; the workgroup whose stages
+// hold the last position also normalises and rotates the new keys, writes
+// the new K/V rows to the pools and adds the new tokens to its partial from
+// the copies below (every split's loads stop before the new positions, so
+// no workgroup reads a row while it is written).  Extra LDS: cos / sin of
+// every new position and rotation pair, the two norm weights, the new rows.
+constexpr int kM128New = 8;  // new tokens per sequence, at most
+
+template <int D>
+struct M128Pro {
+  float cs[kM128New][D / 2];
+  float sn[kM128New][D / 2];
+  float wq[D];
+  float wk[D];
+  uint16_t knew[kM128New][D] __attribute__((aligned(16)));
+  uint16_t vnew[kM128New][D] __attribute__((aligned(16)));
+};
+
+template <int D>
+struct M128FusedStore {
+  M128Lds<D> m;
+  M128Pro<D> f;
+};
+
+// One query row in the B-operand layout of S^T = K Q^T (this lane: dims
+// 32 ks + 8 g + e, packed bf16 pairs in qb[ks]) normalised with inv and the
+// weights w, then rotated below dim 64 HK: pair i = d mod 32 HK, partner in
+// k-step ks +- HK of the same lane, cos / sin cs[i], sn[i].  Element by
+// element the arithmetic of row_norm_rope_cs (prologue_math.h); only the
+// norm's sum of squares runs in this layout's order.
+template <int D, int HK>
+__device__ __forceinline__ void m128_q_rope(u32x4_t (&qb)[D / 32], float inv, const float* w, const float* cs,
+                                            const float* sn, int g) {
+  constexpr int KS = D / 32;
+  if constexpr (2 * HK <= KS) {
+    float y[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wd = qb[ks][e / 2];
+        const float x = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+        y[ks][e] = x * inv * w[32 * ks + 8 * g + e];
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        r[e] = y[ks][e];
+        if constexpr (HK > 0) {
+          if (ks < 2 * HK) {
+            const int i = 32 * (ks % HK) + 8 * g + e;
+            if (ks < HK)
+              r[e] = y[ks][e] * cs[i] - y[ks + HK < KS ? ks + HK : KS - 1][e] * sn[i];
+            else
+              r[e] = y[ks][e] * cs[i] + y[ks >= HK ? ks - HK : 0][e] * sn[i];
+          }
+        }
+      }
+      qb[ks] = u32x4_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                       pack_bf16x2(r[6], r[7])};
+    }
+  }
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) const char lds_cchar_t;
@@ -181,8 +251,12 @@ __device__ __forceinline__ void lds_read_tr4(u32x4_t (&va)[4], const char* lo, c
 // (its n_pages_plan pages from pg_begin), not pages: split sp takes stages
 // sp * base + min(sp, rem) .. + base (+1 while sp < rem), so the splits are
 // balanced to within one stage and a split may start and end inside a page.
-template <int D, int DH, class Store = M128Store<D>>
-__device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp, const int h, const int s) {
+// FUSED: the prologue inline (Store = M128FusedStore<D>, inputs in f; a.q
+// unused), for the rows of one launch (row_base 0) and q_len <= kM128New,
+// with R = 0, 64 or a multiple of 128 (the host checks).
+template <int D, int DH, class Store = M128Store<D>, bool FUSED = false>
+__device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp, const int h, const int s,
+                                                const FusedArgs& f = FusedArgs{}) {
   static_assert(DH == 1 || DH == 2, "rows per wave group");
   M128Lds<D>& sh = g_lds<Store>.m;
   using C = M128Cfg<D, DH>;
@@ -227,9 +301,37 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   u32x4_t qb[C::KS];
   {
     const int rc = row_ok ? rr : 0;
-    const uint16_t* qp = a.q + ((static_cast<size_t>(s_row) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G) * D;
+    const size_t hd = (static_cast<size_t>(s_row) * a.q_len + rc / a.G) * a.H_q + h * a.G + rc % a.G;
+    // (fused: the raw row, the q half of qg)
+    const uint16_t* qp = FUSED ? f.qg + hd * 2 * D : a.q + hd * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qb[ks] = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g);
+  }
+  // fused: the norm weights (a float4 per thread, staged through LDS), the
+  // raw K/V row of new token min(wave, q_len - 1) (lane l: dims l + 64 m),
+  // and the gate block of the launch's rows (16-byte chunks, copied by
+  // split 0) -- all unconditional, indexes clamped
+  constexpr int E = D / 64;
+  constexpr int NGC = (16 * NRG) * (D / 8) / (64 * kM128Waves);  // gate chunks per thread
+  static_assert(NGC >= 1 && (16 * NRG) * (D / 8) % (64 * kM128Waves) == 0, "gate chunks cover the rows");
+  [[maybe_unused]] float4 w_st{};
+  [[maybe_unused]] uint16_t k_raw[E], v_raw[E];
+  [[maybe_unused]] u32x4_t gate_ch[NGC];
+  if constexpr (FUSED) {
+    w_st = reinterpret_cast<const float4*>(tid < D / 4 ? f.w_q : f.w_k)[tid % (D / 4)];
+    const size_t kr = ((static_cast<size_t>(s) * a.q_len + min(wave, a.q_len - 1)) * a.H_kv + h) * D;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      k_raw[m] = f.k_new[kr + lane + 64 * m];
+      v_raw[m] = f.v_new[kr + lane + 64 * m];
+    }
+#pragma unroll
+    for (int c = 0; c < NGC; ++c) {
+      const int ch = tid + 64 * kM128Waves * c;
+      const int r = min(ch / (D / 8), a.rows - 1);
+      const size_t hd = (static_cast<size_t>(s) * a.q_len + r / a.G) * a.H_q + h * a.G + r % a.G;
+      gate_ch[c] = *reinterpret_cast<const u32x4_t*>(f.qg + hd * 2 * D + D + 8 * (ch % (D / 8)));
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // the scalar results are needed from here on
@@ -241,15 +343,19 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   // pg_begin; a length past the plan's pages would leave tokens no split reads)
   const bool bad_len = a.fixed_len < 0 && (L - a.q_len < a.pg_begin * P || L < a.q_len || L > a.max_pages * P ||
                                            L > (a.pg_begin + a.n_pages_plan) * P);
-  const int tok_end = bad_len ? tok0 : max(min(tok_plan_end, L), tok0);  // this split's tokens: [tok0, tok_end)
+  // fused: the loads stop before the new positions, and the split whose
+  // stages hold the last position owns the new tokens
+  const int kv_end = FUSED ? L - a.q_len : L;
+  const bool own = FUSED && !bad_len && L - 1 >= tok0 && L - 1 < tok_plan_end;
+  const int tok_end = bad_len ? tok0 : max(min(tok_plan_end, kv_end), tok0);  // this split's tokens: [tok0, tok_end)
   const int npg = tok_end > tok0 ? (tok_end - 1) / P - pg0 + 1 : 0;     // pages holding them
   const int n_it = (tok_end - tok0 + kM128Tok - 1) / kM128Tok;
   int errs = (bad_len && tid == 0) ? HAD_DERR_SEQLEN : 0;
   // visible keys of this lane's row (causal inside the draft; a prefix pass
   // sees the whole prefix), and the bound below which every row sees every
   // split token
-  const int lim = (row_ok && a.fixed_len < 0) ? (L - a.q_len + rr / a.G + 1) : L;
-  const int vis_all = min(tok_end, a.fixed_len >= 0 ? L : L - a.q_len + 1);
+  const int lim = FUSED ? kv_end : (row_ok && a.fixed_len < 0) ? (L - a.q_len + rr / a.G + 1) : L;
+  const int vis_all = min(tok_end, FUSED ? kv_end : a.fixed_len >= 0 ? L : L - a.q_len + 1);
   const int last_pg = max(npg - 1, 0);
 
   // LDS loads of stage it into buffer b, page id pid (-1: out of range),
@@ -313,8 +419,12 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
       ++nx_pg;
     }
   };
+  // (fused: only the first stage before the setup barrier -- the setup's
+  // small loads of the raw q rows, the gate block and the weights return
+  // sooner behind a smaller burst -- and the others right after it)
+  constexpr int NE = FUSED ? 1 : NB - 1;
 #pragma unroll
-  for (int r = 0; r < NB - 1; ++r) {
+  for (int r = 0; r < NE; ++r) {
     issue(r, r, (pid0[r] >= 0 && pid0[r] < a.num_pages) ? pid0[r] : -1, nx_pg, nx_off);
     step();
   }
@@ -330,14 +440,106 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
     const bool wb = __any(errs & HAD_DERR_PAGE);
     if (lane == 0) sh.badw[wave] = wb;
   }
+  if constexpr (FUSED) {
+    // cos / sin of pair i at new position t, and the norm weights -> LDS
+    M128Pro<D>& F = g_lds<Store>.f;
+    const int half = f.R / 2;
+    for (int e = tid; e < a.q_len * half; e += 64 * kM128Waves) {
+      const int t = e / half, i = e - t * half;
+      rope_cs(L - a.q_len + t, i, f.rope_coef, F.cs[t][i], F.sn[t][i]);
+    }
+    if (tid < D / 2) *reinterpret_cast<float4*>((tid < D / 4 ? F.wq : F.wk) + 4 * (tid % (D / 4))) = w_st;
+  }
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) qb[ks] = row_ok ? qb[ks] : u32x4_t{0u, 0u, 0u, 0u};
   m128_barrier<63>();  // the page list is in LDS; the first stages stay in flight
+#pragma unroll
+  for (int r = NE; r < NB - 1; ++r) {
+    issue(r, r, (pid0[r] >= 0 && pid0[r] < a.num_pages) ? pid0[r] : -1, nx_pg, nx_off);
+    step();
+  }
   // the scores of a stage whose page id is out of range are dropped (its K
   // and V read as zeros)
   int any_bad = 0;
 #pragma unroll
   for (int w = 0; w < kM128Waves; ++w) any_bad |= sh.badw[w];
+  if constexpr (FUSED) {
+    M128Pro<D>& F = g_lds<Store>.f;
+    // this lane's query row: RMSNorm over the four lanes of the row, rotation
+    const int jq = (row_ok ? rr : 0) / a.G;
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float lo = bf16_lo(qb[ks][w]), hi = bf16_hi(qb[ks][w]);
+        ss += lo * lo;
+        ss += hi * hi;
+      }
+    ss = sum_xor32(sum_xor16(ss));
+    const float inv = 1.f / sqrtf(ss / static_cast<float>(D) + f.eps);
+    const float* cs = F.cs[min(jq, kM128New - 1)];
+    const float* sn = F.sn[min(jq, kM128New - 1)];
+    switch (f.R / 64) {  // k-steps between rotation partners (R = 0, 64, 128 or 256)
+      case 0: m128_q_rope<D, 0>(qb, inv, F.wq, cs, sn, g); break;
+      case 1: m128_q_rope<D, 1>(qb, inv, F.wq, cs, sn, g); break;
+      case 2: m128_q_rope<D, 2>(qb, inv, F.wq, cs, sn, g); break;
+      default: m128_q_rope<D, 4>(qb, inv, F.wq, cs, sn, g); break;
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qb[ks] = row_ok ? qb[ks] : u32x4_t{0u, 0u, 0u, 0u};
+    // split 0: q (one wave of each pair) and the gate half to the outputs
+    if (sp == 0) {
+      if (f.q_out && row_ok && dh == 0) {
+        const size_t hd = (static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + rr % a.G;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) *reinterpret_cast<u32x4_t*>(f.q_out + hd * D + 32 * ks + 8 * g) = qb[ks];
+      }
+#pragma unroll
+      for (int c = 0; c < NGC; ++c) {
+        const int ch = tid + 64 * kM128Waves * c, r = ch / (D / 8);
+        if (r < a.rows) {
+          const size_t hd = (static_cast<size_t>(s) * a.q_len + r / a.G) * a.H_q + h * a.G + r % a.G;
+          *reinterpret_cast<u32x4_t*>(f.gate_out + hd * D + 8 * (ch % (D / 8))) = gate_ch[c];
+        }
+      }
+    }
+    // the owner: new key `wave` normalised and rotated (the prologue's own
+    // row arithmetic, so the pool rows equal the prologue kernel's bits),
+    // into LDS and, with V, into the pools
+    if (own && wave < a.q_len) {
+      const int pid_new = pt_row[min(L - a.q_len + wave, a.max_pages * P - 1) / P];  // (L >= q_len when own)
+      RowIn<D> kin;
+      float cs_e[E], sn_e[E];
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const int d = lane + 64 * m;
+        kin.x[m] = k_raw[m];
+        kin.w[m] = F.wk[d];
+        cs_e[m] = 1.f;
+        sn_e[m] = 0.f;
+        if (64 * m < f.R && d < f.R) {
+          cs_e[m] = F.cs[wave][d % (f.R / 2)];
+          sn_e[m] = F.sn[wave][d % (f.R / 2)];
+        }
+      }
+      uint16_t y[E];
+      row_norm_rope_cs<D>(kin, cs_e, sn_e, f.R, f.eps, nullptr, lane, y);
+      const int pos = L - a.q_len + wave;
+      const bool pok = pid_new >= 0 && pid_new < a.num_pages;
+      const size_t dst = ((static_cast<size_t>(pok ? pid_new : 0) * a.H_kv + h) * P + pos % P) * D;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        F.knew[wave][lane + 64 * m] = y[m];
+        F.vnew[wave][lane + 64 * m] = v_raw[m];
+        if (pok) {
+          f.k_pool[dst + lane + 64 * m] = y[m];
+          f.v_pool[dst + lane + 64 * m] = v_raw[m];
+        }
+      }
+      if (!pok && lane == 0) errs |= HAD_DERR_PAGE;
+    }
+  }
 
   f32x4_t o[C::MB];
 #pragma unroll
@@ -475,6 +677,56 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   if (errs) atomicOr(&sh.err, errs);
   __syncthreads();
   if (tid == 0 && sh.err) set_err(a.d_err, sh.err);
+  if constexpr (FUSED) {
+    // the owner adds the new tokens (causal inside the draft: row rr's
+    // token rr / G sees new tokens 0 .. rr / G) from the LDS copies; the
+    // four lanes of a row form the same scores, so m and l stay row-uniform
+    if (own && wave_active) {
+      M128Pro<D>& F = g_lds<Store>.f;
+      const int jq = (row_ok ? rr : 0) / a.G;
+      float sc[kM128New];
+      float mx = m_run;
+#pragma unroll
+      for (int t = 0; t < kM128New; ++t) {
+        float dsum = 0.f;
+        if (t < a.q_len) {
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(&F.knew[t][32 * ks + 8 * g]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) dsum = dot2_bf16(qb[ks][w], kv[w], dsum);
+          }
+          dsum = sum_xor32(sum_xor16(dsum));
+        }
+        sc[t] = (t < a.q_len && t <= jq) ? dsum * sl2 : -INFINITY;
+        mx = fmaxf(mx, sc[t]);
+      }
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+      float pt[kM128New], lsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < kM128New; ++t) {
+        pt[t] = (sc[t] == -INFINITY) ? 0.f : bf16_to_f32(f32_to_bf16(__builtin_amdgcn_exp2f(sc[t] - mx)));
+        lsum += pt[t];
+      }
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) o[mb] = o[mb] * alpha;
+#pragma unroll
+      for (int t = 0; t < kM128New; ++t) {
+        if (t < a.q_len) {
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) {
+            const uint2 vv = *reinterpret_cast<const uint2*>(&F.vnew[t][16 * (C::MB * dh + mb) + 4 * g]);
+            o[mb][0] += pt[t] * bf16_lo(vv.x);
+            o[mb][1] += pt[t] * bf16_hi(vv.x);
+            o[mb][2] += pt[t] * bf16_lo(vv.y);
+            o[mb][3] += pt[t] * bf16_hi(vv.y);
+          }
+        }
+      }
+      m_run = mx;
+    }
+  }
   if (row_ok) {
     const size_t unit = (static_cast<size_t>(s_row) * a.H_kv + h) * a.ns_total + a.split_offset + sp;
     float* op = a.ws_o + (unit * a.ws_rows + rr) * D + 16 * C::MB * dh;

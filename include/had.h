@@ -514,13 +514,19 @@ int had_decode_attn_cascade_combine(const had_attn_desc *d, const had_attn_prefi
  * rows, the unit whose split holds the last position normalises and rotates
  * the T new keys, writes the new K/V rows to the pools and adds the new
  * tokens to its partial from on-chip copies; then the usual merge writes
- * out.  At 16 rows or more (the MFMA path) every unit would redo many rows'
- * prologue, so it runs once as had_qk_norm_rope_gate, writing q to
- * pp->q_out or, when that is NULL, to the workspace's ws_q block.
+ * out.  The same holds at 16..128 rows on the MFMA path when pages hold a
+ * multiple of 32 tokens (16..64 rows only at head_dim >= 128), the rotary
+ * dims are 0, 64 or a multiple of 128, and qg, w_q, w_k, gate_out and q_out
+ * are 16-byte aligned: every unit forms its query rows in the MFMA operand
+ * registers.  Other MFMA shapes run the prologue once as
+ * had_qk_norm_rope_gate, writing q to pp->q_out or, when that is NULL, to
+ * the workspace's ws_q block.
  *
  * Results: out as had_decode_attn with q = the q_out of had_qk_norm_rope_gate
- * (same bits for q; the attention sums differ in order only); gate_out, the
- * pools and (when non-NULL) q_out as had_qk_norm_rope_gate.
+ * (the attention sums differ in order only); gate_out, the pools and (when
+ * non-NULL) q_out as had_qk_norm_rope_gate -- the same bits, except that
+ * where the MFMA path forms q inline the RMSNorm's fp32 sum of squares runs
+ * in another order, so an element of q may differ by one bf16 ulp.
  *
  * d and pd describe the same layer (n_seqs, T = q_len, heads, head_dim, pool
  * geometry must agree, else HAD_ERR_INVALID_ARG); pp supplies every pointer

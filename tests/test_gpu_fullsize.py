@@ -207,19 +207,32 @@ def test_speculative_verify_rollback_256k():
     qg, k, v, w_q, w_k = _prologue_inputs(seed, 1, T, H_q)
     gq, gk, gv, gal, gbe = _gdn_inputs(seed, 1, T)
     pt_d, lens_d = to_dev(table), to_dev(lens)
-    q_out, _ = had.qk_norm_rope_gate(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), pt_d, lens_d, kd, vd,
-                                     R, BASE, EPS, d_err=err)
-    out1 = had.decode_attn(q_out, kd, vd, pt_d, lens_d, max_seq_len=L0 + 2 * T, d_err=err)
+    # the benchmark's call: had_decode_attn_layer with the prologue inside
+    # the MFMA partial, gated output, 256 splits
+    q_out = torch.empty((1, T, H_q, D), dtype=torch.bfloat16, device=DEV)
+    out1, gate1 = had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), pt_d, lens_d, kd,
+                                        vd, R, BASE, EPS, max_seq_len=L0 + 2 * T, q_out=q_out, d_err=err, gated=True)
     o1 = had.gdn_state_update(pool_d, to_dev(np.array([cur], np.int32)), to_dev(np.array([outs], np.int32)),
                               to_dev(gq), to_dev(gk), to_dev(gv), to_dev(gal), to_dev(gbe), d_err=err)
     torch.cuda.synchronize()
     assert err.item() == 0
+    assert had.decode_attn_plan(had.attn_desc((1, T, H_q, D), tuple(kd.shape), max_pages, max_seq_len=L0 + 2 * T,
+                                              gated=True))[0] == 256
     ckpt = pool_d.cpu().numpy()
 
     q_ref, k_new, v_new = _oracle_prologue(qg, k, v, w_q, w_k, 0, np.arange(L0, L0 + T))
+    # q, the gate and the new K/V rows (q and k within 1 bf16 ulp of the fp64
+    # value, the gate and v bit-exact)
+    assert np.all(np.abs(bf16.to_f64(bits_of(q_out)[0]) - q_ref) <= bf16.ulp(q_ref))
+    assert np.array_equal(bits_of(gate1)[0], bits_of(qg)[0, :, :, 1])
+    kb1, vb1 = bits_of(kd), bits_of(vd)
+    for t in range(T):
+        page, row = pages1[(L0 + t) // P], (L0 + t) % P
+        assert np.all(np.abs(bf16.to_f64(kb1[page, :, row]) - k_new[t]) <= bf16.ulp(k_new[t]))
+        assert np.array_equal(vb1[page, :, row], bits_of(v)[0, t])
     K0, V0 = _context(kb, vb, pages1, L0)
     ref1 = A.attention(q_ref, np.concatenate([K0, k_new]), np.concatenate([V0, v_new]), scale)
-    assert_attn_close(out1[0], ref1)
+    assert_attn_close(out1[0], Pr.output_gate(ref1, bf16.to_f64(bits_of(qg)[0, :, :, 1])))
     S = pool0[cur].astype(np.float64)
     for t in range(T):
         S, o_ref = gdn.sequential_heads(S, _gdn_f64(gq)[0, t:t + 1], _gdn_f64(gk)[0, t:t + 1], _gdn_f64(gv)[0, t:t + 1],

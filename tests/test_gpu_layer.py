@@ -106,15 +106,21 @@ def test_new_tokens_straddle_splits(H_q):
     _check_against_oracle(c)
 
 
-# 16 to 64 rows at head_dim >= 128 with pages of a multiple of 32 tokens:
-# the prologue kernel, then the MFMA partial that loads K and V straight
-# into LDS with wave pairs
+# The MFMA partial that loads K and V straight into LDS (pages of a
+# multiple of 32 tokens; 16..64 rows at head_dim >= 128 with wave pairs,
+# 65..128 rows with a wave per 16 rows): with the prologue inside it when
+# the rotary dims are 0, 64 or a multiple of 128, else after the prologue
+# kernel (32 rotary dims below)
 @pytest.mark.parametrize("lens,T,H_q,H_kv,D,R,P", [
     ([3000, 41], 2, 16, 1, 128, 128, 32),     # 32 rows, whole head rotated, a 41-token sequence
     ([5000], 8, 8, 1, 256, 64, 96),           # 8 new tokens (one per wave), 96-token pages
     ([1000, 700], 4, 4, 1, 256, 256, 64),     # 16 rows: one wave pair
-    ([900], 3, 16, 2, 128, 32, 32),           # 48 rows per KV head, two KV heads, 32 rotary dims
+    ([900], 3, 16, 2, 128, 32, 32),           # 48 rows per KV head, two KV heads, 32 rotary dims (prologue kernel)
     ([32 * 10 + 3], 4, 16, 1, 256, 64, 32),   # the new tokens across a page boundary
+    ([600], 4, 20, 1, 128, 64, 32),           # 80 rows, a wave per 16 rows
+    ([400, 90], 8, 16, 1, 64, 64, 32),        # 128 rows at head_dim 64
+    ([2000], 4, 16, 1, 256, 0, 64),           # no rotation
+    ([700, 300], 2, 32, 2, 256, 128, 64),     # 64 rows per KV head, two KV heads, 128 rotary dims
 ])
 def test_mfma_layer_matches_oracle(lens, T, H_q, H_kv, D, R, P):
     c = _run(3100 + sum(lens) % 997 + T, lens, T, H_q, H_kv, D, R, P)
@@ -137,8 +143,13 @@ def test_mfma_layer_matches_two_call_path():
                                    to_dev(c["w_k"]), to_dev(c["pt"]), to_dev(c["L"]), kd2, vd2, R)
     out2 = had.decode_attn(q2, kd2, vd2, to_dev(c["pt"]), to_dev(c["L"]), deterministic=True)
     torch.cuda.synchronize()
-    # the prologue arithmetic is shared: q, gate and the written pools agree bit for bit
-    assert np.array_equal(bits_of(c["q_out"]), bits_of(q2))
+    # the layer runs the prologue inside the MFMA partial (q rows in the
+    # MFMA operand layout): the gate and the written pools agree bit for bit
+    # (the keys use the prologue kernel's own row arithmetic); q within one
+    # bf16 ulp, since the norm's fp32 sum of squares runs in another order
+    qa, qb = bf16.to_f64(bits_of(c["q_out"])), bf16.to_f64(bits_of(q2))
+    assert np.all(np.abs(qa - qb) <= bf16.ulp(qb))
+    assert np.mean(qa != qb) < 0.01
     assert np.array_equal(bits_of(c["gate"]), bits_of(g2))
     assert np.array_equal(bits_of(c["kd"]), bits_of(kd2), equal_nan=True)
     assert np.array_equal(bits_of(c["vd"]), bits_of(vd2), equal_nan=True)
@@ -146,17 +157,22 @@ def test_mfma_layer_matches_two_call_path():
     assert np.abs(a - b).max() <= 4e-3
 
 
-def test_mfma_layer_bad_new_token_page_is_reported():
+@pytest.mark.parametrize("R", [32, 64])
+def test_mfma_layer_bad_new_token_page_is_reported(R):
+    # (R = 32: the prologue kernel; R = 64: the prologue inside the partial)
     _, k_pool, v_pool, pt, L = paged_case(3400, [200], 4, 16, 1, 128, 32)
     pt = pt.copy()
     pt[0, 199 // 32] = 10 ** 6                     # the page of the new tokens: out of range
     qg, k, v, w_q, w_k = _inputs(3400, 1, 4, 16, 1, 128)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    print("case bad new-token page (MFMA, 64 rows)", flush=True)
+    kd, vd = to_dev(k_pool), to_dev(v_pool)
+    print("case bad new-token page (MFMA, 64 rows, R=%d)" % R, flush=True)
     had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L),
-                          to_dev(k_pool), to_dev(v_pool), 32, d_err=err)
+                          kd, vd, R, d_err=err)
     torch.cuda.synchronize()
     assert err.item() & had.DERR_PAGE
+    assert np.array_equal(bits_of(kd), bits_of(k_pool), equal_nan=True)   # nothing written
+    assert np.array_equal(bits_of(vd), bits_of(v_pool), equal_nan=True)
 
 
 @pytest.mark.parametrize("L,num_splits", [(666, 7), (643, 13), (700, 5)])
@@ -232,8 +248,13 @@ def test_fused_matches_two_call_path():
                                    to_dev(c["w_k"]), to_dev(c["pt"]), to_dev(c["L"]), kd2, vd2, R)
     out2 = had.decode_attn(q2, kd2, vd2, to_dev(c["pt"]), to_dev(c["L"]), deterministic=True)
     torch.cuda.synchronize()
-    # the prologue arithmetic is shared: q, gate and the written pools agree bit for bit
-    assert np.array_equal(bits_of(c["q_out"]), bits_of(q2))
+    # the layer runs the prologue inside the MFMA partial (q rows in the
+    # MFMA operand layout): the gate and the written pools agree bit for bit
+    # (the keys use the prologue kernel's own row arithmetic); q within one
+    # bf16 ulp, since the norm's fp32 sum of squares runs in another order
+    qa, qb = bf16.to_f64(bits_of(c["q_out"])), bf16.to_f64(bits_of(q2))
+    assert np.all(np.abs(qa - qb) <= bf16.ulp(qb))
+    assert np.mean(qa != qb) < 0.01
     assert np.array_equal(bits_of(c["gate"]), bits_of(g2))
     assert np.array_equal(bits_of(c["kd"]), bits_of(kd2), equal_nan=True)
     assert np.array_equal(bits_of(c["vd"]), bits_of(vd2), equal_nan=True)
@@ -289,18 +310,20 @@ def test_length_beyond_the_split_plan_is_reported_and_writes_nothing():
     assert err.item() & had.DERR_SEQLEN
     assert np.array_equal(bits_of(kd), bits_of(k_pool), equal_nan=True)
     assert np.array_equal(bits_of(vd), bits_of(v_pool), equal_nan=True)
-    # the same on the MFMA path (64 rows)
-    _, k_pool, v_pool, pt, L = paged_case(2902, [1000], 4, 16, 1, 128, 64)
-    qg, k, v, w_q, w_k = _inputs(2902, 1, 4, 16, 1, 128)
-    kd, vd = to_dev(k_pool), to_dev(v_pool)
-    err.zero_()
-    print("case length past the plan (MFMA layer, 64 rows)", flush=True)
-    had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L), kd, vd,
-                          32, max_seq_len=900, d_err=err)
-    torch.cuda.synchronize()
-    assert err.item() & had.DERR_SEQLEN
-    assert np.array_equal(bits_of(kd), bits_of(k_pool), equal_nan=True)
-    assert np.array_equal(bits_of(vd), bits_of(v_pool), equal_nan=True)
+    # the same on the MFMA path (64 rows; the prologue kernel at 32 rotary
+    # dims, the prologue inside the partial at 64)
+    for R in (32, 64):
+        _, k_pool, v_pool, pt, L = paged_case(2902, [1000], 4, 16, 1, 128, 64)
+        qg, k, v, w_q, w_k = _inputs(2902, 1, 4, 16, 1, 128)
+        kd, vd = to_dev(k_pool), to_dev(v_pool)
+        err.zero_()
+        print("case length past the plan (MFMA layer, 64 rows, R=%d)" % R, flush=True)
+        had.decode_attn_layer(to_dev(qg), to_dev(k), to_dev(v), to_dev(w_q), to_dev(w_k), to_dev(pt), to_dev(L), kd,
+                              vd, R, max_seq_len=900, d_err=err)
+        torch.cuda.synchronize()
+        assert err.item() & had.DERR_SEQLEN
+        assert np.array_equal(bits_of(kd), bits_of(k_pool), equal_nan=True)
+        assert np.array_equal(bits_of(vd), bits_of(v_pool), equal_nan=True)
     # the plain call, VALU (8 rows) and MFMA (64 rows), reports it too
     for H_q, q_len in ((8, 1), (16, 4)):
         q, kp, vp, pt2, L2 = paged_case(2901 + H_q, [1000], q_len, H_q, 1, 128, 64)
