@@ -153,8 +153,8 @@ def test_gdn_prefill_replays_equal_eager_runs(n_segments):
 
 
 def test_speculative_layer_replays_equal_eager_runs():
-    # 16 query heads x 4 drafts per KV head: prologue kernel + MFMA partials
-    # + combine, gated output; 3 replays at different lengths
+    # 16 query heads x 4 drafts per KV head: the MFMA partial with the
+    # prologue inside + combine, gated output; 3 replays at different lengths
     P, H_q, H_kv, D, R, T = 64, 16, 1, 256, 64, 4
     L0 = 2500
     _, k_pool, v_pool, pt, _ = paged_case(7100, [L0 + 3 * T], 1, H_q, H_kv, D, P)
