@@ -85,6 +85,24 @@ def test_batch_with_shared_input_slot_and_zero_state():
     _run_and_check(4, 3, 1, 2, 128, 64, 10, [4, 4, -1], [[1], [2], [9]])
 
 
+# grids of 1024 waves or more run four waves per workgroup: a batch of 16
+# sequences x 8 heads of 128 x 128 (permuted slots, as the prefix-shared
+# batch), 4 drafts x 4 sequences, d_v 64 and d_k 64
+@pytest.mark.parametrize("seed,S,T,H,dk,dv", [
+    (11, 16, 1, 8, 128, 128),
+    (12, 4, 4, 8, 128, 128),
+    (13, 16, 1, 4, 128, 64),
+    (14, 32, 1, 2, 64, 64),
+])
+def test_batch_grids_with_four_waves_per_workgroup(seed, S, T, H, dk, dv):
+    assert S * H * (dv // 4) >= 1024
+    n_slots = S * (T + 1) + 2
+    perm = synth.permutation(n_slots, synth.seed_of(seed, 60))
+    in_idx = perm[:S].tolist()
+    out_idx = perm[S:S + S * T].reshape(S, T).tolist()
+    _run_and_check(seed, S, T, H, dk, dv, n_slots, in_idx, out_idx)
+
+
 def test_in_place_single_token():
     _run_and_check(5, 1, 1, 2, 64, 128, 3, [1], [[1]])
 
