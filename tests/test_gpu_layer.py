@@ -121,6 +121,8 @@ def test_new_tokens_straddle_splits(H_q):
     ([400, 90], 8, 16, 1, 64, 64, 32),        # 128 rows at head_dim 64
     ([2000], 4, 16, 1, 256, 0, 64),           # no rotation
     ([700, 300], 2, 32, 2, 256, 128, 64),     # 64 rows per KV head, two KV heads, 128 rotary dims
+    ([4, 300], 4, 16, 1, 128, 64, 32),        # a context of the new tokens only, next to a longer one
+    ([97], 1, 16, 1, 128, 128, 32),           # 16 rows, one new token
 ])
 def test_mfma_layer_matches_oracle(lens, T, H_q, H_kv, D, R, P):
     c = _run(3100 + sum(lens) % 997 + T, lens, T, H_q, H_kv, D, R, P)

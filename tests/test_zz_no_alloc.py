@@ -31,19 +31,22 @@ def _layer_inputs(seed, L, T, H_q, D, P):
 
 @pytest.mark.parametrize("gated", [False, True])
 def test_static_workspace_layer_equals_caller_workspace_layer(gated):
-    R = 64
-    # (seed, context incl. new tokens, new tokens, query heads, head_dim, page size): larger first
-    cases = [(9100, 20000, 4, 16, 256, 64), (9101, 9000, 1, 8, 256, 64), (9102, 700, 1, 8, 128, 16)]
-    for seed, L, T, H_q, D, P in cases:
-        print("case static workspace: L=%d T=%d H_q=%d D=%d gated=%d" % (L, T, H_q, D, gated), flush=True)
+    # (seed, context incl. new tokens, new tokens, query heads, head_dim, page size, rotary dims): larger
+    # first; 64 rows with 64 rotary dims run the prologue inside the MFMA partial, with 32 as its own
+    # kernel writing q to the workspace's q block
+    cases = [(9100, 20000, 4, 16, 256, 64, 64), (9103, 12000, 4, 16, 256, 64, 32), (9101, 9000, 1, 8, 256, 64, 64),
+             (9102, 700, 1, 8, 128, 16, 64)]
+    for seed, L, T, H_q, D, P, R in cases:
+        print("case static workspace: L=%d T=%d H_q=%d D=%d R=%d gated=%d" % (L, T, H_q, D, R, gated), flush=True)
         qg, k, v, w_q, w_k, kd, vd, pt, lens = _layer_inputs(seed, L, T, H_q, D, P)
         kd2, vd2 = kd.clone(), vd.clone()
         err = torch.zeros(1, dtype=torch.int32, device=DEV)
         out_a = torch.empty((1, T, H_q, D), dtype=torch.bfloat16, device=DEV)
         gate_a = torch.empty_like(out_a)
         out_b, gate_b = torch.empty_like(out_a), torch.empty_like(out_a)
-        # at 16 rows or more the prologue's q goes to the workspace's q block
-        # unless the caller asks for it: leave it there on the MFMA case
+        # at 16 rows or more q is written only when the caller asks for it
+        # (where the prologue runs as its own kernel it goes to the
+        # workspace's q block instead): leave q_out unset on the MFMA cases
         mfma = T * H_q >= 16
         q_a = None if mfma else torch.empty_like(out_a)
         q_b = None if mfma else torch.empty_like(out_a)
