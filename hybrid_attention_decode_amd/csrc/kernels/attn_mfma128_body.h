@@ -309,10 +309,12 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
   }
   // fused: the norm weights (a float4 per thread, staged through LDS), the
   // raw K/V row of new token min(wave, q_len - 1) (lane l: dims l + 64 m),
-  // and the gate block of the launch's rows (16-byte chunks, copied by
-  // split 0) -- all unconditional, indexes clamped
+  // and this split's share of the gate block of the launch's rows (16-byte
+  // chunks sp, sp + ns, sp + 2 ns, ...: every split copies a few, rather
+  // than every split loading the whole block for split 0 to copy) -- all
+  // unconditional, indexes clamped
   constexpr int E = D / 64;
-  constexpr int NGC = (16 * NRG) * (D / 8) / (64 * kM128Waves);  // gate chunks per thread
+  constexpr int NGC = (16 * NRG) * (D / 8) / (64 * kM128Waves);  // gate chunks per thread, at most
   static_assert(NGC >= 1 && (16 * NRG) * (D / 8) % (64 * kM128Waves) == 0, "gate chunks cover the rows");
   [[maybe_unused]] float4 w_st{};
   [[maybe_unused]] uint16_t k_raw[E], v_raw[E];
@@ -327,8 +329,8 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
     }
 #pragma unroll
     for (int c = 0; c < NGC; ++c) {
-      const int ch = tid + 64 * kM128Waves * c;
-      const int r = min(ch / (D / 8), a.rows - 1);
+      const int ch = min(sp + a.num_splits * (tid + 64 * kM128Waves * c), a.rows * (D / 8) - 1);
+      const int r = ch / (D / 8);
       const size_t hd = (static_cast<size_t>(s) * a.q_len + r / a.G) * a.H_q + h * a.G + r % a.G;
       gate_ch[c] = *reinterpret_cast<const u32x4_t*>(f.qg + hd * 2 * D + D + 8 * (ch % (D / 8)));
     }
@@ -488,20 +490,19 @@ __device__ __forceinline__ void mfma128_partial(const ValuArgs& a, const int sp,
     }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qb[ks] = row_ok ? qb[ks] : u32x4_t{0u, 0u, 0u, 0u};
-    // split 0: q (one wave of each pair) and the gate half to the outputs
-    if (sp == 0) {
-      if (f.q_out && row_ok && dh == 0) {
-        const size_t hd = (static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + rr % a.G;
+    // split 0: q (one wave of each pair) to the optional output; every
+    // split: its gate chunks
+    if (sp == 0 && f.q_out && row_ok && dh == 0) {
+      const size_t hd = (static_cast<size_t>(s) * a.q_len + jq) * a.H_q + h * a.G + rr % a.G;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) *reinterpret_cast<u32x4_t*>(f.q_out + hd * D + 32 * ks + 8 * g) = qb[ks];
-      }
+      for (int ks = 0; ks < C::KS; ++ks) *reinterpret_cast<u32x4_t*>(f.q_out + hd * D + 32 * ks + 8 * g) = qb[ks];
+    }
 #pragma unroll
-      for (int c = 0; c < NGC; ++c) {
-        const int ch = tid + 64 * kM128Waves * c, r = ch / (D / 8);
-        if (r < a.rows) {
-          const size_t hd = (static_cast<size_t>(s) * a.q_len + r / a.G) * a.H_q + h * a.G + r % a.G;
-          *reinterpret_cast<u32x4_t*>(f.gate_out + hd * D + 8 * (ch % (D / 8))) = gate_ch[c];
-        }
+    for (int c = 0; c < NGC; ++c) {
+      const int ch = sp + a.num_splits * (tid + 64 * kM128Waves * c), r = ch / (D / 8);
+      if (r < a.rows) {
+        const size_t hd = (static_cast<size_t>(s) * a.q_len + r / a.G) * a.H_q + h * a.G + r % a.G;
+        *reinterpret_cast<u32x4_t*>(f.gate_out + hd * D + 8 * (ch % (D / 8))) = gate_ch[c];
       }
     }
     // the owner: new key `wave` normalised and rotated (the prologue's own
