@@ -103,6 +103,17 @@ def test_batch_grids_with_four_waves_per_workgroup(seed, S, T, H, dk, dv):
     _run_and_check(seed, S, T, H, dk, dv, n_slots, in_idx, out_idx)
 
 
+def test_batch_grid_in_place_and_zero_states():
+    # a grouped grid (16 x 8 x 32 waves) where every sequence writes the
+    # slot it reads, two of them from the zero state (-1) into fresh slots
+    S, H, dk, dv, n_slots = 16, 8, 128, 128, 20
+    in_idx = list(range(S))
+    out_idx = [[s] for s in range(S)]
+    in_idx[3], out_idx[3] = -1, [17]
+    in_idx[9], out_idx[9] = -1, [18]
+    _run_and_check(15, S, 1, H, dk, dv, n_slots, in_idx, out_idx)
+
+
 def test_in_place_single_token():
     _run_and_check(5, 1, 1, 2, 64, 128, 3, [1], [[1]])
 
